@@ -1,0 +1,168 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts MLP block with
+ * MXFP4 expert weights.
+ *
+ * The layer, as the pages state it (Perplexity, "GPT-OSS el dia 0", section
+ * "MLP: barreja d'experts dispersos (MoE)" and section "Nuclis per a GPT-OSS /
+ * MoE"): a router scores every expert for every token, the top-k experts are
+ * kept and their weights are a softmax over the selected logits only; dispatch
+ * groups each expert's tokens; each expert is a SwiGLU MLP whose projections
+ * carry biases; the combine is the routing-weighted sum of the expert outputs.
+ * gpt-oss-20b keeps 4 of 32 experts, gpt-oss-120b 4 of 128 (Unsloth tutorial
+ * mirror, "第39章 使用 Unsloth 微调 gpt-oss", paragraph "解释"), and the expert
+ * weights are MXFP4 (same paragraph; "GPT-OSS el dia 0", section "GPT-OSS a Hopper").
+ *
+ * Calling convention, common to every entry point:
+ *   - Pointers marked [device] are HIP device pointers; the caller allocates and
+ *     owns every buffer, including the workspace. The library allocates nothing,
+ *     frees nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *     call only enqueues kernels on it and returns; no call synchronises the
+ *     host, and no call reads device data on the host (expert counts stay on
+ *     the device). Order between calls comes from the stream.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call returns an error and enqueues nothing. Device-side data are
+ *     trusted: an expert index >= E in topk_idx, or a scale byte of 255 (NaN),
+ *     is undefined behaviour.
+ *   - A launch failure returns MOE_ERR_HIP; moe_last_error() then holds the
+ *     runtime's message (thread-local, valid until the next call on the thread).
+ *   - Outputs are bitwise reproducible run to run: no floating-point atomics.
+ *   - Calls are thread-safe; concurrent calls need distinct workspaces.
+ *
+ * Data formats:
+ *   bf16    raw bfloat16 bit patterns in uint16_t.
+ *   MXFP4   (OCP Microscaling Formats v1.0) a matrix W[N][K] is stored as
+ *           codes[N][K/2]: element k in byte k>>1, low nibble when k is even,
+ *           high nibble when odd, each a 4-bit E2M1 code (sign, 2 exponent bits
+ *           with bias 1, 1 mantissa bit: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6);
+ *           scales[N][K/32]: one E8M0 byte s per 32 consecutive K elements,
+ *           value 2^(s-127). Element (n,k) = E2M1(code) * 2^(scales[n][k/32]-127).
+ *           For all E experts the arrays are [E][N][K/2] and [E][N][K/32].
+ *   pair    q = t*k + j names slot j of token t; P = T*k pairs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer        */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement      */
+  MOE_ERR_WORKSPACE = -3,   /* ws_bytes smaller than moe_workspace_bytes(dims)   */
+  MOE_ERR_HIP = -4          /* the HIP runtime reported an error on launch       */
+} moe_status;
+
+/* Layer dimensions: T tokens, model width d, expert FFN width F, E experts,
+ * k experts per token. Supported: T >= 1, d and F multiples of 64 (MX blocks of
+ * 32 and the kernels' K step), d <= 16384, F <= 16384, 1 <= k <= 8, k <= E <= 256. */
+typedef struct {
+  int32_t T, d, F, E, k;
+} moe_dims;
+
+/* One MXFP4 weight tensor for all experts, [device] pointers (layout above). */
+typedef struct {
+  const uint8_t* codes;  /* [E][N][K/2]  */
+  const uint8_t* scales; /* [E][N][K/32] */
+} moe_mxfp4;
+
+typedef uint16_t moe_bf16;
+
+/* Bytes of workspace that moe_route, moe_permute and moe_expert_ffn_mxfp4 need
+ * for `dims` (one buffer serves all three; it may be reused across calls on
+ * one stream). Pure host function; returns 0 for invalid dims. */
+size_t moe_workspace_bytes(moe_dims dims);
+
+/* Router GEMM, top-k, softmax over the selected logits.
+ * ("GPT-OSS el dia 0", section "MLP": softmax after top-k; section "Nuclis per a
+ * GPT-OSS / MoE": the softmax runs over the top-k selected experts only. The
+ * router is not quantised: CSDN "GPT-OSS-120B 4-bit 量化技术深度解析", section
+ * "Unsloth 4-bit量化技术解析".)
+ *   x         [device] bf16  [T][d]   token activations
+ *   w_router  [device] fp32  [d][E]   router weight (row k holds all experts)
+ *   b_router  [device] fp32  [E]      router bias, or NULL for none
+ *   topk_idx  [device] int32 [T][k]   out: selected experts, ordered by logit
+ *                                     descending; exact ties -> lower index first
+ *   topk_w    [device] fp32  [T][k]   out: softmax of the selected logits
+ * Logits are computed in float64 on the device, so the selection is the exact
+ * top-k of the real-valued logits except where two logits differ by less than
+ * ~1e-12 (relative to their magnitude). */
+moe_status moe_route(moe_dims dims, const moe_bf16* x, const float* w_router,
+                     const float* b_router, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: token-to-expert histogram, exclusive scan and a stable permutation.
+ * ("GPT-OSS el dia 0", section "Nuclis per a GPT-OSS / MoE": dispatch selects
+ * each expert's tokens.)
+ *   topk_idx    [device] int32 [T][k]  routing from moe_route (values in [0,E))
+ *   counts      [device] int32 [E]     out: pairs routed to each expert
+ *   offsets     [device] int32 [E+1]   out: exclusive prefix sum, offsets[E] = P
+ *   sorted_pair [device] int32 [P]     out: pairs grouped by expert, ascending
+ *                                      token order inside an expert (value q)
+ *   pair_row    [device] int32 [P]     out: inverse, pair_row[sorted_pair[p]] = p
+ * Each token must name distinct experts (as moe_route guarantees). */
+moe_status moe_permute(moe_dims dims, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped expert FFN in dispatch order, MXFP4 weights.
+ * For every expert e and row p in [offsets[e], offsets[e+1]), with
+ * t = sorted_pair[p] / k:
+ *   g = x[t] Wg[e]^T + b_gate[e],  u = x[t] Wu[e]^T + b_up[e],
+ *   h = silu(g) * u,               y_sorted[p] = h Wd[e]^T + b_down[e].
+ * ("GPT-OSS el dia 0", section "MLP": SwiGLU, experts with biases; section
+ * "Nuclis per a GPT-OSS / MoE": biases loaded into the GEMM accumulators.)
+ *   x         [device] bf16 [T][d]
+ *   sorted_pair, offsets  [device] from moe_permute
+ *   w_gate, w_up          MXFP4 [E][F][d] (N = F, K = d)
+ *   w_down                MXFP4 [E][d][F] (N = d, K = F)
+ *   b_gate, b_up [device] bf16 [E][F];  b_down [device] bf16 [E][d]
+ *   y_sorted  [device] fp32 [P][d]  out: per-pair expert output, bias included
+ * The activations are re-encoded on the device for the matrix cores (two-term
+ * MXFP6 per 32-element block); accumulation is fp32. Code and scale pointers
+ * must be 16-byte aligned. */
+moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x,
+                                const int32_t* sorted_pair, const int32_t* offsets,
+                                moe_mxfp4 w_gate, moe_mxfp4 w_up, moe_mxfp4 w_down,
+                                const moe_bf16* b_gate, const moe_bf16* b_up,
+                                const moe_bf16* b_down, float* y_sorted,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Atomic-free weighted combine back to token order:
+ *   out[t] = bf16( sum_{j=0..k-1} topk_w[t][j] * y_sorted[pair_row[t*k+j]] ),
+ * summed in fp32 in fixed j order, rounded once to nearest even.
+ * ("GPT-OSS el dia 0", section "Nuclis per a GPT-OSS / MoE": combine is the
+ * weighted accumulation of the expert outputs.)
+ *   y_sorted [device] fp32 [P][d]; pair_row [device] int32 [P];
+ *   topk_w   [device] fp32 [T][k]; out [device] bf16 [T][d]. */
+moe_status moe_combine(moe_dims dims, const float* y_sorted, const int32_t* pair_row,
+                       const float* topk_w, moe_bf16* out, void* stream);
+
+/* RMSNorm of each row (the pre-norm of a transformer block; rms_norm_eps = 1e-5
+ * per CSDN "GPT-OSS-120B 4-bit 量化技术深度解析", section "推理优化"):
+ *   out[t] = bf16( x[t] / sqrt(mean_i x[t][i]^2 + eps) * gain ), fp32 arithmetic.
+ *   x, out [device] bf16 [T][d]; gain [device] bf16 [d]. d a multiple of 8. */
+moe_status moe_rmsnorm(int32_t T, int32_t d, const moe_bf16* x, const moe_bf16* gain,
+                       float eps, moe_bf16* out, void* stream);
+
+/* Residual add: out = bf16(x + m), fp32 add, round to nearest even. out may
+ * alias x. x, m, out [device] bf16 [T][d]; d a multiple of 8. */
+moe_status moe_residual_add(int32_t T, int32_t d, const moe_bf16* x, const moe_bf16* m,
+                            moe_bf16* out, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Detail of the last error on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

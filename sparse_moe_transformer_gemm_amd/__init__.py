@@ -1,0 +1,250 @@
+"""Python binding of the MI355X MXFP4 sparse-MoE library (libmoe_mi355x.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind
+the C ABI declared in include/moe.h. torch provides device memory and the
+current stream; no torch operator computes any part of the layer here, and there
+is no fallback: if the library is missing or a call fails, an exception says so.
+
+The names follow the C ABI: route, permute, expert_ffn_mxfp4, combine (plus
+rmsnorm and residual_add for a pre-norm stack, and workspace_bytes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch  # imported before the library so that it binds to torch's HIP runtime
+
+__all__ = [
+    "MoeError", "Dims", "MXFP4", "library_path", "lib", "workspace_bytes", "route",
+    "permute", "expert_ffn_mxfp4", "combine", "rmsnorm", "residual_add", "forward",
+    "ExpertWeights", "EXPORTED",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmoe_mi355x.so"
+EXPORTED = (
+    "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine",
+    "moe_rmsnorm", "moe_residual_add", "moe_status_string", "moe_last_error",
+)
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("F", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32)]
+
+
+class MXFP4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return os.environ.get("MOE_MI355X_LIB", os.path.join(_HERE, _LIB_NAME))
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise MoeError(f"{path} not found: build it with "
+                       f"`python -m sparse_moe_transformer_gemm_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    L.moe_workspace_bytes.argtypes = [Dims]
+    L.moe_workspace_bytes.restype = sz
+    L.moe_route.argtypes = [Dims, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_permute.argtypes = [Dims, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_ffn_mxfp4.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp,
+                                       vp, sz, vp]
+    L.moe_combine.argtypes = [Dims, vp, vp, vp, vp, vp]
+    L.moe_rmsnorm.argtypes = [i32, i32, vp, vp, ctypes.c_float, vp, vp]
+    L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp]
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine", "moe_rmsnorm",
+              "moe_residual_add"):
+        getattr(L, f).restype = ctypes.c_int
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        L = lib()
+        raise MoeError(f"{what}: {L.moe_status_string(status).decode()} "
+                       f"({status}): {L.moe_last_error().decode()}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, shape, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr()
+
+
+@dataclass
+class ExpertWeights:
+    """Device tensors of one MoE layer (the layout of include/moe.h)."""
+    w_router: torch.Tensor            # fp32 [d][E]
+    b_router: Optional[torch.Tensor]  # fp32 [E] or None
+    gate_codes: torch.Tensor          # u8 [E][F][d/2]
+    gate_scales: torch.Tensor         # u8 [E][F][d/32]
+    up_codes: torch.Tensor
+    up_scales: torch.Tensor
+    down_codes: torch.Tensor          # u8 [E][d][F/2]
+    down_scales: torch.Tensor         # u8 [E][d][F/32]
+    b_gate: torch.Tensor              # bf16 [E][F]
+    b_up: torch.Tensor                # bf16 [E][F]
+    b_down: torch.Tensor              # bf16 [E][d]
+
+    @property
+    def dims(self):
+        d, E = self.w_router.shape
+        F = self.gate_codes.shape[1]
+        return d, F, E
+
+
+def _dims(T, d, F, E, k) -> Dims:
+    return Dims(int(T), int(d), int(F), int(E), int(k))
+
+
+def workspace_bytes(T: int, d: int, F: int, E: int, k: int) -> int:
+    n = lib().moe_workspace_bytes(_dims(T, d, F, E, k))
+    if n == 0:
+        raise MoeError(f"unsupported dims T={T} d={d} F={F} E={E} k={k}")
+    return n
+
+
+def route(x, w_router, b_router, k: int, ws, topk_idx=None, topk_w=None):
+    T, d = x.shape
+    E = w_router.shape[1]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    dims = _dims(T, d, 64, E, k)
+    b = None if b_router is None else _dev(b_router, torch.float32, (E,), "b_router")
+    _check(lib().moe_route(dims, _dev(x, torch.bfloat16, (T, d), "x"),
+                           _dev(w_router, torch.float32, (d, E), "w_router"), b,
+                           _dev(topk_idx, torch.int32, (T, k), "topk_idx"),
+                           _dev(topk_w, torch.float32, (T, k), "topk_w"),
+                           ws.data_ptr(), ws.numel() * ws.element_size(), _stream()), "moe_route")
+    return topk_idx, topk_w
+
+
+def permute(topk_idx, E: int, ws, out=None):
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        out = (torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev))
+    counts, offsets, sorted_pair, pair_row = out
+    _check(lib().moe_permute(_dims(T, 64, 64, E, k), _dev(topk_idx, torch.int32, (T, k), "topk_idx"),
+                             _dev(counts, torch.int32, (E,), "counts"),
+                             _dev(offsets, torch.int32, (E + 1,), "offsets"),
+                             _dev(sorted_pair, torch.int32, (T * k,), "sorted_pair"),
+                             _dev(pair_row, torch.int32, (T * k,), "pair_row"),
+                             ws.data_ptr(), ws.numel() * ws.element_size(), _stream()),
+           "moe_permute")
+    return counts, offsets, sorted_pair, pair_row
+
+
+def expert_ffn_mxfp4(x, sorted_pair, offsets, w: ExpertWeights, k: int, ws, y_sorted=None):
+    T, d = x.shape
+    dw, F, E = w.dims
+    if dw != d:
+        raise ValueError("x width does not match the router weight")
+    P = T * k
+    if y_sorted is None:
+        y_sorted = torch.empty((P, d), dtype=torch.float32, device=x.device)
+    u8 = torch.uint8
+    mg = MXFP4(_dev(w.gate_codes, u8, (E, F, d // 2), "gate_codes"),
+               _dev(w.gate_scales, u8, (E, F, d // 32), "gate_scales"))
+    mu = MXFP4(_dev(w.up_codes, u8, (E, F, d // 2), "up_codes"),
+               _dev(w.up_scales, u8, (E, F, d // 32), "up_scales"))
+    md = MXFP4(_dev(w.down_codes, u8, (E, d, F // 2), "down_codes"),
+               _dev(w.down_scales, u8, (E, d, F // 32), "down_scales"))
+    _check(lib().moe_expert_ffn_mxfp4(
+        _dims(T, d, F, E, k), _dev(x, torch.bfloat16, (T, d), "x"),
+        _dev(sorted_pair, torch.int32, (P,), "sorted_pair"),
+        _dev(offsets, torch.int32, (E + 1,), "offsets"), mg, mu, md,
+        _dev(w.b_gate, torch.bfloat16, (E, F), "b_gate"),
+        _dev(w.b_up, torch.bfloat16, (E, F), "b_up"),
+        _dev(w.b_down, torch.bfloat16, (E, d), "b_down"),
+        _dev(y_sorted, torch.float32, (P, d), "y_sorted"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream()), "moe_expert_ffn_mxfp4")
+    return y_sorted
+
+
+def combine(y_sorted, pair_row, topk_w, out=None):
+    T, k = topk_w.shape
+    P, d = y_sorted.shape
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=y_sorted.device)
+    _check(lib().moe_combine(_dims(T, d, 64, max(k, 1), k),
+                             _dev(y_sorted, torch.float32, (T * k, d), "y_sorted"),
+                             _dev(pair_row, torch.int32, (T * k,), "pair_row"),
+                             _dev(topk_w, torch.float32, (T, k), "topk_w"),
+                             _dev(out, torch.bfloat16, (T, d), "out"), _stream()), "moe_combine")
+    return out
+
+
+def rmsnorm(x, gain, eps: float = 1e-5, out=None):
+    T, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().moe_rmsnorm(T, d, _dev(x, torch.bfloat16, (T, d), "x"),
+                             _dev(gain, torch.bfloat16, (d,), "gain"), float(eps),
+                             _dev(out, torch.bfloat16, (T, d), "out"), _stream()), "moe_rmsnorm")
+    return out
+
+
+def residual_add(x, m, out=None):
+    T, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().moe_residual_add(T, d, _dev(x, torch.bfloat16, (T, d), "x"),
+                                  _dev(m, torch.bfloat16, (T, d), "m"),
+                                  _dev(out, torch.bfloat16, (T, d), "out"), _stream()),
+           "moe_residual_add")
+    return out
+
+
+def forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict] = None) -> dict:
+    """The whole block: the four calls in order on the current stream. `bufs`, if
+    given, supplies preallocated outputs (keys as in the returned dict)."""
+    T, d = x.shape
+    _, F, E = w.dims
+    b = bufs or {}
+    idx, tw = route(x, w.w_router, w.b_router, k, ws, b.get("topk_idx"), b.get("topk_w"))
+    perm = permute(idx, E, ws, b.get("perm"))
+    y = expert_ffn_mxfp4(x, perm[2], perm[1], w, k, ws, b.get("y_sorted"))
+    out = combine(y, perm[3], tw, b.get("out"))
+    return dict(topk_idx=idx, topk_w=tw, perm=perm, y_sorted=y, out=out)

@@ -1,0 +1,67 @@
+// Shared device helpers and kernel launcher declarations (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Expert owning dispatch row p: the e with offsets[e] <= p < offsets[e+1].
+__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int p) {
+  int lo = 0, hi = E;  // invariant: offsets[lo] <= p < offsets[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; arguments are validated by the caller.
+
+size_t route_workspace_bytes(int T, int d, int E);
+hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b_router,
+                        int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
+                        void* ws, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
+                          hipStream_t stream);
+
+struct FfnArgs {
+  int T, d, F, E, k;
+  const uint16_t* x;
+  const int32_t* sorted_pair;
+  const int32_t* offsets;
+  const uint8_t *wg_codes, *wg_scales, *wu_codes, *wu_scales, *wd_codes, *wd_scales;
+  const uint16_t *b_gate, *b_up, *b_down;
+  float* y_sorted;
+  void* ws;
+};
+size_t ffn_workspace_bytes(int T, int d, int F, int E, int k);
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream);
+
+hipError_t launch_combine(const float* y_sorted, const int32_t* pair_row, const float* topk_w,
+                          int T, int d, int k, uint16_t* out, hipStream_t stream);
+
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gain, int T, int d, float eps,
+                          uint16_t* out, hipStream_t stream);
+hipError_t launch_residual_add(const uint16_t* x, const uint16_t* m, int T, int d,
+                               uint16_t* out, hipStream_t stream);
+
+}  // namespace moe

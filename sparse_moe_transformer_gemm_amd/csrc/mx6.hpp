@@ -1,0 +1,123 @@
+// MX helpers for gfx950's scaled matrix cores.
+//
+// The expert weights are MXFP4 (E2M1 codes, one E8M0 scale per 32 K-elements) and
+// feed V_MFMA_SCALE_F32_32X32X64_F8F6F4 directly as the B operand. The A operand
+// (activations) must be FP8/FP6/FP4 too; a single 6-bit term loses too much, so
+// each 32-element block is stored as two MXFP6-E2M3 terms, hi + lo, each with its
+// own E8M0 scale, and both terms go through the same MFMA accumulator:
+//   hi = RNE_E2M3(v / 2^s1) with s1 = floor(log2 max|v|) - 2   (|hi| <= 7.5, saturated)
+//   r  = v - hi * 2^s1          (exact in fp32)
+//   lo = RNE_E2M3(r / 2^s2) with s2 = floor(log2 max|r|) - 2
+// The pair carries about 8 significant bits relative to the block's largest
+// element, like bf16 does per element.
+//
+// Register layout of the 32x32x64 scaled MFMA (checked on gfx950 with random
+// operands): lane l supplies row (A) / column (B) l%32 and K elements
+// 32*(l/32) .. 32*(l/32)+31; element j sits at bits [w*j, w*j+w) of the
+// little-endian concatenation of the operand VGPRs (w = 6 for FP6 in 6 VGPRs,
+// w = 4 for FP4 in 4 VGPRs); the lane's scale VGPR supplies the E8M0 byte picked
+// by op_sel (value 2^(s-127)) for its 32 elements. The 16 fp32 results of lane l
+// are column l%32, rows 8*(i/4) + 4*(l/32) + (i%4) for i = 0..15.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Encoded activation storage: per row, per 32-element block, 48 bytes of codes
+// (hi term 24 B then lo term 24 B, 6 bits per element, element j at bit 6j) and
+// one uint16 of scales (byte 0 = hi E8M0, byte 1 = lo E8M0).
+constexpr int kEncBytes = 48;
+
+// 2^n for n in [-127, 127] as an fp32 (2^-127 is subnormal).
+__device__ __forceinline__ float pow2i(int n) {
+  return n >= -126 ? __uint_as_float(static_cast<uint32_t>(n + 127) << 23)
+                   : __uint_as_float(0x00400000u);
+}
+
+// floor(log2 a) for a normal positive float; -127 for zero/subnormal input.
+__device__ __forceinline__ int ilog2f(float a) {
+  return static_cast<int>((__float_as_uint(a) >> 23) & 255u) - 127;
+}
+
+// E2M3 magnitude code of |q| (already divided by the block scale), round to
+// nearest even, saturating at 7.5. Magnitudes: code/8 below 2, 2 + (code-16)/4
+// in [2, 4), 4 + (code-24)/2 in [4, 7.5]; all divisions here are exact.
+__device__ __forceinline__ uint32_t e2m3_code(float a) {
+  int c;
+  if (a < 2.0f) {
+    c = static_cast<int>(rintf(a * 8.0f));
+  } else if (a < 4.0f) {
+    c = 16 + static_cast<int>(rintf((a - 2.0f) * 4.0f));
+  } else {
+    c = 24 + static_cast<int>(rintf((a - 4.0f) * 2.0f));
+    c = c > 31 ? 31 : c;
+  }
+  return static_cast<uint32_t>(c);
+}
+
+__device__ __forceinline__ float e2m3_value(uint32_t c) {
+  const float f = static_cast<float>(c);
+  return c < 16u ? f * 0.125f : (c < 24u ? 2.0f + (f - 16.0f) * 0.25f : 4.0f + (f - 24.0f) * 0.5f);
+}
+
+__device__ __forceinline__ void pack6(const uint32_t (&c)[32], uint32_t (&w)[6]) {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) w[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int bit = 6 * j, word = bit >> 5, off = bit & 31;
+    w[word] |= c[j] << off;
+    if (off > 26) w[word + 1] |= c[j] >> (32 - off);
+  }
+}
+
+// Encode one block of 32 floats into two E2M3 terms (codes) and their scales.
+__device__ __forceinline__ void encode_block(const float (&v)[32], uint32_t (&hi)[6],
+                                             uint32_t (&lo)[6], uint32_t& scales) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  int s1 = amax > 0.f ? ilog2f(amax) - 2 : -127;
+  s1 = s1 < -127 ? -127 : s1;
+  const float inv1 = pow2i(-s1 > 127 ? 127 : -s1), sc1 = pow2i(s1);
+  uint32_t c[32];
+  float r[32];
+  float ramax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t m = e2m3_code(fabsf(v[j]) * inv1);
+    const uint32_t sign = __float_as_uint(v[j]) >> 31;
+    c[j] = (sign << 5) | m;
+    const float back = e2m3_value(m) * sc1;
+    r[j] = v[j] - (sign ? -back : back);
+    ramax = fmaxf(ramax, fabsf(r[j]));
+  }
+  pack6(c, hi);
+  int s2 = ramax > 0.f ? ilog2f(ramax) - 2 : -127;
+  s2 = s2 < -127 ? -127 : s2;
+  const float inv2 = pow2i(-s2 > 127 ? 127 : -s2);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t m = e2m3_code(fabsf(r[j]) * inv2);
+    c[j] = ((__float_as_uint(r[j]) >> 31) << 5) | m;
+  }
+  pack6(c, lo);
+  scales = static_cast<uint32_t>(s1 + 127) | (static_cast<uint32_t>(s2 + 127) << 8);
+}
+
+// D += A(FP6 E2M3, scale byte OPA of sa) x B(FP4 E2M1, scale byte 0 of sb).
+template <int OPA>
+__device__ __forceinline__ v16f mfma_f6f4(const v8i& a, const v8i& b, const v16f& c, int sa,
+                                          int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 4, OPA, sa, 0, sb);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+}  // namespace moe

@@ -1,0 +1,111 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the
+HIP path through the C ABI, and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_moe_transformer_gemm_amd as moe
+import synth
+
+DEV = "cuda:0"
+TIE = 1e-6  # routing margin below which either order/choice is accepted
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def bits_host(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def weights_dev(L: synth.LayerParams) -> moe.ExpertWeights:
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return moe.ExpertWeights(
+        w_router=torch.from_numpy(L.w_router).to(DEV),
+        b_router=None if L.b_router is None else torch.from_numpy(L.b_router).to(DEV),
+        gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales),
+        up_codes=u8(L.up.codes), up_scales=u8(L.up.scales),
+        down_codes=u8(L.down.codes), down_scales=u8(L.down.scales),
+        b_gate=bf16_dev(L.b_gate), b_up=bf16_dev(L.b_up), b_down=bf16_dev(L.b_down))
+
+
+def workspace(T, d, F, E, k) -> torch.Tensor:
+    return torch.empty(moe.workspace_bytes(T, d, F, E, k), dtype=torch.uint8, device=DEV)
+
+
+def run_layer(x_bits: np.ndarray, L: synth.LayerParams, k: int, keep_y: bool = True) -> dict:
+    """One forward pass of the block on the GPU; every stage's output on the host."""
+    T, d = x_bits.shape
+    E = L.w_router.shape[1]
+    F = L.gate.codes.shape[1]
+    w = weights_dev(L)
+    ws = workspace(T, d, F, E, k)
+    x = bf16_dev(x_bits)
+    r = moe.forward(x, w, k, ws)
+    torch.cuda.synchronize()
+    out = dict(idx=r["topk_idx"].cpu().numpy(), w=r["topk_w"].cpu().numpy(),
+               counts=r["perm"][0].cpu().numpy(), offsets=r["perm"][1].cpu().numpy(),
+               sorted_pair=r["perm"][2].cpu().numpy(), pair_row=r["perm"][3].cpu().numpy(),
+               out=bits_host(r["out"]))
+    if keep_y:
+        out["y_sorted"] = r["y_sorted"].cpu().numpy()
+    return out
+
+
+def check_routing(idx_gpu: np.ndarray, w_gpu: np.ndarray, logits: np.ndarray, k: int) -> dict:
+    """Routing parity. Exact ordered match is required for every token whose
+    oracle top-(k+1) logits are separated by at least TIE; for a token with a
+    near-tie inside the top k the sets must match (weights compared per expert);
+    for a near-tie at the k/k+1 boundary the GPU's set must be a valid top-k.
+    Weights: |w - softmax(oracle logits of the GPU's set)| <= 1e-6."""
+    T, E = logits.shape
+    order = np.argsort(-logits, axis=1, kind="stable")
+    srt = np.take_along_axis(logits, order, axis=1)
+    m = min(k + 1, E)
+    gaps = -np.diff(srt[:, :m], axis=1) if m > 1 else np.full((T, 0), np.inf)
+    inner = (gaps[:, :k - 1] < TIE).any(axis=1) if k > 1 else np.zeros(T, bool)
+    boundary = (gaps[:, k - 1] < TIE) if E > k else np.zeros(T, bool)
+    n_exact = 0
+    for t in range(T):
+        ref = order[t, :k]
+        if not inner[t] and not boundary[t]:
+            assert np.array_equal(idx_gpu[t], ref), (t, idx_gpu[t], ref, srt[t, :m])
+            n_exact += 1
+        elif not boundary[t]:
+            assert set(idx_gpu[t]) == set(ref), (t, idx_gpu[t], ref)
+        else:
+            kth = srt[t, k - 1]
+            assert len(set(idx_gpu[t])) == k
+            assert all(logits[t, e] >= kth - TIE for e in idx_gpu[t]), t
+        sel = logits[t, idx_gpu[t]]
+        ex = np.exp(sel - sel.max())
+        wref = ex / ex.sum()
+        assert np.max(np.abs(w_gpu[t] - wref)) <= 1e-6, (t, w_gpu[t], wref)
+    return dict(exact=n_exact, inner_ties=int(inner.sum()), boundary_ties=int(boundary.sum()))
+
+
+def check_permute(g: dict, E: int) -> None:
+    c, o, s, r = oracle.permute(g["idx"], E)
+    assert np.array_equal(g["counts"], c)
+    assert np.array_equal(g["offsets"], o)
+    assert np.array_equal(g["sorted_pair"], s)
+    assert np.array_equal(g["pair_row"], r)
+
+
+def oracle_tokens(x_bits: np.ndarray, L: synth.LayerParams, k: int, tokens: np.ndarray,
+                  idx_gpu: np.ndarray) -> np.ndarray:
+    """Oracle output for selected tokens, routed with the GPU's expert choice (the
+    routing itself is checked separately); float64, unrounded."""
+    x = oracle.bf16_to_f64(x_bits[tokens])
+    logits = oracle.router_logits(x, L.w_router, L.b_router)
+    idx = idx_gpu[tokens]
+    w = oracle.softmax_selected(logits, idx)
+    out = np.zeros((tokens.size, L.down.codes.shape[1]))
+    for e in np.unique(idx):
+        rows, slots = np.nonzero(idx == e)
+        y = oracle.expert_ffn(x[rows], *oracle.moe._expert_weights(L, int(e)))
+        out[rows] += w[rows, slots][:, None] * y
+    return out

@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/moe.h declares, and rejects bad arguments before launching
+anything. Every call here fails validation, so no HIP API is reached."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _ensure_built():
+    import sparse_moe_transformer_gemm_amd as m
+    if not os.path.exists(m.library_path()):
+        from sparse_moe_transformer_gemm_amd import build
+        build.build()
+    return m
+
+
+@pytest.fixture(scope="module")
+def moe():
+    return _ensure_built()
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine",
+              "moe_workspace_bytes"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(moe):
+    L = moe.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert set(_declared_functions()) == set(moe.EXPORTED)
+
+
+def test_library_is_gfx950_and_dynamic(moe):
+    out = os.popen(f"readelf -d {moe.library_path()}").read()
+    assert "libamdhip64.so" in out
+
+
+def test_workspace_bytes(moe):
+    L = moe.lib()
+    D = moe.Dims
+    assert L.moe_workspace_bytes(D(16, 2880, 2880, 32, 4)) > 0
+    assert L.moe_workspace_bytes(D(8192, 2880, 2880, 32, 4)) >= 8192 * 4 * 2880
+    assert L.moe_workspace_bytes(D(0, 2880, 2880, 32, 4)) == 0       # T < 1
+    assert L.moe_workspace_bytes(D(16, 2880 + 32, 2880, 32, 4)) == 0  # d % 64
+    assert L.moe_workspace_bytes(D(16, 2880, 2880, 3, 4)) == 0       # k > E
+    assert L.moe_workspace_bytes(D(16, 2880, 2880, 512, 4)) == 0     # E > 256
+    assert L.moe_workspace_bytes(D(16, 2880, 2880, 32, 9)) == 0      # k > 8
+
+
+FAKE = 0x10000  # an aligned, non-null address that is never dereferenced
+
+
+def test_route_validation(moe):
+    L = moe.lib()
+    D = moe.Dims
+    ok = D(16, 512, 512, 32, 4)
+    ws = L.moe_workspace_bytes(ok)
+    assert L.moe_route(ok, None, FAKE, None, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.moe_route(ok, FAKE + 2, FAKE, None, FAKE, FAKE, FAKE, ws, None) == -1  # misaligned
+    assert b"aligned" in L.moe_last_error()
+    assert L.moe_route(ok, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws - 256, None) == -3
+    assert L.moe_route(D(16, 512, 512, 300, 4), FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == -2
+    assert L.moe_route(D(16, 500, 512, 32, 4), FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.moe_route(ok, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, ws, None) == -1
+
+
+def test_permute_validation(moe):
+    L = moe.lib()
+    D = moe.Dims
+    ok = D(16, 512, 512, 32, 4)
+    ws = L.moe_workspace_bytes(ok)
+    assert L.moe_permute(ok, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.moe_permute(D(16, 512, 512, 32, 0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.moe_permute(ok, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, None) == -1
+
+
+def test_ffn_validation(moe):
+    L = moe.lib()
+    D = moe.Dims
+    ok = D(16, 512, 512, 32, 4)
+    ws = L.moe_workspace_bytes(ok)
+    m = moe.MXFP4(FAKE, FAKE)
+    bad = moe.MXFP4(FAKE, None)
+    args = [FAKE, FAKE, FAKE, m, m, m, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+    a = list(args); a[3] = bad
+    assert L.moe_expert_ffn_mxfp4(ok, *a) == -1
+    a = list(args); a[11] = 16
+    assert L.moe_expert_ffn_mxfp4(ok, *a) == -3
+    assert L.moe_expert_ffn_mxfp4(D(16, 512, 544, 32, 4), *args) == -1  # F % 64
+    assert L.moe_expert_ffn_mxfp4(D(70000, 512, 512, 32, 4), *args) == -2  # T too big
+
+
+def test_combine_norm_validation(moe):
+    L = moe.lib()
+    D = moe.Dims
+    assert L.moe_combine(D(16, 512, 512, 32, 4), FAKE, FAKE, None, FAKE, None) == -1
+    assert L.moe_rmsnorm(16, 12, FAKE, FAKE, 1e-5, FAKE, None) == -1
+    assert L.moe_rmsnorm(16, 512, FAKE, FAKE, -1.0, FAKE, None) == -1
+    assert L.moe_residual_add(0, 512, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_status_strings(moe):
+    L = moe.lib()
+    for s, txt in ((0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small"),
+                   (-4, b"HIP runtime error")):
+        assert L.moe_status_string(s) == txt
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    import sparse_moe_transformer_gemm_amd as m
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setenv("MOE_MI355X_LIB", str(tmp_path / "missing.so"))
+    with pytest.raises(m.MoeError):
+        m.lib()
