@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Throughput of the MXFP4 sparse-MoE block on one MI355X.
+
+One step = one pass of the whole block (moe_route -> moe_permute ->
+moe_expert_ffn_mxfp4 -> moe_combine) over one batch of T tokens whose inputs are
+already resident in HBM. The headline workload is the decode-shaped gpt-oss-20b
+layer (T=16, d=F=2880, E=32, top-4), which is bound by streaming the MXFP4
+weights from HBM; the prefill-shaped layer (T=8192) is reported beside it
+against the MXFP4 matrix-core peak.
+
+Timing: W untimed warmup steps, then K timed steps bracketed by
+torch.cuda.synchronize(); the weights rotate over R identical copies (R * layer
+bytes >= 1.5 GB) so the 256 MB last-level cache cannot hold them. HIP events on
+the launch stream bracket the expert-FFN call inside every timed step; its
+average duration gives the roofline figure. The timed output is checked against
+the CPU oracle in the same run, and the oracle is timed on the host cores as
+the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
+                       [--no-cpu-baseline] [--workload 1]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4/MXFP6 matrix throughput, published
+METRIC = "MoE layer tokens/s; % HBM peak (T=16) and % MXFP4 MFMA peak (T=8192)"
+
+
+def expert_bytes(d: int, F: int) -> int:
+    """Algorithmic bytes of one expert: 3 MXFP4 matrices (0.5 B/elt + 1 B per 32)
+    and its bf16 biases (2F + d)."""
+    return 3 * (d * F // 2 + d * F // 32) + 2 * (2 * F + d)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--secondary", type=int, default=2, help="second workload (-1: none)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def run_gpu(cfg: int, steps: int, warmup: int, log) -> dict:
+    import torch
+
+    import sparse_moe_transformer_gemm_amd as moe
+
+    dev = "cuda:0"
+    w = synth.workload(cfg)
+    L = w.layers[0]
+    T, d, F, E, k = w.T, w.d, w.F, w.E, w.k
+    layer_bytes = E * expert_bytes(d, F) + 4 * d * E
+    R = max(1, int(np.ceil(1.5e9 / layer_bytes)))
+    log(f"[bench] workload {w.name}: T={T} d={d} F={F} E={E} k={k}; {R} weight copies")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    copies = []
+    for _ in range(R):
+        copies.append(moe.ExpertWeights(
+            w_router=torch.from_numpy(L.w_router).to(dev),
+            b_router=None if L.b_router is None else torch.from_numpy(L.b_router).to(dev),
+            gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales),
+            up_codes=u8(L.up.codes), up_scales=u8(L.up.scales),
+            down_codes=u8(L.down.codes), down_scales=u8(L.down.scales),
+            b_gate=bf16(L.b_gate), b_up=bf16(L.b_up), b_down=bf16(L.b_down)))
+    x = bf16(w.x)
+    ws = torch.empty(moe.workspace_bytes(T, d, F, E, k), dtype=torch.uint8, device=dev)
+    P = T * k
+    bufs = dict(
+        topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+        topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+        perm=(torch.empty(E, dtype=torch.int32, device=dev),
+              torch.empty(E + 1, dtype=torch.int32, device=dev),
+              torch.empty(P, dtype=torch.int32, device=dev),
+              torch.empty(P, dtype=torch.int32, device=dev)),
+        y_sorted=torch.empty((P, d), dtype=torch.float32, device=dev),
+        out=torch.empty((T, d), dtype=torch.bfloat16, device=dev))
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+
+    def step(i, timed):
+        wt = copies[i % R]
+        idx, tw = moe.route(x, wt.w_router, wt.b_router, k, ws, bufs["topk_idx"], bufs["topk_w"])
+        perm = moe.permute(idx, E, ws, bufs["perm"])
+        if timed:
+            ev[i][0].record()
+        y = moe.expert_ffn_mxfp4(x, perm[2], perm[1], wt, k, ws, bufs["y_sorted"])
+        if timed:
+            ev[i][1].record()
+        moe.combine(y, perm[3], tw, bufs["out"])
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    counts = bufs["perm"][0].cpu().numpy()
+    U = int((counts > 0).sum())
+    out_bits = bufs["out"].view(torch.int16).cpu().numpy().view(np.uint16)
+    idx_gpu = bufs["topk_idx"].cpu().numpy()
+
+    ffn_bytes = U * expert_bytes(d, F) + 2 * T * d
+    layer_alg_bytes = ffn_bytes + 4 * d * E + (4 * E if L.b_router is not None else 0) + 2 * T * d
+    flops = 2.0 * T * k * 3 * d * F
+    res = dict(
+        workload=w.name, T=T, d=d, F=F, E=E, k=k, seed=w.seed, weight_copies=R,
+        experts_touched=U, ms_per_step=ms_step, tokens_per_s=T / (ms_step / 1e3),
+        ffn_ms=ffn_ms, ffn_alg_bytes=ffn_bytes, layer_alg_bytes=layer_alg_bytes,
+        ffn_gbs=ffn_bytes / (ffn_ms / 1e3) / 1e9, ffn_tflops=flops / (ffn_ms / 1e3) / 1e12,
+        layer_gbs=layer_alg_bytes / (ms_step / 1e3) / 1e9,
+        layer_tflops=flops / (ms_step / 1e3) / 1e12, flops=flops,
+        _out_bits=out_bits, _idx=idx_gpu, _workload=w)
+    log(f"[bench] {w.name}: {ms_step * 1e3:.1f} us/step, ffn {ffn_ms * 1e3:.1f} us, "
+        f"{res['tokens_per_s']:.4g} tok/s, ffn {res['ffn_gbs']:.0f} GB/s / {res['ffn_tflops']:.0f} TFLOP/s")
+    del copies, ws, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
+def oracle_check(res: dict, log) -> dict:
+    """Compare the timed run's output with the CPU oracle (tolerance of the parity tests)."""
+    import oracle
+    w = res["_workload"]
+    L = w.layers[0]
+    t0 = time.perf_counter()
+    ref = oracle.moe_layer(w.x, L, w.k)
+    dt = time.perf_counter() - t0
+    out = oracle.bf16_to_f64(res["_out_bits"])
+    err = np.abs(out - ref["out"])
+    rms = float(np.sqrt(np.mean(ref["out"] ** 2)))
+    _, e2 = np.frexp(np.abs(ref["out"]))
+    excess = float(np.maximum(err - np.ldexp(1.0, e2 - 9), 0).max() / rms)
+    mean_rel = float(err.sum() / np.abs(ref["out"]).sum())
+    ok = bool(np.array_equal(res["_idx"], ref["idx"]) and excess <= 2e-2 and mean_rel <= 5e-3)
+    log(f"[bench] oracle check: routing equal {np.array_equal(res['_idx'], ref['idx'])}, "
+        f"excess {excess:.3g}, mean rel {mean_rel:.3g} -> {'ok' if ok else 'FAIL'}")
+    return dict(ok=ok, excess_over_rms=excess, mean_rel=mean_rel,
+                literal_over_rms=float(err.max() / rms), oracle_seconds=dt)
+
+
+def cpu_baseline(res: dict, seconds: float, log) -> dict:
+    """The oracle as it stands, on the host cores, on a bounded sample: whole
+    layer passes over the same workload's tokens until `seconds` have elapsed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the visible CPUs
+        threads = os.cpu_count() or 1
+    w = res["_workload"]
+    L = w.layers[0]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.moe_layer(w.x, L, w.k)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    v = n * w.T / dt
+    log(f"[bench] cpu oracle: {n} passes of {w.T} tokens in {dt:.1f} s -> {v:.3g} tok/s on {threads} threads")
+    return dict(value=v, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{n} full passes of the {w.name} workload ({w.T} tokens each), numpy float64")
+
+
+def main():
+    args = parse()
+    log = lambda s: print(s, file=sys.stderr, flush=True)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              f"(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    main_res = run_gpu(args.workload, args.steps, args.warmup, log)
+    check = oracle_check(main_res, log) if args.workload in (0, 1) else None
+    sec = None
+    if not args.no_secondary and args.secondary >= 0:
+        s = run_gpu(args.secondary, max(10, args.steps // 4), max(3, args.warmup // 4), log)
+        sec = {
+            "workload": s["workload"], "T": s["T"], "tokens_per_s": s["tokens_per_s"],
+            "ms_per_step": s["ms_per_step"], "experts_touched": s["experts_touched"],
+            "roofline": {"bound": "mfma", "kernel": "moe_expert_ffn_mxfp4",
+                         "achieved": s["ffn_tflops"], "peak": MXFP4_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": s["ffn_tflops"] / MXFP4_PEAK_TFLOPS,
+                         "traffic": None},
+            "layer_frac_mxfp4_peak": s["layer_tflops"] / MXFP4_PEAK_TFLOPS,
+            "ffn_ms": s["ffn_ms"],
+        }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(main_res, args.cpu_seconds, log)
+
+    r = main_res
+    line = {
+        "metric": METRIC,
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 weights x 2-term mxfp6 activations, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"{r['workload']}: T={r['T']} d={r['d']} F={r['F']} E={r['E']} "
+                               f"top-{r['k']}, seed {r['seed']}",
+                   "global_batch": r["T"], "weight_copies": r["weight_copies"],
+                   "experts_touched": r["experts_touched"]},
+        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_mxfp4",
+                     "achieved": r["ffn_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["ffn_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": r["ffn_alg_bytes"], "avg_launch_ms": r["ffn_ms"]},
+        "layer_frac_hbm_peak": r["layer_gbs"] / HBM_PEAK_GBS,
+        "cpu_baseline": cpu,
+        "parity": check,
+        "secondary": sec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,7 @@
 
 #include <initializer_list>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.hpp"
 
 namespace {

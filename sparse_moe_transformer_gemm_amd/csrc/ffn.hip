@@ -117,7 +117,8 @@ struct Prefill {
   static constexpr int NW = GATEUP ? NF / 2 : NF;      // output column frags per wave
   static constexpr int EP_PITCH = NW * 32 + 4;        // floats
   static constexpr int EPI = GATEUP ? 4 * 64 * EP_PITCH * 4 : 0;
-  static constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+  static constexpr int SINK = (2 * STAGE > EPI ? 2 * STAGE : EPI);  // 16-byte dump slot
+  static constexpr int SMEM = SINK + 16;
   static constexpr int A_CHUNKS = kBM * 6;             // 16-byte chunks per stage
   static constexpr int A_PER_T = (A_CHUNKS + 255) / 256;
   static constexpr int B_CHUNKS = BNB * 2;
@@ -158,67 +159,63 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const En
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, half = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // ---- per-thread global sources (fixed across K steps)
+  // ---- per-thread global sources (fixed across K steps). Every load is
+  // unconditional: rows past the expert's count read its last row (results
+  // discarded), chunk indices past the tile are clamped and their LDS stores go
+  // to a sink slot, so the compiler can keep the prefetch in flight.
+  const int rows_valid = min(kBM, cnt - m0);
   const uint8_t* a_src[C::A_PER_T];
   int a_lds[C::A_PER_T];
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
-    const int c = tid + 256 * i;
+    const int c = min(tid + 256 * i, C::A_CHUNKS - 1);
     const int row = c / 6, part = c - row * 6;
-    a_src[i] = nullptr;
-    a_lds[i] = row * kAPitch + part * 16;
-    if (c < C::A_CHUNKS && row < cnt - m0) {
-      const int p = off + m0 + row;
-      const int src = GATEUP ? a.sorted_pair[p] / a.k : p;
-      a_src[i] = ain.codes + (size_t)src * nblkK * kEncBytes + part * 16;
-    }
+    a_lds[i] = tid + 256 * i < C::A_CHUNKS ? row * kAPitch + part * 16 : C::SINK;
+    const int p = off + m0 + min(row, rows_valid - 1);
+    const int src = GATEUP ? a.sorted_pair[p] / a.k : p;
+    a_src[i] = ain.codes + (size_t)src * nblkK * kEncBytes + part * 16;
   }
-  const uint16_t* as_src = nullptr;
-  if (tid < kBM && tid < cnt - m0) {
-    const int p = off + m0 + tid;
+  const uint16_t* as_src;
+  {
+    const int p = off + m0 + min(tid & (kBM - 1), rows_valid - 1);
     const int src = GATEUP ? a.sorted_pair[p] / a.k : p;
     as_src = ain.scales + (size_t)src * nblkK;
   }
+  auto b_row = [&](int brow, const uint8_t*& codes, const uint8_t*& scales) {
+    int n;
+    if (GATEUP) {
+      const int w = brow / (NF * 32), f = (brow / 32) % NF, cc = brow & 31;
+      const bool up = f >= C::NW;
+      n = ncol0 + w * C::NW * 32 + (up ? f - C::NW : f) * 32 + cc;
+      codes = up ? a.wu_codes : a.wg_codes;
+      scales = up ? a.wu_scales : a.wg_scales;
+    } else {
+      n = ncol0 + brow;
+      codes = a.wd_codes;
+      scales = a.wd_scales;
+    }
+    codes += ((size_t)e * N + n) * (K / 2);
+    scales += ((size_t)e * N + n) * nblkK;
+  };
   const uint8_t* b_src[C::B_PER_T];
+  int b_lds[C::B_PER_T];
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
-    const int c = tid + 256 * i;
-    b_src[i] = nullptr;
-    if (c < C::B_CHUNKS) {
-      const int brow = c >> 1, part = c & 1;
-      const uint8_t* base;
-      int n;
-      if (GATEUP) {
-        const int w = brow / (NF * 32), f = (brow / 32) % NF, cc = brow & 31;
-        const bool up = f >= C::NW;
-        n = ncol0 + w * C::NW * 32 + (up ? f - C::NW : f) * 32 + cc;
-        base = up ? a.wu_codes : a.wg_codes;
-      } else {
-        n = ncol0 + brow;
-        base = a.wd_codes;
-      }
-      b_src[i] = base + ((size_t)e * N + n) * (K / 2) + part * 16;
-    }
+    const int c = min(tid + 256 * i, C::B_CHUNKS - 1);
+    const uint8_t* sc;
+    b_row(c >> 1, b_src[i], sc);
+    b_src[i] += (c & 1) * 16;
+    b_lds[i] = tid + 256 * i < C::B_CHUNKS ? C::A_BYTES + C::AS_BYTES + (c >> 1) * kBPitch + (c & 1) * 16
+                                           : C::SINK;
   }
   const uint8_t* bs_src[C::BS_PER_T];
+  int bs_lds[C::BS_PER_T];
 #pragma unroll
   for (int i = 0; i < C::BS_PER_T; ++i) {
-    const int brow = tid + 256 * i;
-    bs_src[i] = nullptr;
-    if (brow < C::BNB) {
-      const uint8_t* base;
-      int n;
-      if (GATEUP) {
-        const int w = brow / (NF * 32), f = (brow / 32) % NF, cc = brow & 31;
-        const bool up = f >= C::NW;
-        n = ncol0 + w * C::NW * 32 + (up ? f - C::NW : f) * 32 + cc;
-        base = up ? a.wu_scales : a.wg_scales;
-      } else {
-        n = ncol0 + brow;
-        base = a.wd_scales;
-      }
-      bs_src[i] = base + ((size_t)e * N + n) * nblkK;
-    }
+    const int brow = min(tid + 256 * i, C::BNB - 1);
+    const uint8_t* co;
+    b_row(brow, co, bs_src[i]);
+    bs_lds[i] = tid + 256 * i < C::BNB ? C::A_BYTES + C::AS_BYTES + C::B_BYTES + brow * 2 : C::SINK;
   }
 
   uint4 ra[C::A_PER_T], rb[C::B_PER_T];
@@ -227,41 +224,31 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const En
 
   auto load_stage = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i)
-      ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + s * 96) : make_uint4(0, 0, 0, 0);
-    ras = as_src ? *reinterpret_cast<const uint32_t*>(as_src + 2 * s) : 0u;
+    for (int i = 0; i < C::A_PER_T; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + s * 96);
+    ras = *reinterpret_cast<const uint32_t*>(as_src + 2 * s);
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i)
-      if (b_src[i]) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + s * 32);
+    for (int i = 0; i < C::B_PER_T; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + s * 32);
 #pragma unroll
-    for (int i = 0; i < C::BS_PER_T; ++i)
-      if (bs_src[i]) rbs[i] = *reinterpret_cast<const uint16_t*>(bs_src[i] + 2 * s);
+    for (int i = 0; i < C::BS_PER_T; ++i) rbs[i] = *reinterpret_cast<const uint16_t*>(bs_src[i] + 2 * s);
   };
   auto store_stage = [&](int buf) {
     uint8_t* st = smem + buf * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i) {
-      if (tid + 256 * i < C::A_CHUNKS) {
-        uint2* d = reinterpret_cast<uint2*>(st + a_lds[i]);
-        d[0] = make_uint2(ra[i].x, ra[i].y);
-        d[1] = make_uint2(ra[i].z, ra[i].w);
-      }
+      uint2* d = reinterpret_cast<uint2*>(a_lds[i] == C::SINK ? smem + C::SINK : st + a_lds[i]);
+      d[0] = make_uint2(ra[i].x, ra[i].y);
+      d[1] = make_uint2(ra[i].z, ra[i].w);
     }
     if (tid < kBM) reinterpret_cast<uint32_t*>(st + C::A_BYTES)[tid] = ras;
-    uint8_t* bst = st + C::A_BYTES + C::AS_BYTES;
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i) {
-      const int c = tid + 256 * i;
-      if (c < C::B_CHUNKS) {
-        uint2* d = reinterpret_cast<uint2*>(bst + (c >> 1) * kBPitch + (c & 1) * 16);
-        d[0] = make_uint2(rb[i].x, rb[i].y);
-        d[1] = make_uint2(rb[i].z, rb[i].w);
-      }
+      uint2* d = reinterpret_cast<uint2*>(b_lds[i] == C::SINK ? smem + C::SINK : st + b_lds[i]);
+      d[0] = make_uint2(rb[i].x, rb[i].y);
+      d[1] = make_uint2(rb[i].z, rb[i].w);
     }
-    uint16_t* bss = reinterpret_cast<uint16_t*>(bst + C::B_BYTES);
 #pragma unroll
     for (int i = 0; i < C::BS_PER_T; ++i)
-      if (tid + 256 * i < C::BNB) bss[tid + 256 * i] = rbs[i];
+      *reinterpret_cast<uint16_t*>(bs_lds[i] == C::SINK ? smem + C::SINK : st + bs_lds[i]) = rbs[i];
   };
 
   // ---- accumulators start at the bias of their output column
@@ -381,18 +368,64 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const En
 
 // ------------------------------------------------------------------ decode
 
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void grouped_decode(const FfnArgs a, const EncIn ain,
+// Weight streaming for few rows per expert. One workgroup per (expert, 64 output
+// columns); wavefront w owns columns 16w..16w+15 over the full K and uses the
+// 16x16x128 scaled MFMA (16 rows = one decode-sized row tile). K is processed in
+// super-stages of kSS 128-deep steps: per super-stage every wavefront issues all
+// its weight loads (straight from HBM into MFMA registers) while the workgroup
+// stages the expert's activation rows for the same K window in LDS, so each
+// super-stage costs one memory latency and the activations are read from L2
+// once per workgroup instead of once per wavefront. Small register and LDS
+// footprints keep many workgroups per CU, and with them enough bytes in flight.
+//
+// 16x16x128 layout (checked on gfx950): lane l supplies row/column l%16 and K
+// elements 32*(l/16) .. +31 of the step; result lane l holds column l%16, rows
+// 4*(l/16) + i, i = 0..3.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int OPA>
+__device__ __forceinline__ v4f mfma16_f6f4(const v8i& a, const v8i& b, const v4f& c, int sa,
+                                           int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 2, 4, OPA, sa, 0, sb);
+}
+
+constexpr int kDecSS = 4;                  // 128-deep K steps per stage
+constexpr int kDecWB = 4 * kDecSS;         // 32-element blocks per K window
+constexpr int kDecAPitch = kDecWB * kEncBytes + 8;  // LDS bytes per activation row (padded)
+constexpr int kDecAChunks = 16 * kDecWB * 3;        // 16-byte chunks of the activation window
+constexpr int kDecAPerT = kDecAChunks / 256;        // ... per thread
+constexpr int kDecASPerT = 16 * kDecWB / 256;       // activation scale entries per thread
+constexpr int kDecBSPerT = 64 * kDecWB / 256;       // weight scale bytes per thread
+static_assert(kDecSS % 4 == 0, "the window staging splits evenly over 256 threads");
+static_assert(kDecAChunks % 256 == 0 && (16 * kDecWB) % 256 == 0 && (64 * kDecWB) % 256 == 0,
+              "window staging must divide evenly");
+
+// Gate/up: waves 0,1 stream the gate rows of 32 h-columns, waves 2,3 the up rows
+// of the same columns (one matrix per wave keeps the register footprint small);
+// down: 4 waves x 16 output columns. Weights for stage s+1 are in flight while
+// stage s is computed (two register buffers), and the activation window is
+// double-buffered in LDS. All global reads are buffer loads: K blocks past the
+// end (the half step when K % 128 == 64) read zero codes, so they add nothing.
+// NSTAGE > 0 fixes the number of K stages at compile time so the stage loop is
+// fully unrolled: with a runtime trip count the compiler copies the loop-carried
+// weight buffers at the back edge, which waits for the prefetch and serialises
+// the pipeline. NSTAGE == 0 is the generic runtime loop for any K.
+template <bool GATEUP, int NSTAGE>
+__global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const EncIn ain,
                                                       const EncOut hout) {
-  constexpr int NM = GATEUP ? 2 : 1;  // weight matrices streamed (gate+up, or down)
-  __shared__ __attribute__((aligned(16))) float red[3 * 64 * 16 * NM];
-  __shared__ __attribute__((aligned(16))) float htile[32 * 33];
+  constexpr int COLS = GATEUP ? 32 : 64;  // output columns per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][16 * kDecAPitch];
+  __shared__ uint16_t sAs[2][16 * kDecWB];
+  __shared__ uint8_t sBs[2][64 * kDecWB];   // weight scales of the window: [wave*16 + col][blk]
+  __shared__ __attribute__((aligned(16))) float gtile[GATEUP ? 2 * 16 * 36 : 4];
+  __shared__ uint8_t escratch[GATEUP ? 8 * 64 : 4];
 
   const int K = GATEUP ? a.d : a.F;
   const int N = GATEUP ? a.F : a.d;
   const int nblkK = K / 32;
-  const int nsteps = K / 64;
-  const int ncb = N / 32;
+  const int nst = (K + 127) / 128;   // 128-deep steps (the last may be half: K % 128 == 64)
+  const int nstage = NSTAGE > 0 ? NSTAGE : (nst + kDecSS - 1) / kDecSS;
+  const int ncb = N / COLS;
   const int e = blockIdx.x / ncb;
   const int j = blockIdx.x - e * ncb;
   const int off = a.offsets[e];
@@ -400,128 +433,167 @@ __global__ __launch_bounds__(256) void grouped_decode(const FfnArgs a, const Enc
   if (cnt == 0) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, half = lane >> 5;
-  const int s_begin = wave * nsteps / 4, s_end = (wave + 1) * nsteps / 4;
-  const int n = j * 32 + lr;
-  const uint8_t* wc[NM];
-  const uint8_t* wsc[NM];
-  float bias[NM];
-  if (GATEUP) {
-    wc[0] = a.wg_codes + ((size_t)e * N + n) * (K / 2) + half * 16;
-    wsc[0] = a.wg_scales + ((size_t)e * N + n) * nblkK + half;
-    bias[0] = bf16_to_f32(a.b_gate[(size_t)e * N + n]);
-    wc[NM - 1] = a.wu_codes + ((size_t)e * N + n) * (K / 2) + half * 16;
-    wsc[NM - 1] = a.wu_scales + ((size_t)e * N + n) * nblkK + half;
-    bias[NM - 1] = bf16_to_f32(a.b_up[(size_t)e * N + n]);
-  } else {
-    wc[0] = a.wd_codes + ((size_t)e * N + n) * (K / 2) + half * 16;
-    wsc[0] = a.wd_scales + ((size_t)e * N + n) * nblkK + half;
-    bias[0] = bf16_to_f32(a.b_down[(size_t)e * N + n]);
-  }
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+  const int n = GATEUP ? j * 32 + (wave & 1) * 16 + l16 : j * 64 + wave * 16 + l16;
+  const bool up = GATEUP && wave >= 2;
+  const uint8_t* codes = GATEUP ? (up ? a.wu_codes : a.wg_codes) : a.wd_codes;
+  const uint8_t* scales = GATEUP ? (up ? a.wu_scales : a.wg_scales) : a.wd_scales;
+  const rsrc_t wr = make_rsrc(codes + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
+  const rsrc_t sr = make_rsrc(scales + (size_t)e * N * nblkK, (uint32_t)(N * nblkK));
+  const float bias = bf16_to_f32((GATEUP ? (up ? a.b_up : a.b_gate) : a.b_down)[(size_t)e * N + n]);
+  const uint32_t wrow = (uint32_t)n * (K / 2);
+  // the weight-scale row this thread stages: column (wave, tid % 16) of the workgroup
+  const uint32_t srow_t = (uint32_t)(GATEUP ? j * 32 + (wave & 1) * 16 + (tid & 15)
+                                            : j * 64 + wave * 16 + (tid & 15)) * nblkK;
+  // activation rows: gathered tokens (gate/up) or this expert's rows of h (down)
+  const rsrc_t ar = GATEUP ? make_rsrc(ain.codes, (uint32_t)((size_t)a.T * nblkK * kEncBytes))
+                           : make_rsrc(ain.codes + (size_t)off * nblkK * kEncBytes,
+                                       (uint32_t)((size_t)cnt * nblkK * kEncBytes));
+  const rsrc_t asr = GATEUP ? make_rsrc(ain.scales, (uint32_t)((size_t)a.T * nblkK * 2))
+                            : make_rsrc(ain.scales + (size_t)off * nblkK, (uint32_t)(cnt * nblkK * 2));
 
-  for (int m0 = 0; m0 < cnt; m0 += 32) {
-    const int row = m0 + lr;
-    const bool valid = row < cnt;
-    int src = 0;
-    if (valid) src = GATEUP ? a.sorted_pair[off + row] / a.k : off + row;
-    const uint8_t* ap = ain.codes + ((size_t)src * nblkK + half) * kEncBytes;
-    const uint16_t* asp = ain.scales + (size_t)src * nblkK + half;
-
-    v16f acc[NM];
+  for (int m0 = 0; m0 < cnt; m0 += 16) {
+    const int rows = min(16, cnt - m0);
+    // This thread's share of the activation window: fixed (row, block, part)
+    // chunks; rows past the count and blocks past K read as zero.
+    uint32_t arow[kDecAPerT];
+    int alds[kDecAPerT], ablk[kDecAPerT];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int i = 0; i < kDecAPerT; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / (kDecWB * 3), rem = c - row * (kDecWB * 3);
+      const int blk = rem / 3, part = rem - blk * 3;
+      alds[i] = row * kDecAPitch + blk * kEncBytes + part * 16;
+      ablk[i] = blk;
+      const int src = GATEUP ? a.sorted_pair[off + m0 + min(row, rows - 1)] / a.k : m0 + row;
+      arow[i] = row < rows ? (uint32_t)(src * nblkK * kEncBytes + part * 16) : kOutOfRange;
+    }
+    uint32_t asrow[kDecASPerT];
+    int asblk[kDecASPerT];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[m][i] = wave == 0 ? bias[m] : 0.f;
-
-    for (int s0 = s_begin; s0 < s_end; s0 += 4) {
-      uint4 w[4][NM];
-      int ws[4][NM];
-      uint4 x0[4], x1[4], x2[4];
-      int xs[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = s0 + u;
-        if (s < s_end) {
-#pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            w[u][m] = *reinterpret_cast<const uint4*>(wc[m] + s * 32);
-            ws[u][m] = wsc[m][2 * s];
-          }
-          if (valid) {
-            const uint4* xp = reinterpret_cast<const uint4*>(ap + s * 2 * kEncBytes);
-            x0[u] = xp[0];
-            x1[u] = xp[1];
-            x2[u] = xp[2];
-            xs[u] = asp[2 * s];
-          } else {
-            x0[u] = x1[u] = x2[u] = make_uint4(0, 0, 0, 0);
-            xs[u] = 0;
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (s0 + u < s_end) {
-          const v8i ahi = {(int)x0[u].x, (int)x0[u].y, (int)x0[u].z, (int)x0[u].w,
-                           (int)x1[u].x, (int)x1[u].y, 0, 0};
-          const v8i alo = {(int)x1[u].z, (int)x1[u].w, (int)x2[u].x, (int)x2[u].y,
-                           (int)x2[u].z, (int)x2[u].w, 0, 0};
-#pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            const v8i b = {(int)w[u][m].x, (int)w[u][m].y, (int)w[u][m].z, (int)w[u][m].w, 0, 0, 0, 0};
-            acc[m] = mfma_f6f4<0>(ahi, b, acc[m], xs[u], ws[u][m]);
-            acc[m] = mfma_f6f4<1>(alo, b, acc[m], xs[u], ws[u][m]);
-          }
-        }
-      }
+    for (int i = 0; i < kDecASPerT; ++i) {
+      const int ent = tid + 256 * i;
+      const int row = ent / kDecWB;
+      asblk[i] = ent - row * kDecWB;
+      const int src = GATEUP ? a.sorted_pair[off + m0 + min(row, rows - 1)] / a.k : m0 + row;
+      asrow[i] = row < rows ? (uint32_t)(src * nblkK * 2) : kOutOfRange;
     }
 
-    // fixed-order reduction of the four K-quarters through LDS
-    __syncthreads();
-    if (wave > 0) {
+    v4f acc = v4f{bias, bias, bias, bias};
+    uint4 w0[kDecSS], w1[kDecSS];
+    uint4 ra[kDecAPerT];
+    uint32_t ras[kDecASPerT], rbs[kDecBSPerT];
+
+    auto load_w = [&](int st, uint4 (&w)[kDecSS]) {
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+      for (int u = 0; u < kDecSS; ++u) {
+        const int blk = (st * kDecSS + u) * 4 + q;
+        w[u] = bload16(wr, blk < nblkK ? wrow + blk * 16 : kOutOfRange);
+      }
+    };
+    auto load_a = [&](int st) {
+      const int kb0 = st * kDecWB;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) red[(((wave - 1) * NM + m) * 16 + i) * 64 + lane] = acc[m][i];
-    }
-    __syncthreads();
-    if (wave == 0) {
+      for (int i = 0; i < kDecAPerT; ++i) {
+        const int blk = kb0 + ablk[i];
+        ra[i] = bload16(ar, blk < nblkK && arow[i] != kOutOfRange ? arow[i] + blk * kEncBytes
+                                                                  : kOutOfRange);
+      }
 #pragma unroll
-      for (int w2 = 0; w2 < 3; ++w2)
+      for (int i = 0; i < kDecASPerT; ++i) {
+        const int blk = kb0 + asblk[i];
+        ras[i] = bload2(asr, blk < nblkK && asrow[i] != kOutOfRange ? asrow[i] + blk * 2
+                                                                    : kOutOfRange);
+      }
+      // weight scales of the window: column (wave, tid%16), kDecBSPerT consecutive
+      // blocks starting at ((tid>>4)&3) * kDecBSPerT
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+      for (int i = 0; i < kDecBSPerT; ++i) {
+        const int blk = kb0 + ((tid >> 4) & 3) * kDecBSPerT + i;
+        rbs[i] = bload1(sr, blk < nblkK ? srow_t + blk : kOutOfRange);
+      }
+    };
+    auto store_a = [&](int buf) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[m][i] += red[((w2 * NM + m) * 16 + i) * 64 + lane];
-      if constexpr (GATEUP) {
+      for (int i = 0; i < kDecAPerT; ++i) {
+        uint2* d = reinterpret_cast<uint2*>(sA[buf] + alds[i]);
+        d[0] = make_uint2(ra[i].x, ra[i].y);
+        d[1] = make_uint2(ra[i].z, ra[i].w);
+      }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 8 * (i >> 2) + 4 * half + (i & 3);
-          htile[r * 33 + lr] = silu_mul(acc[0][i], acc[1][i]);
-        }
-      } else {
+      for (int i = 0; i < kDecASPerT; ++i) sAs[buf][tid + 256 * i] = static_cast<uint16_t>(ras[i]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = m0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (r < cnt) a.y_sorted[(size_t)(off + r) * N + n] = acc[0][i];
+      for (int i = 0; i < kDecBSPerT; ++i)
+        sBs[buf][(wave * 16 + (tid & 15)) * kDecWB + ((tid >> 4) & 3) * kDecBSPerT + i] =
+            static_cast<uint8_t>(rbs[i]);
+    };
+    // compute stage st from LDS buffer st&1 and weight buffer w; meanwhile the
+    // loads of stage st+1 (activations, then weights into wn) are in flight
+    auto stage = [&](int st, uint4 (&w)[kDecSS], uint4 (&wn)[kDecSS]) {
+      const bool more = st + 1 < nstage;
+      if (more) {
+        load_a(st + 1);
+        load_w(st + 1, wn);
+      }
+      const int buf = st & 1;
+#pragma unroll
+      for (int u = 0; u < kDecSS; ++u) {
+        if (st * kDecSS + u < nst) {
+          const uint8_t* pa = sA[buf] + l16 * kDecAPitch + (4 * u + q) * kEncBytes;
+          const uint2 h0 = lds64(pa), h1 = lds64(pa + 8), h2 = lds64(pa + 16);
+          const uint2 g0 = lds64(pa + 24), g1 = lds64(pa + 32), g2 = lds64(pa + 40);
+          const v8i ahi = {(int)h0.x, (int)h0.y, (int)h1.x, (int)h1.y, (int)h2.x, (int)h2.y, 0, 0};
+          const v8i alo = {(int)g0.x, (int)g0.y, (int)g1.x, (int)g1.y, (int)g2.x, (int)g2.y, 0, 0};
+          const int as = sAs[buf][l16 * kDecWB + 4 * u + q];
+          const int bs = sBs[buf][(wave * 16 + l16) * kDecWB + 4 * u + q];
+          const v8i b = {(int)w[u].x, (int)w[u].y, (int)w[u].z, (int)w[u].w, 0, 0, 0, 0};
+          acc = mfma16_f6f4<0>(ahi, b, acc, as, bs);
+          acc = mfma16_f6f4<1>(alo, b, acc, as, bs);
         }
       }
-    }
-    if constexpr (GATEUP) {
+      if (more) store_a((st + 1) & 1);
       __syncthreads();
-      if (wave == 0 && lane < 32 && m0 + lane < cnt) {
-        float v[32];
+    };
+
+    __syncthreads();  // LDS of the previous row tile is no longer read
+    load_a(0);
+    load_w(0, w0);
+    store_a(0);
+    __syncthreads();
+    if constexpr (NSTAGE > 0) {
 #pragma unroll
-        for (int c = 0; c < 32; ++c) v[c] = htile[lane * 33 + c];
-        uint32_t hw[6], lw[6], sc;
-        encode_block(v, hw, lw, sc);
-        const int p = off + m0 + lane;
-        const int nblkF = a.F / 32;
-        uint4* dst = reinterpret_cast<uint4*>(hout.codes + ((size_t)p * nblkF + j) * kEncBytes);
-        dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        dst[1] = make_uint4(hw[4], hw[5], lw[0], lw[1]);
-        dst[2] = make_uint4(lw[2], lw[3], lw[4], lw[5]);
-        hout.scales[(size_t)p * nblkF + j] = static_cast<uint16_t>(sc);
+      for (int st = 0; st < NSTAGE; st += 2) {
+        stage(st, w0, w1);
+        if (st + 1 < NSTAGE) stage(st + 1, w1, w0);
       }
+    } else {
+      for (int st = 0; st < nstage; st += 2) {
+        stage(st, w0, w1);
+        if (st + 1 < nstage) stage(st + 1, w1, w0);
+      }
+    }
+
+    if constexpr (GATEUP) {
+      // waves 0,1 hold g, waves 2,3 hold u for the same 16 rows x 32 columns;
+      // then each half wavefront encodes one row's 32-column block of h
+      float* t = gtile + (wave >> 1) * 16 * 36;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[(4 * q + i) * 36 + (wave & 1) * 16 + l16] = acc[i];
+      __syncthreads();
+      const int nblkF = a.F / 32;
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int row = pass * 8 + (tid >> 5), col = tid & 31;
+        const float h = silu_mul(gtile[row * 36 + col], gtile[16 * 36 + row * 36 + col]);
+        const size_t rec = (size_t)(off + m0 + min(row, rows - 1)) * nblkF + j;
+        encode_group32(h, escratch + (tid >> 5) * 64, hout.codes + rec * kEncBytes,
+                       hout.scales + rec, row < rows);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i < rows) a.y_sorted[(size_t)(off + m0 + 4 * q + i) * N + n] = acc[i];
     }
   }
 }
@@ -557,6 +629,24 @@ hipError_t launch_prefill(const FfnArgs& a, EncIn ain, EncOut hout, const int32_
   return hipGetLastError();
 }
 
+template <bool GATEUP>
+hipError_t launch_decode(const FfnArgs& a, EncIn ain, EncOut hout, hipStream_t stream) {
+  const int K = GATEUP ? a.d : a.F;
+  const int N = GATEUP ? a.F : a.d;
+  const dim3 grid(a.E * (N / (GATEUP ? 32 : 64)));
+  const int nstage = ((K + 127) / 128 + kDecSS - 1) / kDecSS;
+#define MOE_DECODE_CASE(S) \
+  case S: hipLaunchKernelGGL((grouped_decode<GATEUP, S>), grid, dim3(256), 0, stream, a, ain, hout); break;
+  switch (nstage) {
+    MOE_DECODE_CASE(1) MOE_DECODE_CASE(2) MOE_DECODE_CASE(3) MOE_DECODE_CASE(4)
+    MOE_DECODE_CASE(5) MOE_DECODE_CASE(6) MOE_DECODE_CASE(7) MOE_DECODE_CASE(8)
+    MOE_DECODE_CASE(9) MOE_DECODE_CASE(10) MOE_DECODE_CASE(11) MOE_DECODE_CASE(12)
+    default: hipLaunchKernelGGL((grouped_decode<GATEUP, 0>), grid, dim3(256), 0, stream, a, ain, hout);
+  }
+#undef MOE_DECODE_CASE
+  return hipGetLastError();
+}
+
 // Largest column-fragment count per wave that tiles N exactly (64*q columns per
 // workgroup, q in {3, 2, 1}).
 int pick_q(int N) { return N % 192 == 0 ? 3 : (N % 128 == 0 ? 2 : 1); }
@@ -583,12 +673,8 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
 
   if (a.T <= kDecodeMaxT) {
-    hipLaunchKernelGGL(grouped_decode<true>, dim3(a.E * (a.F / 32)), dim3(256), 0, stream, a, xin,
-                       hout);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_decode<false>, dim3(a.E * (a.d / 32)), dim3(256), 0, stream, a, hin,
-                       hout);
-    return hipGetLastError();
+    if ((err = launch_decode<true>(a, xin, hout, stream)) != hipSuccess) return err;
+    return launch_decode<false>(a, hin, hout, stream);
   }
 
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);

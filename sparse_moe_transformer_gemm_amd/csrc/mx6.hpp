@@ -109,6 +109,131 @@ __device__ __forceinline__ void encode_block(const float (&v)[32], uint32_t (&hi
   scales = static_cast<uint32_t>(s1 + 127) | (static_cast<uint32_t>(s2 + 127) << 8);
 }
 
+// Same encoding for 32 floats held in LDS (or any memory) at v[0..31]; the
+// buffer is overwritten with the residuals. Uses few registers: the values are
+// re-read in three passes (max, hi term + residual, lo term).
+__device__ __forceinline__ void encode_block_mem(float* v, uint32_t (&hi)[6], uint32_t (&lo)[6],
+                                                 uint32_t& scales) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  int s1 = amax > 0.f ? ilog2f(amax) - 2 : -127;
+  s1 = s1 < -127 ? -127 : s1;
+  const float inv1 = pow2i(-s1 > 127 ? 127 : -s1), sc1 = pow2i(s1);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) hi[i] = lo[i] = 0u;
+  float ramax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float x = v[j];
+    const uint32_t m = e2m3_code(fabsf(x) * inv1);
+    const uint32_t sign = __float_as_uint(x) >> 31;
+    const uint32_t c = (sign << 5) | m;
+    const int bit = 6 * j, word = bit >> 5, off = bit & 31;
+    hi[word] |= c << off;
+    if (off > 26) hi[word + 1] |= c >> (32 - off);
+    const float back = e2m3_value(m) * sc1;
+    const float r = x - (sign ? -back : back);
+    v[j] = r;
+    ramax = fmaxf(ramax, fabsf(r));
+  }
+  int s2 = ramax > 0.f ? ilog2f(ramax) - 2 : -127;
+  s2 = s2 < -127 ? -127 : s2;
+  const float inv2 = pow2i(-s2 > 127 ? 127 : -s2);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float r = v[j];
+    const uint32_t c = ((__float_as_uint(r) >> 31) << 5) | e2m3_code(fabsf(r) * inv2);
+    const int bit = 6 * j, word = bit >> 5, off = bit & 31;
+    lo[word] |= c << off;
+    if (off > 26) lo[word + 1] |= c >> (32 - off);
+  }
+  scales = static_cast<uint32_t>(s1 + 127) | (static_cast<uint32_t>(s2 + 127) << 8);
+}
+
+// The same encoding done by a group of 32 lanes (a half wavefront), one element
+// per lane: j = lane & 31 holds element j of the block. The block maxima are
+// shuffle reductions inside the half wavefront; the 6-bit codes are packed
+// through `scratch` (64 bytes of LDS per group) and 12 lanes store the 48-byte
+// record (lane j < 6: hi word j, 6 <= j < 12: lo word j-6) plus lane 0 the scales.
+// Every thread of the workgroup must call it (it contains a barrier); `store`
+// false computes without writing (rows past the count).
+__device__ __forceinline__ void encode_group32(float v, uint8_t* scratch, uint8_t* dst_codes,
+                                               uint16_t* dst_scales, bool store) {
+  const int j = threadIdx.x & 31;
+  float amax = fabsf(v);
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  int s1 = amax > 0.f ? ilog2f(amax) - 2 : -127;
+  s1 = s1 < -127 ? -127 : s1;
+  const uint32_t m1 = e2m3_code(fabsf(v) * pow2i(-s1 > 127 ? 127 : -s1));
+  const uint32_t sign1 = __float_as_uint(v) >> 31;
+  const float back = e2m3_value(m1) * pow2i(s1);
+  const float r = v - (sign1 ? -back : back);
+  float ramax = fabsf(r);
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) ramax = fmaxf(ramax, __shfl_xor(ramax, o));
+  int s2 = ramax > 0.f ? ilog2f(ramax) - 2 : -127;
+  s2 = s2 < -127 ? -127 : s2;
+  const uint32_t m2 = e2m3_code(fabsf(r) * pow2i(-s2 > 127 ? 127 : -s2));
+  scratch[j] = static_cast<uint8_t>((sign1 << 5) | m1);
+  scratch[32 + j] = static_cast<uint8_t>(((__float_as_uint(r) >> 31) << 5) | m2);
+  __syncthreads();
+  if (store && j < 12) {
+    const uint8_t* c = scratch + (j < 6 ? 0 : 32);
+    const int w = j < 6 ? j : j - 6;   // word w holds bits [32w, 32w+32) of the 192-bit field
+    uint32_t word = 0;
+#pragma unroll
+    for (int t = 0; t < 7; ++t) {
+      const int code = (32 * w) / 6 + t;       // codes overlapping this word
+      if (code < 32) {
+        const int bit = 6 * code - 32 * w;     // position of the code's bit 0 in the word
+        const uint32_t cv = c[code];
+        if (bit >= 0 && bit < 32) word |= cv << bit;
+        else if (bit < 0 && bit > -6) word |= cv >> (-bit);
+      }
+    }
+    reinterpret_cast<uint32_t*>(dst_codes)[j] = word;
+    if (j == 0)
+      *dst_scales = static_cast<uint16_t>((s1 + 127) | ((s2 + 127) << 8));
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void store_enc(uint8_t* dst_codes, const uint32_t (&hw)[6],
+                                          const uint32_t (&lw)[6]) {
+  uint4* dst = reinterpret_cast<uint4*>(dst_codes);
+  dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  dst[1] = make_uint4(hw[4], hw[5], lw[0], lw[1]);
+  dst[2] = make_uint4(lw[2], lw[3], lw[4], lw[5]);
+}
+
+// ------------------------------------------------------------------ buffer loads
+// Raw buffer loads: a 128-bit resource (base, size in bytes) held in SGPRs plus a
+// 32-bit per-lane byte offset. Offsets at or past the size read as zero without
+// touching memory, which is how out-of-range K blocks and rows are padded.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword3 0x00020000: raw (untyped) 32-bit data, the usual value on CDNA
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // every resource here is < 2 GiB
+
 // D += A(FP6 E2M3, scale byte OPA of sa) x B(FP4 E2M1, scale byte 0 of sb).
 template <int OPA>
 __device__ __forceinline__ v16f mfma_f6f4(const v8i& a, const v8i& b, const v16f& c, int sa,

@@ -1,83 +1,142 @@
 // Router: logits = x W_r + b_r in float64, then per token the top-k experts and a
 // softmax over the k selected logits only (Perplexity, "GPT-OSS el dia 0",
-// section "MLP" and section "Nuclis per a GPT-OSS / MoE").
+// section "MLP" and section "Nuclis per a GPT-OSS / MoE"; the router weight is
+// not quantised: CSDN "GPT-OSS-120B 4-bit 量化技术深度解析", section
+// "Unsloth 4-bit量化技术解析").
 //
-// Two kernels:
-//   route_logits  grid (token tiles, K slices). Each block holds 16 tokens and all
-//                 E experts; x and W_r are staged through LDS in 32-deep K tiles and
-//                 accumulated in float64. When there are few token tiles (decode)
-//                 K is split across blocks so the chip fills; partial sums go to
-//                 the workspace as [slice][T][E].
-//   route_topk    one wavefront per token: sums the slices in fixed order, then k
-//                 rounds of a wave-wide (max logit, min index) reduction pick the
-//                 experts; the softmax is taken in float64 and stored as fp32.
-// Logits in float64 make the selection exact except where two logits differ by
-// less than ~1e-12 relative; the summation order is fixed, so the result is
-// deterministic.
+// Float64 logits make the selection the exact top-k of the real-valued logits
+// except where two logits differ by less than ~1e-12 relative, and the fixed
+// summation order makes it deterministic.
+//
+// Three kernels:
+//   route_widen   W_r (fp32 [d][E]) -> float64 [d][Epad] in the workspace
+//                 (Epad = E rounded up to 32, zero padded).
+//   route_logits  grid (256-token blocks, K slices, 32-expert groups). One lane
+//                 per token, 32 float64 accumulators per lane; each 64-deep K
+//                 chunk of W is staged once in LDS and read as broadcasts by all
+//                 four wavefronts. Partial sums [slice][T][E] are written through
+//                 an LDS transpose so the stores coalesce.
+//   route_select  one workgroup per token: the K-slice partials are reduced in a
+//                 fixed order (+ bias), then k rounds of a wavefront-wide
+//                 (max logit, lowest index) reduction pick the experts and the
+//                 softmax over the picked logits is taken in float64.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kTM = 16;       // tokens per block
-constexpr int kKT = 32;       // K depth of one LDS tile
+constexpr int kTok = 256;     // tokens per logits block (4 wavefronts, one lane per token)
+constexpr int kEG = 32;       // experts per group (accumulators per lane)
+constexpr int kKC = 64;       // K depth of one LDS stage
 constexpr int kMaxE = 256;
+constexpr int kTargetBlocks = 480;
 
-int route_kslices(int T, int d) {
-  int tiles = (T + kTM - 1) / kTM;
-  int ktiles = d / kKT;
-  if (tiles >= 256) return 1;
-  int want = (512 + tiles - 1) / tiles;
-  return want < ktiles ? want : ktiles;
+struct RoutePlan {
+  int Epad, ngroups, tblocks, kslice, nslices;
+};
+
+RoutePlan route_plan(int T, int d, int E) {
+  RoutePlan p;
+  p.Epad = (E + kEG - 1) / kEG * kEG;
+  p.ngroups = p.Epad / kEG;
+  p.tblocks = (T + kTok - 1) / kTok;
+  const int base = p.tblocks * p.ngroups;
+  int want = (kTargetBlocks + base - 1) / base;
+  const int kstages = d / kKC;
+  if (want > kstages) want = kstages;
+  if (want < 1) want = 1;
+  p.kslice = (kstages + want - 1) / want * kKC;
+  p.nslices = (d + p.kslice - 1) / p.kslice;
+  return p;
+}
+
+__global__ __launch_bounds__(256) void route_widen(const float* __restrict__ w, int d, int E,
+                                                   int Epad, double* __restrict__ w64) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i >= (size_t)d * Epad) return;
+  const int k = static_cast<int>(i / Epad), e = static_cast<int>(i % Epad);
+  w64[i] = e < E ? static_cast<double>(w[(size_t)k * E + e]) : 0.0;
 }
 
 __global__ __launch_bounds__(256) void route_logits(const uint16_t* __restrict__ x,
-                                                    const float* __restrict__ w, int T, int d,
-                                                    int E, int kslice,
+                                                    const double* __restrict__ w64, int T, int d,
+                                                    int E, int Epad, int kslice,
                                                     double* __restrict__ partial) {
-  __shared__ double xs[kTM][kKT + 1];
-  __shared__ double wt[kKT][kMaxE];
-  const int t0 = blockIdx.x * kTM;
-  const int kbeg = blockIdx.y * kslice;
-  const int kend = min(d, kbeg + kslice);
+  // two W stages of [kKC][kEG] doubles (32 KB) during the K loop; the same memory
+  // then holds the [kTok][kEG+1] transpose of the accumulators (67.6 KB)
+  __shared__ __attribute__((aligned(16))) double smem[kTok * (kEG + 1)];
   const int tid = threadIdx.x;
-  const int tt = tid >> 4;   // token of this thread inside the tile
-  const int el = tid & 15;   // experts el, el+16, ...
-  const int ne = (E + 15) >> 4;
+  const int t = blockIdx.x * kTok + tid;
+  const int slice = blockIdx.y, eg = blockIdx.z;
+  const int k0 = slice * kslice;
+  const int k1 = min(d, k0 + kslice);
+  const bool valid = t < T;
+  const bool wave_live = blockIdx.x * kTok + (tid & ~63) < T;  // uniform per wavefront
 
-  double acc[16];
+  double acc[kEG];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0;
+  for (int e = 0; e < kEG; ++e) acc[e] = 0.0;
 
-  for (int k0 = kbeg; k0 < kend; k0 += kKT) {
-    for (int i = tid; i < kTM * kKT; i += 256) {
-      int r = i / kKT, c = i % kKT, t = t0 + r, kk = k0 + c;
-      xs[r][c] = (t < T && kk < kend) ? static_cast<double>(bf16_to_f32(x[(size_t)t * d + kk])) : 0.0;
-    }
-    for (int i = tid; i < kKT * E; i += 256) {
-      int r = i / E, c = i % E, kk = k0 + r;
-      wt[r][c] = (kk < kend) ? static_cast<double>(w[(size_t)kk * E + c]) : 0.0;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < kKT; ++kk) {
-      const double xv = xs[tt][kk];
+  // stage loader: the 64x32 W chunk is 1024 double2 = 4 per thread
+  const double* wsrc = w64 + (size_t)eg * kEG;
+  double2 pre[4];
+  auto load = [&](int kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = el + 16 * i;
-        if (i < ne && e < E) acc[i] = fma(xv, wt[kk][e], acc[i]);
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;           // double2 index in the chunk
+      const int kk = c >> 4, e2 = (c & 15) * 2;
+      pre[i] = (kb + kk < k1) ? *reinterpret_cast<const double2*>(wsrc + (size_t)(kb + kk) * Epad + e2)
+                              : make_double2(0.0, 0.0);
+    }
+  };
+  auto store = [&](int buf) {
+    double2* dst = reinterpret_cast<double2*>(smem + buf * kKC * kEG);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[tid + 256 * i] = pre[i];
+  };
+
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(valid ? t : 0) * d);
+  const int nst = (k1 - k0 + kKC - 1) / kKC;
+  load(k0);
+  store(0);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int kb = k0 + s * kKC;
+    if (s + 1 < nst) load(kb + kKC);
+    if (wave_live) {
+      const double2* ws2 = reinterpret_cast<const double2*>(smem + (s & 1) * kKC * kEG);
+      const int kend = min(kKC, k1 - kb);
+      for (int k8 = 0; k8 < kend; k8 += 8) {
+        const uint4 xv = valid ? xr[(kb + k8) >> 3] : make_uint4(0, 0, 0, 0);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const double xd = static_cast<double>(bf16_to_f32(h & 1 ? (xw[h >> 1] >> 16) : (xw[h >> 1] & 0xffffu)));
+          const double2* wrow = ws2 + (k8 + h) * (kEG / 2);
+#pragma unroll
+          for (int e2 = 0; e2 < kEG / 2; ++e2) {
+            const double2 wv = wrow[e2];
+            acc[2 * e2] = fma(xd, wv.x, acc[2 * e2]);
+            acc[2 * e2 + 1] = fma(xd, wv.y, acc[2 * e2 + 1]);
+          }
+        }
       }
     }
+    if (s + 1 < nst) store((s + 1) & 1);
     __syncthreads();
   }
-  const int t = t0 + tt;
-  if (t < T) {
-    double* dst = partial + ((size_t)blockIdx.y * T + t) * E;
+
+  // transpose through LDS so that the partial stores are contiguous
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = el + 16 * i;
-      if (i < ne && e < E) dst[e] = acc[i];
-    }
+  for (int e = 0; e < kEG; ++e) smem[tid * (kEG + 1) + e] = acc[e];
+  __syncthreads();
+  const int ebase = eg * kEG;
+  const int ne = min(kEG, E - ebase);
+  for (int i = tid; i < kTok * kEG; i += 256) {
+    const int tl = i / kEG, e = i % kEG;
+    const int tt = blockIdx.x * kTok + tl;
+    if (tt < T && e < ne)
+      partial[((size_t)slice * T + tt) * E + ebase + e] = smem[tl * (kEG + 1) + e];
   }
 }
 
@@ -85,27 +144,39 @@ __device__ __forceinline__ bool better(double va, int ea, double vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
-__global__ __launch_bounds__(256) void route_topk(const double* __restrict__ partial, int KS,
-                                                  const float* __restrict__ bias, int T, int E,
-                                                  int k, int32_t* __restrict__ topk_idx,
-                                                  float* __restrict__ topk_w) {
-  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  if (t >= T) return;  // uniform per wavefront
+__global__ __launch_bounds__(256) void route_select(const double* __restrict__ partial, int KS,
+                                                    const float* __restrict__ bias, int T, int E,
+                                                    int k, int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ topk_w) {
+  __shared__ double part[256];
+  __shared__ double logit[kMaxE];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int G = 256 / E;
+  if (tid < G * E) {
+    const int e = tid % E, g = tid / E;
+    double s = 0.0;
+#pragma unroll 4
+    for (int ks = g; ks < KS; ks += G) s += partial[((size_t)ks * T + t) * E + e];
+    part[g * E + e] = s;
+  }
+  __syncthreads();
+  if (tid < E) {
+    double v = 0.0;
+    for (int g = 0; g < G; ++g) v += part[g * E + tid];
+    if (bias) v += static_cast<double>(bias[tid]);
+    logit[tid] = v;
+  }
+  __syncthreads();
+  if (tid >= kWave) return;
+  const int lane = tid;
 
   double v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + kWave * i;
-    double s = -INFINITY;
-    if (e < E) {
-      s = 0.0;
-      for (int ks = 0; ks < KS; ++ks) s += partial[((size_t)ks * T + t) * E + e];
-      if (bias) s += static_cast<double>(bias[e]);
-    }
-    v[i] = s;
+    v[i] = e < E ? logit[e] : -INFINITY;
   }
-
   unsigned taken = 0;
   double sel_v[8];
   int sel_e[8];
@@ -138,7 +209,6 @@ __global__ __launch_bounds__(256) void route_topk(const double* __restrict__ par
       if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
     }
   }
-
   double den = 0.0;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -152,27 +222,33 @@ __global__ __launch_bounds__(256) void route_topk(const double* __restrict__ par
   }
 }
 
+size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
 }  // namespace
 
 size_t route_workspace_bytes(int T, int d, int E) {
-  return (size_t)route_kslices(T, d) * T * E * sizeof(double);
+  const RoutePlan p = route_plan(T, d, E);
+  return al256((size_t)d * p.Epad * sizeof(double)) +
+         al256((size_t)p.nslices * T * E * sizeof(double));
 }
 
 hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b_router, int T,
                         int d, int E, int k, int32_t* topk_idx, float* topk_w, void* ws,
                         hipStream_t stream) {
-  const int KS = route_kslices(T, d);
-  const int ktiles = d / kKT;
-  const int kslice = ((ktiles + KS - 1) / KS) * kKT;
-  const int KSeff = (d + kslice - 1) / kslice;
-  double* partial = static_cast<double*>(ws);
-  dim3 g1((T + kTM - 1) / kTM, KSeff);
-  hipLaunchKernelGGL(route_logits, g1, dim3(256), 0, stream, x, w_router, T, d, E, kslice, partial);
+  const RoutePlan p = route_plan(T, d, E);
+  double* w64 = static_cast<double*>(ws);
+  double* partial = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) +
+                                              al256((size_t)d * p.Epad * sizeof(double)));
+  const size_t nw = (size_t)d * p.Epad;
+  hipLaunchKernelGGL(route_widen, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
+                     w_router, d, E, p.Epad, w64);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dim3 g2((T + 3) / 4);
-  hipLaunchKernelGGL(route_topk, g2, dim3(256), 0, stream, partial, KSeff, b_router, T, E, k,
-                     topk_idx, topk_w);
+  hipLaunchKernelGGL(route_logits, dim3(p.tblocks, p.nslices, p.ngroups), dim3(256), 0, stream, x,
+                     w64, T, d, E, p.Epad, p.kslice, partial);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(route_select, dim3(T), dim3(256), 0, stream, partial, p.nslices, b_router, T,
+                     E, k, topk_idx, topk_w);
   return hipGetLastError();
 }
 
