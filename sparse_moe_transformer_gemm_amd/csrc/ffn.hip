@@ -46,9 +46,13 @@ size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 // ------------------------------------------------------------------ encode x
 
-__global__ __launch_bounds__(256) void encode_rows(const uint16_t* __restrict__ x, int rows,
-                                                   int K, uint8_t* __restrict__ codes,
-                                                   uint16_t* __restrict__ scales) {
+// Activation encoding, two shapes: few rows (decode) -- one (row, 32-element
+// block) per half wavefront, lane j takes element j and the block is encoded
+// cooperatively (short latency); many rows (prefill) -- one block per thread
+// (no barriers, throughput).
+__global__ __launch_bounds__(256) void encode_rows_thread(const uint16_t* __restrict__ x, int rows,
+                                                          int K, uint8_t* __restrict__ codes,
+                                                          uint16_t* __restrict__ scales) {
   const int nblk = K / 32;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * nblk) return;
@@ -66,11 +70,20 @@ __global__ __launch_bounds__(256) void encode_rows(const uint16_t* __restrict__ 
   }
   uint32_t hi[6], lo[6], sc;
   encode_block(v, hi, lo, sc);
-  uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)idx * kEncBytes);
-  dst[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  dst[1] = make_uint4(hi[4], hi[5], lo[0], lo[1]);
-  dst[2] = make_uint4(lo[2], lo[3], lo[4], lo[5]);
+  store_enc(codes + (size_t)idx * kEncBytes, hi, lo);
   scales[idx] = static_cast<uint16_t>(sc);
+}
+
+__global__ __launch_bounds__(256) void encode_rows(const uint16_t* __restrict__ x, int rows,
+                                                   int K, uint8_t* __restrict__ codes,
+                                                   uint16_t* __restrict__ scales) {
+  __shared__ uint8_t scratch[8 * 64];
+  const int nrec = rows * (K / 32);
+  const int g = blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int gg = g < nrec ? g : nrec - 1;
+  const float v = bf16_to_f32(x[(size_t)gg * 32 + (threadIdx.x & 31)]);
+  encode_group32(v, scratch + (threadIdx.x >> 5) * 64, codes + (size_t)gg * kEncBytes,
+                 scales + gg, g < nrec);
 }
 
 // ------------------------------------------------------------------ tile table
@@ -390,6 +403,8 @@ __device__ __forceinline__ v4f mfma16_f6f4(const v8i& a, const v8i& b, const v4f
 }
 
 constexpr int kDecSS = 4;                  // 128-deep K steps per stage
+constexpr int kDecPF = 2;                  // stages of loads in flight ahead of the one computed
+constexpr int kDecMaxStages = 8;           // decode kernels cover K <= kDecMaxStages * kDecSS * 128
 constexpr int kDecWB = 4 * kDecSS;         // 32-element blocks per K window
 constexpr int kDecAPitch = kDecWB * kEncBytes + 8;  // LDS bytes per activation row (padded)
 constexpr int kDecAChunks = 16 * kDecWB * 3;        // 16-byte chunks of the activation window
@@ -402,18 +417,19 @@ static_assert(kDecAChunks % 256 == 0 && (16 * kDecWB) % 256 == 0 && (64 * kDecWB
 
 // Gate/up: waves 0,1 stream the gate rows of 32 h-columns, waves 2,3 the up rows
 // of the same columns (one matrix per wave keeps the register footprint small);
-// down: 4 waves x 16 output columns. Weights for stage s+1 are in flight while
-// stage s is computed (two register buffers), and the activation window is
-// double-buffered in LDS. All global reads are buffer loads: K blocks past the
-// end (the half step when K % 128 == 64) read zero codes, so they add nothing.
-// NSTAGE > 0 fixes the number of K stages at compile time so the stage loop is
-// fully unrolled: with a runtime trip count the compiler copies the loop-carried
-// weight buffers at the back edge, which waits for the prefetch and serialises
-// the pipeline. NSTAGE == 0 is the generic runtime loop for any K.
+// down: 4 waves x 16 output columns. The stage loop is unrolled at compile time
+// (NSTAGE stages of kDecSS steps): the weight codes of stage s+kDecPF and the
+// activation window (+ both kinds of scales) of stage s+kDecPF are issued while
+// stage s is computed, held in register rings, and the window is copied to LDS
+// one stage before it is read. Loads are issued in the order they are consumed,
+// so waiting for one never waits for a younger one (the vector memory counter
+// retires in order). All global reads are buffer loads: K blocks past the end
+// (the half step when K % 128 == 64) and rows past the count read as zero.
 template <bool GATEUP, int NSTAGE>
 __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const EncIn ain,
-                                                      const EncOut hout) {
+                                                         const EncOut hout) {
   constexpr int COLS = GATEUP ? 32 : 64;  // output columns per workgroup
+  constexpr int PF = kDecPF;
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][16 * kDecAPitch];
   __shared__ uint16_t sAs[2][16 * kDecWB];
   __shared__ uint8_t sBs[2][64 * kDecWB];   // weight scales of the window: [wave*16 + col][blk]
@@ -424,7 +440,6 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
   const int N = GATEUP ? a.F : a.d;
   const int nblkK = K / 32;
   const int nst = (K + 127) / 128;   // 128-deep steps (the last may be half: K % 128 == 64)
-  const int nstage = NSTAGE > 0 ? NSTAGE : (nst + kDecSS - 1) / kDecSS;
   const int ncb = N / COLS;
   const int e = blockIdx.x / ncb;
   const int j = blockIdx.x - e * ncb;
@@ -455,8 +470,6 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
 
   for (int m0 = 0; m0 < cnt; m0 += 16) {
     const int rows = min(16, cnt - m0);
-    // This thread's share of the activation window: fixed (row, block, part)
-    // chunks; rows past the count and blocks past K read as zero.
     uint32_t arow[kDecAPerT];
     int alds[kDecAPerT], ablk[kDecAPerT];
 #pragma unroll
@@ -480,62 +493,70 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
       asrow[i] = row < rows ? (uint32_t)(src * nblkK * 2) : kOutOfRange;
     }
 
-    v4f acc = v4f{bias, bias, bias, bias};
-    uint4 w0[kDecSS], w1[kDecSS];
-    uint4 ra[kDecAPerT];
-    uint32_t ras[kDecASPerT], rbs[kDecBSPerT];
-
-    auto load_w = [&](int st, uint4 (&w)[kDecSS]) {
+    // one stage's worth of loads for this thread
+    struct Packet {
+      uint4 w[kDecSS];              // weight codes (MFMA B operand, this lane)
+      uint4 a[kDecAPerT];           // activation window chunks (staged to LDS)
+      uint32_t as[kDecASPerT];      // activation scales (staged)
+      uint32_t bs[kDecBSPerT];      // weight scales (staged)
+    };
+    // The stage's distance along K goes into the uniform buffer offset, so the
+    // per-lane offsets are the same in every stage; only the last stage can hold
+    // blocks past K, and only there are lanes redirected out of range.
+    auto issue = [&](int st, Packet& pk) {
+      const bool last = st == NSTAGE - 1;
+      const uint32_t wso = (uint32_t)st * kDecSS * 64;    // weight bytes per 128-deep step: 64
 #pragma unroll
       for (int u = 0; u < kDecSS; ++u) {
-        const int blk = (st * kDecSS + u) * 4 + q;
-        w[u] = bload16(wr, blk < nblkK ? wrow + blk * 16 : kOutOfRange);
+        const bool live = !last || (st * kDecSS + u) * 4 + q < nblkK;
+        pk.w[u] = bload16(wr, live ? wrow + (u * 4 + q) * 16 : kOutOfRange, wso);
       }
-    };
-    auto load_a = [&](int st) {
       const int kb0 = st * kDecWB;
 #pragma unroll
       for (int i = 0; i < kDecAPerT; ++i) {
-        const int blk = kb0 + ablk[i];
-        ra[i] = bload16(ar, blk < nblkK && arow[i] != kOutOfRange ? arow[i] + blk * kEncBytes
-                                                                  : kOutOfRange);
+        const bool live = !last || kb0 + ablk[i] < nblkK;
+        pk.a[i] = bload16(ar, live ? arow[i] + ablk[i] * kEncBytes : kOutOfRange,
+                          (uint32_t)kb0 * kEncBytes);
       }
 #pragma unroll
       for (int i = 0; i < kDecASPerT; ++i) {
-        const int blk = kb0 + asblk[i];
-        ras[i] = bload2(asr, blk < nblkK && asrow[i] != kOutOfRange ? asrow[i] + blk * 2
-                                                                    : kOutOfRange);
+        const bool live = !last || kb0 + asblk[i] < nblkK;
+        pk.as[i] = bload2(asr, live ? asrow[i] + asblk[i] * 2 : kOutOfRange, (uint32_t)kb0 * 2);
       }
-      // weight scales of the window: column (wave, tid%16), kDecBSPerT consecutive
-      // blocks starting at ((tid>>4)&3) * kDecBSPerT
 #pragma unroll
       for (int i = 0; i < kDecBSPerT; ++i) {
-        const int blk = kb0 + ((tid >> 4) & 3) * kDecBSPerT + i;
-        rbs[i] = bload1(sr, blk < nblkK ? srow_t + blk : kOutOfRange);
+        const int bl = ((tid >> 4) & 3) * kDecBSPerT + i;
+        const bool live = !last || kb0 + bl < nblkK;
+        pk.bs[i] = bload1(sr, live ? srow_t + bl : kOutOfRange, (uint32_t)kb0);
       }
     };
-    auto store_a = [&](int buf) {
+    auto stage_to_lds = [&](const Packet& pk, int buf) {
 #pragma unroll
       for (int i = 0; i < kDecAPerT; ++i) {
         uint2* d = reinterpret_cast<uint2*>(sA[buf] + alds[i]);
-        d[0] = make_uint2(ra[i].x, ra[i].y);
-        d[1] = make_uint2(ra[i].z, ra[i].w);
+        d[0] = make_uint2(pk.a[i].x, pk.a[i].y);
+        d[1] = make_uint2(pk.a[i].z, pk.a[i].w);
       }
 #pragma unroll
-      for (int i = 0; i < kDecASPerT; ++i) sAs[buf][tid + 256 * i] = static_cast<uint16_t>(ras[i]);
+      for (int i = 0; i < kDecASPerT; ++i) sAs[buf][tid + 256 * i] = static_cast<uint16_t>(pk.as[i]);
 #pragma unroll
       for (int i = 0; i < kDecBSPerT; ++i)
         sBs[buf][(wave * 16 + (tid & 15)) * kDecWB + ((tid >> 4) & 3) * kDecBSPerT + i] =
-            static_cast<uint8_t>(rbs[i]);
+            static_cast<uint8_t>(pk.bs[i]);
     };
-    // compute stage st from LDS buffer st&1 and weight buffer w; meanwhile the
-    // loads of stage st+1 (activations, then weights into wn) are in flight
-    auto stage = [&](int st, uint4 (&w)[kDecSS], uint4 (&wn)[kDecSS]) {
-      const bool more = st + 1 < nstage;
-      if (more) {
-        load_a(st + 1);
-        load_w(st + 1, wn);
-      }
+
+    v4f acc = v4f{bias, bias, bias, bias};
+    Packet ring[PF + 1];
+    __syncthreads();  // LDS of the previous row tile is no longer read
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (p < NSTAGE) issue(p, ring[p]);
+    stage_to_lds(ring[0], 0);
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < NSTAGE; ++st) {
+      if (st + PF < NSTAGE) issue(st + PF, ring[(st + PF) % (PF + 1)]);
+      const Packet& cur = ring[st % (PF + 1)];
       const int buf = st & 1;
 #pragma unroll
       for (int u = 0; u < kDecSS; ++u) {
@@ -547,31 +568,13 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
           const v8i alo = {(int)g0.x, (int)g0.y, (int)g1.x, (int)g1.y, (int)g2.x, (int)g2.y, 0, 0};
           const int as = sAs[buf][l16 * kDecWB + 4 * u + q];
           const int bs = sBs[buf][(wave * 16 + l16) * kDecWB + 4 * u + q];
-          const v8i b = {(int)w[u].x, (int)w[u].y, (int)w[u].z, (int)w[u].w, 0, 0, 0, 0};
+          const v8i b = {(int)cur.w[u].x, (int)cur.w[u].y, (int)cur.w[u].z, (int)cur.w[u].w, 0, 0, 0, 0};
           acc = mfma16_f6f4<0>(ahi, b, acc, as, bs);
           acc = mfma16_f6f4<1>(alo, b, acc, as, bs);
         }
       }
-      if (more) store_a((st + 1) & 1);
+      if (st + 1 < NSTAGE) stage_to_lds(ring[(st + 1) % (PF + 1)], (st + 1) & 1);
       __syncthreads();
-    };
-
-    __syncthreads();  // LDS of the previous row tile is no longer read
-    load_a(0);
-    load_w(0, w0);
-    store_a(0);
-    __syncthreads();
-    if constexpr (NSTAGE > 0) {
-#pragma unroll
-      for (int st = 0; st < NSTAGE; st += 2) {
-        stage(st, w0, w1);
-        if (st + 1 < NSTAGE) stage(st + 1, w1, w0);
-      }
-    } else {
-      for (int st = 0; st < nstage; st += 2) {
-        stage(st, w0, w1);
-        if (st + 1 < nstage) stage(st + 1, w1, w0);
-      }
     }
 
     if constexpr (GATEUP) {
@@ -640,12 +643,14 @@ hipError_t launch_decode(const FfnArgs& a, EncIn ain, EncOut hout, hipStream_t s
   switch (nstage) {
     MOE_DECODE_CASE(1) MOE_DECODE_CASE(2) MOE_DECODE_CASE(3) MOE_DECODE_CASE(4)
     MOE_DECODE_CASE(5) MOE_DECODE_CASE(6) MOE_DECODE_CASE(7) MOE_DECODE_CASE(8)
-    MOE_DECODE_CASE(9) MOE_DECODE_CASE(10) MOE_DECODE_CASE(11) MOE_DECODE_CASE(12)
-    default: hipLaunchKernelGGL((grouped_decode<GATEUP, 0>), grid, dim3(256), 0, stream, a, ain, hout);
+    default: return hipErrorInvalidValue;  // callers route K beyond this to the prefill kernel
   }
 #undef MOE_DECODE_CASE
+  static_assert(kDecMaxStages == 8, "keep the cases above in step with kDecMaxStages");
   return hipGetLastError();
 }
+
+bool decode_fits(int K) { return ((K + 127) / 128 + kDecSS - 1) / kDecSS <= kDecMaxStages; }
 
 // Largest column-fragment count per wave that tiles N exactly (64*q columns per
 // workgroup, q in {3, 2, 1}).
@@ -667,29 +672,41 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   int32_t* tp = reinterpret_cast<int32_t*>(ws + L.tp);
 
   const int nx = a.T * (a.d / 32);
-  hipLaunchKernelGGL(encode_rows, dim3((nx + 255) / 256), dim3(256), 0, stream, a.x, a.T, a.d,
-                     xout.codes, xout.scales);
+  if (nx <= 16384)
+    hipLaunchKernelGGL(encode_rows, dim3((nx + 7) / 8), dim3(256), 0, stream, a.x, a.T, a.d,
+                       xout.codes, xout.scales);
+  else
+    hipLaunchKernelGGL(encode_rows_thread, dim3((nx + 255) / 256), dim3(256), 0, stream, a.x, a.T,
+                       a.d, xout.codes, xout.scales);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  if (a.T <= kDecodeMaxT) {
-    if ((err = launch_decode<true>(a, xin, hout, stream)) != hipSuccess) return err;
-    return launch_decode<false>(a, hin, hout, stream);
+  // Per GEMM: the weight-streaming decode kernel for few rows per expert and K
+  // it can unroll, the LDS-tiled kernel otherwise (both read/write the same
+  // encoded layouts, so they can be mixed).
+  const bool dec_gu = a.T <= kDecodeMaxT && decode_fits(a.d);
+  const bool dec_dn = a.T <= kDecodeMaxT && decode_fits(a.F);
+  if (!dec_gu || !dec_dn) {
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  switch (pick_q(a.F)) {
-    case 3: err = launch_prefill<6, true>(a, xin, hout, tp, stream); break;
-    case 2: err = launch_prefill<4, true>(a, xin, hout, tp, stream); break;
-    default: err = launch_prefill<2, true>(a, xin, hout, tp, stream); break;
+  if (dec_gu) {
+    err = launch_decode<true>(a, xin, hout, stream);
+  } else {
+    switch (pick_q(a.F)) {
+      case 3: err = launch_prefill<6, true>(a, xin, hout, tp, stream); break;
+      case 2: err = launch_prefill<4, true>(a, xin, hout, tp, stream); break;
+      default: err = launch_prefill<2, true>(a, xin, hout, tp, stream); break;
+    }
   }
   if (err != hipSuccess) return err;
+  if (dec_dn) return launch_decode<false>(a, hin, hout, stream);
   switch (pick_q(a.d)) {
     case 3: return launch_prefill<3, false>(a, hin, hout, tp, stream);
     case 2: return launch_prefill<2, false>(a, hin, hout, tp, stream);
     default: return launch_prefill<1, false>(a, hin, hout, tp, stream);
   }
 }
+
 
 }  // namespace moe

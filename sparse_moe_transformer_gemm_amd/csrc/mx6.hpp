@@ -219,20 +219,24 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
-  const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+// `off` is the per-lane byte offset (VGPR), `soff` an optional wave-uniform one
+// (SGPR); a lane whose `off` is kOutOfRange reads zero.
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
   return make_uint4(t[0], t[1], t[2], t[3]);
 }
-__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
 }
-__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
 }
-__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, 0);
 }
-constexpr uint32_t kOutOfRange = 0x80000000u;  // every resource here is < 2 GiB
+// Every resource here is < 1 GiB and every uniform offset < 1 GiB, so a lane
+// offset of 2^31 stays out of range whatever uniform offset is added to it.
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // D += A(FP6 E2M3, scale byte OPA of sa) x B(FP4 E2M1, scale byte 0 of sb).
 template <int OPA>

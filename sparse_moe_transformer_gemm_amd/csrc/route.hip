@@ -8,7 +8,8 @@
 // except where two logits differ by less than ~1e-12 relative, and the fixed
 // summation order makes it deterministic.
 //
-// Three kernels:
+// Few tokens (T <= 64): route_partial_small + route_select (below). Otherwise
+// three kernels:
 //   route_widen   W_r (fp32 [d][E]) -> float64 [d][Epad] in the workspace
 //                 (Epad = E rounded up to 32, zero padded).
 //   route_logits  grid (256-token blocks, K slices, 32-expert groups). One lane
@@ -222,11 +223,73 @@ __global__ __launch_bounds__(256) void route_select(const double* __restrict__ p
   }
 }
 
+// Few tokens (decode): one workgroup per 64-deep K slice computes every (token,
+// expert) partial dot product of its slice in float64, with the slice of W_r
+// (read once, coalesced) and of x held in LDS; route_select then reduces the
+// d/64 slices in order. No widened copy of W_r is needed.
+constexpr int kSmallT = 64;
+
+__global__ __launch_bounds__(256) void route_partial_small(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ w, int T,
+                                                           int d, int E,
+                                                           double* __restrict__ partial) {
+  __shared__ float ws[64 * kMaxE];      // W_r rows k0..k0+63, all experts (fp32 is exact)
+  __shared__ float xs[kSmallT * 65];    // x[t][k0..k0+63] as fp32 (bf16 is exact in fp32)
+  const int k0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  // all loads of the slice are issued before any is used: W rows k0..k0+63 are
+  // 16*E float4 (E is a multiple of 4 here or handled by the scalar tail),
+  // x[t][k0..k0+63] is 8 uint4 per token
+  const int nw4 = (64 * E) / 4;
+  float4 wv[kMaxE / 16];
+#pragma unroll
+  for (int i = 0; i < kMaxE / 16; ++i) {
+    const int c = tid + 256 * i;
+    wv[i] = c < nw4 ? reinterpret_cast<const float4*>(w + (size_t)k0 * E)[c] : make_float4(0, 0, 0, 0);
+  }
+  uint4 xv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;        // (token, 8-element chunk)
+    const int t = c >> 3, ch = c & 7;
+    xv[i] = t < T ? reinterpret_cast<const uint4*>(x + (size_t)t * d + k0)[ch] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxE / 16; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nw4) reinterpret_cast<float4*>(ws)[c] = wv[i];
+  }
+  for (int i = nw4 * 4 + tid; i < 64 * E; i += 256) ws[i] = w[(size_t)k0 * E + i];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    const int t = c >> 3, ch = c & 7;
+    if (t < T) {
+      const uint32_t u[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        xs[t * 65 + ch * 8 + 2 * h] = bf16_to_f32(u[h] & 0xffffu);
+        xs[t * 65 + ch * 8 + 2 * h + 1] = bf16_to_f32(u[h] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < T * E; p += 256) {
+    const int t = p / E, e = p - t * E;
+    double acc = 0.0;
+#pragma unroll 8
+    for (int kk = 0; kk < 64; ++kk)
+      acc = fma(static_cast<double>(xs[t * 65 + kk]), static_cast<double>(ws[kk * E + e]), acc);
+    partial[((size_t)blockIdx.x * T + t) * E + e] = acc;
+  }
+}
+
 size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
 size_t route_workspace_bytes(int T, int d, int E) {
+  if (T <= kSmallT) return al256((size_t)(d / 64) * T * E * sizeof(double));
   const RoutePlan p = route_plan(T, d, E);
   return al256((size_t)d * p.Epad * sizeof(double)) +
          al256((size_t)p.nslices * T * E * sizeof(double));
@@ -235,6 +298,16 @@ size_t route_workspace_bytes(int T, int d, int E) {
 hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b_router, int T,
                         int d, int E, int k, int32_t* topk_idx, float* topk_w, void* ws,
                         hipStream_t stream) {
+  hipError_t err;
+  if (T <= kSmallT) {
+    double* partial = static_cast<double*>(ws);
+    hipLaunchKernelGGL(route_partial_small, dim3(d / 64), dim3(256), 0, stream, x, w_router, T, d,
+                       E, partial);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(route_select, dim3(T), dim3(256), 0, stream, partial, d / 64, b_router, T,
+                       E, k, topk_idx, topk_w);
+    return hipGetLastError();
+  }
   const RoutePlan p = route_plan(T, d, E);
   double* w64 = static_cast<double*>(ws);
   double* partial = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) +
@@ -242,7 +315,7 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
   const size_t nw = (size_t)d * p.Epad;
   hipLaunchKernelGGL(route_widen, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
                      w_router, d, E, p.Epad, w64);
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_logits, dim3(p.tblocks, p.nslices, p.ngroups), dim3(256), 0, stream, x,
                      w64, T, d, E, p.Epad, p.kslice, partial);
