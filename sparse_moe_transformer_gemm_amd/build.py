@@ -55,7 +55,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # --no-undefined: a kernel whose host stub was not emitted fails here, not at load time
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

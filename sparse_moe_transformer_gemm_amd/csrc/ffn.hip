@@ -11,14 +11,15 @@
 //
 // Two kernel shapes, chosen on the host from T (expert row counts stay on the
 // device):
-//   prefill  128-row x (64*NF)-column output tiles per workgroup, 2x2 wavefronts,
-//            A and B staged through LDS in 64-deep K steps (double buffered, rows
-//            padded so the fragment reads are bank-conflict free). The grid is an
-//            upper bound on the number of (row tile, column tile) pairs; a tile
-//            table built on the device maps a workgroup to its expert, and
-//            surplus workgroups exit. Workgroup ids are remapped so each XCD
-//            (dispatch is round-robin over the 8 XCDs) works on a contiguous
-//            range of tiles, sharing A rows and expert weights in its own L2.
+//   prefill  128 dispatch rows x 64*NF weight rows per workgroup, 2x2 wavefronts,
+//            K in 128-deep stages copied from global memory straight into LDS
+//            (three stages in flight), laid out in MFMA fragment order. The grid
+//            is an upper bound on the number of (row tile, column tile) pairs; a
+//            tile table built on the device maps a workgroup to its expert, and
+//            surplus workgroups exit. Tiles are rastered in groups of a few row
+//            tiles x all column tiles and each XCD (dispatch is round-robin over
+//            the 8 XCDs) takes a contiguous range of them, so resident
+//            workgroups share A rows and expert weights in their L2.
 //   decode   weight streaming for few rows per expert: one workgroup per
 //            (expert, 32 output columns), the four wavefronts split K, stream the
 //            weights straight from HBM into MFMA registers, and reduce their
@@ -29,8 +30,7 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 128;        // rows per prefill tile
-constexpr int kAPitch = 104;    // LDS bytes per A row per K step: 2 blocks x 48 B + 8 pad
-constexpr int kBPitch = 40;     // LDS bytes per B row per K step: 2 blocks x 16 B + 8 pad
+constexpr int kPrefGM = 8;      // row tiles per raster group of the prefill grid
 constexpr int kDecodeMaxT = 64; // decode kernels when T <= this
 
 struct EncIn {
@@ -119,25 +119,65 @@ __device__ __forceinline__ uint2 lds64(const uint8_t* p) {
 
 // ------------------------------------------------------------------ prefill
 
+// One workgroup = 128 dispatch rows x 64*NF weight rows, 2x2 wavefronts; wave
+// (wm, wn) owns rows 64wm..64wm+63 (two 32-row fragments) and NF 32-row weight
+// fragments (for gate/up: NF/2 gate and NF/2 up fragments of the same h-columns,
+// so SwiGLU can be applied to the tile).
+//
+// K advances in 128-deep stages (four 32-element blocks) that are copied from
+// global memory straight into LDS by buffer-to-LDS loads (lane i of a copy
+// writes LDS bytes [16i, 16i+16) for 16-byte copies and the dword 4i for 4- and
+// 2-byte ones, zero-extended), three stages in
+// flight: the copy of stage t+2 is issued when stage t is computed. Each stage
+// is laid out in MFMA fragment order, so every fragment read is one contiguous
+// 16-byte-per-lane LDS read: within a stage, lane half h of a 32x32x64 MFMA
+// takes blocks 2h (first MFMA step) and 2h+1 (second), the same permutation of K
+// for A and B, which makes every lane's share of a stage contiguous in global
+// memory as well. Rows past the tile's count, blocks past K and stages past the
+// end are read as zero through the resource's range check.
 template <int NF, bool GATEUP>
 struct Prefill {
-  static constexpr int BNB = 2 * NF * 32;  // B rows (weight rows) per workgroup
-  static constexpr int A_BYTES = kBM * kAPitch;
-  static constexpr int AS_BYTES = kBM * 4;
-  static constexpr int B_BYTES = BNB * kBPitch;
-  static constexpr int BS_BYTES = BNB * 2;
-  static constexpr int STAGE = A_BYTES + AS_BYTES + B_BYTES + BS_BYTES;
-  static constexpr int NW = GATEUP ? NF / 2 : NF;      // output column frags per wave
-  static constexpr int EP_PITCH = NW * 32 + 4;        // floats
-  static constexpr int EPI = GATEUP ? 4 * 64 * EP_PITCH * 4 : 0;
-  static constexpr int SINK = (2 * STAGE > EPI ? 2 * STAGE : EPI);  // 16-byte dump slot
-  static constexpr int SMEM = SINK + 16;
-  static constexpr int A_CHUNKS = kBM * 6;             // 16-byte chunks per stage
-  static constexpr int A_PER_T = (A_CHUNKS + 255) / 256;
-  static constexpr int B_CHUNKS = BNB * 2;
-  static constexpr int B_PER_T = (B_CHUNKS + 255) / 256;
-  static constexpr int BS_PER_T = (BNB + 255) / 256;
+  static constexpr int BN = 64 * NF;                   // weight rows per workgroup
+  static constexpr int NFR = 2 * NF;                   // 32-row weight fragments
+  static constexpr int MROWS = GATEUP ? BN / 2 : BN;   // output columns per workgroup
+  static constexpr int FM = GATEUP ? NF / 2 : NF;      // fragments per matrix per wave
+  // stage layout in LDS (bytes)
+  static constexpr int A_OFF = 0;                          // [wm][mf][step][lane][48]
+  static constexpr int AS_OFF = A_OFF + 8 * 64 * kEncBytes; // [wm][mf][lane][4]
+  static constexpr int B_OFF = AS_OFF + 4 * 64 * 4;         // [frag][step][lane][16]
+  static constexpr int BS_OFF = B_OFF + NFR * 2 * 64 * 16;  // [frag][lane][4] (2 bytes used)
+  static constexpr int NBS = (NFR + 3) / 4 * 4;             // scale copies, padded to 4 waves
+  static constexpr int STAGE = BS_OFF + NBS * 256;
+  // copies per wave per stage: A codes, A scales, B codes, B scales
+  static constexpr int NA = 24 / 4;
+  static constexpr int NB = NFR * 2 / 4;
+  static constexpr int NBSW = NBS / 4;
+  static constexpr int PER_WAVE = NA + 1 + NB + NBSW;
+  static constexpr int EP_PITCH = 36;                  // floats per row of the SwiGLU staging tile
+  static_assert(!GATEUP || NF % 2 == 0, "gate/up tiles pair gate and up fragments");
+  static_assert(PER_WAVE <= 63, "one stage of copies must fit the vector memory counter");
+  static_assert(3 * STAGE <= 160 * 1024, "three stage buffers must fit the 160 KB of LDS");
+  static_assert(!GATEUP || 2 * 64 * EP_PITCH * 4 <= STAGE, "SwiGLU staging of two waves must fit a stage buffer");
 };
+
+// s_waitcnt with only the vector memory counter bounded (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at max).
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Buffer-to-LDS copy of SIZE bytes per lane (16, 4 or 2) into `lds` (wave-uniform).
+template <int SIZE>
+__device__ __forceinline__ void lds_copy(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  static_assert(SIZE == 16 || SIZE == 4 || SIZE == 2, "copy sizes used here");
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds, 16, voff, soff, 0, 0);
+  else if constexpr (SIZE == 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds, 4, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds, 2, voff, soff, 0, 0);
+}
 
 template <int NF, bool GATEUP>
 __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const EncIn ain,
@@ -145,18 +185,31 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const En
                                                        const int32_t* __restrict__ tile_prefix,
                                                        int ntn) {
   using C = Prefill<NF, GATEUP>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
+  // three stage buffers as separate objects, so the compiler can tell the copy
+  // into one from the reads of another
+  __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[C::STAGE];
 
   const int K = GATEUP ? a.d : a.F;
   const int N = GATEUP ? a.F : a.d;
   const int nblkK = K / 32;
-  const int nsteps = K / 64;
+  const int nsteps = (K + 127) / 128;
   const int E = a.E;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = logical / ntn;
-  const int nt = logical - mt * ntn;
-  if (mt >= tile_prefix[E]) return;
+  // ---- tile of this workgroup. Logical tiles are grouped kPrefGM row tiles x all
+  // column tiles, row tile fastest, so the workgroups resident at one time share
+  // a few row tiles of A and a few column tiles of B in L2; the groups are laid
+  // out contiguously per XCD.
+  const int total_mt = tile_prefix[E];
+  const int G = total_mt * ntn;
+  if ((int)blockIdx.x >= G) return;
+  const int logical = xcd_remap(blockIdx.x, G);
+  const int grp = logical / (kPrefGM * ntn);
+  const int gm = min(kPrefGM, total_mt - grp * kPrefGM);
+  const int r = logical - grp * kPrefGM * ntn;
+  const int nt = r / gm;
+  const int mt = grp * kPrefGM + (r - nt * gm);
   int lo = 0, hi = E;  // tile_prefix[lo] <= mt < tile_prefix[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -166,202 +219,254 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const En
   const int off = a.offsets[e];
   const int cnt = a.offsets[e + 1] - off;
   const int m0 = (mt - tile_prefix[e]) * kBM;
-  const int ncol0 = nt * (C::NW * 64);  // first output column (h column for gate/up)
+  const int rows_valid = min(kBM, cnt - m0);
+  const int col0 = nt * C::MROWS;  // first output column of each matrix in this tile
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 31, half = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // ---- per-thread global sources (fixed across K steps). Every load is
-  // unconditional: rows past the expert's count read its last row (results
-  // discarded), chunk indices past the tile are clamped and their LDS stores go
-  // to a sink slot, so the compiler can keep the prefetch in flight.
-  const int rows_valid = min(kBM, cnt - m0);
-  const uint8_t* a_src[C::A_PER_T];
-  int a_lds[C::A_PER_T];
-#pragma unroll
-  for (int i = 0; i < C::A_PER_T; ++i) {
-    const int c = min(tid + 256 * i, C::A_CHUNKS - 1);
-    const int row = c / 6, part = c - row * 6;
-    a_lds[i] = tid + 256 * i < C::A_CHUNKS ? row * kAPitch + part * 16 : C::SINK;
-    const int p = off + m0 + min(row, rows_valid - 1);
-    const int src = GATEUP ? a.sorted_pair[p] / a.k : p;
-    a_src[i] = ain.codes + (size_t)src * nblkK * kEncBytes + part * 16;
-  }
-  const uint16_t* as_src;
-  {
-    const int p = off + m0 + min(tid & (kBM - 1), rows_valid - 1);
-    const int src = GATEUP ? a.sorted_pair[p] / a.k : p;
-    as_src = ain.scales + (size_t)src * nblkK;
-  }
-  auto b_row = [&](int brow, const uint8_t*& codes, const uint8_t*& scales) {
-    int n;
+  // ---- resources
+  const uint32_t arow_bytes = (uint32_t)nblkK * kEncBytes;
+  const rsrc_t ar = GATEUP ? make_rsrc(ain.codes, (uint32_t)a.T * arow_bytes)
+                           : make_rsrc(ain.codes + (size_t)(off + m0) * arow_bytes,
+                                       (uint32_t)rows_valid * arow_bytes);
+  const rsrc_t asr = GATEUP ? make_rsrc(ain.scales, (uint32_t)a.T * nblkK * 2)
+                            : make_rsrc(ain.scales + (size_t)(off + m0) * nblkK,
+                                        (uint32_t)rows_valid * nblkK * 2);
+  // token of a dispatch pair q = t*k + j: t = floor(q * M / 2^32) with
+  // M = floor((2^32 - 1) / k) + 1, exact for q < 2^32 / k (here q < 2^19)
+  const uint32_t kmagic = 0xFFFFFFFFu / (uint32_t)a.k + 1u;
+  const rsrc_t br0 = make_rsrc((GATEUP ? a.wg_codes : a.wd_codes) + (size_t)e * N * (K / 2),
+                               (uint32_t)N * (K / 2));
+  const rsrc_t bsr0 = make_rsrc((GATEUP ? a.wg_scales : a.wd_scales) + (size_t)e * N * nblkK,
+                                (uint32_t)N * nblkK);
+  const rsrc_t br1 = GATEUP ? make_rsrc(a.wu_codes + (size_t)e * N * (K / 2), (uint32_t)N * (K / 2)) : br0;
+  const rsrc_t bsr1 = GATEUP ? make_rsrc(a.wu_scales + (size_t)e * N * nblkK, (uint32_t)N * nblkK) : bsr0;
+  // weight row of lane c (0..31) of B fragment phi, and whether phi is an up fragment
+  auto frag_up = [&](int phi) { return GATEUP && (phi % NF) >= NF / 2; };
+  auto frag_row = [&](int phi, int c) -> int {
     if (GATEUP) {
-      const int w = brow / (NF * 32), f = (brow / 32) % NF, cc = brow & 31;
-      const bool up = f >= C::NW;
-      n = ncol0 + w * C::NW * 32 + (up ? f - C::NW : f) * 32 + cc;
-      codes = up ? a.wu_codes : a.wg_codes;
-      scales = up ? a.wu_scales : a.wg_scales;
-    } else {
-      n = ncol0 + brow;
-      codes = a.wd_codes;
-      scales = a.wd_scales;
+      const int w = phi / NF, f = phi % NF;
+      return col0 + w * C::FM * 32 + (f < NF / 2 ? f : f - NF / 2) * 32 + c;
     }
-    codes += ((size_t)e * N + n) * (K / 2);
-    scales += ((size_t)e * N + n) * nblkK;
-  };
-  const uint8_t* b_src[C::B_PER_T];
-  int b_lds[C::B_PER_T];
-#pragma unroll
-  for (int i = 0; i < C::B_PER_T; ++i) {
-    const int c = min(tid + 256 * i, C::B_CHUNKS - 1);
-    const uint8_t* sc;
-    b_row(c >> 1, b_src[i], sc);
-    b_src[i] += (c & 1) * 16;
-    b_lds[i] = tid + 256 * i < C::B_CHUNKS ? C::A_BYTES + C::AS_BYTES + (c >> 1) * kBPitch + (c & 1) * 16
-                                           : C::SINK;
-  }
-  const uint8_t* bs_src[C::BS_PER_T];
-  int bs_lds[C::BS_PER_T];
-#pragma unroll
-  for (int i = 0; i < C::BS_PER_T; ++i) {
-    const int brow = min(tid + 256 * i, C::BNB - 1);
-    const uint8_t* co;
-    b_row(brow, co, bs_src[i]);
-    bs_lds[i] = tid + 256 * i < C::BNB ? C::A_BYTES + C::AS_BYTES + C::B_BYTES + brow * 2 : C::SINK;
-  }
-
-  uint4 ra[C::A_PER_T], rb[C::B_PER_T];
-  uint32_t ras = 0;
-  uint16_t rbs[C::BS_PER_T];
-
-  auto load_stage = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + s * 96);
-    ras = *reinterpret_cast<const uint32_t*>(as_src + 2 * s);
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + s * 32);
-#pragma unroll
-    for (int i = 0; i < C::BS_PER_T; ++i) rbs[i] = *reinterpret_cast<const uint16_t*>(bs_src[i] + 2 * s);
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t* st = smem + buf * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-      uint2* d = reinterpret_cast<uint2*>(a_lds[i] == C::SINK ? smem + C::SINK : st + a_lds[i]);
-      d[0] = make_uint2(ra[i].x, ra[i].y);
-      d[1] = make_uint2(ra[i].z, ra[i].w);
-    }
-    if (tid < kBM) reinterpret_cast<uint32_t*>(st + C::A_BYTES)[tid] = ras;
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-      uint2* d = reinterpret_cast<uint2*>(b_lds[i] == C::SINK ? smem + C::SINK : st + b_lds[i]);
-      d[0] = make_uint2(rb[i].x, rb[i].y);
-      d[1] = make_uint2(rb[i].z, rb[i].w);
-    }
-#pragma unroll
-    for (int i = 0; i < C::BS_PER_T; ++i)
-      *reinterpret_cast<uint16_t*>(bs_lds[i] == C::SINK ? smem + C::SINK : st + bs_lds[i]) = rbs[i];
+    return col0 + phi * 32 + c;
   };
 
-  // ---- accumulators start at the bias of their output column
-  v16f acc[2][NF];
+  // ---- biases of this lane's output columns, loaded together with the dispatch
+  // entries below and before the first copies (waiting for them must not wait
+  // for the copies)
+  float bias[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    float b;
-    if (GATEUP) {
-      const bool up = f >= C::NW;
-      const int col = ncol0 + wn * C::NW * 32 + (up ? f - C::NW : f) * 32 + lr;
-      b = bf16_to_f32((up ? a.b_up : a.b_gate)[(size_t)e * N + col]);
-    } else {
-      b = bf16_to_f32(a.b_down[(size_t)e * N + ncol0 + wn * NF * 32 + f * 32 + lr]);
-    }
-#pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mf][f][i] = b;
+    const int phi = wn * NF + f;
+    const uint16_t* bsrc = GATEUP ? (frag_up(phi) ? a.b_up : a.b_gate) : a.b_down;
+    bias[f] = bf16_to_f32(bsrc[(size_t)e * N + frag_row(phi, lr)]);
   }
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
+  // ---- per-lane source offsets of this wave's copies (fixed across stages; the
+  // stage's K distance goes into the uniform offset). The dispatch entries of
+  // the rows are all loaded first (rows past the count read the last row), so
+  // their latencies overlap.
+  int a_rowi[C::NA];
+  uint32_t a_src[C::NA + 1];
+#pragma unroll
+  for (int t = 0; t < C::NA; ++t) {
+    const int q = (wave + 4 * t) * 64 + lane;          // 16-byte slot in the A region
+    const int g = q / 384, rem = q - g * 384;          // g = wm*2 + mf
+    const int l = (rem - (rem / 192) * 192) / 3;
+    a_rowi[t] = (g >> 1) * 64 + (g & 1) * 32 + (l & 31);
+  }
+  const int as_rowi = (wave >> 1) * 64 + (wave & 1) * 32 + lr;
+  if (GATEUP) {
+#pragma unroll
+    for (int t = 0; t <= C::NA; ++t) {
+      const int row = t < C::NA ? a_rowi[t] : as_rowi;
+      a_src[t] = (uint32_t)a.sorted_pair[off + m0 + min(row, rows_valid - 1)];
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int t = 0; t <= C::NA; ++t) a_src[t] = __umulhi(a_src[t], kmagic);
+  } else {
+#pragma unroll
+    for (int t = 0; t <= C::NA; ++t) a_src[t] = (uint32_t)(t < C::NA ? a_rowi[t] : as_rowi);
+  }
+  uint32_t a_off[C::NA];
+  int a_blk[C::NA];
+#pragma unroll
+  for (int t = 0; t < C::NA; ++t) {
+    const int q = (wave + 4 * t) * 64 + lane;
+    const int rem = q - (q / 384) * 384;
+    const int s = rem / 192, rem2 = rem - s * 192;
+    const int l = rem2 / 3, j = rem2 - l * 3;
+    a_blk[t] = 2 * (l >> 5) + s;
+    a_off[t] = a_rowi[t] < rows_valid ? a_src[t] * arow_bytes + a_blk[t] * kEncBytes + j * 16 : kOutOfRange;
+  }
+  const int as_blk = 2 * half;
+  const uint32_t as_off = as_rowi < rows_valid ? a_src[C::NA] * (nblkK * 2) + as_blk * 2 : kOutOfRange;
+  uint32_t b_off[C::NB];
+  int b_blk[C::NB];
+#pragma unroll
+  for (int t = 0; t < C::NB; ++t) {
+    const int i = wave + 4 * t, phi = i >> 1, s = i & 1;
+    b_blk[t] = 2 * half + s;
+    b_off[t] = (uint32_t)frag_row(phi, lr) * (K / 2) + b_blk[t] * 16;
+  }
+  uint32_t bs_off[C::NBSW];
+#pragma unroll
+  for (int t = 0; t < C::NBSW; ++t) {
+    const int phi = wave + 4 * t;
+    bs_off[t] = phi < C::NFR ? (uint32_t)frag_row(phi, lr) * nblkK + 2 * half : kOutOfRange;
+  }
 
-  for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) load_stage(s + 1);
-    const uint8_t* st = smem + (s & 1) * C::STAGE;
-    v8i ahi[2], alo[2];
+  // Copy stage st into LDS buffer `buf`.
+  auto issue = [&](int st, uint8_t* buf) {
+    const int kb = __builtin_amdgcn_readfirstlane(4 * st);
+#pragma unroll
+    for (int t = 0; t < C::NA; ++t)
+      lds_copy<16>(ar, buf + C::A_OFF + (wave + 4 * t) * 1024,
+                   kb + a_blk[t] < nblkK ? a_off[t] : kOutOfRange, kb * kEncBytes);
+    lds_copy<4>(asr, buf + C::AS_OFF + wave * 256, kb + as_blk < nblkK ? as_off : kOutOfRange, kb * 2);
+#pragma unroll
+    for (int t = 0; t < C::NB; ++t) {
+      const int i = wave + 4 * t;
+      lds_copy<16>(frag_up(i >> 1) ? br1 : br0, buf + C::B_OFF + i * 1024,
+                   kb + b_blk[t] < nblkK ? b_off[t] : kOutOfRange, kb * 16);
+    }
+#pragma unroll
+    for (int t = 0; t < C::NBSW; ++t) {
+      const int phi = wave + 4 * t;
+      lds_copy<2>(frag_up(phi) ? bsr1 : bsr0, buf + C::BS_OFF + phi * 256,
+                  kb + 2 * half < nblkK ? bs_off[t] : kOutOfRange, kb);
+    }
+  };
+
+  v16f acc[2][NF];
+
+  // Compute one stage out of LDS buffer `buf`: both MFMA steps' fragments are
+  // read first, then 2 x 2 x NF x 2 scaled MFMAs (hi and lo terms of A).
+  auto compute = [&](const uint8_t* buf, int st) {
+    // Padding stages past K compute nothing. A half stage at the end of K (K % 128
+    // == 64) still takes both MFMA steps: each holds one valid block (block 2h+s
+    // of lane half h) and one zero block.
+    if (4 * st >= nblkK) return;
+    v8i ahi[2][2], alo[2][2];
     int sa[2];
 #pragma unroll
     for (int mf = 0; mf < 2; ++mf) {
-      const int row = wm * 64 + mf * 32 + lr;
-      const uint8_t* p = st + row * kAPitch + half * 48;
-      const uint2 h0 = lds64(p), h1 = lds64(p + 8), h2 = lds64(p + 16);
-      const uint2 l0 = lds64(p + 24), l1 = lds64(p + 32), l2 = lds64(p + 40);
-      ahi[mf] = v8i{(int)h0.x, (int)h0.y, (int)h1.x, (int)h1.y, (int)h2.x, (int)h2.y, 0, 0};
-      alo[mf] = v8i{(int)l0.x, (int)l0.y, (int)l1.x, (int)l1.y, (int)l2.x, (int)l2.y, 0, 0};
-      sa[mf] = *reinterpret_cast<const uint16_t*>(st + C::A_BYTES + row * 4 + half * 2);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint4* p = reinterpret_cast<const uint4*>(
+            buf + C::A_OFF + ((wm * 2 + mf) * 2 + s) * 64 * kEncBytes + lane * kEncBytes);
+        const uint4 q0 = p[0], q1 = p[1], q2 = p[2];
+        ahi[mf][s] = v8i{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, 0, 0};
+        alo[mf][s] = v8i{(int)q1.z, (int)q1.w, (int)q2.x, (int)q2.y, (int)q2.z, (int)q2.w, 0, 0};
+      }
+      sa[mf] = reinterpret_cast<const int*>(buf + C::AS_OFF + (wm * 2 + mf) * 256)[lane];
     }
-    const uint8_t* bst = st + C::A_BYTES + C::AS_BYTES;
-    v8i b[NF];
-    int sb[NF];
+    v8i bf[NF][2];
+    int sbs[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const int brow = wn * NF * 32 + f * 32 + lr;
-      const uint8_t* q = bst + brow * kBPitch + half * 16;
-      const uint2 b0 = lds64(q), b1 = lds64(q + 8);
-      b[f] = v8i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y, 0, 0, 0, 0};
-      sb[f] = bst[C::B_BYTES + brow * 2 + half];
+      const int phi = wn * NF + f;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint4 q = reinterpret_cast<const uint4*>(buf + C::B_OFF + (phi * 2 + s) * 1024)[lane];
+        bf[f][s] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      }
+      sbs[f] = reinterpret_cast<const int*>(buf + C::BS_OFF + phi * 256)[lane];
     }
+    // step 0: scale bytes 0 (A hi), 1 (A lo), 0 (B); step 1: bytes 2, 3, 1
 #pragma unroll
     for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) acc[mf][f] = mfma_f6f4<0>(ahi[mf], b[f], acc[mf][f], sa[mf], sb[f]);
+      for (int f = 0; f < NF; ++f) {
+        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ahi[mf][0], bf[f][0], acc[mf][f], 2, 4,
+                                                                    0, sa[mf], 0, sbs[f]);
+        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo[mf][0], bf[f][0], acc[mf][f], 2, 4,
+                                                                    1, sa[mf], 0, sbs[f]);
+      }
 #pragma unroll
     for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) acc[mf][f] = mfma_f6f4<1>(alo[mf], b[f], acc[mf][f], sa[mf], sb[f]);
-    if (s + 1 < nsteps) store_stage((s + 1) & 1);
-    __syncthreads();
+      for (int f = 0; f < NF; ++f) {
+        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ahi[mf][1], bf[f][1], acc[mf][f], 2, 4,
+                                                                    2, sa[mf], 1, sbs[f]);
+        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo[mf][1], bf[f][1], acc[mf][f], 2, 4,
+                                                                    3, sa[mf], 1, sbs[f]);
+      }
+  };
+
+  // One step: wait for this wave's copies of stage st (the next stage's copies
+  // stay in flight), barrier (everyone's copies of st have landed and everyone
+  // has finished reading the buffer that the copy issued next overwrites),
+  // copy stage st+2, compute stage st.
+  auto step = [&](int st, const uint8_t* cur, uint8_t* nxt2) {
+    MOE_WAIT_VMCNT(C::PER_WAVE);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS access moves across the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    issue(st + 2, nxt2);
+    compute(cur, st);
+  };
+
+  // ---- accumulators start at the bias of their output column
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mf][f][i] = bias[f];
+  __builtin_amdgcn_sched_barrier(0);
+
+  issue(0, st0);
+  issue(1, st1);
+  // Steps go in threes (one per buffer); stages past the end copy zeros and
+  // compute nothing.
+  for (int t = 0; t < nsteps; t += 3) {
+    step(t, st0, st2);
+    step(t + 1, st1, st0);
+    step(t + 2, st2, st1);
   }
+  MOE_WAIT_VMCNT(0);
+  __syncthreads();
 
   if constexpr (GATEUP) {
-    // h = silu(g) * u into LDS (the staging buffers are free after the last sync),
-    // then one lane per row encodes its 32-column blocks as two-term MXFP6.
-    float* ep = reinterpret_cast<float*>(smem) + wave * 64 * C::EP_PITCH;
+    // h = silu(g) * u; per gate fragment f, the wave's two 32x32 tiles go to
+    // LDS as 64 rows x 32 columns and each lane encodes one row's 32-column
+    // block as two-term MXFP6.
+    float* ep = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 64 * C::EP_PITCH;
+    const int nblkF = a.F / 32;
+    const int grow = m0 + wm * 64 + lane;
 #pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
+    for (int f = 0; f < C::FM; ++f) {
 #pragma unroll
-      for (int f = 0; f < C::NW; ++f)
+      for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          ep[r * C::EP_PITCH + f * 32 + lr] = silu_mul(acc[mf][f][i], acc[mf][f + C::NW][i]);
+          const int rr = mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const float g = acc[mf][f][i], u = acc[mf][f + C::FM][i];
+          ep[rr * C::EP_PITCH + lr] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
         }
-    __syncthreads();
-    const int grow = m0 + wm * 64 + lane;
-    if (grow < cnt) {
-      const int p = off + grow;
-      const int nblkF = a.F / 32;
+      __builtin_amdgcn_wave_barrier();
+      float v[32];
+      const float4* src = reinterpret_cast<const float4*>(ep + lane * C::EP_PITCH);
 #pragma unroll
-      for (int f = 0; f < C::NW; ++f) {
-        float v[32];
-        const float4* src = reinterpret_cast<const float4*>(ep + lane * C::EP_PITCH + f * 32);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 t = src[q];
-          v[4 * q] = t.x;
-          v[4 * q + 1] = t.y;
-          v[4 * q + 2] = t.z;
-          v[4 * q + 3] = t.w;
-        }
-        uint32_t hw[6], lw[6], sc;
-        encode_block(v, hw, lw, sc);
-        const int blk = (ncol0 + wn * C::NW * 32 + f * 32) / 32;
-        uint4* dst = reinterpret_cast<uint4*>(hout.codes + ((size_t)p * nblkF + blk) * kEncBytes);
-        dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        dst[1] = make_uint4(hw[4], hw[5], lw[0], lw[1]);
-        dst[2] = make_uint4(lw[2], lw[3], lw[4], lw[5]);
-        hout.scales[(size_t)p * nblkF + blk] = static_cast<uint16_t>(sc);
+      for (int q = 0; q < 8; ++q) {
+        const float4 t4 = src[q];
+        v[4 * q] = t4.x;
+        v[4 * q + 1] = t4.y;
+        v[4 * q + 2] = t4.z;
+        v[4 * q + 3] = t4.w;
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t hw[6], lw[6], sc;
+      encode_block(v, hw, lw, sc);
+      if (grow < cnt) {
+        const size_t rec = (size_t)(off + grow) * nblkF + (col0 + wn * C::FM * 32 + f * 32) / 32;
+        store_enc(hout.codes + rec * kEncBytes, hw, lw);
+        hout.scales[rec] = static_cast<uint16_t>(sc);
       }
     }
   } else {
@@ -369,9 +474,9 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const En
     for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = m0 + wm * 64 + mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (r < cnt) {
-          float* yr = a.y_sorted + (size_t)(off + r) * N + ncol0 + wn * NF * 32 + lr;
+        const int rr = wm * 64 + mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (rr < rows_valid) {
+          float* yr = a.y_sorted + (size_t)(off + m0 + rr) * N + col0 + wn * NF * 32 + lr;
 #pragma unroll
           for (int f = 0; f < NF; ++f) yr[f * 32] = acc[mf][f][i];
         }
@@ -623,7 +728,7 @@ template <int NF, bool GATEUP>
 hipError_t launch_prefill(const FfnArgs& a, EncIn ain, EncOut hout, const int32_t* tp,
                           hipStream_t stream) {
   const int N = GATEUP ? a.F : a.d;
-  const int ntn = N / (Prefill<NF, GATEUP>::NW * 64);
+  const int ntn = N / Prefill<NF, GATEUP>::MROWS;
   const int P = a.T * a.k;
   const int mt_max = (P + kBM - 1) / kBM + (a.E < P ? a.E : P);
   const long long grid = (long long)mt_max * ntn;
@@ -651,10 +756,6 @@ hipError_t launch_decode(const FfnArgs& a, EncIn ain, EncOut hout, hipStream_t s
 }
 
 bool decode_fits(int K) { return ((K + 127) / 128 + kDecSS - 1) / kDecSS <= kDecMaxStages; }
-
-// Largest column-fragment count per wave that tiles N exactly (64*q columns per
-// workgroup, q in {3, 2, 1}).
-int pick_q(int N) { return N % 192 == 0 ? 3 : (N % 128 == 0 ? 2 : 1); }
 
 }  // namespace
 
@@ -690,22 +791,23 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  // Column tiles: the widest that divides N (gate/up: 32*NF h-columns, down:
+  // 64*NF output columns per workgroup).
   if (dec_gu) {
     err = launch_decode<true>(a, xin, hout, stream);
+  } else if (a.F % 192 == 0) {
+    err = launch_prefill<6, true>(a, xin, hout, tp, stream);
+  } else if (a.F % 128 == 0) {
+    err = launch_prefill<4, true>(a, xin, hout, tp, stream);
   } else {
-    switch (pick_q(a.F)) {
-      case 3: err = launch_prefill<6, true>(a, xin, hout, tp, stream); break;
-      case 2: err = launch_prefill<4, true>(a, xin, hout, tp, stream); break;
-      default: err = launch_prefill<2, true>(a, xin, hout, tp, stream); break;
-    }
+    err = launch_prefill<2, true>(a, xin, hout, tp, stream);
   }
   if (err != hipSuccess) return err;
   if (dec_dn) return launch_decode<false>(a, hin, hout, stream);
-  switch (pick_q(a.d)) {
-    case 3: return launch_prefill<3, false>(a, hin, hout, tp, stream);
-    case 2: return launch_prefill<2, false>(a, hin, hout, tp, stream);
-    default: return launch_prefill<1, false>(a, hin, hout, tp, stream);
-  }
+  if (a.d % 320 == 0) return launch_prefill<5, false>(a, hin, hout, tp, stream);
+  if (a.d % 192 == 0) return launch_prefill<3, false>(a, hin, hout, tp, stream);
+  if (a.d % 128 == 0) return launch_prefill<2, false>(a, hin, hout, tp, stream);
+  return launch_prefill<1, false>(a, hin, hout, tp, stream);
 }
 
 

@@ -75,37 +75,52 @@ __device__ __forceinline__ void pack6(const uint32_t (&c)[32], uint32_t (&w)[6])
   }
 }
 
-// Encode one block of 32 floats into two E2M3 terms (codes) and their scales.
+// Block exponent of a two-term block: floor(log2 amax) - 2 puts the largest
+// magnitude in [4, 8) of the E2M3 range; blocks whose maximum is below 2^-124
+// (zero blocks included) get the smallest normal scale 2^-126.
+__device__ __forceinline__ int block_exp(float amax) {
+  const int s = ilog2f(amax) - 2;
+  return s < -126 ? -126 : s;
+}
+
+typedef uint32_t v6u __attribute__((ext_vector_type(6)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+
+// Encode one block of 32 floats into two E2M3 terms (codes) and their scales,
+// with the gfx950 scaled conversions: V_CVT_SCALEF32_2XPK16_FP6_F32 divides by
+// the scale, rounds to nearest even and saturates at 7.5, packing its first
+// operand into the even and its second into the odd element positions;
+// V_CVT_SCALEF32_PK32_F32_FP6 decodes the 32 codes back (times the scale), so
+// the residual v - hi is exact.
 __device__ __forceinline__ void encode_block(const float (&v)[32], uint32_t (&hi)[6],
                                              uint32_t (&lo)[6], uint32_t& scales) {
   float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  int s1 = amax > 0.f ? ilog2f(amax) - 2 : -127;
-  s1 = s1 < -127 ? -127 : s1;
-  const float inv1 = pow2i(-s1 > 127 ? 127 : -s1), sc1 = pow2i(s1);
-  uint32_t c[32];
-  float r[32];
+  const int s1 = block_exp(amax);
+  const float sc1 = pow2i(s1);
+  v16f ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = v[2 * i];
+    od[i] = v[2 * i + 1];
+  }
+  const v6u h = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, sc1);
+  const v32f back = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(h, sc1);
   float ramax = 0.f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t m = e2m3_code(fabsf(v[j]) * inv1);
-    const uint32_t sign = __float_as_uint(v[j]) >> 31;
-    c[j] = (sign << 5) | m;
-    const float back = e2m3_value(m) * sc1;
-    r[j] = v[j] - (sign ? -back : back);
-    ramax = fmaxf(ramax, fabsf(r[j]));
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = v[2 * i] - back[2 * i];
+    od[i] = v[2 * i + 1] - back[2 * i + 1];
+    ramax = fmaxf(ramax, fmaxf(fabsf(ev[i]), fabsf(od[i])));
   }
-  pack6(c, hi);
-  int s2 = ramax > 0.f ? ilog2f(ramax) - 2 : -127;
-  s2 = s2 < -127 ? -127 : s2;
-  const float inv2 = pow2i(-s2 > 127 ? 127 : -s2);
+  const int s2 = block_exp(ramax);
+  const v6u l = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, pow2i(s2));
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t m = e2m3_code(fabsf(r[j]) * inv2);
-    c[j] = ((__float_as_uint(r[j]) >> 31) << 5) | m;
+  for (int i = 0; i < 6; ++i) {
+    hi[i] = h[i];
+    lo[i] = l[i];
   }
-  pack6(c, lo);
   scales = static_cast<uint32_t>(s1 + 127) | (static_cast<uint32_t>(s2 + 127) << 8);
 }
 
@@ -117,9 +132,8 @@ __device__ __forceinline__ void encode_block_mem(float* v, uint32_t (&hi)[6], ui
   float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  int s1 = amax > 0.f ? ilog2f(amax) - 2 : -127;
-  s1 = s1 < -127 ? -127 : s1;
-  const float inv1 = pow2i(-s1 > 127 ? 127 : -s1), sc1 = pow2i(s1);
+  const int s1 = block_exp(amax);
+  const float inv1 = pow2i(-s1), sc1 = pow2i(s1);
 #pragma unroll
   for (int i = 0; i < 6; ++i) hi[i] = lo[i] = 0u;
   float ramax = 0.f;
@@ -137,9 +151,8 @@ __device__ __forceinline__ void encode_block_mem(float* v, uint32_t (&hi)[6], ui
     v[j] = r;
     ramax = fmaxf(ramax, fabsf(r));
   }
-  int s2 = ramax > 0.f ? ilog2f(ramax) - 2 : -127;
-  s2 = s2 < -127 ? -127 : s2;
-  const float inv2 = pow2i(-s2 > 127 ? 127 : -s2);
+  const int s2 = block_exp(ramax);
+  const float inv2 = pow2i(-s2);
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
     const float r = v[j];
@@ -164,18 +177,16 @@ __device__ __forceinline__ void encode_group32(float v, uint8_t* scratch, uint8_
   float amax = fabsf(v);
 #pragma unroll
   for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  int s1 = amax > 0.f ? ilog2f(amax) - 2 : -127;
-  s1 = s1 < -127 ? -127 : s1;
-  const uint32_t m1 = e2m3_code(fabsf(v) * pow2i(-s1 > 127 ? 127 : -s1));
+  const int s1 = block_exp(amax);
+  const uint32_t m1 = e2m3_code(fabsf(v) * pow2i(-s1));
   const uint32_t sign1 = __float_as_uint(v) >> 31;
   const float back = e2m3_value(m1) * pow2i(s1);
   const float r = v - (sign1 ? -back : back);
   float ramax = fabsf(r);
 #pragma unroll
   for (int o = 16; o >= 1; o >>= 1) ramax = fmaxf(ramax, __shfl_xor(ramax, o));
-  int s2 = ramax > 0.f ? ilog2f(ramax) - 2 : -127;
-  s2 = s2 < -127 ? -127 : s2;
-  const uint32_t m2 = e2m3_code(fabsf(r) * pow2i(-s2 > 127 ? 127 : -s2));
+  const int s2 = block_exp(ramax);
+  const uint32_t m2 = e2m3_code(fabsf(r) * pow2i(-s2));
   scratch[j] = static_cast<uint8_t>((sign1 << 5) | m1);
   scratch[32 + j] = static_cast<uint8_t>(((__float_as_uint(r) >> 31) << 5) | m2);
   __syncthreads();
