@@ -106,6 +106,13 @@ __global__ __launch_bounds__(256) void tile_prefix_kernel(const int32_t* __restr
   if (t == 0) tp[0] = 0;
 }
 
+// Division by a runtime divisor d >= 1 as a multiply: x / d = (x * m) >> 32 with
+// m = ceil(2^32 / d), exact for x < 2^32 / d (here x < 2^20).
+__device__ __forceinline__ uint64_t div_magic(uint32_t d) { return ((1ull << 32) + d - 1) / d; }
+__device__ __forceinline__ uint32_t div_by(uint32_t x, uint64_t m) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(x) * m) >> 32);
+}
+
 // Workgroup id -> logical tile such that XCD x (ids = x mod 8) owns the
 // contiguous logical range [x*G/8, (x+1)*G/8) (a bijection on [0, G)).
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
@@ -235,9 +242,7 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const En
   const rsrc_t asr = GATEUP ? make_rsrc(ain.scales, (uint32_t)a.T * nblkK * 2)
                             : make_rsrc(ain.scales + (size_t)(off + m0) * nblkK,
                                         (uint32_t)rows_valid * nblkK * 2);
-  // token of a dispatch pair q = t*k + j: t = floor(q * M / 2^32) with
-  // M = floor((2^32 - 1) / k) + 1, exact for q < 2^32 / k (here q < 2^19)
-  const uint32_t kmagic = 0xFFFFFFFFu / (uint32_t)a.k + 1u;
+  const uint64_t kmagic = div_magic((uint32_t)a.k);  // token of dispatch pair q: q / k
   const rsrc_t br0 = make_rsrc((GATEUP ? a.wg_codes : a.wd_codes) + (size_t)e * N * (K / 2),
                                (uint32_t)N * (K / 2));
   const rsrc_t bsr0 = make_rsrc((GATEUP ? a.wg_scales : a.wd_scales) + (size_t)e * N * nblkK,
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const En
     }
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int t = 0; t <= C::NA; ++t) a_src[t] = __umulhi(a_src[t], kmagic);
+    for (int t = 0; t <= C::NA; ++t) a_src[t] = div_by(a_src[t], kmagic);
   } else {
 #pragma unroll
     for (int t = 0; t <= C::NA; ++t) a_src[t] = (uint32_t)(t < C::NA ? a_rowi[t] : as_rowi);
@@ -511,35 +516,43 @@ constexpr int kDecSS = 4;                  // 128-deep K steps per stage
 constexpr int kDecPF = 2;                  // stages of loads in flight ahead of the one computed
 constexpr int kDecMaxStages = 8;           // decode kernels cover K <= kDecMaxStages * kDecSS * 128
 constexpr int kDecWB = 4 * kDecSS;         // 32-element blocks per K window
+constexpr int kDecMaxBlk = kDecMaxStages * kDecWB;  // 32-element blocks of the longest K
 constexpr int kDecAPitch = kDecWB * kEncBytes + 8;  // LDS bytes per activation row (padded)
 constexpr int kDecAChunks = 16 * kDecWB * 3;        // 16-byte chunks of the activation window
 constexpr int kDecAPerT = kDecAChunks / 256;        // ... per thread
-constexpr int kDecASPerT = 16 * kDecWB / 256;       // activation scale entries per thread
-constexpr int kDecBSPerT = 64 * kDecWB / 256;       // weight scale bytes per thread
+constexpr int kDecBSPitch = kDecMaxBlk + 4;         // LDS bytes per weight-scale row (odd dword count)
+constexpr int kDecASPitch = kDecMaxBlk + 2;         // LDS uint16 per activation-scale row (odd dword count)
+constexpr int kDecBSLoads = 64 * kDecMaxBlk / 2 / 256;  // uint16 weight-scale loads per thread (max)
 static_assert(kDecSS % 4 == 0, "the window staging splits evenly over 256 threads");
-static_assert(kDecAChunks % 256 == 0 && (16 * kDecWB) % 256 == 0 && (64 * kDecWB) % 256 == 0,
-              "window staging must divide evenly");
+static_assert(kDecAChunks % 256 == 0, "window staging must divide evenly");
 
 // Gate/up: waves 0,1 stream the gate rows of 32 h-columns, waves 2,3 the up rows
 // of the same columns (one matrix per wave keeps the register footprint small);
-// down: 4 waves x 16 output columns. The stage loop is unrolled at compile time
-// (NSTAGE stages of kDecSS steps): the weight codes of stage s+kDecPF and the
-// activation window (+ both kinds of scales) of stage s+kDecPF are issued while
-// stage s is computed, held in register rings, and the window is copied to LDS
-// one stage before it is read. Loads are issued in the order they are consumed,
-// so waiting for one never waits for a younger one (the vector memory counter
-// retires in order). All global reads are buffer loads: K blocks past the end
-// (the half step when K % 128 == 64) and rows past the count read as zero.
+// down: 4 waves x 16 output columns. The block scales of the workgroup's weight
+// rows (all of K) and of its activation rows are loaded into LDS once, up front,
+// in few coalesced loads. The stage loop is unrolled at compile time (NSTAGE
+// stages of kDecSS steps): the weight codes and the activation window of stage
+// s+kDecPF are issued while stage s is computed, held in register rings, and
+// the window is copied to LDS one stage before it is read. Loads are issued in
+// the order they are consumed, so waiting for one never waits for a younger one
+// (the vector memory counter retires in order). All global reads are buffer
+// loads: K blocks past the end (the half step when K % 128 == 64) and rows past
+// the count read as zero.
 template <bool GATEUP, int NSTAGE>
 __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const EncIn ain,
                                                          const EncOut hout) {
   constexpr int COLS = GATEUP ? 32 : 64;  // output columns per workgroup
   constexpr int PF = kDecPF;
+  // scale loads actually needed for NSTAGE stages
+  constexpr int BSL = (64 * NSTAGE * kDecWB / 2 + 255) / 256;
+  static_assert(BSL <= kDecBSLoads, "scale staging bounds");
+  static_assert(kDecMaxBlk / 2 <= 64, "one activation-scale row per wavefront load");
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][16 * kDecAPitch];
-  __shared__ uint16_t sAs[2][16 * kDecWB];
-  __shared__ uint8_t sBs[2][64 * kDecWB];   // weight scales of the window: [wave*16 + col][blk]
+  // [row][blk] activation scales and [wave*16 + col][blk] weight scales, each with
+  // a 4-byte dump slot at the end for lanes past the last entry
+  __shared__ __attribute__((aligned(4))) uint16_t sAs[16 * kDecASPitch + 2];
+  __shared__ __attribute__((aligned(4))) uint8_t sBs[64 * kDecBSPitch + 4];
   __shared__ __attribute__((aligned(16))) float gtile[GATEUP ? 2 * 16 * 36 : 4];
-  __shared__ uint8_t escratch[GATEUP ? 8 * 64 : 4];
 
   const int K = GATEUP ? a.d : a.F;
   const int N = GATEUP ? a.F : a.d;
@@ -558,23 +571,90 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
   const int n = GATEUP ? j * 32 + (wave & 1) * 16 + l16 : j * 64 + wave * 16 + l16;
   const bool up = GATEUP && wave >= 2;
   const uint8_t* codes = GATEUP ? (up ? a.wu_codes : a.wg_codes) : a.wd_codes;
-  const uint8_t* scales = GATEUP ? (up ? a.wu_scales : a.wg_scales) : a.wd_scales;
   const rsrc_t wr = make_rsrc(codes + (size_t)e * N * (K / 2), (uint32_t)((size_t)N * (K / 2)));
-  const rsrc_t sr = make_rsrc(scales + (size_t)e * N * nblkK, (uint32_t)(N * nblkK));
   const float bias = bf16_to_f32((GATEUP ? (up ? a.b_up : a.b_gate) : a.b_down)[(size_t)e * N + n]);
   const uint32_t wrow = (uint32_t)n * (K / 2);
-  // the weight-scale row this thread stages: column (wave, tid % 16) of the workgroup
-  const uint32_t srow_t = (uint32_t)(GATEUP ? j * 32 + (wave & 1) * 16 + (tid & 15)
-                                            : j * 64 + wave * 16 + (tid & 15)) * nblkK;
   // activation rows: gathered tokens (gate/up) or this expert's rows of h (down)
   const rsrc_t ar = GATEUP ? make_rsrc(ain.codes, (uint32_t)((size_t)a.T * nblkK * kEncBytes))
                            : make_rsrc(ain.codes + (size_t)off * nblkK * kEncBytes,
                                        (uint32_t)((size_t)cnt * nblkK * kEncBytes));
   const rsrc_t asr = GATEUP ? make_rsrc(ain.scales, (uint32_t)((size_t)a.T * nblkK * 2))
                             : make_rsrc(ain.scales + (size_t)off * nblkK, (uint32_t)(cnt * nblkK * 2));
+  const uint64_t kmagic = div_magic((uint32_t)a.k);  // token of dispatch pair q: q / k
+
+  const rsrc_t sg = make_rsrc((GATEUP ? a.wg_scales : a.wd_scales) + (size_t)e * N * nblkK,
+                              (uint32_t)(N * nblkK));
+  const rsrc_t su = GATEUP ? make_rsrc(a.wu_scales + (size_t)e * N * nblkK, (uint32_t)(N * nblkK)) : sg;
+  const int per_row = nblkK / 2;                        // uint16/uint32 entries per scale row
+  const uint64_t prmagic = div_magic((uint32_t)per_row);
+
+  // one stage's worth of loads for this thread
+  struct Packet {
+    uint4 w[kDecSS];              // weight codes (MFMA B operand, this lane)
+    uint4 a[kDecAPerT];           // activation window chunks (staged to LDS)
+  };
+  // The stage's distance along K goes into the uniform buffer offset, so the
+  // per-lane offsets are the same in every stage; only the last stage can hold
+  // blocks past K, and only there are lanes redirected out of range.
+  auto issue_w = [&](int st, Packet& pk) {
+    const bool last = st == NSTAGE - 1;
+    const uint32_t wso = (uint32_t)st * kDecSS * 64;    // weight bytes per 128-deep step: 64
+#pragma unroll
+    for (int u = 0; u < kDecSS; ++u) {
+      const bool live = !last || (st * kDecSS + u) * 4 + q < nblkK;
+      pk.w[u] = bload16(wr, live ? wrow + (u * 4 + q) * 16 : kOutOfRange, wso);
+    }
+  };
 
   for (int m0 = 0; m0 < cnt; m0 += 16) {
     const int rows = min(16, cnt - m0);
+    Packet ring[PF + 1];
+    __syncthreads();  // LDS of the previous row tile is no longer read
+
+    // ---- prologue. Loads are issued in this order: the weight codes of the
+    // first PF stages (they depend on nothing), the weight scales (first row
+    // tile only), the row tile's dispatch entries; then, once those have
+    // arrived, the activation scales and windows. So the prologue costs two
+    // memory latencies, and the first weights arrive meanwhile.
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (p < NSTAGE) issue_w(p, ring[p]);
+    // weight scales of the workgroup's 64 rows, all of K, as uint16 (two blocks)
+    // row after row, so consecutive lanes read consecutive bytes; entries past
+    // the end read zero and go to a dump slot
+    uint32_t bsv[BSL];
+    if (m0 == 0) {
+#pragma unroll
+      for (int i = 0; i < BSL; ++i) {
+        const int idx = tid + 256 * i;
+        const int row = min((int)div_by((uint32_t)idx, prmagic), 63), h = idx - row * per_row;
+        const int w = row >> 4, r = row & 15;
+        const int nn = GATEUP ? j * 32 + (w & 1) * 16 + r : j * 64 + w * 16 + r;
+        const uint32_t o = idx < 64 * per_row ? (uint32_t)nn * nblkK + 2 * h : kOutOfRange;
+        bsv[i] = (GATEUP && w >= 2) ? bload2(su, o) : bload2(sg, o);
+      }
+    }
+    // activation rows: tokens of the row tile's dispatch pairs (gate/up) or the
+    // expert's rows of h (down); rows past the count repeat the last one
+    uint32_t src_row[16];
+    if (GATEUP) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) src_row[r] = (uint32_t)a.sorted_pair[off + m0 + min(r, rows - 1)];
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) src_row[r] = div_by(src_row[r], kmagic);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) src_row[r] = (uint32_t)(m0 + min(r, rows - 1));
+    }
+    // activation scales of the row tile, all of K, as uint32 (two blocks): wave w
+    // loads rows w, w+4, w+8, w+12, lane h the entry h of the row
+    uint32_t asv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave + 4 * i;
+      asv[i] = bload4(asr, row < rows && lane < per_row ? src_row[row] * nblkK * 2 + 4 * lane : kOutOfRange);
+    }
     uint32_t arow[kDecAPerT];
     int alds[kDecAPerT], ablk[kDecAPerT];
 #pragma unroll
@@ -584,55 +664,16 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
       const int blk = rem / 3, part = rem - blk * 3;
       alds[i] = row * kDecAPitch + blk * kEncBytes + part * 16;
       ablk[i] = blk;
-      const int src = GATEUP ? a.sorted_pair[off + m0 + min(row, rows - 1)] / a.k : m0 + row;
-      arow[i] = row < rows ? (uint32_t)(src * nblkK * kEncBytes + part * 16) : kOutOfRange;
+      arow[i] = row < rows ? src_row[row] * nblkK * kEncBytes + part * 16 : kOutOfRange;
     }
-    uint32_t asrow[kDecASPerT];
-    int asblk[kDecASPerT];
-#pragma unroll
-    for (int i = 0; i < kDecASPerT; ++i) {
-      const int ent = tid + 256 * i;
-      const int row = ent / kDecWB;
-      asblk[i] = ent - row * kDecWB;
-      const int src = GATEUP ? a.sorted_pair[off + m0 + min(row, rows - 1)] / a.k : m0 + row;
-      asrow[i] = row < rows ? (uint32_t)(src * nblkK * 2) : kOutOfRange;
-    }
-
-    // one stage's worth of loads for this thread
-    struct Packet {
-      uint4 w[kDecSS];              // weight codes (MFMA B operand, this lane)
-      uint4 a[kDecAPerT];           // activation window chunks (staged to LDS)
-      uint32_t as[kDecASPerT];      // activation scales (staged)
-      uint32_t bs[kDecBSPerT];      // weight scales (staged)
-    };
-    // The stage's distance along K goes into the uniform buffer offset, so the
-    // per-lane offsets are the same in every stage; only the last stage can hold
-    // blocks past K, and only there are lanes redirected out of range.
-    auto issue = [&](int st, Packet& pk) {
+    auto issue_a = [&](int st, Packet& pk) {
       const bool last = st == NSTAGE - 1;
-      const uint32_t wso = (uint32_t)st * kDecSS * 64;    // weight bytes per 128-deep step: 64
-#pragma unroll
-      for (int u = 0; u < kDecSS; ++u) {
-        const bool live = !last || (st * kDecSS + u) * 4 + q < nblkK;
-        pk.w[u] = bload16(wr, live ? wrow + (u * 4 + q) * 16 : kOutOfRange, wso);
-      }
       const int kb0 = st * kDecWB;
 #pragma unroll
       for (int i = 0; i < kDecAPerT; ++i) {
         const bool live = !last || kb0 + ablk[i] < nblkK;
         pk.a[i] = bload16(ar, live ? arow[i] + ablk[i] * kEncBytes : kOutOfRange,
                           (uint32_t)kb0 * kEncBytes);
-      }
-#pragma unroll
-      for (int i = 0; i < kDecASPerT; ++i) {
-        const bool live = !last || kb0 + asblk[i] < nblkK;
-        pk.as[i] = bload2(asr, live ? asrow[i] + asblk[i] * 2 : kOutOfRange, (uint32_t)kb0 * 2);
-      }
-#pragma unroll
-      for (int i = 0; i < kDecBSPerT; ++i) {
-        const int bl = ((tid >> 4) & 3) * kDecBSPerT + i;
-        const bool live = !last || kb0 + bl < nblkK;
-        pk.bs[i] = bload1(sr, live ? srow_t + bl : kOutOfRange, (uint32_t)kb0);
       }
     };
     auto stage_to_lds = [&](const Packet& pk, int buf) {
@@ -642,20 +683,40 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
         d[0] = make_uint2(pk.a[i].x, pk.a[i].y);
         d[1] = make_uint2(pk.a[i].z, pk.a[i].w);
       }
-#pragma unroll
-      for (int i = 0; i < kDecASPerT; ++i) sAs[buf][tid + 256 * i] = static_cast<uint16_t>(pk.as[i]);
-#pragma unroll
-      for (int i = 0; i < kDecBSPerT; ++i)
-        sBs[buf][(wave * 16 + (tid & 15)) * kDecWB + ((tid >> 4) & 3) * kDecBSPerT + i] =
-            static_cast<uint8_t>(pk.bs[i]);
     };
-
-    v4f acc = v4f{bias, bias, bias, bias};
-    Packet ring[PF + 1];
-    __syncthreads();  // LDS of the previous row tile is no longer read
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-      if (p < NSTAGE) issue(p, ring[p]);
+      if (p < NSTAGE) issue_a(p, ring[p]);
+
+    // ---- scales to LDS (their loads are older than the windows': storing them
+    // does not wait for the windows)
+    if (m0 == 0) {
+#pragma unroll
+      for (int i = 0; i < BSL; ++i) {
+        const int idx = tid + 256 * i;
+        const int row = min((int)div_by((uint32_t)idx, prmagic), 63), h = idx - row * per_row;
+        const int o = idx < 64 * per_row ? row * kDecBSPitch + 2 * h : 64 * kDecBSPitch;
+        *reinterpret_cast<uint16_t*>(sBs + o) = static_cast<uint16_t>(bsv[i]);
+      }
+      // blocks nblkK, nblkK+1 are read (with zero codes) by the half step at the
+      // end of K when K % 128 == 64: their scales must be finite, so they are
+      // zeroed (2^-127); they lie in the row padding when K % 128 == 0
+      if (tid < 64) *reinterpret_cast<uint16_t*>(sBs + tid * kDecBSPitch + nblkK) = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave + 4 * i;
+      const int o = lane < per_row ? row * kDecASPitch + 2 * lane : 16 * kDecASPitch;
+      *reinterpret_cast<uint32_t*>(sAs + o) = asv[i];
+    }
+    if (tid < 16)  // zero scales for the two blocks past K, as for the weights
+      *reinterpret_cast<uint32_t*>(sAs + tid * kDecASPitch + nblkK) = 0u;
+
+    v4f acc = v4f{bias, bias, bias, bias};
+    auto issue = [&](int st, Packet& pk) {
+      issue_w(st, pk);
+      issue_a(st, pk);
+    };
     stage_to_lds(ring[0], 0);
     __syncthreads();
 #pragma unroll
@@ -666,13 +727,14 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
 #pragma unroll
       for (int u = 0; u < kDecSS; ++u) {
         if (st * kDecSS + u < nst) {
+          const int blk = st * kDecWB + 4 * u + q;
           const uint8_t* pa = sA[buf] + l16 * kDecAPitch + (4 * u + q) * kEncBytes;
           const uint2 h0 = lds64(pa), h1 = lds64(pa + 8), h2 = lds64(pa + 16);
           const uint2 g0 = lds64(pa + 24), g1 = lds64(pa + 32), g2 = lds64(pa + 40);
           const v8i ahi = {(int)h0.x, (int)h0.y, (int)h1.x, (int)h1.y, (int)h2.x, (int)h2.y, 0, 0};
           const v8i alo = {(int)g0.x, (int)g0.y, (int)g1.x, (int)g1.y, (int)g2.x, (int)g2.y, 0, 0};
-          const int as = sAs[buf][l16 * kDecWB + 4 * u + q];
-          const int bs = sBs[buf][(wave * 16 + l16) * kDecWB + 4 * u + q];
+          const int as = sAs[l16 * kDecASPitch + blk];
+          const int bs = sBs[(wave * 16 + l16) * kDecBSPitch + blk];
           const v8i b = {(int)cur.w[u].x, (int)cur.w[u].y, (int)cur.w[u].z, (int)cur.w[u].w, 0, 0, 0, 0};
           acc = mfma16_f6f4<0>(ahi, b, acc, as, bs);
           acc = mfma16_f6f4<1>(alo, b, acc, as, bs);
@@ -684,19 +746,28 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
 
     if constexpr (GATEUP) {
       // waves 0,1 hold g, waves 2,3 hold u for the same 16 rows x 32 columns;
-      // then each half wavefront encodes one row's 32-column block of h
+      // then one lane per row encodes the row's 32-column block of h
       float* t = gtile + (wave >> 1) * 16 * 36;
 #pragma unroll
       for (int i = 0; i < 4; ++i) t[(4 * q + i) * 36 + (wave & 1) * 16 + l16] = acc[i];
       __syncthreads();
-      const int nblkF = a.F / 32;
+      if (tid < rows) {
+        float v[32];
+        const float4* g4 = reinterpret_cast<const float4*>(gtile + tid * 36);
+        const float4* u4 = reinterpret_cast<const float4*>(gtile + 16 * 36 + tid * 36);
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        const int row = pass * 8 + (tid >> 5), col = tid & 31;
-        const float h = silu_mul(gtile[row * 36 + col], gtile[16 * 36 + row * 36 + col]);
-        const size_t rec = (size_t)(off + m0 + min(row, rows - 1)) * nblkF + j;
-        encode_group32(h, escratch + (tid >> 5) * 64, hout.codes + rec * kEncBytes,
-                       hout.scales + rec, row < rows);
+        for (int c = 0; c < 8; ++c) {
+          const float4 g = g4[c], u = u4[c];
+          v[4 * c] = silu_mul(g.x, u.x);
+          v[4 * c + 1] = silu_mul(g.y, u.y);
+          v[4 * c + 2] = silu_mul(g.z, u.z);
+          v[4 * c + 3] = silu_mul(g.w, u.w);
+        }
+        uint32_t hw[6], lw[6], sc;
+        encode_block(v, hw, lw, sc);
+        const size_t rec = (size_t)(off + m0 + tid) * (a.F / 32) + j;
+        store_enc(hout.codes + rec * kEncBytes, hw, lw);
+        hout.scales[rec] = static_cast<uint16_t>(sc);
       }
     } else {
 #pragma unroll

@@ -57,6 +57,7 @@ def test_decode_workload(gu):
     dict(T=129, d=192, F=320, E=256, k=8, seed=34),      # largest E and k
     dict(T=8, d=4608, F=256, E=4, k=2, seed=38),         # decode path, K beyond the unrolled stage counts
     dict(T=96, d=320, F=4160, E=6, k=3, seed=39),        # prefill path, F not a multiple of 128
+    dict(T=300, d=128, F=64, E=8, k=1, seed=43),         # prefill path, switch routing, K = 64
 ])
 def test_edge_shapes(gu, shape):
     _full_check(gu, synth.tiny_workload(**shape))
