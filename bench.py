@@ -107,7 +107,7 @@ def run_gpu(cfg: int, steps: int, warmup: int, log) -> dict:
 
     copies = []
     for _ in range(R):
-        copies.append(moe.ExpertWeights(
+        copies.append(moe.load_expert_weights(
             w_router=torch.from_numpy(L.w_router).to(dev),
             b_router=None if L.b_router is None else torch.from_numpy(L.b_router).to(dev),
             gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales),
@@ -194,7 +194,7 @@ def run_stack(cfg: int, steps: int, warmup: int, log) -> dict:
     layers = []
     for l in range(w.n_layers):
         L = synth.stack_layer(cfg, l)
-        layers.append((bf16(L.gain), moe.ExpertWeights(
+        layers.append((bf16(L.gain), moe.load_expert_weights(
             w_router=torch.from_numpy(L.w_router).to(dev), b_router=None,
             gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales),
             up_codes=u8(L.up.codes), up_scales=u8(L.up.scales),

@@ -65,11 +65,26 @@ typedef struct {
   int32_t T, d, F, E, k;
 } moe_dims;
 
-/* One MXFP4 weight tensor for all experts, [device] pointers (layout above). */
+/* One MXFP4 weight tensor for all experts in the OCP layout above, [device]
+ * pointers. */
 typedef struct {
   const uint8_t* codes;  /* [E][N][K/2]  */
   const uint8_t* scales; /* [E][N][K/32] */
 } moe_mxfp4;
+
+/* The same tensor repacked by moe_pack_mxfp4 into the order in which gfx950's
+ * scaled matrix cores take their B operand, [device] pointers. With
+ * S = ceil(K/128) steps and G = N/32 row groups:
+ *   codes  [E][G][S][2][64][16 B]: entry (e,g,j,s,l) = the 16 code bytes of row
+ *          32g + l%32, 32-element block 4j + 2*(l/32) + s (byte order as in
+ *          moe_mxfp4); zero for blocks past K.
+ *   scales [E][G][S][64][2 B]: entry (e,g,j,l) = the scale bytes of row 32g + l%32,
+ *          blocks 4j + 2*(l/32) and 4j + 2*(l/32) + 1; zero for blocks past K.
+ * Every code nibble and scale byte is kept; only their order changes. */
+typedef struct {
+  const uint8_t* codes;  /* moe_mxfp4_packed_bytes(E, N, K, 0) bytes */
+  const uint8_t* scales; /* moe_mxfp4_packed_bytes(E, N, K, 1) bytes */
+} moe_mxfp4_packed;
 
 typedef uint16_t moe_bf16;
 
@@ -110,6 +125,26 @@ moe_status moe_permute(moe_dims dims, const int32_t* topk_idx, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the packed form of an [E][N][K] MXFP4 tensor: its codes when
+ * `which` is 0, its scales when 1. Pure host function; 0 for sizes that no
+ * moe_dims can use (E outside 1..256, N or K not a positive multiple of 64, or
+ * above 16384). */
+size_t moe_mxfp4_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t which);
+
+/* Repack an MXFP4 tensor [E][N][K] (OCP layout) into the packed layout that
+ * moe_expert_ffn_mxfp4 streams: a byte permutation, run once when the weights
+ * are loaded (the expert weights are fixed across calls). The layout is the
+ * operand order of gfx950's scaled MFMA, so that every weight load of the
+ * expert GEMMs is a contiguous run (this library's own choice; the pages give
+ * only the MXFP4 format: "GPT-OSS el dia 0", section "GPT-OSS a Hopper", and
+ * "第39章 使用 Unsloth 微调 gpt-oss", paragraph "解释").
+ *   src            [device] codes [E][N][K/2], scales [E][N][K/32], 16-byte aligned
+ *   codes_out      [device] moe_mxfp4_packed_bytes(E, N, K, 0) bytes, 16-byte aligned
+ *   scales_out     [device] moe_mxfp4_packed_bytes(E, N, K, 1) bytes, 16-byte aligned
+ * Output must not overlap the input. Enqueued on `stream` like every call. */
+moe_status moe_pack_mxfp4(int32_t E, int32_t N, int32_t K, moe_mxfp4 src, uint8_t* codes_out,
+                          uint8_t* scales_out, void* stream);
+
 /* Grouped expert FFN in dispatch order, MXFP4 weights.
  * For every expert e and row p in [offsets[e], offsets[e+1]), with
  * t = sorted_pair[p] / k:
@@ -119,16 +154,18 @@ moe_status moe_permute(moe_dims dims, const int32_t* topk_idx, int32_t* counts,
  * "Nuclis per a GPT-OSS / MoE": biases loaded into the GEMM accumulators.)
  *   x         [device] bf16 [T][d]
  *   sorted_pair, offsets  [device] from moe_permute
- *   w_gate, w_up          MXFP4 [E][F][d] (N = F, K = d)
- *   w_down                MXFP4 [E][d][F] (N = d, K = F)
+ *   w_gate, w_up          MXFP4 [E][F][d] (N = F, K = d), packed by moe_pack_mxfp4
+ *   w_down                MXFP4 [E][d][F] (N = d, K = F), packed by moe_pack_mxfp4
  *   b_gate, b_up [device] bf16 [E][F];  b_down [device] bf16 [E][d]
  *   y_sorted  [device] fp32 [P][d]  out: per-pair expert output, bias included
  * The activations are re-encoded on the device for the matrix cores (two-term
  * MXFP6 per 32-element block); accumulation is fp32. Code and scale pointers
- * must be 16-byte aligned. */
+ * must be 16-byte aligned. The weights are read in place: the library keeps
+ * no copy of them. */
 moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x,
                                 const int32_t* sorted_pair, const int32_t* offsets,
-                                moe_mxfp4 w_gate, moe_mxfp4 w_up, moe_mxfp4 w_down,
+                                moe_mxfp4_packed w_gate, moe_mxfp4_packed w_up,
+                                moe_mxfp4_packed w_down,
                                 const moe_bf16* b_gate, const moe_bf16* b_up,
                                 const moe_bf16* b_down, float* y_sorted,
                                 void* ws, size_t ws_bytes, void* stream);

@@ -20,7 +20,7 @@ import torch  # imported before the library so that it binds to torch's HIP runt
 __all__ = [
     "MoeError", "Dims", "MXFP4", "library_path", "lib", "workspace_bytes", "route",
     "permute", "expert_ffn_mxfp4", "combine", "rmsnorm", "residual_add", "forward",
-    "ExpertWeights", "EXPORTED",
+    "ExpertWeights", "EXPORTED", "pack_mxfp4", "packed_bytes", "load_expert_weights",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,6 +28,7 @@ _LIB_NAME = "libmoe_mi355x.so"
 EXPORTED = (
     "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine",
     "moe_rmsnorm", "moe_residual_add", "moe_status_string", "moe_last_error",
+    "moe_mxfp4_packed_bytes", "moe_pack_mxfp4",
 )
 
 
@@ -69,10 +70,13 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_ffn_mxfp4.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp,
                                        vp, sz, vp]
     L.moe_combine.argtypes = [Dims, vp, vp, vp, vp, vp]
+    L.moe_mxfp4_packed_bytes.argtypes = [i32, i32, i32, i32]
+    L.moe_mxfp4_packed_bytes.restype = sz
+    L.moe_pack_mxfp4.argtypes = [i32, i32, i32, MXFP4, vp, vp, vp]
     L.moe_rmsnorm.argtypes = [i32, i32, vp, vp, ctypes.c_float, vp, vp]
     L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine", "moe_rmsnorm",
-              "moe_residual_add"):
+              "moe_residual_add", "moe_pack_mxfp4"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -109,24 +113,64 @@ def _dev(t: torch.Tensor, dtype, shape, name: str) -> int:
 
 @dataclass
 class ExpertWeights:
-    """Device tensors of one MoE layer (the layout of include/moe.h)."""
+    """Device tensors of one MoE layer: the fp32 router, the three MXFP4 expert
+    tensors in the packed layout of moe_pack_mxfp4 (flat uint8), the bf16 biases."""
+    d: int
+    F: int
+    E: int
     w_router: torch.Tensor            # fp32 [d][E]
     b_router: Optional[torch.Tensor]  # fp32 [E] or None
-    gate_codes: torch.Tensor          # u8 [E][F][d/2]
-    gate_scales: torch.Tensor         # u8 [E][F][d/32]
+    gate_codes: torch.Tensor          # packed, from codes [E][F][d/2]
+    gate_scales: torch.Tensor         # packed, from scales [E][F][d/32]
     up_codes: torch.Tensor
     up_scales: torch.Tensor
-    down_codes: torch.Tensor          # u8 [E][d][F/2]
-    down_scales: torch.Tensor         # u8 [E][d][F/32]
+    down_codes: torch.Tensor          # packed, from codes [E][d][F/2]
+    down_scales: torch.Tensor
     b_gate: torch.Tensor              # bf16 [E][F]
     b_up: torch.Tensor                # bf16 [E][F]
     b_down: torch.Tensor              # bf16 [E][d]
 
     @property
     def dims(self):
-        d, E = self.w_router.shape
-        F = self.gate_codes.shape[1]
-        return d, F, E
+        return self.d, self.F, self.E
+
+
+def packed_bytes(E: int, N: int, K: int) -> tuple:
+    """(code bytes, scale bytes) of the packed form of an [E][N][K] MXFP4 tensor."""
+    L = lib()
+    c, s = L.moe_mxfp4_packed_bytes(E, N, K, 0), L.moe_mxfp4_packed_bytes(E, N, K, 1)
+    if c == 0 or s == 0:
+        raise MoeError(f"unsupported MXFP4 tensor shape E={E} N={N} K={K}")
+    return c, s
+
+
+def pack_mxfp4(codes: torch.Tensor, scales: torch.Tensor):
+    """Repack an MXFP4 tensor (codes uint8 [E][N][K/2], scales uint8 [E][N][K/32],
+    OCP layout) into the packed layout; returns two new flat uint8 device tensors."""
+    E, N, Kh = codes.shape
+    K = 2 * Kh
+    c_bytes, s_bytes = packed_bytes(E, N, K)
+    pc = torch.empty(c_bytes, dtype=torch.uint8, device=codes.device)
+    ps = torch.empty(s_bytes, dtype=torch.uint8, device=codes.device)
+    src = MXFP4(_dev(codes, torch.uint8, (E, N, K // 2), "codes"),
+                _dev(scales, torch.uint8, (E, N, K // 32), "scales"))
+    _check(lib().moe_pack_mxfp4(E, N, K, src, pc.data_ptr(), ps.data_ptr(), _stream()),
+           "moe_pack_mxfp4")
+    return pc, ps
+
+
+def load_expert_weights(w_router, b_router, gate_codes, gate_scales, up_codes, up_scales,
+                        down_codes, down_scales, b_gate, b_up, b_down) -> ExpertWeights:
+    """ExpertWeights from device tensors in the OCP layout (include/moe.h): the
+    expert tensors are packed once here; the raw ones may be freed afterwards."""
+    d, E = w_router.shape
+    F = gate_codes.shape[1]
+    gc, gs = pack_mxfp4(gate_codes, gate_scales)
+    uc, us = pack_mxfp4(up_codes, up_scales)
+    dc, ds = pack_mxfp4(down_codes, down_scales)
+    return ExpertWeights(d=int(d), F=int(F), E=int(E), w_router=w_router, b_router=b_router,
+                         gate_codes=gc, gate_scales=gs, up_codes=uc, up_scales=us,
+                         down_codes=dc, down_scales=ds, b_gate=b_gate, b_up=b_up, b_down=b_down)
 
 
 def _dims(T, d, F, E, k) -> Dims:
@@ -185,12 +229,13 @@ def expert_ffn_mxfp4(x, sorted_pair, offsets, w: ExpertWeights, k: int, ws, y_so
     if y_sorted is None:
         y_sorted = torch.empty((P, d), dtype=torch.float32, device=x.device)
     u8 = torch.uint8
-    mg = MXFP4(_dev(w.gate_codes, u8, (E, F, d // 2), "gate_codes"),
-               _dev(w.gate_scales, u8, (E, F, d // 32), "gate_scales"))
-    mu = MXFP4(_dev(w.up_codes, u8, (E, F, d // 2), "up_codes"),
-               _dev(w.up_scales, u8, (E, F, d // 32), "up_scales"))
-    md = MXFP4(_dev(w.down_codes, u8, (E, d, F // 2), "down_codes"),
-               _dev(w.down_scales, u8, (E, d, F // 32), "down_scales"))
+    gb, ub = packed_bytes(E, F, d), packed_bytes(E, d, F)
+    mg = MXFP4(_dev(w.gate_codes, u8, (gb[0],), "gate_codes"),
+               _dev(w.gate_scales, u8, (gb[1],), "gate_scales"))
+    mu = MXFP4(_dev(w.up_codes, u8, (gb[0],), "up_codes"),
+               _dev(w.up_scales, u8, (gb[1],), "up_scales"))
+    md = MXFP4(_dev(w.down_codes, u8, (ub[0],), "down_codes"),
+               _dev(w.down_scales, u8, (ub[1],), "down_scales"))
     _check(lib().moe_expert_ffn_mxfp4(
         _dims(T, d, F, E, k), _dev(x, torch.bfloat16, (T, d), "x"),
         _dev(sorted_pair, torch.int32, (P,), "sorted_pair"),

@@ -7,6 +7,7 @@
 
 #include "moe.h"
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace {
 
@@ -122,9 +123,32 @@ moe_status moe_permute(moe_dims dims, const int32_t* topk_idx, int32_t* counts,
                                         static_cast<hipStream_t>(stream)));
 }
 
+static bool packable(int32_t E, int32_t N, int32_t K) {
+  return E >= 1 && E <= 256 && N >= 64 && K >= 64 && N % 64 == 0 && K % 64 == 0 && N <= 16384 &&
+         K <= 16384;
+}
+
+size_t moe_mxfp4_packed_bytes(int32_t E, int32_t N, int32_t K, int32_t which) {
+  if (!packable(E, N, K) || (which != 0 && which != 1)) return 0;
+  return which == 0 ? moe::packed_codes_bytes(E, N, K) : moe::packed_scales_bytes(E, N, K);
+}
+
+moe_status moe_pack_mxfp4(int32_t E, int32_t N, int32_t K, moe_mxfp4 src, uint8_t* codes_out,
+                          uint8_t* scales_out, void* stream) {
+  g_last_error[0] = 0;
+  if (!packable(E, N, K)) {
+    set_error("%s", "moe_pack_mxfp4: need 1 <= E <= 256 and N, K positive multiples of 64, <= 16384");
+    return MOE_ERR_INVALID_ARG;
+  }
+  MOE_TRY(check_ptrs({src.codes, src.scales, codes_out, scales_out}, "moe_pack_mxfp4"));
+  return hip_status(moe::launch_pack_mxfp4(src.codes, src.scales, E, N, K, codes_out, scales_out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x, const int32_t* sorted_pair,
-                                const int32_t* offsets, moe_mxfp4 w_gate, moe_mxfp4 w_up,
-                                moe_mxfp4 w_down, const moe_bf16* b_gate, const moe_bf16* b_up,
+                                const int32_t* offsets, moe_mxfp4_packed w_gate,
+                                moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                                const moe_bf16* b_gate, const moe_bf16* b_up,
                                 const moe_bf16* b_down, float* y_sorted, void* ws,
                                 size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;

@@ -43,11 +43,17 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t*
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
                           hipStream_t stream);
 
+// Repack one [E][N][K] MXFP4 tensor from the OCP layout into the packed
+// fragment layout (layout.hpp).
+hipError_t launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
+                             uint8_t* codes_out, uint8_t* scales_out, hipStream_t stream);
+
 struct FfnArgs {
   int T, d, F, E, k;
   const uint16_t* x;
   const int32_t* sorted_pair;
   const int32_t* offsets;
+  // weights in the packed fragment layout
   const uint8_t *wg_codes, *wg_scales, *wu_codes, *wu_scales, *wd_codes, *wd_scales;
   const uint16_t *b_gate, *b_up, *b_down;
   float* y_sorted;

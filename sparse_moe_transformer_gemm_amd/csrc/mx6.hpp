@@ -21,16 +21,12 @@
 #pragma once
 
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-
-// Encoded activation storage: per row, per 32-element block, 48 bytes of codes
-// (hi term 24 B then lo term 24 B, 6 bits per element, element j at bit 6j) and
-// one uint16 of scales (byte 0 = hi E8M0, byte 1 = lo E8M0).
-constexpr int kEncBytes = 48;
 
 // 2^n for n in [-127, 127] as an fp32 (2^-127 is subnormal).
 __device__ __forceinline__ float pow2i(int n) {

@@ -23,7 +23,7 @@ def bits_host(t: torch.Tensor) -> np.ndarray:
 
 def weights_dev(L: synth.LayerParams) -> moe.ExpertWeights:
     u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    return moe.ExpertWeights(
+    return moe.load_expert_weights(
         w_router=torch.from_numpy(L.w_router).to(DEV),
         b_router=None if L.b_router is None else torch.from_numpy(L.b_router).to(DEV),
         gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales),

@@ -104,6 +104,24 @@ def test_ffn_validation(moe):
     assert L.moe_expert_ffn_mxfp4(D(70000, 512, 512, 32, 4), *args) == -2  # T too big
 
 
+def test_pack_sizes_and_validation(moe):
+    L = moe.lib()
+    # K = 2880: 23 steps of 128 (the last half used); 2 KB of codes and 128 B of
+    # scales per (32-row group, step)
+    assert L.moe_mxfp4_packed_bytes(32, 2880, 2880, 0) == 32 * 90 * 23 * 2048
+    assert L.moe_mxfp4_packed_bytes(32, 2880, 2880, 1) == 32 * 90 * 23 * 128
+    assert L.moe_mxfp4_packed_bytes(1, 64, 128, 0) == 2 * 1 * 2048
+    assert L.moe_mxfp4_packed_bytes(32, 2880, 2880, 2) == 0      # which
+    assert L.moe_mxfp4_packed_bytes(32, 2880, 2880 + 32, 0) == 0  # K % 64
+    assert L.moe_mxfp4_packed_bytes(0, 2880, 2880, 0) == 0       # E < 1
+    assert L.moe_mxfp4_packed_bytes(257, 2880, 2880, 0) == 0     # E > 256
+    src = moe.MXFP4(FAKE, FAKE)
+    assert L.moe_pack_mxfp4(32, 2880, 2880, moe.MXFP4(FAKE, None), FAKE, FAKE, None) == -1
+    assert L.moe_pack_mxfp4(32, 2880, 2880, src, FAKE + 8, FAKE, None) == -1  # misaligned
+    assert L.moe_pack_mxfp4(32, 2880, 2900, src, FAKE, FAKE, None) == -1
+    assert L.moe_pack_mxfp4(32, 20000, 2880, src, FAKE, FAKE, None) == -1
+
+
 def test_combine_norm_validation(moe):
     L = moe.lib()
     D = moe.Dims
