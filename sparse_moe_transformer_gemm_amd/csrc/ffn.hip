@@ -91,22 +91,36 @@ __global__ __launch_bounds__(256) void encode_rows(const uint16_t* __restrict__ 
 
 // ------------------------------------------------------------------ tile table
 
-// tile_prefix[e] = sum_{e' < e} ceil(count_e' / kBM); tile_prefix[E] = total tiles.
-__global__ __launch_bounds__(256) void tile_prefix_kernel(const int32_t* __restrict__ offsets,
-                                                          int E, int32_t* __restrict__ tp) {
-  __shared__ int s[256];
+// The prefill grid's tile table, built on the device from the expert offsets:
+// table[0].x = number of row tiles (sum over experts of ceil(count / kBM));
+// table[1 + mt] = {expert, first row of the tile within the expert, offsets[e],
+// count_e} for row tile mt, tiles in expert order. One 16-byte load gives a
+// workgroup everything it needs to locate its rows.
+__global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets, int E,
+                                                         int4* __restrict__ table) {
+  __shared__ int s[257];
   const int t = threadIdx.x;
   const int v = t < E ? (offsets[t + 1] - offsets[t] + kBM - 1) / kBM : 0;
-  s[t] = v;
+  s[t + 1] = v;
+  if (t == 0) s[0] = 0;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = t >= off ? s[t - off] : 0;
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of s[1..256]
+    const int add = t >= off ? s[t + 1 - off] : 0;
     __syncthreads();
-    s[t] += add;
+    s[t + 1] += add;
     __syncthreads();
   }
-  if (t < E) tp[t + 1] = s[t];
-  if (t == 0) tp[0] = 0;
+  const int total = s[E];
+  if (t == 0) table[0] = make_int4(total, 0, 0, 0);
+  for (int mt = t; mt < total; mt += 256) {
+    int lo = 0, hi = E;  // s[lo] <= mt < s[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s[mid] <= mt) lo = mid; else hi = mid;
+    }
+    const int o = offsets[lo];
+    table[1 + mt] = make_int4(lo, (mt - s[lo]) * kBM, o, offsets[lo + 1] - o);
+  }
 }
 
 // Division by a runtime divisor d >= 1 as a multiply: x / d = (x * m) >> 32 with
@@ -151,42 +165,79 @@ struct Prefill {
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = A_OFF + kBM * kChunk;
   static constexpr int BS_OFF = B_OFF + NFR * 2 * 1024;
-  static constexpr int STAGE = BS_OFF + NFR * 256;
-  static constexpr int NA = (A_COPIES + 3) / 4;        // A copies per wave (at most)
-  static constexpr int NB = NFR * 2 / 4;               // B copies per wave
-  static constexpr int NBSW = (NFR + 3) / 4;           // scale copies per wave (at most)
-  // copies wave w issues per step
-  static constexpr int copies(int w) { return (A_COPIES - w + 3) / 4 + NB + (NFR - w + 3) / 4; }
   static constexpr int EP_PITCH = 36;                  // floats per row of the SwiGLU staging tile
+  static constexpr int EP_BYTES = 4 * 64 * EP_PITCH * 4;  // staging of all four waves (gate/up)
+  static constexpr int STAGE_DATA = BS_OFF + NFR * 256;
+  // one step's copies, or (gate/up) the epilogue's staging, which reuses a step buffer
+  static constexpr int STAGE = GATEUP && EP_BYTES > STAGE_DATA ? EP_BYTES : STAGE_DATA;
+  static constexpr int NA = (A_COPIES + 3) / 4;        // A copies per wave (at most)
+  // Weight copies are dealt out per matrix (gate and up for gate/up, the single
+  // down matrix otherwise), so the matrix of every copy is known at compile time.
+  static constexpr int NMAT = GATEUP ? 2 : 1;
+  static constexpr int GPM = NFR / NMAT;               // groups per matrix
+  static constexpr int NBM = 2 * GPM / 4;              // code copies per wave and matrix
+  static constexpr int NSM = (GPM + 3) / 4;            // scale copies per wave and matrix (at most)
+  static constexpr int cnt_lt(int n, int w) { return n > w ? (n - w + 3) / 4 : 0; }  // #t: 4t + w < n
+  // copies wave w issues per step
+  static constexpr int copies(int w) { return cnt_lt(A_COPIES, w) + NMAT * (NBM + cnt_lt(GPM, w)); }
   static_assert(kBM * kChunkPieces % 64 == 0, "A copies are whole instructions");
   static_assert(!GATEUP || NF % 2 == 0, "gate/up tiles pair gate and up groups");
-  static_assert(copies(0) <= 63, "one step of copies must fit the vector memory counter");
+  static_assert(2 * GPM % 4 == 0, "code copies split evenly over the four waves");
+  static_assert(2 * copies(0) <= 63 && 2 * copies(1) <= 63, "two steps of copies must fit the vector memory counter");
   static_assert(3 * STAGE <= 160 * 1024, "three step buffers must fit the 160 KB of LDS");
-  static_assert(!GATEUP || 2 * 64 * EP_PITCH * 4 <= STAGE, "SwiGLU staging of two waves must fit a step buffer");
+  static_assert(!GATEUP || EP_BYTES <= STAGE, "SwiGLU staging of the four waves must fit one step buffer");
 };
 
 // s_waitcnt with only the vector memory counter bounded (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at max).
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at max),
+// and with only the LDS/scalar counter at zero.
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+#define MOE_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14))
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// Buffer-to-LDS copy of SIZE bytes per lane (16 or 2) into `lds` (wave-uniform).
-template <int SIZE>
-__device__ __forceinline__ void lds_copy(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  static_assert(SIZE == 16 || SIZE == 2, "copy sizes used here");
-  if constexpr (SIZE == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds, 16, voff, soff, 0, 0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds, 2, voff, soff, 0, 0);
+// Buffer resource as four SGPRs (base, stride 0, size in bytes, raw 32-bit
+// data): the form the inline-asm copies below take.
+__device__ __forceinline__ v4i rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_ptr)p);
+}
+// Buffer-to-LDS copy of SIZE bytes per lane (16 or 2) to the LDS address `lds`
+// (wave-uniform); out-of-range lanes write zeros. Written as inline asm so that
+// the compiler does not guard every LDS read with a wait for all copies in flight
+// (it cannot tell which buffer a copy writes); the kernel bounds the vector
+// memory counter itself before each barrier. The asm sets M0 itself and has no
+// register outputs.
+template <int SIZE>
+__device__ __forceinline__ void lds_copy(v4i r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  static_assert(SIZE == 16 || SIZE == 2, "copy sizes used here");
+  // the resource, M0 and the uniform offset live in SGPRs (no-ops when the
+  // compiler already knows the values are uniform)
+  r = v4i{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+          __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  soff = __builtin_amdgcn_readfirstlane(soff);
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+
+template <int V>
+struct IC {
+  static constexpr int v = V;
+};
 
 template <int NF, bool GATEUP>
 __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const uint8_t* __restrict__ ain,
                                                        uint8_t* __restrict__ hout,
-                                                       const int32_t* __restrict__ tile_prefix,
-                                                       int ntn) {
+                                                       const int4* __restrict__ tiles, int ntn) {
   using C = Prefill<NF, GATEUP>;
   // three step buffers as separate objects, so the compiler can tell the copy
   // into one from the reads of another
@@ -197,291 +248,365 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
   const int N = GATEUP ? a.F : a.d;
   const int nblkK = K / 32;
   const int nst = nsteps_of(K);
-  const int E = a.E;
 
-  // ---- tile of this workgroup. Logical tiles are grouped kPrefGM row tiles x all
-  // column tiles, row tile fastest, so the workgroups resident at one time share
-  // a few row tiles of A and a few column tiles of B in L2; the groups are laid
-  // out contiguously per XCD.
-  const int total_mt = tile_prefix[E];
+  // ---- persistent schedule. Logical tiles are grouped kPrefGM row tiles x all
+  // column tiles, row tile fastest, and each XCD (workgroups are dispatched
+  // round-robin over the 8 XCDs) owns a contiguous range of logical tiles, which
+  // its workgroups take in turn: the tiles in flight on one XCD at any time are
+  // consecutive, so they share a few row tiles of A and a few column tiles of B
+  // in that XCD's L2.
+  const int total_mt = __builtin_amdgcn_readfirstlane(tiles[0].x);
   const int G = total_mt * ntn;
-  if ((int)blockIdx.x >= G) return;
-  const int logical = xcd_remap(blockIdx.x, G);
-  const int grp = logical / (kPrefGM * ntn);
-  const int gm = min(kPrefGM, total_mt - grp * kPrefGM);
-  const int r = logical - grp * kPrefGM * ntn;
-  const int nt = r / gm;
-  const int mt = grp * kPrefGM + (r - nt * gm);
-  int lo = 0, hi = E;  // tile_prefix[lo] <= mt < tile_prefix[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_prefix[mid] <= mt) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int off = a.offsets[e];
-  const int cnt = a.offsets[e + 1] - off;
-  const int m0 = (mt - tile_prefix[e]) * kBM;
-  const int rows_valid = min(kBM, cnt - m0);
-  const int col0 = nt * C::MROWS;  // first output column of each matrix in this tile
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
+  const int per = G >> 3, rem = G & 7;
+  const int xbeg = xcd * per + min(xcd, rem);
+  const int xend = xbeg + per + (xcd < rem ? 1 : 0);
+  int logical = xbeg + slot;
+  if (logical >= xend) return;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
   const int lane = tid & 63, lr = lane & 31, half = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
-
-  // ---- resources
   const uint32_t apitch = (uint32_t)nst * kChunk;
-  const rsrc_t ar = GATEUP ? make_rsrc(ain, (uint32_t)a.T * apitch)
-                           : make_rsrc(ain + (size_t)(off + m0) * apitch, (uint32_t)rows_valid * apitch);
   const uint64_t kmagic = div_magic((uint32_t)a.k);  // token of dispatch pair q: q / k
-  const size_t gstride = (size_t)nst * kWStep;        // packed code bytes per 32-row group
-  const size_t sstride = (size_t)nst * kWSStep;       // packed scale bytes per 32-row group
-  const size_t egroups = (size_t)e * (N / 32);
-  const rsrc_t br0 = make_rsrc((GATEUP ? a.wg_codes : a.wd_codes) + egroups * gstride,
-                               (uint32_t)((N / 32) * gstride));
-  const rsrc_t bsr0 = make_rsrc((GATEUP ? a.wg_scales : a.wd_scales) + egroups * sstride,
-                                (uint32_t)((N / 32) * sstride));
-  const rsrc_t br1 = GATEUP ? make_rsrc(a.wu_codes + egroups * gstride, (uint32_t)((N / 32) * gstride)) : br0;
-  const rsrc_t bsr1 = GATEUP ? make_rsrc(a.wu_scales + egroups * sstride, (uint32_t)((N / 32) * sstride)) : bsr0;
-  // first weight row of group phi, and whether phi is an up group
-  auto frag_up = [&](int phi) { return GATEUP && (phi % NF) >= NF / 2; };
-  auto frag_row = [&](int phi) -> int {
+  const uint32_t gstride = (uint32_t)nst * kWStep;    // packed code bytes per 32-row group
+  const uint32_t sstride = (uint32_t)nst * kWSStep;   // packed scale bytes per 32-row group
+  const uint32_t lane16 = lane * 16, lane2 = lane * 2;
+
+  // Copy i = wave + 4t of A covers 16-byte pieces 64i + lane: row (64i + lane) / 13,
+  // piece (64i + lane) % 13 (the same for every tile and step). Bit t of a_pad:
+  // the piece holds blocks 2, 3 of the step (pieces 6..11).
+  int a_row[C::NA];
+  uint32_t a_pad = 0, a_piece16[C::NA];
+#pragma unroll
+  for (int t = 0; t < C::NA; ++t) {
+    const int q = (wave + 4 * t) * 64 + lane;
+    a_row[t] = q / kChunkPieces;
+    const int piece = q - a_row[t] * kChunkPieces;
+    a_piece16[t] = piece * 16;
+    a_pad |= (piece >= 6 && piece < 12) ? 1u << t : 0u;
+  }
+  // Weight copies of matrix m: code copy t covers matrix-local copy c = 4t + wave,
+  // i.e. half c & 1 of group c >> 1; scale copy t covers group 4t + wave.
+  auto group_of = [&](int m, int gg) -> int {
+    if (GATEUP) return (gg / (NF / 2)) * NF + m * (NF / 2) + gg % (NF / 2);
+    return gg;
+  };
+  // first weight row of group phi within its matrix, relative to the tile's col0
+  auto group_row = [&](int phi) -> int {
     if (GATEUP) {
       const int w = phi / NF, f = phi % NF;
-      return col0 + w * C::FM * 32 + (f < NF / 2 ? f : f - NF / 2) * 32;
+      return w * C::FM * 32 + (f < NF / 2 ? f : f - NF / 2) * 32;
     }
-    return col0 + phi * 32;
+    return phi * 32;
   };
 
-  // ---- biases of this lane's output columns, loaded together with the dispatch
-  // entries below and before the first copies (waiting for them must not wait
-  // for the copies)
+  // ---- per-tile state (all wave-uniform)
+  int e, m0, off, cnt, rows_valid, col0;
+  v4i ar, br0, br1, bsr0, bsr1;
+  uint32_t a_off[C::NA];  // per-lane A source offsets (step 0)
   float bias[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int phi = wn * NF + f;
-    const uint16_t* bsrc = GATEUP ? (frag_up(phi) ? a.b_up : a.b_gate) : a.b_down;
-    bias[f] = bf16_to_f32(bsrc[(size_t)e * N + frag_row(phi) + lr]);
-  }
 
-  // ---- per-lane source offsets of this wave's A copies (fixed across steps; the
-  // step's K distance goes into the uniform offset). Copy i = wave + 4t covers
-  // 16-byte pieces 64i + lane: row (64i + lane) / 13, piece (64i + lane) % 13.
-  int a_piece[C::NA];
-  uint32_t a_src[C::NA];
+  // A tile's table entry, column tile, dispatch entries (gate/up: the token of
+  // each A copy's row) and raw bf16 biases are fetched ahead of time: the entry
+  // two tiles ahead, the rest one tile ahead, each only after the loads it
+  // depends on have completed, so fetching never makes this wave wait. R holds
+  // everything for the next tile, E the entry of the one after; each is refilled
+  // in place right after it has been consumed, so no loaded value is ever copied
+  // (a copy would wait for its load).
+  struct Pre {
+    int4 ent;
+    int nt;
+    uint32_t src[C::NA];
+    uint32_t bias[NF];  // raw bf16 (never combined before use: that would wait for the loads)
+  };
+  auto fetch_entry = [&](int lg, Pre& P) {
+    const int grp = lg / (kPrefGM * ntn);
+    const int gm = min(kPrefGM, total_mt - grp * kPrefGM);
+    const int r = lg - grp * kPrefGM * ntn;
+    P.nt = r / gm;
+    P.ent = tiles[1 + grp * kPrefGM + (r - P.nt * gm)];
+  };
+  auto fetch_rest = [&](const Pre& Ein, Pre& P) {
+    P.ent = Ein.ent;
+    P.nt = Ein.nt;
+    const int pe = __builtin_amdgcn_readfirstlane(P.ent.x);
+    const int pm0 = __builtin_amdgcn_readfirstlane(P.ent.y), poff = __builtin_amdgcn_readfirstlane(P.ent.z);
+    const int rv = min(kBM, __builtin_amdgcn_readfirstlane(P.ent.w) - pm0);
 #pragma unroll
-  for (int t = 0; t < C::NA; ++t) {
-    const int q = (wave + 4 * t) * 64 + lane;
-    const int row = q / kChunkPieces;
-    a_piece[t] = q - row * kChunkPieces;
-    a_src[t] = (uint32_t)min(row, rows_valid - 1);
-  }
-  if (GATEUP) {
+    for (int t = 0; t < C::NA; ++t) {
+      const int row = min(a_row[t], rv - 1);
+      P.src[t] = GATEUP ? (uint32_t)a.sorted_pair[poff + pm0 + row] : (uint32_t)row;
+    }
 #pragma unroll
-    for (int t = 0; t < C::NA; ++t) a_src[t] = (uint32_t)a.sorted_pair[off + m0 + a_src[t]];
-    asm volatile("" ::: "memory");
+    for (int f = 0; f < NF; ++f) {
+      const int phi = wn * NF + f;
+      const bool upg = GATEUP && f >= NF / 2;
+      const uint16_t* bsrc = GATEUP ? (upg ? a.b_up : a.b_gate) : a.b_down;
+      P.bias[f] = bsrc[(size_t)pe * N + P.nt * C::MROWS + group_row(phi) + lr];
+    }
+  };
+  auto setup = [&](const Pre& P) {
+    e = __builtin_amdgcn_readfirstlane(P.ent.x);
+    m0 = __builtin_amdgcn_readfirstlane(P.ent.y);
+    off = __builtin_amdgcn_readfirstlane(P.ent.z);
+    cnt = __builtin_amdgcn_readfirstlane(P.ent.w);
+    rows_valid = min(kBM, cnt - m0);
+    col0 = __builtin_amdgcn_readfirstlane(P.nt) * C::MROWS;
+    ar = GATEUP ? rsrc4(ain, (uint32_t)a.T * apitch)
+                : rsrc4(ain + (size_t)(off + m0) * apitch, (uint32_t)rows_valid * apitch);
+    const size_t eb = (size_t)e * (N / 32) * gstride, es = (size_t)e * (N / 32) * sstride;
+    br0 = rsrc4((GATEUP ? a.wg_codes : a.wd_codes) + eb, (uint32_t)(N / 32) * gstride);
+    br1 = rsrc4((GATEUP ? a.wu_codes : a.wd_codes) + eb, (uint32_t)(N / 32) * gstride);
+    bsr0 = rsrc4((GATEUP ? a.wg_scales : a.wd_scales) + es, (uint32_t)(N / 32) * sstride);
+    bsr1 = rsrc4((GATEUP ? a.wu_scales : a.wd_scales) + es, (uint32_t)(N / 32) * sstride);
 #pragma unroll
-    for (int t = 0; t < C::NA; ++t) a_src[t] = div_by(a_src[t], kmagic);
-  }
-  uint32_t a_off[C::NA];
+    for (int t = 0; t < C::NA; ++t) {
+      const uint32_t tok = GATEUP ? div_by(P.src[t], kmagic) : P.src[t];
+      const bool ok = wave + 4 * t < C::A_COPIES && a_row[t] < rows_valid;
+      a_off[t] = ok ? tok * apitch + a_piece16[t] : kOutOfRange;
+    }
 #pragma unroll
-  for (int t = 0; t < C::NA; ++t) {
-    const int q = (wave + 4 * t) * 64 + lane;
-    const bool ok = wave + 4 * t < C::A_COPIES && q / kChunkPieces < rows_valid;
-    a_off[t] = ok ? a_src[t] * apitch + a_piece[t] * 16 : kOutOfRange;
-  }
-  // B copies: copy i = wave + 4t is half i & 1 of group i >> 1; scale copy t is
-  // group wave + 4t. Only the lane offset varies across lanes.
-  uint32_t b_off[C::NB];
-#pragma unroll
-  for (int t = 0; t < C::NB; ++t) {
-    const int i = wave + 4 * t;
-    b_off[t] = (uint32_t)(frag_row(i >> 1) / 32) * (uint32_t)gstride + (i & 1) * 1024 + lane * 16;
-  }
-  uint32_t bs_off[C::NBSW];
-#pragma unroll
-  for (int t = 0; t < C::NBSW; ++t) {
-    const int phi = wave + 4 * t;
-    bs_off[t] = phi < C::NFR ? (uint32_t)(frag_row(phi) / 32) * (uint32_t)sstride + lane * 2 : kOutOfRange;
-  }
+    for (int f = 0; f < NF; ++f) bias[f] = bf16_to_f32((uint16_t)P.bias[f]);
+  };
 
-  // Copy step st into LDS buffer `buf`.
+  // Copy step st of the current tile into LDS buffer `buf`. Weight copies read
+  // one contiguous kilobyte: the lane offset is lane*16, the group and step go
+  // into the uniform offset.
   auto issue = [&](int st, uint8_t* buf) {
     const bool live = st < nst;
     const bool halfst = 4 * st + 2 >= nblkK;  // blocks 2, 3 of this step are past K
+    const uint32_t base = lds_addr(buf);
 #pragma unroll
     for (int t = 0; t < C::NA; ++t) {
-      const int i = wave + 4 * t;
-      if (i < C::A_COPIES) {
-        const bool pad = halfst && a_piece[t] >= 6 && a_piece[t] < 12;
-        lds_copy<16>(ar, buf + C::A_OFF + i * 1024, live && !pad ? a_off[t] : kOutOfRange,
+      if (wave + 4 * t < C::A_COPIES) {
+        const bool pad = halfst && ((a_pad >> t) & 1u);
+        lds_copy<16>(ar, base + (wave + 4 * t) * 1024, live && !pad ? a_off[t] : kOutOfRange,
                      (uint32_t)st * kChunk);
       }
     }
 #pragma unroll
-    for (int t = 0; t < C::NB; ++t) {
-      const int i = wave + 4 * t;
-      lds_copy<16>(frag_up(i >> 1) ? br1 : br0, buf + C::B_OFF + i * 1024,
-                   live ? b_off[t] : kOutOfRange, (uint32_t)st * kWStep);
-    }
+    for (int m = 0; m < C::NMAT; ++m) {
 #pragma unroll
-    for (int t = 0; t < C::NBSW; ++t) {
-      const int phi = wave + 4 * t;
-      if (phi < C::NFR)
-        lds_copy<2>(frag_up(phi) ? bsr1 : bsr0, buf + C::BS_OFF + phi * 256,
-                    live ? bs_off[t] : kOutOfRange, (uint32_t)st * kWSStep);
+      for (int t = 0; t < C::NBM; ++t) {
+        const int c = 4 * t + wave, phi = group_of(m, c >> 1), s = c & 1;
+        const uint32_t so = (uint32_t)((col0 + group_row(phi)) / 32) * gstride + s * 1024 + (uint32_t)st * kWStep;
+        lds_copy<16>(m ? br1 : br0, base + C::B_OFF + (phi * 2 + s) * 1024, live ? lane16 : kOutOfRange, so);
+      }
+#pragma unroll
+      for (int t = 0; t < C::NSM; ++t) {
+        const int gg = 4 * t + wave;
+        if (gg < C::GPM) {
+          const int phi = group_of(m, gg);
+          const uint32_t so = (uint32_t)((col0 + group_row(phi)) / 32) * sstride + (uint32_t)st * kWSStep;
+          lds_copy<2>(m ? bsr1 : bsr0, base + C::BS_OFF + phi * 256, live ? lane2 : kOutOfRange, so);
+        }
+      }
     }
   };
 
-  // Wait until this wave's copies of the step about to be computed have landed;
-  // the next step's copies (issued after it) stay in flight.
-  auto wait_step = [&]() {
-    if (wave == 0) MOE_WAIT_VMCNT(C::copies(0));
-    else if (wave == 1) MOE_WAIT_VMCNT(C::copies(1));
-    else if (wave == 2) MOE_WAIT_VMCNT(C::copies(2));
-    else MOE_WAIT_VMCNT(C::copies(3));
+  // Wait until at most `nb` steps of this wave's copies are still in flight.
+  auto wait_copies = [&](auto NB) {
+    constexpr int nb = decltype(NB)::v;
+    if (wave == 0) MOE_WAIT_VMCNT(nb * C::copies(0));
+    else if (wave == 1) MOE_WAIT_VMCNT(nb * C::copies(1));
+    else if (wave == 2) MOE_WAIT_VMCNT(nb * C::copies(2));
+    else MOE_WAIT_VMCNT(nb * C::copies(3));
   };
 
   v16f acc[2][NF];
 
-  // Compute one step out of LDS buffer `buf`: both MFMA halves' fragments are
-  // read first, then 2 x 2 x NF x 2 scaled MFMAs (hi and lo terms of A).
-  auto compute = [&](const uint8_t* buf, int st) {
-    // Steps past K compute nothing. A half step at the end of K (K % 128 == 64)
-    // still takes both MFMA halves: lane half 0 holds blocks 0, 1 (valid), lane
-    // half 1 zero codes with their scale bytes forced finite.
-    if (st >= nst) return;
-    const bool halfst = 4 * st + 2 >= nblkK;
-    v8i ahi[2][2], alo[2][2];
+  // The fragments of one MFMA half of a step: in lane half h, block 2h + s of A
+  // (both terms and their scales) and of B.
+  struct Half {
+    v8i ahi[2], alo[2];
     int sa[2];
+    v8i b[NF];
+    int sb[NF];
+    bool halfst;  // the step's blocks 2, 3 are past K
+  };
+  // The scale dwords of a step serve both halves: half 0 reads them, half 1
+  // takes them from `from` (half 0 of the same step) without touching LDS.
+  auto read_half = [&](const uint8_t* buf, int st, auto S, Half& h, const Half& from) {
+    constexpr int s = decltype(S)::v;
+    h.halfst = 4 * st + 2 >= nblkK;
 #pragma unroll
     for (int mf = 0; mf < 2; ++mf) {
       const uint8_t* rowp = buf + C::A_OFF + (wm * 64 + mf * 32 + lr) * kChunk;
-      const uint4* p = reinterpret_cast<const uint4*>(rowp + half * 96);
-      const uint4 q0 = p[0], q1 = p[1], q2 = p[2], q3 = p[3], q4 = p[4], q5 = p[5];
-      ahi[mf][0] = v8i{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, 0, 0};
-      alo[mf][0] = v8i{(int)q1.z, (int)q1.w, (int)q2.x, (int)q2.y, (int)q2.z, (int)q2.w, 0, 0};
-      ahi[mf][1] = v8i{(int)q3.x, (int)q3.y, (int)q3.z, (int)q3.w, (int)q4.x, (int)q4.y, 0, 0};
-      alo[mf][1] = v8i{(int)q4.z, (int)q4.w, (int)q5.x, (int)q5.y, (int)q5.z, (int)q5.w, 0, 0};
-      const int s = *reinterpret_cast<const int*>(rowp + kChunkScales + 4 * half);
-      sa[mf] = halfst && half ? 0 : s;
+      load_block_terms(rowp + half * 96 + s * kEncBytes, h.ahi[mf], h.alo[mf]);
+      h.sa[mf] = s == 0 ? *reinterpret_cast<const int*>(rowp + kChunkScales + 4 * half) : from.sa[mf];
     }
-    v8i bf[NF][2];
-    int sbs[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int phi = wn * NF + f;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint4 q = reinterpret_cast<const uint4*>(buf + C::B_OFF + (phi * 2 + s) * 1024)[lane];
-        bf[f][s] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      }
-      sbs[f] = reinterpret_cast<const int*>(buf + C::BS_OFF + phi * 256)[lane];
+      h.b[f] = fp4_operand(reinterpret_cast<const v4i*>(buf + C::B_OFF + (phi * 2 + s) * 1024)[lane]);
+      h.sb[f] = s == 0 ? reinterpret_cast<const int*>(buf + C::BS_OFF + phi * 256)[lane] : from.sb[f];
     }
-    // half 0: scale bytes 0 (A hi), 1 (A lo), 0 (B); half 1: bytes 2, 3, 1
+  };
+  // 2 x NF x 2 scaled MFMAs: the hi terms of all tiles, then the lo terms, so
+  // that no MFMA waits on the accumulator of the one just before it. Scale
+  // bytes: A hi 2s, A lo 2s+1, B s. A half step at the end of K (K % 128 == 64)
+  // still takes both MFMA halves: lane half 0 holds blocks 0, 1 (valid), lane
+  // half 1 zero codes whose scale bytes (never written) are forced finite.
+  auto mma_half = [&](const Half& h, auto S) {
+    constexpr int s = decltype(S)::v;
+    int sa[2];
+#pragma unroll
+    for (int mf = 0; mf < 2; ++mf) sa[mf] = h.halfst && half ? 0 : h.sa[mf];
 #pragma unroll
     for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ahi[mf][0], bf[f][0], acc[mf][f], 2, 4,
-                                                                    0, sa[mf], 0, sbs[f]);
-        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo[mf][0], bf[f][0], acc[mf][f], 2, 4,
-                                                                    1, sa[mf], 0, sbs[f]);
-      }
+      for (int f = 0; f < NF; ++f)
+        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(h.ahi[mf], h.b[f], acc[mf][f], 2, 4,
+                                                                    2 * s, sa[mf], s, h.sb[f]);
 #pragma unroll
     for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ahi[mf][1], bf[f][1], acc[mf][f], 2, 4,
-                                                                    2, sa[mf], 1, sbs[f]);
-        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo[mf][1], bf[f][1], acc[mf][f], 2, 4,
-                                                                    3, sa[mf], 1, sbs[f]);
-      }
+      for (int f = 0; f < NF; ++f)
+        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(h.alo[mf], h.b[f], acc[mf][f], 2, 4,
+                                                                    2 * s + 1, sa[mf], s, h.sb[f]);
   };
 
-  // One step: wait for this wave's copies of step st, barrier (everyone's copies
-  // of st have landed and everyone has finished reading the buffer that the copy
-  // issued next overwrites), copy step st+2, compute step st.
-  auto step = [&](int st, const uint8_t* cur, uint8_t* nxt2) {
-    wait_step();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");  // no LDS access moves across the barrier
-    __builtin_amdgcn_sched_barrier(0);
-    issue(st + 2, nxt2);
-    compute(cur, st);
-  };
-
-  // ---- accumulators start at the bias of their output column
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-#pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mf][f][i] = bias[f];
-  __builtin_amdgcn_sched_barrier(0);
-
+  // ---- first tile (its fetches wait; later tiles' do not)
+  Pre R, E;
+  bool more = logical + nslot < xend, more2 = logical + 2 * nslot < xend;
+  {
+    Pre e0, p0, e1;
+    fetch_entry(logical, e0);
+    if (more) fetch_entry(logical + nslot, e1);
+    if (more2) fetch_entry(logical + 2 * nslot, E);
+    fetch_rest(e0, p0);
+    if (more) fetch_rest(e1, R);
+    setup(p0);
+  }
   issue(0, st0);
   issue(1, st1);
-  // Steps go in threes (one per buffer); steps past the end copy zeros and
-  // compute nothing.
-  for (int t = 0; t < nst; t += 3) {
-    step(t, st0, st2);
-    step(t + 1, st1, st0);
-    step(t + 2, st2, st1);
-  }
-  MOE_WAIT_VMCNT(0);
-  __syncthreads();
+  issue(2, st2);
 
-  if constexpr (GATEUP) {
-    // h = silu(g) * u; per gate group f, the wave's two 32x32 tiles go to LDS as
-    // 64 rows x 32 columns and each lane encodes one row's 32-column block as
-    // two-term MXFP6 into the row's step chunk.
-    float* ep = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 64 * C::EP_PITCH;
-    const uint32_t hpitch = (uint32_t)nsteps_of(a.F) * kChunk;
-    const int grow = m0 + wm * 64 + lane;
+  for (;;) {
 #pragma unroll
-    for (int f = 0; f < C::FM; ++f) {
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mf][f][i] = bias[f];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- main loop, software-pipelined: the LDS reads of one MFMA half overlap
+    // the MFMAs of the other. Per step st (its data in `c0`, half 0 already in
+    // registers): read half 1, compute half 0; then, once every wave has read
+    // `c0` and step st+1 has landed (barrier), copy step st+3 into `c0`, read
+    // half 0 of step st+1 from `c1` and compute half 1. Three steps of copies
+    // are in flight ahead of the one being read.
+    Half h0, h1;
+    wait_copies(IC<2>{});
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    read_half(st0, 0, IC<0>{}, h0, h0);
+    auto body = [&](int st, uint8_t* c0, const uint8_t* c1) {
+      if (st < nst) {
+        read_half(c0, st, IC<1>{}, h1, h0);
+        __builtin_amdgcn_sched_barrier(0);  // the reads go out before the MFMAs they overlap
+        mma_half(h0, IC<0>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_WAIT_LGKM0();      // this wave's reads of `c0` are complete
+      wait_copies(IC<1>{});  // its copies of step st+1 have landed
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");  // no LDS access moves across the barrier
+      __builtin_amdgcn_sched_barrier(0);
+      issue(st + 3, c0);
+      if (st + 1 < nst) read_half(c1, st + 1, IC<0>{}, h0, h0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < nst) mma_half(h1, IC<1>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Steps go in threes (one per buffer); steps past the end copy zeros and
+    // compute nothing.
+    for (int t = 0; t < nst; t += 3) {
+      body(t, st0, st1);
+      body(t + 1, st1, st2);
+      body(t + 2, st2, st0);
+    }
+    MOE_WAIT_VMCNT(0);
+    __syncthreads();
+
+    // ---- this tile's output coordinates; the next tile's first steps are copied
+    // while this tile's epilogue runs (gate/up stages through st2, so its third
+    // step waits for the epilogue); the fetches for the tiles after it are
+    // issued after the epilogue and complete while the next tile is computed
+    const int c_off = off, c_m0 = m0, c_cnt = cnt, c_rows = rows_valid, c_col0 = col0;
+    const bool more3 = logical + 3 * nslot < xend;
+    if (more) {
+      setup(R);
+      issue(0, st0);
+      issue(1, st1);
+      if (!GATEUP) issue(2, st2);
+    }
+
+    if constexpr (GATEUP) {
+      // h = silu(g) * u; per gate group f, the wave's two 32x32 tiles go to LDS as
+      // 64 rows x 32 columns and each lane encodes one row's 32-column block as
+      // two-term MXFP6 into the row's step chunk.
+      float* ep = reinterpret_cast<float*>(st2) + wave * 64 * C::EP_PITCH;
+      const uint32_t hpitch = (uint32_t)nsteps_of(a.F) * kChunk;
+      const int grow = c_m0 + wm * 64 + lane;
+#pragma unroll
+      for (int f = 0; f < C::FM; ++f) {
+#pragma unroll
+        for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rr = mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const float g = acc[mf][f][i], u = acc[mf][f + C::FM][i];
+            ep[rr * C::EP_PITCH + lr] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+          }
+        __builtin_amdgcn_wave_barrier();
+        float v[32];
+        const float4* src = reinterpret_cast<const float4*>(ep + lane * C::EP_PITCH);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 t4 = src[q];
+          v[4 * q] = t4.x;
+          v[4 * q + 1] = t4.y;
+          v[4 * q + 2] = t4.z;
+          v[4 * q + 3] = t4.w;
+        }
+        __builtin_amdgcn_wave_barrier();
+        uint32_t hw[6], lw[6], sc;
+        encode_block(v, hw, lw, sc);
+        if (grow < c_cnt) {
+          const int b = (c_col0 + wn * C::FM * 32 + f * 32) / 32;
+          uint8_t* hrow = hout + (size_t)(c_off + grow) * hpitch;
+          store_enc(hrow + enc_codes_at(b), hw, lw);
+          *reinterpret_cast<uint16_t*>(hrow + enc_scale_at(b)) = static_cast<uint16_t>(sc);
+        }
+      }
+    } else {
 #pragma unroll
       for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int rr = mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const float g = acc[mf][f][i], u = acc[mf][f + C::FM][i];
-          ep[rr * C::EP_PITCH + lr] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-        }
-      __builtin_amdgcn_wave_barrier();
-      float v[32];
-      const float4* src = reinterpret_cast<const float4*>(ep + lane * C::EP_PITCH);
+          const int rr = wm * 64 + mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (rr < c_rows) {
+            float* yr = a.y_sorted + (size_t)(c_off + c_m0 + rr) * N + c_col0 + wn * NF * 32 + lr;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 t4 = src[q];
-        v[4 * q] = t4.x;
-        v[4 * q + 1] = t4.y;
-        v[4 * q + 2] = t4.z;
-        v[4 * q + 3] = t4.w;
-      }
-      __builtin_amdgcn_wave_barrier();
-      uint32_t hw[6], lw[6], sc;
-      encode_block(v, hw, lw, sc);
-      if (grow < cnt) {
-        const int b = (col0 + wn * C::FM * 32 + f * 32) / 32;
-        uint8_t* hrow = hout + (size_t)(off + grow) * hpitch;
-        store_enc(hrow + enc_codes_at(b), hw, lw);
-        *reinterpret_cast<uint16_t*>(hrow + enc_scale_at(b)) = static_cast<uint16_t>(sc);
-      }
+            for (int f = 0; f < NF; ++f) yr[f * 32] = acc[mf][f][i];
+          }
+        }
     }
-  } else {
-#pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rr = wm * 64 + mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (rr < rows_valid) {
-          float* yr = a.y_sorted + (size_t)(off + m0 + rr) * N + col0 + wn * NF * 32 + lr;
-#pragma unroll
-          for (int f = 0; f < NF; ++f) yr[f * 32] = acc[mf][f][i];
-        }
-      }
+    if (!more) break;
+    if (more2) fetch_rest(E, R);
+    if (more3) fetch_entry(logical + 3 * nslot, E);
+    if (GATEUP) {
+      __syncthreads();  // every wave is done with st2
+      issue(2, st2);
+    }
+    logical += nslot;
+    more = more2;
+    more2 = more3;
   }
 }
 
@@ -675,14 +800,12 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
         const int jj = st * kDecSS + u;
         if (jj < nst) {
           const uint8_t* rowp = sA[buf] + l16 * kDecAPitch + u * kChunk;
-          const uint4* pa = reinterpret_cast<const uint4*>(rowp + q * kEncBytes);
-          const uint4 x0 = pa[0], x1 = pa[1], x2 = pa[2];
-          const v8i ahi = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, 0, 0};
-          const v8i alo = {(int)x1.z, (int)x1.w, (int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w, 0, 0};
+          v8i ahi, alo;
+          load_block_terms(rowp + q * kEncBytes, ahi, alo);
           int as = *reinterpret_cast<const uint16_t*>(rowp + kChunkScales + 2 * q);
           if (4 * jj + 2 >= nblkK && q >= 2) as = 0;  // blocks past K: zero codes, finite scales
           const int bs = bsrow[jj * 64] >> (8 * (q & 1));
-          const v8i b = {(int)cur.w[u].x, (int)cur.w[u].y, (int)cur.w[u].z, (int)cur.w[u].w, 0, 0, 0, 0};
+          const v8i b = fp4_operand(v4i{(int)cur.w[u].x, (int)cur.w[u].y, (int)cur.w[u].z, (int)cur.w[u].w});
           acc = mfma16_f6f4<0>(ahi, b, acc, as, bs);
           acc = mfma16_f6f4<1>(alo, b, acc, as, bs);
         }
@@ -727,27 +850,34 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
 // ------------------------------------------------------------------ host side
 
 struct WsLayout {
-  size_t x, h, tp, total;
+  size_t x, h, tiles, total;
 };
+
+// upper bound on the number of prefill row tiles: sum over experts of ceil(count / kBM)
+int max_row_tiles(int T, int E, int k) {
+  const int P = T * k;
+  return (P + kBM - 1) / kBM + (E < P ? E : P);
+}
 
 WsLayout ws_layout(int T, int d, int F, int E, int k) {
   WsLayout L;
   const size_t P = (size_t)T * k;
   L.x = 0;
   L.h = L.x + align256((size_t)T * nsteps_of(d) * kChunk);
-  L.tp = L.h + align256(P * nsteps_of(F) * kChunk);
-  L.total = L.tp + align256((size_t)(E + 1) * 4);
+  L.tiles = L.h + align256(P * nsteps_of(F) * kChunk);
+  L.total = L.tiles + align256((size_t)(1 + max_row_tiles(T, E, k)) * sizeof(int4));
   return L;
 }
 
 template <int NF, bool GATEUP>
-hipError_t launch_prefill(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, const int32_t* tp,
-                          hipStream_t stream) {
+hipError_t launch_prefill(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, const int4* tp,
+                          int ncu, hipStream_t stream) {
   const int N = GATEUP ? a.F : a.d;
   const int ntn = N / Prefill<NF, GATEUP>::MROWS;
-  const int P = a.T * a.k;
-  const int mt_max = (P + kBM - 1) / kBM + (a.E < P ? a.E : P);
-  const long long grid = (long long)mt_max * ntn;
+  // persistent: one workgroup per CU (the LDS holds one), 8 per XCD at least
+  const long long tiles_max = (long long)max_row_tiles(a.T, a.E, a.k) * ntn;
+  long long grid = ncu < tiles_max ? ncu : tiles_max;
+  grid = grid < 8 ? 8 : grid & ~7LL;
   hipLaunchKernelGGL((grouped_prefill<NF, GATEUP>), dim3((unsigned)grid), dim3(256), 0, stream, a,
                      ain, hout, tp, ntn);
   return hipGetLastError();
@@ -781,10 +911,14 @@ size_t ffn_workspace_bytes(int T, int d, int F, int E, int k) {
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   const WsLayout L = ws_layout(a.T, a.d, a.F, a.E, a.k);
+  int dev = 0, ncu = 0;
+  hipError_t qerr = hipGetDevice(&dev);
+  if (qerr == hipSuccess) qerr = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (qerr != hipSuccess) return qerr;
   uint8_t* ws = static_cast<uint8_t*>(a.ws);
   uint8_t* xenc = ws + L.x;
   uint8_t* henc = ws + L.h;
-  int32_t* tp = reinterpret_cast<int32_t*>(ws + L.tp);
+  int4* tp = reinterpret_cast<int4*>(ws + L.tiles);
 
   const int nx = a.T * (a.d / 32);
   if (nx <= 16384)
@@ -801,7 +935,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   const bool dec_gu = a.T <= kDecodeMaxT && decode_fits(a.d);
   const bool dec_dn = a.T <= kDecodeMaxT && decode_fits(a.F);
   if (!dec_gu || !dec_dn) {
-    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // Column tiles: the widest that divides N (gate/up: 32*NF h-columns, down:
@@ -809,18 +943,18 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   if (dec_gu) {
     err = launch_decode<true>(a, xenc, henc, stream);
   } else if (a.F % 192 == 0) {
-    err = launch_prefill<6, true>(a, xenc, henc, tp, stream);
+    err = launch_prefill<6, true>(a, xenc, henc, tp, ncu, stream);
   } else if (a.F % 128 == 0) {
-    err = launch_prefill<4, true>(a, xenc, henc, tp, stream);
+    err = launch_prefill<4, true>(a, xenc, henc, tp, ncu, stream);
   } else {
-    err = launch_prefill<2, true>(a, xenc, henc, tp, stream);
+    err = launch_prefill<2, true>(a, xenc, henc, tp, ncu, stream);
   }
   if (err != hipSuccess) return err;
   if (dec_dn) return launch_decode<false>(a, henc, henc, stream);
-  if (a.d % 320 == 0) return launch_prefill<5, false>(a, henc, henc, tp, stream);
-  if (a.d % 192 == 0) return launch_prefill<3, false>(a, henc, henc, tp, stream);
-  if (a.d % 128 == 0) return launch_prefill<2, false>(a, henc, henc, tp, stream);
-  return launch_prefill<1, false>(a, henc, henc, tp, stream);
+  if (a.d % 320 == 0) return launch_prefill<5, false>(a, henc, henc, tp, ncu, stream);
+  if (a.d % 192 == 0) return launch_prefill<3, false>(a, henc, henc, tp, ncu, stream);
+  if (a.d % 128 == 0) return launch_prefill<2, false>(a, henc, henc, tp, ncu, stream);
+  return launch_prefill<1, false>(a, henc, henc, tp, ncu, stream);
 }
 
 }  // namespace moe

@@ -26,7 +26,40 @@
 namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+
+// MFMA operands built from loads without register copies: the FP6 operand uses
+// 6 of its 8 registers and the FP4 operand 4; the unused ones are left undefined
+// (shuffle index -1) rather than zeroed, so every load can land directly in the
+// operand's registers.
+__device__ __forceinline__ v8i fp6_operand(v4i w03, v2i w45) {
+  const v4i t = __builtin_shufflevector(w45, w45, 0, 1, -1, -1);
+  return __builtin_shufflevector(w03, t, 0, 1, 2, 3, 4, 5, -1, -1);
+}
+__device__ __forceinline__ v8i fp6_operand(v2i w01, v4i w25) {
+  const v4i t = __builtin_shufflevector(w01, w01, 0, 1, -1, -1);
+  return __builtin_shufflevector(t, w25, 0, 1, 4, 5, 6, 7, -1, -1);
+}
+__device__ __forceinline__ v8i fp4_operand(v4i w) {
+  return __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+// One encoded 32-element block in LDS (48 bytes at p, 16-byte aligned): hi term
+// in bytes 0..23, lo term in bytes 24..47. The lo term is read through an LDS
+// address the compiler cannot relate to p, so that it does not fuse the hi
+// term's last 8 bytes and the lo term's first 8 into one 16-byte read (which
+// would then need register copies to assemble the operands, and those copies
+// wait for the read).
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+typedef __attribute__((address_space(3))) const v2i lds_v2i;
+__device__ __forceinline__ void load_block_terms(const uint8_t* p, v8i& hi, v8i& lo) {
+  const uint32_t a = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint8_t*)p;
+  uint32_t b = a + 24;
+  asm volatile("" : "+v"(b));
+  hi = fp6_operand(*(lds_v4i*)(size_t)a, *(lds_v2i*)(size_t)(a + 16));
+  lo = fp6_operand(*(lds_v2i*)(size_t)b, *(lds_v4i*)(size_t)(b + 8));
+}
 
 // 2^n for n in [-127, 127] as an fp32 (2^-127 is subnormal).
 __device__ __forceinline__ float pow2i(int n) {
