@@ -91,16 +91,18 @@ __global__ __launch_bounds__(256) void encode_rows(const uint16_t* __restrict__ 
 
 // ------------------------------------------------------------------ tile table
 
-// The prefill grid's tile table, built on the device from the expert offsets:
-// table[0].x = number of row tiles (sum over experts of ceil(count / kBM));
+// Row-tile table of the grouped GEMMs, built on the device from the expert
+// offsets (BM = 128 rows for the prefill tiles, 16 for the decode passes):
+// table[0].x = number of row tiles (sum over experts of ceil(count / BM));
 // table[1 + mt] = {expert, first row of the tile within the expert, offsets[e],
 // count_e} for row tile mt, tiles in expert order. One 16-byte load gives a
 // workgroup everything it needs to locate its rows.
+template <int BM>
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int4* __restrict__ table) {
   __shared__ int s[257];
   const int t = threadIdx.x;
-  const int v = t < E ? (offsets[t + 1] - offsets[t] + kBM - 1) / kBM : 0;
+  const int v = t < E ? (offsets[t + 1] - offsets[t] + BM - 1) / BM : 0;
   s[t + 1] = v;
   if (t == 0) s[0] = 0;
   __syncthreads();
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
       if (s[mid] <= mt) lo = mid; else hi = mid;
     }
     const int o = offsets[lo];
-    table[1 + mt] = make_int4(lo, (mt - s[lo]) * kBM, o, offsets[lo + 1] - o);
+    table[1 + mt] = make_int4(lo, (mt - s[lo]) * BM, o, offsets[lo + 1] - o);
   }
 }
 
@@ -612,21 +614,24 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
 
 // ------------------------------------------------------------------ decode
 
-// Weight streaming for few rows per expert. One workgroup per (expert, 32
-// h-columns) for gate/up -- waves 0,1 stream the two 16-row halves of the gate
-// group, waves 2,3 those of the up group -- or per (expert, 64 output columns)
-// for down -- wave w streams the 16-row half w&1 of group 2j + w/2. Each
-// wavefront uses the 16x16x128 scaled MFMA (16 rows = one decode-sized row
-// tile) over the whole of K. K is processed in stages of kDecSS steps, fully
-// unrolled at compile time (NSTAGE stages): the weight codes and the activation
-// window of stage s+kDecPF are issued while stage s is computed, held in
-// register rings, and the window is copied to LDS one stage before it is read,
-// so the activations are read from L2 once per workgroup rather than once per
-// wavefront. Loads are issued in the order they are consumed, so waiting for one
-// never waits for a younger one (the vector memory counter retires in order).
-// All global reads are buffer loads: blocks past K and rows past the count read
-// as zero. The packed weight scales of the workgroup's two groups (all of K) are
-// staged in LDS once.
+// Weight streaming for few rows per expert, persistent. The work is a list of
+// items (expert pass, column group): a pass is up to 16 dispatch rows of one
+// expert (the decode tile table), a column group is 32 h-columns for gate/up
+// -- waves 0,1 stream the two 16-row halves of the gate group, waves 2,3 those
+// of the up group -- or 64 output columns for down -- wave w streams the 16-row
+// half w&1 of group 2j + w/2. Each workgroup takes every G-th item of the list.
+// Each wavefront uses the 16x16x128 scaled MFMA (16 rows = one pass) over the
+// whole of K, in stages of kDecSS steps, fully unrolled (NSTAGE stages, a
+// multiple of the ring depth so the ring continues from one item to the next):
+// the weight codes and the activation window of stage s+kDecPF are issued while
+// stage s is computed, held in a register ring, and the window is copied to LDS
+// one stage before it is read, so the activations are read from L2 once per
+// workgroup. The last kDecPF stages of an item issue the first stages of the
+// workgroup's next item, whose table entry, dispatch entries, bias and packed
+// weight scales were fetched one item ahead (the entry two items ahead): the
+// weight stream never drains between items. Loads are issued in the order they
+// are consumed, so waiting for one never waits for a younger one. All global
+// reads are buffer loads: blocks past K and rows past the count read as zero.
 //
 // 16x16x128 layout (checked on gfx950): lane l supplies row/column l%16 and K
 // elements 32*(l/16) .. +31 of the step; result lane l holds column l%16, rows
@@ -639,192 +644,240 @@ __device__ __forceinline__ v4f mfma16_f6f4(const v8i& a, const v8i& b, const v4f
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 2, 4, OPA, sa, 0, sb);
 }
 
+constexpr int kDecRows = 16;                         // dispatch rows per pass
 constexpr int kDecSS = 4;                            // 128-deep steps per stage
 constexpr int kDecPF = 2;                            // stages of loads in flight ahead of the one computed
-constexpr int kDecMaxStages = 8;                     // decode kernels cover K <= kDecMaxStages * kDecSS * 128
-constexpr int kDecMaxSteps = kDecMaxStages * kDecSS;
+constexpr int kDecMaxSteps = 32;                     // decode kernels cover K <= 32 * 128
 constexpr int kDecAPitch = kDecSS * kChunk + 16;     // LDS bytes per activation row (padded: no bank conflicts)
-constexpr int kDecAPieces = 16 * kDecSS * kChunkPieces;  // 16-byte pieces of one stage's window
+constexpr int kDecAPieces = kDecRows * kDecSS * kChunkPieces;  // 16-byte pieces of one stage's window
 constexpr int kDecAPerT = (kDecAPieces + 255) / 256;     // ... per thread (at most)
 static_assert(kDecMaxSteps * kWSStep / 16 <= 256, "one scale piece per thread and group");
 
 template <bool GATEUP, int NSTAGE>
 __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const uint8_t* __restrict__ ain,
-                                                         uint8_t* __restrict__ hout) {
-  constexpr int COLS = GATEUP ? 32 : 64;  // output columns per workgroup
+                                                         uint8_t* __restrict__ hout,
+                                                         const int4* __restrict__ passes) {
+  constexpr int COLS = GATEUP ? 32 : 64;  // output columns per item
   constexpr int PF = kDecPF;
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][16 * kDecAPitch];
-  // packed weight scales of the two groups: [group][step][lane] uint16
-  __shared__ __attribute__((aligned(16))) uint16_t sBs[2 * kDecMaxSteps * 64];
-  __shared__ __attribute__((aligned(16))) float gtile[GATEUP ? 2 * 16 * 36 : 4];
+  static_assert(NSTAGE % (PF + 1) == 0, "the ring continues across items");
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kDecRows * kDecAPitch];
+  // packed weight scales of an item's two groups, by item parity: [item&1][group][step][lane] uint16
+  __shared__ __attribute__((aligned(16))) uint16_t sBs[2][2 * kDecMaxSteps * 64];
+  __shared__ __attribute__((aligned(16))) float gtile[GATEUP ? 2 * kDecRows * 36 : 4];
 
   const int K = GATEUP ? a.d : a.F;
   const int N = GATEUP ? a.F : a.d;
   const int nblkK = K / 32;
   const int nst = nsteps_of(K);      // 128-deep steps (the last may be half: K % 128 == 64)
-  const int ncb = N / COLS;
-  const int e = blockIdx.x / ncb;
-  const int j = blockIdx.x - e * ncb;
-  const int off = a.offsets[e];
-  const int cnt = a.offsets[e + 1] - off;
-  if (cnt == 0) return;
+  const int ncol = N / COLS;
+  const int nitems = __builtin_amdgcn_readfirstlane(passes[0].x) * ncol;
+  const int G = gridDim.x;
+  int item = blockIdx.x;
+  if (item >= nitems) return;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
   const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
   const int sub = wave & 1;                          // 16-row half of the group
-  const int g = GATEUP ? j : 2 * j + (wave >> 1);    // this wave's 32-row weight group
   const bool up = GATEUP && wave >= 2;
-  const int n = 32 * g + 16 * sub + l16;             // output column of this lane
-  const uint8_t* codes = GATEUP ? (up ? a.wu_codes : a.wg_codes) : a.wd_codes;
-  const size_t gstride = (size_t)nst * kWStep;
-  const rsrc_t wr = make_rsrc(codes + ((size_t)e * (N / 32) + g) * gstride, (uint32_t)gstride);
+  const uint32_t apitch = (uint32_t)nst * kChunk;
+  const uint32_t gstride = (uint32_t)nst * kWStep, sstride = (uint32_t)nst * kWSStep;
+  const uint64_t kmagic = div_magic((uint32_t)a.k);  // token of dispatch pair q: q / k
   // lane (column l16, K sub-block q): half q&1, lane 32*(q/2) + 16*sub + l16 of the packed step
   const uint32_t wl = (uint32_t)(q & 1) * 1024 + (uint32_t)((q >> 1) * 32 + 16 * sub + l16) * 16;
-  const float bias = bf16_to_f32((GATEUP ? (up ? a.b_up : a.b_gate) : a.b_down)[(size_t)e * N + n]);
-  const uint32_t apitch = (uint32_t)nst * kChunk;
-  // activation rows: gathered tokens (gate/up) or this expert's rows of h (down)
-  const rsrc_t ar = GATEUP ? make_rsrc(ain, (uint32_t)a.T * apitch)
-                           : make_rsrc(ain + (size_t)off * apitch, (uint32_t)cnt * apitch);
-  const uint64_t kmagic = div_magic((uint32_t)a.k);  // token of dispatch pair q: q / k
+  const uint8_t* codes = GATEUP ? (up ? a.wu_codes : a.wg_codes) : a.wd_codes;
+  const uint16_t* bias_src = GATEUP ? (up ? a.b_up : a.b_gate) : a.b_down;
+  const rsrc_t ar_x = make_rsrc(ain, (uint32_t)a.T * apitch);
 
-  const size_t sstride = (size_t)nst * kWSStep;
-  const uint8_t* s0 = (GATEUP ? a.wg_scales : a.wd_scales) + ((size_t)e * (N / 32) + (GATEUP ? j : 2 * j)) * sstride;
-  const uint8_t* s1 = GATEUP ? a.wu_scales + ((size_t)e * (N / 32) + j) * sstride : s0 + sstride;
-  const rsrc_t rs0 = make_rsrc(s0, (uint32_t)sstride), rs1 = make_rsrc(s1, (uint32_t)sstride);
+  // window piece c = tid + 256i: row c / 52, step u = (c % 52) / 13, piece c % 13
+  int alds[kDecAPerT], au[kDecAPerT], ap[kDecAPerT], arw[kDecAPerT];
+#pragma unroll
+  for (int i = 0; i < kDecAPerT; ++i) {
+    const int c = tid + 256 * i;
+    arw[i] = c / (kDecSS * kChunkPieces);
+    const int rem = c - arw[i] * (kDecSS * kChunkPieces);
+    au[i] = rem / kChunkPieces;
+    ap[i] = rem - au[i] * kChunkPieces;
+    alds[i] = arw[i] * kDecAPitch + au[i] * kChunk + ap[i] * 16;
+  }
 
-  // one stage's worth of loads for this thread
+  // ---- what an item needs, fetched ahead: the table entry (two items ahead),
+  // then (one item ahead) the dispatch entries of the window rows, the bias of
+  // this lane's column and the packed scales of the item's two groups
+  struct Ahead {
+    int4 ent;          // {expert, first row within the expert, offsets[e], count_e}
+    int j;             // column group
+    uint32_t src[kDecAPerT];
+    uint32_t bias;
+    uint4 bs0, bs1;
+  };
+  auto fetch_entry = [&](int it, Ahead& A) {
+    A.j = it % ncol;
+    A.ent = passes[1 + it / ncol];
+  };
+  auto fetch_rest = [&](Ahead& A) {
+    const int e = __builtin_amdgcn_readfirstlane(A.ent.x);
+    const int m0 = __builtin_amdgcn_readfirstlane(A.ent.y), off = __builtin_amdgcn_readfirstlane(A.ent.z);
+    const int rows = min(kDecRows, __builtin_amdgcn_readfirstlane(A.ent.w) - m0);
+    const int j = A.j;
+#pragma unroll
+    for (int i = 0; i < kDecAPerT; ++i) {
+      const int r = min(arw[i], rows - 1);
+      A.src[i] = GATEUP ? (uint32_t)a.sorted_pair[off + m0 + r] : (uint32_t)(off + m0 + r);
+    }
+    const int g = GATEUP ? j : 2 * j + (wave >> 1);
+    A.bias = bias_src[(size_t)e * N + 32 * g + 16 * sub + l16];
+    const uint8_t* s0 = (GATEUP ? a.wg_scales : a.wd_scales) + ((size_t)e * (N / 32) + (GATEUP ? j : 2 * j)) * sstride;
+    const uint8_t* s1 = GATEUP ? a.wu_scales + ((size_t)e * (N / 32) + j) * sstride : s0 + sstride;
+    const uint32_t o = tid < nst * (kWSStep / 16) ? (uint32_t)tid * 16 : kOutOfRange;
+    A.bs0 = bload16(make_rsrc(s0, sstride), o);
+    A.bs1 = bload16(make_rsrc(s1, sstride), o);
+  };
+
+  // ---- the item being issued (its weight resource and window offsets)
+  struct Issue {
+    rsrc_t wr, ar;
+    uint32_t arow[kDecAPerT];
+  };
+  auto make_issue = [&](const Ahead& A, Issue& I) {
+    const int e = __builtin_amdgcn_readfirstlane(A.ent.x);
+    const int m0 = __builtin_amdgcn_readfirstlane(A.ent.y);
+    const int rows = min(kDecRows, __builtin_amdgcn_readfirstlane(A.ent.w) - m0);
+    const int g = GATEUP ? A.j : 2 * A.j + (wave >> 1);
+    I.wr = make_rsrc(codes + ((size_t)e * (N / 32) + g) * gstride, gstride);
+    I.ar = GATEUP ? ar_x : make_rsrc(ain, (uint32_t)(a.T * a.k) * apitch);
+#pragma unroll
+    for (int i = 0; i < kDecAPerT; ++i) {
+      const int c = tid + 256 * i;
+      const bool ok = c < kDecAPieces && arw[i] < rows;
+      const uint32_t row = GATEUP ? div_by(A.src[i], kmagic) : A.src[i];
+      I.arow[i] = ok ? row * apitch + (uint32_t)(au[i] * kChunk + ap[i] * 16) : kOutOfRange;
+    }
+  };
+
+  // One ring slot: the weights of a stage and the activation window of the
+  // stage after it. The window is copied to LDS at the end of the stage before
+  // the one that reads it, so it travels in the batch of loads of that earlier
+  // stage: copying it then never waits for loads younger than the ones the
+  // stage just computed already needed (the vector memory counter retires in
+  // order).
   struct Packet {
     uint4 w[kDecSS];              // weight codes (MFMA B operand, this lane)
-    uint4 a[kDecAPerT];           // activation window pieces (staged to LDS)
+    uint4 a[kDecAPerT];           // activation window pieces of the next stage (staged to LDS)
   };
-  // The step's distance along K goes into the uniform buffer offset, so the
-  // per-lane offsets are the same in every stage. In a half step at the end of K
-  // the lanes of sub-blocks 2, 3 read nothing.
-  auto issue_w = [&](int st, Packet& pk) {
+  // Stage st of an item: the step's distance along K goes into the uniform
+  // buffer offset, so the per-lane offsets are the same in every stage. In a
+  // half step at the end of K the lanes of sub-blocks 2, 3 read nothing.
+  auto issue_w = [&](const Issue& I, int st, Packet& pk) {
 #pragma unroll
     for (int u = 0; u < kDecSS; ++u) {
       const int jj = st * kDecSS + u;
       const bool live = jj < nst && (4 * jj + 2 < nblkK || q < 2);
-      pk.w[u] = bload16(wr, live ? wl : kOutOfRange, (uint32_t)jj * kWStep);
+      pk.w[u] = bload16(I.wr, live ? wl : kOutOfRange, (uint32_t)jj * kWStep);
+    }
+  };
+  auto issue_a = [&](const Issue& I, int st, uint4 (&dst)[kDecAPerT]) {
+#pragma unroll
+    for (int i = 0; i < kDecAPerT; ++i) {
+      const int jj = st * kDecSS + au[i];
+      const bool pad = 4 * jj + 2 >= nblkK && ap[i] >= 6 && ap[i] < 12;
+      dst[i] = bload16(I.ar, jj < nst && !pad ? I.arow[i] : kOutOfRange, (uint32_t)(st * kDecSS) * kChunk);
+    }
+  };
+  auto stage_to_lds = [&](const uint4 (&win)[kDecAPerT], int buf) {
+#pragma unroll
+    for (int i = 0; i < kDecAPerT; ++i)
+      if (tid + 256 * i < kDecAPieces) *reinterpret_cast<uint4*>(sA[buf] + alds[i]) = win[i];
+  };
+  auto scales_to_lds = [&](const Ahead& A, int par) {
+    if (tid < nst * (kWSStep / 16)) {
+      *reinterpret_cast<uint4*>(sBs[par] + tid * 8) = A.bs0;
+      *reinterpret_cast<uint4*>(sBs[par] + kDecMaxSteps * 64 + tid * 8) = A.bs1;
     }
   };
 
-  for (int m0 = 0; m0 < cnt; m0 += 16) {
-    const int rows = min(16, cnt - m0);
-    Packet ring[PF + 1];
-    __syncthreads();  // LDS of the previous row tile is no longer read
+  // ---- prologue: the first item's data (these fetches wait), the next item's
+  // rest and the entry of the one after
+  Ahead cur, nxt, nn;
+  bool has1 = item + G < nitems, has2 = item + 2 * G < nitems;
+  fetch_entry(item, cur);
+  if (has1) fetch_entry(item + G, nxt);
+  if (has2) fetch_entry(item + 2 * G, nn);
+  fetch_rest(cur);
+  if (has1) fetch_rest(nxt);
+  Issue ic, in;
+  make_issue(cur, ic);
+  Packet ring[PF + 1];
+  {
+    uint4 win0[kDecAPerT];
+    issue_a(ic, 0, win0);
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      issue_w(ic, p, ring[p]);
+      if (p + 1 < NSTAGE) issue_a(ic, p + 1, ring[p].a);
+    }
+    scales_to_lds(cur, 0);
+    stage_to_lds(win0, 0);
+  }
+  __syncthreads();
 
-    // ---- prologue. Loads are issued in this order: the weight codes of the
-    // first PF stages (they depend on nothing), the weight scales (first row
-    // tile only), the window pieces' dispatch entries; then, once those have
-    // arrived, the activation windows. So the prologue costs two memory
-    // latencies, and the first weights arrive meanwhile.
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-      if (p < NSTAGE) issue_w(p, ring[p]);
-    uint4 bsv0, bsv1;
-    if (m0 == 0) {
-      const uint32_t o = tid < nst * (kWSStep / 16) ? (uint32_t)tid * 16 : kOutOfRange;
-      bsv0 = bload16(rs0, o);
-      bsv1 = bload16(rs1, o);
+  for (int n = 0;; ++n) {
+    const int par = n & 1;
+    const int m0 = __builtin_amdgcn_readfirstlane(cur.ent.y);
+    const int off = __builtin_amdgcn_readfirstlane(cur.ent.z);
+    const int rows = min(kDecRows, __builtin_amdgcn_readfirstlane(cur.ent.w) - m0);
+    const int j = cur.j;
+    const int pb = (n * NSTAGE) & 1;  // window buffer of this item's stage 0
+    v4f acc;
+    {
+      const float b = bf16_to_f32((uint16_t)cur.bias);
+      acc = v4f{b, b, b, b};
     }
-    // window piece c = tid + 256i: row c / 52, step u = (c % 52) / 13, piece c % 13
-    uint32_t arow[kDecAPerT];
-    int alds[kDecAPerT], au[kDecAPerT], ap[kDecAPerT];
-#pragma unroll
-    for (int i = 0; i < kDecAPerT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (kDecSS * kChunkPieces), rem = c - row * (kDecSS * kChunkPieces);
-      au[i] = rem / kChunkPieces;
-      ap[i] = rem - au[i] * kChunkPieces;
-      alds[i] = row * kDecAPitch + au[i] * kChunk + ap[i] * 16;
-      arow[i] = (uint32_t)min(row, rows - 1);
-    }
-    if (GATEUP) {
-#pragma unroll
-      for (int i = 0; i < kDecAPerT; ++i) arow[i] = (uint32_t)a.sorted_pair[off + m0 + arow[i]];
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int i = 0; i < kDecAPerT; ++i) arow[i] = div_by(arow[i], kmagic);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kDecAPerT; ++i) arow[i] += (uint32_t)m0;
-    }
-#pragma unroll
-    for (int i = 0; i < kDecAPerT; ++i) {
-      const int c = tid + 256 * i;
-      const bool ok = c < kDecAPieces && c / (kDecSS * kChunkPieces) < rows;
-      arow[i] = ok ? arow[i] * apitch + (uint32_t)(au[i] * kChunk + ap[i] * 16) : kOutOfRange;
-    }
-    auto issue_a = [&](int st, Packet& pk) {
-#pragma unroll
-      for (int i = 0; i < kDecAPerT; ++i) {
-        const int jj = st * kDecSS + au[i];
-        const bool pad = 4 * jj + 2 >= nblkK && ap[i] >= 6 && ap[i] < 12;
-        pk.a[i] = bload16(ar, jj < nst && !pad ? arow[i] : kOutOfRange,
-                          (uint32_t)(st * kDecSS) * kChunk);
-      }
-    };
-    auto stage_to_lds = [&](const Packet& pk, int buf) {
-#pragma unroll
-      for (int i = 0; i < kDecAPerT; ++i)
-        if (tid + 256 * i < kDecAPieces) *reinterpret_cast<uint4*>(sA[buf] + alds[i]) = pk.a[i];
-    };
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-      if (p < NSTAGE) issue_a(p, ring[p]);
-
-    // ---- weight scales to LDS (their loads are older than the windows': storing
-    // them does not wait for the windows)
-    if (m0 == 0 && tid < nst * (kWSStep / 16)) {
-      *reinterpret_cast<uint4*>(sBs + tid * 8) = bsv0;
-      *reinterpret_cast<uint4*>(sBs + kDecMaxSteps * 64 + tid * 8) = bsv1;
-    }
-
-    v4f acc = v4f{bias, bias, bias, bias};
-    auto issue = [&](int st, Packet& pk) {
-      issue_w(st, pk);
-      issue_a(st, pk);
-    };
-    const uint16_t* bsrow = sBs + (wave >> 1) * kDecMaxSteps * 64 + (q >> 1) * 32 + 16 * sub + l16;
-    stage_to_lds(ring[0], 0);
-    __syncthreads();
+    const uint16_t* bsrow = sBs[par] + (wave >> 1) * kDecMaxSteps * 64 + (q >> 1) * 32 + 16 * sub + l16;
 #pragma unroll
     for (int st = 0; st < NSTAGE; ++st) {
-      if (st + PF < NSTAGE) issue(st + PF, ring[(st + PF) % (PF + 1)]);
-      const Packet& cur = ring[st % (PF + 1)];
-      const int buf = st & 1;
+      // slot of stage st + PF: its weights and the window of the stage after it,
+      // of this item or of the next
+      if (st == NSTAGE - PF - 1 && has1) make_issue(nxt, in);
+      Packet& pn = ring[(st + PF) % (PF + 1)];
+      if (st + PF < NSTAGE) issue_w(ic, st + PF, pn);
+      else if (has1) issue_w(in, st + PF - NSTAGE, pn);
+      if (st + PF + 1 < NSTAGE) issue_a(ic, st + PF + 1, pn.a);
+      else if (has1) issue_a(in, st + PF + 1 - NSTAGE, pn.a);
+      const Packet& pc = ring[st % (PF + 1)];
+      const uint8_t* wbuf = sA[(pb + st) & 1];
 #pragma unroll
       for (int u = 0; u < kDecSS; ++u) {
         const int jj = st * kDecSS + u;
         if (jj < nst) {
-          const uint8_t* rowp = sA[buf] + l16 * kDecAPitch + u * kChunk;
+          const uint8_t* rowp = wbuf + l16 * kDecAPitch + u * kChunk;
           v8i ahi, alo;
           load_block_terms(rowp + q * kEncBytes, ahi, alo);
           int as = *reinterpret_cast<const uint16_t*>(rowp + kChunkScales + 2 * q);
           if (4 * jj + 2 >= nblkK && q >= 2) as = 0;  // blocks past K: zero codes, finite scales
           const int bs = bsrow[jj * 64] >> (8 * (q & 1));
-          const v8i b = fp4_operand(v4i{(int)cur.w[u].x, (int)cur.w[u].y, (int)cur.w[u].z, (int)cur.w[u].w});
+          const v8i b = fp4_operand(v4i{(int)pc.w[u].x, (int)pc.w[u].y, (int)pc.w[u].z, (int)pc.w[u].w});
           acc = mfma16_f6f4<0>(ahi, b, acc, as, bs);
           acc = mfma16_f6f4<1>(alo, b, acc, as, bs);
         }
       }
-      if (st + 1 < NSTAGE) stage_to_lds(ring[(st + 1) % (PF + 1)], (st + 1) & 1);
+      if (st == NSTAGE - 1 && has1) scales_to_lds(nxt, par ^ 1);
+      if (st + 1 < NSTAGE || has1) stage_to_lds(pc.a, (pb + st + 1) & 1);
       __syncthreads();
     }
 
+    // ---- epilogue of this item (the next item's first stages are in flight)
     if constexpr (GATEUP) {
       // waves 0,1 hold g, waves 2,3 hold u for the same 16 rows x 32 columns;
       // then one lane per row encodes the row's 32-column block of h
-      float* t = gtile + (wave >> 1) * 16 * 36;
+      float* t = gtile + (wave >> 1) * kDecRows * 36;
 #pragma unroll
       for (int i = 0; i < 4; ++i) t[(4 * q + i) * 36 + sub * 16 + l16] = acc[i];
       __syncthreads();
       if (tid < rows) {
         float v[32];
         const float4* g4 = reinterpret_cast<const float4*>(gtile + tid * 36);
-        const float4* u4 = reinterpret_cast<const float4*>(gtile + 16 * 36 + tid * 36);
+        const float4* u4 = reinterpret_cast<const float4*>(gtile + kDecRows * 36 + tid * 36);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const float4 gg = g4[c], uu = u4[c];
@@ -840,23 +893,38 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
         *reinterpret_cast<uint16_t*>(hrow + enc_scale_at(j)) = static_cast<uint16_t>(sc);
       }
     } else {
+      const int nout = 32 * (2 * j + (wave >> 1)) + 16 * sub + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (4 * q + i < rows) a.y_sorted[(size_t)(off + m0 + 4 * q + i) * N + n] = acc[i];
+        if (4 * q + i < rows) a.y_sorted[(size_t)(off + m0 + 4 * q + i) * N + nout] = acc[i];
     }
+    if (!has1) break;
+    // advance: nxt becomes current; its rest was fetched one item ago, the
+    // entry after it two items ago
+    const bool has3 = item + 3 * G < nitems;
+    item += G;
+    cur = nxt;
+    ic = in;
+    if (has2) {
+      nxt = nn;
+      fetch_rest(nxt);
+    }
+    if (has3) fetch_entry(item + 2 * G, nn);
+    has1 = has2;
+    has2 = has3;
   }
 }
 
 // ------------------------------------------------------------------ host side
 
 struct WsLayout {
-  size_t x, h, tiles, total;
+  size_t x, h, tiles, passes, total;
 };
 
-// upper bound on the number of prefill row tiles: sum over experts of ceil(count / kBM)
-int max_row_tiles(int T, int E, int k) {
+// upper bound on the number of row tiles of BM rows: sum over experts of ceil(count / BM)
+int max_row_tiles(int T, int E, int k, int BM) {
   const int P = T * k;
-  return (P + kBM - 1) / kBM + (E < P ? E : P);
+  return (P + BM - 1) / BM + (E < P ? E : P);
 }
 
 WsLayout ws_layout(int T, int d, int F, int E, int k) {
@@ -865,7 +933,8 @@ WsLayout ws_layout(int T, int d, int F, int E, int k) {
   L.x = 0;
   L.h = L.x + align256((size_t)T * nsteps_of(d) * kChunk);
   L.tiles = L.h + align256(P * nsteps_of(F) * kChunk);
-  L.total = L.tiles + align256((size_t)(1 + max_row_tiles(T, E, k)) * sizeof(int4));
+  L.passes = L.tiles + align256((size_t)(1 + max_row_tiles(T, E, k, kBM)) * sizeof(int4));
+  L.total = L.passes + align256((size_t)(1 + max_row_tiles(T, E, k, kDecRows)) * sizeof(int4));
   return L;
 }
 
@@ -875,7 +944,7 @@ hipError_t launch_prefill(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, c
   const int N = GATEUP ? a.F : a.d;
   const int ntn = N / Prefill<NF, GATEUP>::MROWS;
   // persistent: one workgroup per CU (the LDS holds one), 8 per XCD at least
-  const long long tiles_max = (long long)max_row_tiles(a.T, a.E, a.k) * ntn;
+  const long long tiles_max = (long long)max_row_tiles(a.T, a.E, a.k, kBM) * ntn;
   long long grid = ncu < tiles_max ? ncu : tiles_max;
   grid = grid < 8 ? 8 : grid & ~7LL;
   hipLaunchKernelGGL((grouped_prefill<NF, GATEUP>), dim3((unsigned)grid), dim3(256), 0, stream, a,
@@ -883,25 +952,49 @@ hipError_t launch_prefill(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, c
   return hipGetLastError();
 }
 
-template <bool GATEUP>
-hipError_t launch_decode(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, hipStream_t stream) {
-  const int K = GATEUP ? a.d : a.F;
+template <bool GATEUP, int NSTAGE>
+hipError_t launch_decode_n(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, const int4* passes,
+                           int ncu, hipStream_t stream) {
   const int N = GATEUP ? a.F : a.d;
-  const dim3 grid(a.E * (N / (GATEUP ? 32 : 64)));
-  const int nstage = (nsteps_of(K) + kDecSS - 1) / kDecSS;
-#define MOE_DECODE_CASE(S) \
-  case S: hipLaunchKernelGGL((grouped_decode<GATEUP, S>), grid, dim3(256), 0, stream, a, ain, hout); break;
-  switch (nstage) {
-    MOE_DECODE_CASE(1) MOE_DECODE_CASE(2) MOE_DECODE_CASE(3) MOE_DECODE_CASE(4)
-    MOE_DECODE_CASE(5) MOE_DECODE_CASE(6) MOE_DECODE_CASE(7) MOE_DECODE_CASE(8)
-    default: return hipErrorInvalidValue;  // callers route K beyond this to the prefill kernel
-  }
-#undef MOE_DECODE_CASE
-  static_assert(kDecMaxStages == 8, "keep the cases above in step with kDecMaxStages");
+  const long long items_max = (long long)max_row_tiles(a.T, a.E, a.k, kDecRows) * (N / (GATEUP ? 32 : 64));
+  int occ = 0;
+  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, grouped_decode<GATEUP, NSTAGE>, 256, 0);
+  if (err != hipSuccess) return err;
+  long long grid = (long long)ncu * (occ > 0 ? occ : 1);
+  if (grid > items_max) grid = items_max;
+  hipLaunchKernelGGL((grouped_decode<GATEUP, NSTAGE>), dim3((unsigned)grid), dim3(256), 0, stream, a, ain,
+                     hout, passes);
   return hipGetLastError();
 }
 
-bool decode_fits(int K) { return (nsteps_of(K) + kDecSS - 1) / kDecSS <= kDecMaxStages; }
+// Stages of kDecSS steps, rounded up to a multiple of the ring depth.
+int decode_stages(int K) {
+  const int s = (nsteps_of(K) + kDecSS - 1) / kDecSS;
+  return (s + kDecPF) / (kDecPF + 1) * (kDecPF + 1);
+}
+
+// Stage counts M * (kDecPF + 1) for M = 1 .. (enough for kDecMaxSteps).
+constexpr int kDecMaxM = ((kDecMaxSteps + kDecSS - 1) / kDecSS + kDecPF) / (kDecPF + 1);
+template <bool GATEUP, int M>
+hipError_t launch_decode_m(int nstage, const FfnArgs& a, const uint8_t* ain, uint8_t* hout,
+                           const int4* passes, int ncu, hipStream_t stream) {
+  if constexpr (M == 0) {
+    return hipErrorInvalidValue;  // callers route K beyond this to the prefill kernel
+  } else {
+    if (nstage == M * (kDecPF + 1))
+      return launch_decode_n<GATEUP, M * (kDecPF + 1)>(a, ain, hout, passes, ncu, stream);
+    return launch_decode_m<GATEUP, M - 1>(nstage, a, ain, hout, passes, ncu, stream);
+  }
+}
+
+template <bool GATEUP>
+hipError_t launch_decode(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, const int4* passes, int ncu,
+                         hipStream_t stream) {
+  return launch_decode_m<GATEUP, kDecMaxM>(decode_stages(GATEUP ? a.d : a.F), a, ain, hout, passes, ncu,
+                                            stream);
+}
+
+bool decode_fits(int K) { return nsteps_of(K) <= kDecMaxSteps; }
 
 }  // namespace
 
@@ -934,14 +1027,19 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   // encoded layouts, so they can be mixed).
   const bool dec_gu = a.T <= kDecodeMaxT && decode_fits(a.d);
   const bool dec_dn = a.T <= kDecodeMaxT && decode_fits(a.F);
+  int4* pp = reinterpret_cast<int4*>(ws + L.passes);
   if (!dec_gu || !dec_dn) {
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);
+    hipLaunchKernelGGL(tile_table_kernel<kBM>, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (dec_gu || dec_dn) {
+    hipLaunchKernelGGL(tile_table_kernel<kDecRows>, dim3(1), dim3(256), 0, stream, a.offsets, a.E, pp);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // Column tiles: the widest that divides N (gate/up: 32*NF h-columns, down:
   // 64*NF output columns per workgroup).
   if (dec_gu) {
-    err = launch_decode<true>(a, xenc, henc, stream);
+    err = launch_decode<true>(a, xenc, henc, pp, ncu, stream);
   } else if (a.F % 192 == 0) {
     err = launch_prefill<6, true>(a, xenc, henc, tp, ncu, stream);
   } else if (a.F % 128 == 0) {
@@ -950,7 +1048,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
     err = launch_prefill<2, true>(a, xenc, henc, tp, ncu, stream);
   }
   if (err != hipSuccess) return err;
-  if (dec_dn) return launch_decode<false>(a, henc, henc, stream);
+  if (dec_dn) return launch_decode<false>(a, henc, henc, pp, ncu, stream);
   if (a.d % 320 == 0) return launch_prefill<5, false>(a, henc, henc, tp, ncu, stream);
   if (a.d % 192 == 0) return launch_prefill<3, false>(a, henc, henc, tp, ncu, stream);
   if (a.d % 128 == 0) return launch_prefill<2, false>(a, henc, henc, tp, ncu, stream);
