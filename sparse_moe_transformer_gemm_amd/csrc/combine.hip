@@ -3,7 +3,9 @@
 // experts' outputs). Atomic-free: each output element is owned by one thread,
 // which gathers the token's k expert rows through pair_row and sums them in
 // fixed slot order in fp32, then rounds once to bf16 (nearest even).
-// Memory-bound: 16-byte loads of y, 8-byte stores of out; one block per token row.
+// Memory-bound: 16-byte loads of y, 8-byte stores of out; one block per (token
+// row, 1024 columns), one 4-column chunk per thread, so all of a thread's k
+// loads are in flight at once.
 #include "common.hpp"
 
 namespace moe {
@@ -24,7 +26,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
   }
   uint2* o = reinterpret_cast<uint2*>(out + (size_t)t * d);
-  for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c < d / 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -47,8 +50,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_row, const float* topk_w,
                           int T, int d, int k, uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, y_sorted, pair_row, topk_w, d,
-                     k, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(T, (d / 4 + 255) / 256), dim3(256), 0, stream, y_sorted,
+                     pair_row, topk_w, d, k, out);
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ namespace {
 constexpr int kBM = 128;        // rows per prefill tile
 constexpr int kPrefGM = 8;      // row tiles per raster group of the prefill grid
 constexpr int kDecodeMaxT = 64; // decode kernels when T <= this
+constexpr int kDecRows = 16;    // dispatch rows per decode pass
 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
@@ -44,6 +45,57 @@ __device__ __forceinline__ uint32_t enc_pitch(int K) { return (uint32_t)nsteps_o
 __device__ __forceinline__ uint32_t enc_codes_at(int b) { return (b >> 2) * kChunk + (b & 3) * kEncBytes; }
 __device__ __forceinline__ uint32_t enc_scale_at(int b) { return (b >> 2) * kChunk + kChunkScales + (b & 3) * 2; }
 
+// ------------------------------------------------------------------ tile table
+
+// Row-tile table of the grouped GEMMs, built on the device from the expert
+// offsets by one workgroup (BM = 128 rows for the prefill tiles, 16 for the
+// decode passes; `s` is 257 ints of LDS):
+// table[0].x = number of row tiles (sum over experts of ceil(count / BM));
+// table[1 + mt] = {expert, first row of the tile within the expert, offsets[e],
+// count_e} for row tile mt, tiles in expert order. One 16-byte load gives a
+// workgroup everything it needs to locate its rows.
+template <int BM>
+__device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ offsets, int E,
+                                                 int4* __restrict__ table, int* s) {
+  const int t = threadIdx.x;
+  const int v = t < E ? (offsets[t + 1] - offsets[t] + BM - 1) / BM : 0;
+  s[t + 1] = v;
+  if (t == 0) s[0] = 0;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of s[1..256]
+    const int add = t >= off ? s[t + 1 - off] : 0;
+    __syncthreads();
+    s[t + 1] += add;
+    __syncthreads();
+  }
+  const int total = s[E];
+  if (t == 0) table[0] = make_int4(total, 0, 0, 0);
+  for (int mt = t; mt < total; mt += 256) {
+    int lo = 0, hi = E;  // s[lo] <= mt < s[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s[mid] <= mt) lo = mid; else hi = mid;
+    }
+    const int o = offsets[lo];
+    table[1 + mt] = make_int4(lo, (mt - s[lo]) * BM, o, offsets[lo + 1] - o);
+  }
+}
+
+// The tables the GEMMs of this call need, built by one extra workgroup of the
+// activation encoder (same launch); either pointer may be null.
+struct TableJob {
+  const int32_t* offsets;
+  int E;
+  int4* tiles;   // 128-row prefill tiles
+  int4* passes;  // 16-row decode passes
+};
+__device__ __forceinline__ void build_tables(const TableJob& tj) {
+  __shared__ int s[257];
+  if (tj.tiles) build_tile_table<kBM>(tj.offsets, tj.E, tj.tiles, s);
+  __syncthreads();
+  if (tj.passes) build_tile_table<kDecRows>(tj.offsets, tj.E, tj.passes, s);
+}
+
 // ------------------------------------------------------------------ encode x
 
 // Activation encoding, two shapes: few rows (decode) -- one (row, 32-element
@@ -51,7 +103,12 @@ __device__ __forceinline__ uint32_t enc_scale_at(int b) { return (b >> 2) * kChu
 // cooperatively (short latency); many rows (prefill) -- one block per thread
 // (no barriers, throughput).
 __global__ __launch_bounds__(256) void encode_rows_thread(const uint16_t* __restrict__ x, int rows,
-                                                          int K, uint8_t* __restrict__ enc) {
+                                                          int K, uint8_t* __restrict__ enc,
+                                                          const TableJob tj) {
+  if (blockIdx.x == gridDim.x - 1) {
+    build_tables(tj);
+    return;
+  }
   const int nblk = K / 32;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * nblk) return;
@@ -76,7 +133,11 @@ __global__ __launch_bounds__(256) void encode_rows_thread(const uint16_t* __rest
 }
 
 __global__ __launch_bounds__(256) void encode_rows(const uint16_t* __restrict__ x, int rows,
-                                                   int K, uint8_t* __restrict__ enc) {
+                                                   int K, uint8_t* __restrict__ enc, const TableJob tj) {
+  if (blockIdx.x == gridDim.x - 1) {
+    build_tables(tj);
+    return;
+  }
   __shared__ uint8_t scratch[8 * 64];
   const int nblk = K / 32;
   const int nrec = rows * nblk;
@@ -87,42 +148,6 @@ __global__ __launch_bounds__(256) void encode_rows(const uint16_t* __restrict__ 
   uint8_t* r = enc + (size_t)row * enc_pitch(K);
   encode_group32(v, scratch + (threadIdx.x >> 5) * 64, r + enc_codes_at(b),
                  reinterpret_cast<uint16_t*>(r + enc_scale_at(b)), g < nrec);
-}
-
-// ------------------------------------------------------------------ tile table
-
-// Row-tile table of the grouped GEMMs, built on the device from the expert
-// offsets (BM = 128 rows for the prefill tiles, 16 for the decode passes):
-// table[0].x = number of row tiles (sum over experts of ceil(count / BM));
-// table[1 + mt] = {expert, first row of the tile within the expert, offsets[e],
-// count_e} for row tile mt, tiles in expert order. One 16-byte load gives a
-// workgroup everything it needs to locate its rows.
-template <int BM>
-__global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets, int E,
-                                                         int4* __restrict__ table) {
-  __shared__ int s[257];
-  const int t = threadIdx.x;
-  const int v = t < E ? (offsets[t + 1] - offsets[t] + BM - 1) / BM : 0;
-  s[t + 1] = v;
-  if (t == 0) s[0] = 0;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of s[1..256]
-    const int add = t >= off ? s[t + 1 - off] : 0;
-    __syncthreads();
-    s[t + 1] += add;
-    __syncthreads();
-  }
-  const int total = s[E];
-  if (t == 0) table[0] = make_int4(total, 0, 0, 0);
-  for (int mt = t; mt < total; mt += 256) {
-    int lo = 0, hi = E;  // s[lo] <= mt < s[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s[mid] <= mt) lo = mid; else hi = mid;
-    }
-    const int o = offsets[lo];
-    table[1 + mt] = make_int4(lo, (mt - s[lo]) * BM, o, offsets[lo + 1] - o);
-  }
 }
 
 // Division by a runtime divisor d >= 1 as a multiply: x / d = (x * m) >> 32 with
@@ -644,7 +669,6 @@ __device__ __forceinline__ v4f mfma16_f6f4(const v8i& a, const v8i& b, const v4f
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 2, 4, OPA, sa, 0, sb);
 }
 
-constexpr int kDecRows = 16;                         // dispatch rows per pass
 constexpr int kDecSS = 4;                            // 128-deep steps per stage
 constexpr int kDecPF = 2;                            // stages of loads in flight ahead of the one computed
 constexpr int kDecMaxSteps = 32;                     // decode kernels cover K <= 32 * 128
@@ -828,7 +852,9 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
     const int rows = min(kDecRows, __builtin_amdgcn_readfirstlane(cur.ent.w) - m0);
     const int j = cur.j;
     const int pb = (n * NSTAGE) & 1;  // window buffer of this item's stage 0
-    v4f acc;
+    // two accumulators (hi and lo terms), so consecutive MFMAs do not depend on
+    // each other; summed once at the end of the item
+    v4f acc, acc2 = v4f{0.f, 0.f, 0.f, 0.f};
     {
       const float b = bf16_to_f32((uint16_t)cur.bias);
       acc = v4f{b, b, b, b};
@@ -858,7 +884,7 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
           const int bs = bsrow[jj * 64] >> (8 * (q & 1));
           const v8i b = fp4_operand(v4i{(int)pc.w[u].x, (int)pc.w[u].y, (int)pc.w[u].z, (int)pc.w[u].w});
           acc = mfma16_f6f4<0>(ahi, b, acc, as, bs);
-          acc = mfma16_f6f4<1>(alo, b, acc, as, bs);
+          acc2 = mfma16_f6f4<1>(alo, b, acc2, as, bs);
         }
       }
       if (st == NSTAGE - 1 && has1) scales_to_lds(nxt, par ^ 1);
@@ -867,6 +893,7 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
     }
 
     // ---- epilogue of this item (the next item's first stages are in flight)
+    acc += acc2;
     if constexpr (GATEUP) {
       // waves 0,1 hold g, waves 2,3 hold u for the same 16 rows x 32 columns;
       // then one lane per row encodes the row's 32-column block of h
@@ -1013,29 +1040,23 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   uint8_t* henc = ws + L.h;
   int4* tp = reinterpret_cast<int4*>(ws + L.tiles);
 
-  const int nx = a.T * (a.d / 32);
-  if (nx <= 16384)
-    hipLaunchKernelGGL(encode_rows, dim3((nx + 7) / 8), dim3(256), 0, stream, a.x, a.T, a.d, xenc);
-  else
-    hipLaunchKernelGGL(encode_rows_thread, dim3((nx + 255) / 256), dim3(256), 0, stream, a.x, a.T,
-                       a.d, xenc);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
   // Per GEMM: the weight-streaming decode kernel for few rows per expert and K
   // it can unroll, the LDS-tiled kernel otherwise (both read/write the same
   // encoded layouts, so they can be mixed).
   const bool dec_gu = a.T <= kDecodeMaxT && decode_fits(a.d);
   const bool dec_dn = a.T <= kDecodeMaxT && decode_fits(a.F);
   int4* pp = reinterpret_cast<int4*>(ws + L.passes);
-  if (!dec_gu || !dec_dn) {
-    hipLaunchKernelGGL(tile_table_kernel<kBM>, dim3(1), dim3(256), 0, stream, a.offsets, a.E, tp);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  if (dec_gu || dec_dn) {
-    hipLaunchKernelGGL(tile_table_kernel<kDecRows>, dim3(1), dim3(256), 0, stream, a.offsets, a.E, pp);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
+  const TableJob tj{a.offsets, a.E, (!dec_gu || !dec_dn) ? tp : nullptr, (dec_gu || dec_dn) ? pp : nullptr};
+
+  // x is encoded once; one extra workgroup of the same launch builds the tables
+  const int nx = a.T * (a.d / 32);
+  if (nx <= 16384)
+    hipLaunchKernelGGL(encode_rows, dim3((nx + 7) / 8 + 1), dim3(256), 0, stream, a.x, a.T, a.d, xenc, tj);
+  else
+    hipLaunchKernelGGL(encode_rows_thread, dim3((nx + 255) / 256 + 1), dim3(256), 0, stream, a.x, a.T,
+                       a.d, xenc, tj);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   // Column tiles: the widest that divides N (gate/up: 32*NF h-columns, down:
   // 64*NF output columns per workgroup).
   if (dec_gu) {

@@ -145,33 +145,13 @@ __device__ __forceinline__ bool better(double va, int ea, double vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
-__global__ __launch_bounds__(256) void route_select(const double* __restrict__ partial, int KS,
-                                                    const float* __restrict__ bias, int T, int E,
-                                                    int k, int32_t* __restrict__ topk_idx,
-                                                    float* __restrict__ topk_w) {
-  __shared__ double part[256];
-  __shared__ double logit[kMaxE];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int G = 256 / E;
-  if (tid < G * E) {
-    const int e = tid % E, g = tid / E;
-    double s = 0.0;
-#pragma unroll 4
-    for (int ks = g; ks < KS; ks += G) s += partial[((size_t)ks * T + t) * E + e];
-    part[g * E + e] = s;
-  }
-  __syncthreads();
-  if (tid < E) {
-    double v = 0.0;
-    for (int g = 0; g < G; ++g) v += part[g * E + tid];
-    if (bias) v += static_cast<double>(bias[tid]);
-    logit[tid] = v;
-  }
-  __syncthreads();
-  if (tid >= kWave) return;
-  const int lane = tid;
-
+// Top-k of the E logits in `logit` (LDS, float64) for token t, by the first
+// wavefront: k rounds of a wavefront-wide (max logit, lowest index) reduction,
+// then the softmax over the picked logits in float64, stored as fp32.
+__device__ __forceinline__ void select_topk(const double* logit, int t, int E, int k,
+                                            int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w) {
+  const int lane = threadIdx.x;
   double v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -221,6 +201,33 @@ __global__ __launch_bounds__(256) void route_select(const double* __restrict__ p
       topk_w[(size_t)t * k + j] = static_cast<float>(exp(sel_v[j] - sel_v[0]) / den);
     }
   }
+}
+
+__global__ __launch_bounds__(256) void route_select(const double* __restrict__ partial, int KS,
+                                                    const float* __restrict__ bias, int T, int E,
+                                                    int k, int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ topk_w) {
+  __shared__ double part[256];
+  __shared__ double logit[kMaxE];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int G = 256 / E;
+  if (tid < G * E) {
+    const int e = tid % E, g = tid / E;
+    double s = 0.0;
+#pragma unroll 4
+    for (int ks = g; ks < KS; ks += G) s += partial[((size_t)ks * T + t) * E + e];
+    part[g * E + e] = s;
+  }
+  __syncthreads();
+  if (tid < E) {
+    double v = 0.0;
+    for (int g = 0; g < G; ++g) v += part[g * E + tid];
+    if (bias) v += static_cast<double>(bias[tid]);
+    logit[tid] = v;
+  }
+  __syncthreads();
+  if (tid < kWave) select_topk(logit, t, E, k, topk_idx, topk_w);
 }
 
 // Few tokens (decode): one workgroup per 64-deep K slice computes every (token,
