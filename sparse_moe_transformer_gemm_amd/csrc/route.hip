@@ -18,9 +18,9 @@
 //                 four wavefronts. Partial sums [slice][T][E] are written through
 //                 an LDS transpose so the stores coalesce.
 //   route_select  one workgroup per token: the K-slice partials are reduced in a
-//                 fixed order (+ bias), then k rounds of a wavefront-wide
-//                 (max logit, lowest index) reduction pick the experts and the
-//                 softmax over the picked logits is taken in float64.
+//                 fixed order (+ bias), each expert's rank in (logit desc, index
+//                 asc) order picks the top k, and the softmax over the picked
+//                 logits is taken in float64.
 #include "common.hpp"
 
 namespace moe {
@@ -145,61 +145,34 @@ __device__ __forceinline__ bool better(double va, int ea, double vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
-// Top-k of the E logits in `logit` (LDS, float64) for token t, by the first
-// wavefront: k rounds of a wavefront-wide (max logit, lowest index) reduction,
-// then the softmax over the picked logits in float64, stored as fp32.
+// Top-k of the E logits in `logit` (LDS, float64) for token t, by the whole
+// workgroup: the rank of expert e is the number of experts that come before it
+// in the order (larger logit first, lower index on equal logits). Ranks are
+// distinct, so the experts of rank < k are the top k in order; a NaN logit has
+// been stored as -inf. Then the softmax over the picked logits in float64, each
+// of the k lanes summing the k exponentials in rank order, stored as fp32.
 __device__ __forceinline__ void select_topk(const double* logit, int t, int E, int k,
+                                            double* sel_v, int* sel_e,
                                             int32_t* __restrict__ topk_idx,
                                             float* __restrict__ topk_w) {
-  const int lane = threadIdx.x;
-  double v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + kWave * i;
-    v[i] = e < E ? logit[e] : -INFINITY;
-  }
-  unsigned taken = 0;
-  double sel_v[8];
-  int sel_e[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    sel_v[j] = 0.0;
-    sel_e[j] = 0;
-    if (j < k) {
-      double bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + kWave * i;
-        if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-          bv = v[i];
-          be = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const double ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        if (better(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      sel_v[j] = bv;
-      sel_e[j] = be;
-      if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
+  const int tid = threadIdx.x;
+  if (tid < E) {
+    const double v = logit[tid];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < E; ++j) rank += better(logit[j], j, v, tid) ? 1 : 0;
+    if (rank < k) {
+      sel_v[rank] = v;
+      sel_e[rank] = tid;
     }
   }
-  double den = 0.0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < k) den += exp(sel_v[j] - sel_v[0]);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < k && lane == j) {
-      topk_idx[(size_t)t * k + j] = sel_e[j];
-      topk_w[(size_t)t * k + j] = static_cast<float>(exp(sel_v[j] - sel_v[0]) / den);
-    }
+  __syncthreads();
+  if (tid < k) {
+    const double m = sel_v[0];
+    double den = 0.0;
+    for (int j = 0; j < k; ++j) den += exp(sel_v[j] - m);
+    topk_idx[(size_t)t * k + tid] = sel_e[tid];
+    topk_w[(size_t)t * k + tid] = static_cast<float>(exp(sel_v[tid] - m) / den);
   }
 }
 
@@ -209,6 +182,8 @@ __global__ __launch_bounds__(256) void route_select(const double* __restrict__ p
                                                     float* __restrict__ topk_w) {
   __shared__ double part[256];
   __shared__ double logit[kMaxE];
+  __shared__ double sel_v[8];
+  __shared__ int sel_e[8];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int G = 256 / E;
@@ -224,10 +199,10 @@ __global__ __launch_bounds__(256) void route_select(const double* __restrict__ p
     double v = 0.0;
     for (int g = 0; g < G; ++g) v += part[g * E + tid];
     if (bias) v += static_cast<double>(bias[tid]);
-    logit[tid] = v;
+    logit[tid] = v == v ? v : -INFINITY;
   }
   __syncthreads();
-  if (tid < kWave) select_topk(logit, t, E, k, topk_idx, topk_w);
+  select_topk(logit, t, E, k, sel_v, sel_e, topk_idx, topk_w);
 }
 
 // Few tokens (decode): one workgroup per 64-deep K slice computes every (token,
@@ -283,11 +258,12 @@ __global__ __launch_bounds__(256) void route_partial_small(const uint16_t* __res
   __syncthreads();
   for (int p = tid; p < T * E; p += 256) {
     const int t = p / E, e = p - t * E;
-    double acc = 0.0;
-#pragma unroll 8
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // four chains (kk mod 4), summed in a fixed order
+#pragma unroll
     for (int kk = 0; kk < 64; ++kk)
-      acc = fma(static_cast<double>(xs[t * 65 + kk]), static_cast<double>(ws[kk * E + e]), acc);
-    partial[((size_t)blockIdx.x * T + t) * E + e] = acc;
+      acc[kk & 3] = fma(static_cast<double>(xs[t * 65 + kk]), static_cast<double>(ws[kk * E + e]),
+                        acc[kk & 3]);
+    partial[((size_t)blockIdx.x * T + t) * E + e] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
 }
 
