@@ -88,9 +88,9 @@ typedef struct {
 
 typedef uint16_t moe_bf16;
 
-/* Bytes of workspace that moe_route, moe_permute and moe_expert_ffn_mxfp4 need
- * for `dims` (one buffer serves all three; it may be reused across calls on
- * one stream). Pure host function; returns 0 for invalid dims. */
+/* Bytes of workspace that moe_route, moe_permute, moe_expert_ffn_mxfp4 and
+ * moe_forward need for `dims` (one buffer serves all of them; it may be reused
+ * across calls on one stream). Pure host function; returns 0 for invalid dims. */
 size_t moe_workspace_bytes(moe_dims dims);
 
 /* Router GEMM, top-k, softmax over the selected logits.
@@ -179,6 +179,28 @@ moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x,
  *   topk_w   [device] fp32 [T][k]; out [device] bf16 [T][d]. */
 moe_status moe_combine(moe_dims dims, const float* y_sorted, const int32_t* pair_row,
                        const float* topk_w, moe_bf16* out, void* stream);
+
+/* The whole block in one call: moe_route, moe_permute, moe_expert_ffn_mxfp4 and
+ * moe_combine in that order, with the same arguments and the same output bytes
+ * (every intermediate output is written as those calls write it). For
+ * decode-sized batches (T <= 64 and d, F <= 4096) routing, permutation and the
+ * activation encode are fused into two launches, so the block takes five
+ * launches instead of eight. ("GPT-OSS el dia 0", section "MLP" and section
+ * "Nuclis per a GPT-OSS / MoE": route, dispatch, expert FFNs, combine.)
+ *   x, w_router, b_router          as for moe_route (b_router may be NULL)
+ *   w_gate, w_up, w_down, biases   as for moe_expert_ffn_mxfp4 (packed weights)
+ *   topk_idx, topk_w               [device] out, as from moe_route
+ *   counts, offsets, sorted_pair, pair_row  [device] out, as from moe_permute
+ *   y_sorted                       [device] out, fp32 [P][d]
+ *   out                            [device] out, bf16 [T][d]
+ *   ws, ws_bytes                   workspace of at least moe_workspace_bytes(dims)
+ * Errors as for the four calls; all checks happen before the first launch. */
+moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
+                       const float* b_router, moe_mxfp4_packed w_gate, moe_mxfp4_packed w_up,
+                       moe_mxfp4_packed w_down, const moe_bf16* b_gate, const moe_bf16* b_up,
+                       const moe_bf16* b_down, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
+                       float* y_sorted, moe_bf16* out, void* ws, size_t ws_bytes, void* stream);
 
 /* RMSNorm of each row (the pre-norm of a transformer block; rms_norm_eps = 1e-5
  * per CSDN "GPT-OSS-120B 4-bit 量化技术深度解析", section "推理优化"):

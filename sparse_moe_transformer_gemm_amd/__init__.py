@@ -21,6 +21,7 @@ __all__ = [
     "MoeError", "Dims", "MXFP4", "library_path", "lib", "workspace_bytes", "route",
     "permute", "expert_ffn_mxfp4", "combine", "rmsnorm", "residual_add", "forward",
     "ExpertWeights", "EXPORTED", "pack_mxfp4", "packed_bytes", "load_expert_weights",
+    "forward_calls",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +29,7 @@ _LIB_NAME = "libmoe_mi355x.so"
 EXPORTED = (
     "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine",
     "moe_rmsnorm", "moe_residual_add", "moe_status_string", "moe_last_error",
-    "moe_mxfp4_packed_bytes", "moe_pack_mxfp4",
+    "moe_mxfp4_packed_bytes", "moe_pack_mxfp4", "moe_forward",
 )
 
 
@@ -70,13 +71,15 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_ffn_mxfp4.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp,
                                        vp, sz, vp]
     L.moe_combine.argtypes = [Dims, vp, vp, vp, vp, vp]
+    L.moe_forward.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp, vp, vp, vp,
+                              vp, vp, vp, vp, vp, sz, vp]
     L.moe_mxfp4_packed_bytes.argtypes = [i32, i32, i32, i32]
     L.moe_mxfp4_packed_bytes.restype = sz
     L.moe_pack_mxfp4.argtypes = [i32, i32, i32, MXFP4, vp, vp, vp]
     L.moe_rmsnorm.argtypes = [i32, i32, vp, vp, ctypes.c_float, vp, vp]
     L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine", "moe_rmsnorm",
-              "moe_residual_add", "moe_pack_mxfp4"):
+              "moe_residual_add", "moe_pack_mxfp4", "moe_forward"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -220,14 +223,8 @@ def permute(topk_idx, E: int, ws, out=None):
     return counts, offsets, sorted_pair, pair_row
 
 
-def expert_ffn_mxfp4(x, sorted_pair, offsets, w: ExpertWeights, k: int, ws, y_sorted=None):
-    T, d = x.shape
-    dw, F, E = w.dims
-    if dw != d:
-        raise ValueError("x width does not match the router weight")
-    P = T * k
-    if y_sorted is None:
-        y_sorted = torch.empty((P, d), dtype=torch.float32, device=x.device)
+def _packed_args(w: ExpertWeights):
+    d, F, E = w.dims
     u8 = torch.uint8
     gb, ub = packed_bytes(E, F, d), packed_bytes(E, d, F)
     mg = MXFP4(_dev(w.gate_codes, u8, (gb[0],), "gate_codes"),
@@ -236,6 +233,18 @@ def expert_ffn_mxfp4(x, sorted_pair, offsets, w: ExpertWeights, k: int, ws, y_so
                _dev(w.up_scales, u8, (gb[1],), "up_scales"))
     md = MXFP4(_dev(w.down_codes, u8, (ub[0],), "down_codes"),
                _dev(w.down_scales, u8, (ub[1],), "down_scales"))
+    return mg, mu, md
+
+
+def expert_ffn_mxfp4(x, sorted_pair, offsets, w: ExpertWeights, k: int, ws, y_sorted=None):
+    T, d = x.shape
+    dw, F, E = w.dims
+    if dw != d:
+        raise ValueError("x width does not match the router weight")
+    P = T * k
+    if y_sorted is None:
+        y_sorted = torch.empty((P, d), dtype=torch.float32, device=x.device)
+    mg, mu, md = _packed_args(w)
     _check(lib().moe_expert_ffn_mxfp4(
         _dims(T, d, F, E, k), _dev(x, torch.bfloat16, (T, d), "x"),
         _dev(sorted_pair, torch.int32, (P,), "sorted_pair"),
@@ -282,9 +291,58 @@ def residual_add(x, m, out=None):
     return out
 
 
+def _outputs(T, d, E, k, dev, bufs: Optional[dict]) -> dict:
+    b = dict(bufs or {})
+    P = T * k
+    if b.get("topk_idx") is None:
+        b["topk_idx"] = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if b.get("topk_w") is None:
+        b["topk_w"] = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if b.get("perm") is None:
+        b["perm"] = (torch.empty(E, dtype=torch.int32, device=dev),
+                     torch.empty(E + 1, dtype=torch.int32, device=dev),
+                     torch.empty(P, dtype=torch.int32, device=dev),
+                     torch.empty(P, dtype=torch.int32, device=dev))
+    if b.get("y_sorted") is None:
+        b["y_sorted"] = torch.empty((P, d), dtype=torch.float32, device=dev)
+    if b.get("out") is None:
+        b["out"] = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    return b
+
+
 def forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict] = None) -> dict:
-    """The whole block: the four calls in order on the current stream. `bufs`, if
+    """The whole block in one call (moe_forward) on the current stream. `bufs`, if
     given, supplies preallocated outputs (keys as in the returned dict)."""
+    T, d = x.shape
+    dw, F, E = w.dims
+    if dw != d:
+        raise ValueError("x width does not match the router weight")
+    P = T * k
+    b = _outputs(T, d, E, k, x.device, bufs)
+    counts, offsets, sorted_pair, pair_row = b["perm"]
+    mg, mu, md = _packed_args(w)
+    br = None if w.b_router is None else _dev(w.b_router, torch.float32, (E,), "b_router")
+    _check(lib().moe_forward(
+        _dims(T, d, F, E, k), _dev(x, torch.bfloat16, (T, d), "x"),
+        _dev(w.w_router, torch.float32, (d, E), "w_router"), br, mg, mu, md,
+        _dev(w.b_gate, torch.bfloat16, (E, F), "b_gate"),
+        _dev(w.b_up, torch.bfloat16, (E, F), "b_up"),
+        _dev(w.b_down, torch.bfloat16, (E, d), "b_down"),
+        _dev(b["topk_idx"], torch.int32, (T, k), "topk_idx"),
+        _dev(b["topk_w"], torch.float32, (T, k), "topk_w"),
+        _dev(counts, torch.int32, (E,), "counts"),
+        _dev(offsets, torch.int32, (E + 1,), "offsets"),
+        _dev(sorted_pair, torch.int32, (P,), "sorted_pair"),
+        _dev(pair_row, torch.int32, (P,), "pair_row"),
+        _dev(b["y_sorted"], torch.float32, (P, d), "y_sorted"),
+        _dev(b["out"], torch.bfloat16, (T, d), "out"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream()), "moe_forward")
+    return dict(topk_idx=b["topk_idx"], topk_w=b["topk_w"], perm=b["perm"],
+                y_sorted=b["y_sorted"], out=b["out"])
+
+
+def forward_calls(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict] = None) -> dict:
+    """The whole block as the four separate calls in order on the current stream."""
     T, d = x.shape
     _, F, E = w.dims
     b = bufs or {}

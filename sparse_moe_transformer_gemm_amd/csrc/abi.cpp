@@ -65,6 +65,10 @@ size_t workspace_for(const moe_dims& m) {
   size_t a = moe::route_workspace_bytes(m.T, m.d, m.E);
   size_t b = moe::ffn_workspace_bytes(m.T, m.d, m.F, m.E, m.k);
   size_t r = a > b ? a : b;
+  if (moe::forward_front_fits(m.T, m.d, m.F, m.k)) {
+    const size_t c = moe::forward_front_bytes(m.T, m.d, m.F, m.E, m.k);
+    r = r > c ? r : c;
+  }
   return (r + 255) & ~static_cast<size_t>(255);
 }
 
@@ -178,6 +182,59 @@ moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x, const int32_t*
   a.y_sorted = y_sorted;
   a.ws = ws;
   return hip_status(moe::launch_expert_ffn(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
+                       const float* b_router, moe_mxfp4_packed w_gate, moe_mxfp4_packed w_up,
+                       moe_mxfp4_packed w_down, const moe_bf16* b_gate, const moe_bf16* b_up,
+                       const moe_bf16* b_down, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
+                       float* y_sorted, moe_bf16* out, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_ptrs({x, w_router, w_gate.codes, w_gate.scales, w_up.codes, w_up.scales,
+                      w_down.codes, w_down.scales, b_gate, b_up, b_down, topk_idx, topk_w,
+                      counts, offsets, sorted_pair, pair_row, y_sorted, out},
+                     "moe_forward"));
+  if (b_router && !aligned16(b_router)) {
+    set_error("%s", "b_router not 16-byte aligned");
+    return MOE_ERR_INVALID_ARG;
+  }
+  MOE_TRY(check_ws(dims, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::FfnArgs a;
+  a.T = dims.T;
+  a.d = dims.d;
+  a.F = dims.F;
+  a.E = dims.E;
+  a.k = dims.k;
+  a.x = x;
+  a.sorted_pair = sorted_pair;
+  a.offsets = offsets;
+  a.wg_codes = w_gate.codes;
+  a.wg_scales = w_gate.scales;
+  a.wu_codes = w_up.codes;
+  a.wu_scales = w_up.scales;
+  a.wd_codes = w_down.codes;
+  a.wd_scales = w_down.scales;
+  a.b_gate = b_gate;
+  a.b_up = b_up;
+  a.b_down = b_down;
+  a.y_sorted = y_sorted;
+  a.ws = ws;
+  const bool front = moe::forward_front_fits(dims.T, dims.d, dims.F, dims.k);
+  if (front) {
+    MOE_TRY(hip_status(moe::launch_forward_front(x, w_router, b_router, dims.T, dims.d, dims.F,
+                                                 dims.E, dims.k, topk_idx, topk_w, counts, offsets,
+                                                 sorted_pair, pair_row, ws, s)));
+  } else {
+    MOE_TRY(hip_status(moe::launch_route(x, w_router, b_router, dims.T, dims.d, dims.E, dims.k,
+                                         topk_idx, topk_w, ws, s)));
+    MOE_TRY(hip_status(moe::launch_permute(topk_idx, dims.T, dims.E, dims.k, counts, offsets,
+                                           sorted_pair, pair_row, s)));
+  }
+  MOE_TRY(hip_status(moe::launch_expert_ffn(a, s, front)));
+  return hip_status(moe::launch_combine(y_sorted, pair_row, topk_w, dims.T, dims.d, dims.k, out, s));
 }
 
 moe_status moe_combine(moe_dims dims, const float* y_sorted, const int32_t* pair_row,

@@ -60,7 +60,22 @@ struct FfnArgs {
   void* ws;
 };
 size_t ffn_workspace_bytes(int T, int d, int F, int E, int k);
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream);
+// Both expert GEMMs take the weight-streaming decode kernels at this shape.
+bool ffn_decode_shape(int T, int d, int F);
+// front_done: x is already encoded and the pass table built in the workspace
+// (by launch_forward_front); decode shape only.
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_done = false);
+
+// Fused route + permute + activation encode of the whole-block call, for the
+// shapes where forward_front_fits; its scratch follows the FFN workspace and
+// forward_front_bytes is the total.
+bool forward_front_fits(int T, int d, int F, int k);
+size_t forward_front_bytes(int T, int d, int F, int E, int k);
+hipError_t launch_forward_front(const uint16_t* x, const float* w_router, const float* b_router,
+                                int T, int d, int F, int E, int k, int32_t* topk_idx,
+                                float* topk_w, int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_pair, int32_t* pair_row, void* ws,
+                                hipStream_t stream);
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_row, const float* topk_w,
                           int T, int d, int k, uint16_t* out, hipStream_t stream);

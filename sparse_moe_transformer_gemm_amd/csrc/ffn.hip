@@ -27,59 +27,14 @@
 //            (expert, 32 h-columns) or (expert, 64 output columns); each
 //            wavefront streams one 16-row half of a packed 32-row group straight
 //            from HBM into MFMA registers (16x16x128 MFMA, 16 rows per pass).
+#include "ffn_dev.hpp"
 #include "mx6.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kBM = 128;        // rows per prefill tile
 constexpr int kPrefGM = 8;      // row tiles per raster group of the prefill grid
 constexpr int kDecodeMaxT = 64; // decode kernels when T <= this
-constexpr int kDecRows = 16;    // dispatch rows per decode pass
-
-size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
-
-__device__ __forceinline__ uint32_t enc_pitch(int K) { return (uint32_t)nsteps_of(K) * kChunk; }
-
-// Byte offsets of block b's codes and scales inside an encoded row.
-__device__ __forceinline__ uint32_t enc_codes_at(int b) { return (b >> 2) * kChunk + (b & 3) * kEncBytes; }
-__device__ __forceinline__ uint32_t enc_scale_at(int b) { return (b >> 2) * kChunk + kChunkScales + (b & 3) * 2; }
-
-// ------------------------------------------------------------------ tile table
-
-// Row-tile table of the grouped GEMMs, built on the device from the expert
-// offsets by one workgroup (BM = 128 rows for the prefill tiles, 16 for the
-// decode passes; `s` is 257 ints of LDS):
-// table[0].x = number of row tiles (sum over experts of ceil(count / BM));
-// table[1 + mt] = {expert, first row of the tile within the expert, offsets[e],
-// count_e} for row tile mt, tiles in expert order. One 16-byte load gives a
-// workgroup everything it needs to locate its rows.
-template <int BM>
-__device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ offsets, int E,
-                                                 int4* __restrict__ table, int* s) {
-  const int t = threadIdx.x;
-  const int v = t < E ? (offsets[t + 1] - offsets[t] + BM - 1) / BM : 0;
-  s[t + 1] = v;
-  if (t == 0) s[0] = 0;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of s[1..256]
-    const int add = t >= off ? s[t + 1 - off] : 0;
-    __syncthreads();
-    s[t + 1] += add;
-    __syncthreads();
-  }
-  const int total = s[E];
-  if (t == 0) table[0] = make_int4(total, 0, 0, 0);
-  for (int mt = t; mt < total; mt += 256) {
-    int lo = 0, hi = E;  // s[lo] <= mt < s[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s[mid] <= mt) lo = mid; else hi = mid;
-    }
-    const int o = offsets[lo];
-    table[1 + mt] = make_int4(lo, (mt - s[lo]) * BM, o, offsets[lo + 1] - o);
-  }
-}
 
 // The tables the GEMMs of this call need, built by one extra workgroup of the
 // activation encoder (same launch); either pointer may be null.
@@ -138,16 +93,7 @@ __global__ __launch_bounds__(256) void encode_rows(const uint16_t* __restrict__ 
     build_tables(tj);
     return;
   }
-  __shared__ uint8_t scratch[8 * 64];
-  const int nblk = K / 32;
-  const int nrec = rows * nblk;
-  const int g = blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int gg = g < nrec ? g : nrec - 1;
-  const int row = gg / nblk, b = gg - row * nblk;
-  const float v = bf16_to_f32(x[(size_t)gg * 32 + (threadIdx.x & 31)]);
-  uint8_t* r = enc + (size_t)row * enc_pitch(K);
-  encode_group32(v, scratch + (threadIdx.x >> 5) * 64, r + enc_codes_at(b),
-                 reinterpret_cast<uint16_t*>(r + enc_scale_at(b)), g < nrec);
+  encode_rows_group(x, rows, K, enc, blockIdx.x);
 }
 
 // Division by a runtime divisor d >= 1 as a multiply: x / d = (x * m) >> 32 with
@@ -944,27 +890,6 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
 
 // ------------------------------------------------------------------ host side
 
-struct WsLayout {
-  size_t x, h, tiles, passes, total;
-};
-
-// upper bound on the number of row tiles of BM rows: sum over experts of ceil(count / BM)
-int max_row_tiles(int T, int E, int k, int BM) {
-  const int P = T * k;
-  return (P + BM - 1) / BM + (E < P ? E : P);
-}
-
-WsLayout ws_layout(int T, int d, int F, int E, int k) {
-  WsLayout L;
-  const size_t P = (size_t)T * k;
-  L.x = 0;
-  L.h = L.x + align256((size_t)T * nsteps_of(d) * kChunk);
-  L.tiles = L.h + align256(P * nsteps_of(F) * kChunk);
-  L.passes = L.tiles + align256((size_t)(1 + max_row_tiles(T, E, k, kBM)) * sizeof(int4));
-  L.total = L.passes + align256((size_t)(1 + max_row_tiles(T, E, k, kDecRows)) * sizeof(int4));
-  return L;
-}
-
 template <int NF, bool GATEUP>
 hipError_t launch_prefill(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, const int4* tp,
                           int ncu, hipStream_t stream) {
@@ -1029,7 +954,11 @@ size_t ffn_workspace_bytes(int T, int d, int F, int E, int k) {
   return ws_layout(T, d, F, E, k).total;
 }
 
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
+bool ffn_decode_shape(int T, int d, int F) {
+  return T <= kDecodeMaxT && decode_fits(d) && decode_fits(F);
+}
+
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_done) {
   const WsLayout L = ws_layout(a.T, a.d, a.F, a.E, a.k);
   int dev = 0, ncu = 0;
   hipError_t qerr = hipGetDevice(&dev);
@@ -1049,14 +978,20 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   const TableJob tj{a.offsets, a.E, (!dec_gu || !dec_dn) ? tp : nullptr, (dec_gu || dec_dn) ? pp : nullptr};
 
   // x is encoded once; one extra workgroup of the same launch builds the tables
-  const int nx = a.T * (a.d / 32);
-  if (nx <= 16384)
-    hipLaunchKernelGGL(encode_rows, dim3((nx + 7) / 8 + 1), dim3(256), 0, stream, a.x, a.T, a.d, xenc, tj);
-  else
-    hipLaunchKernelGGL(encode_rows_thread, dim3((nx + 255) / 256 + 1), dim3(256), 0, stream, a.x, a.T,
-                       a.d, xenc, tj);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  // (or the fused front end has done both: decode shape only)
+  hipError_t err = hipSuccess;
+  if (front_done) {
+    if (!dec_gu || !dec_dn) return hipErrorInvalidValue;
+  } else {
+    const int nx = a.T * (a.d / 32);
+    if (nx <= 16384)
+      hipLaunchKernelGGL(encode_rows, dim3((nx + 7) / 8 + 1), dim3(256), 0, stream, a.x, a.T, a.d, xenc, tj);
+    else
+      hipLaunchKernelGGL(encode_rows_thread, dim3((nx + 255) / 256 + 1), dim3(256), 0, stream, a.x, a.T,
+                         a.d, xenc, tj);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   // Column tiles: the widest that divides N (gate/up: 32*NF h-columns, down:
   // 64*NF output columns per workgroup).
   if (dec_gu) {

@@ -14,100 +14,18 @@
 // ascending pair order = ascending token order). Only integer LDS atomics are
 // used, so the output is deterministic.
 #include "common.hpp"
+#include "permute_dev.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunk = 2048;
-constexpr int kMaxE = 256;
-
-__global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ idx, int P,
-                                                           int E, int32_t* __restrict__ counts,
-                                                           int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ sorted_pair,
-                                                           int32_t* __restrict__ pair_row) {
-  __shared__ int total[kMaxE];
-  __shared__ int before[kMaxE];
-  __shared__ int scan[kMaxE];
-  __shared__ int run[kMaxE];
-  __shared__ int wcnt[kThreads / kWave][kMaxE];
-
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int lane = tid & (kWave - 1);
-  const int start = blockIdx.x * kChunk;
-  const int end = min(P, start + kChunk);
-
-  for (int e = tid; e < kMaxE; e += kThreads) {
-    total[e] = 0;
-    before[e] = 0;
-    run[e] = 0;
-    for (int w = 0; w < kThreads / kWave; ++w) wcnt[w][e] = 0;
-  }
-  __syncthreads();
-
-  for (int q = tid; q < P; q += kThreads) {
-    const int e = idx[q];
-    atomicAdd(&total[e], 1);
-    if (q < start) atomicAdd(&before[e], 1);
-  }
-  __syncthreads();
-
-  // exclusive scan of total[0..E) (Hillis-Steele over 256 entries)
-  int val = (tid < E) ? total[tid] : 0;
-  scan[tid] = val;
-  __syncthreads();
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    int add = (tid >= off) ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  const int excl = scan[tid] - val;
-  __syncthreads();
-  scan[tid] = excl;
-  if (blockIdx.x == 0 && tid < E) {
-    counts[tid] = val;
-    offsets[tid] = excl;
-    if (tid == E - 1) offsets[E] = excl + val;
-  }
-  __syncthreads();
-
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-
-  for (int s = start; s < end; s += kThreads) {
-    const int q = s + tid;
-    const bool valid = q < end;
-    const int e = valid ? idx[q] : 0;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t set = __ballot(valid && bit);
-      same &= bit ? set : ~set;
-    }
-    const int rank = __popcll(same & lower);
-    if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
-    __syncthreads();
-    if (valid) {
-      int pos = scan[e] + before[e] + run[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-      sorted_pair[pos] = q;
-      pair_row[q] = pos;
-    }
-    __syncthreads();
-    if (tid < E) {
-      int add = 0;
-      for (int w = 0; w < kThreads / kWave; ++w) {
-        add += wcnt[w][tid];
-        wcnt[w][tid] = 0;
-      }
-      run[tid] += add;
-    }
-    __syncthreads();
-  }
+__global__ __launch_bounds__(pm::kThreads) void permute_kernel(const int32_t* __restrict__ idx, int P,
+                                                               int E, int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_pair,
+                                                               int32_t* __restrict__ pair_row) {
+  pm::permute_chunk(idx, P, E, blockIdx.x * pm::kChunk, blockIdx.x == 0, counts, offsets, sorted_pair,
+                    pair_row);
 }
 
 }  // namespace
@@ -116,8 +34,8 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t*
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
                           hipStream_t stream) {
   const int P = T * k;
-  const int blocks = (P + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(kThreads), 0, stream, topk_idx, P, E,
+  const int blocks = (P + pm::kChunk - 1) / pm::kChunk;
+  hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(pm::kThreads), 0, stream, topk_idx, P, E,
                      counts, offsets, sorted_pair, pair_row);
   return hipGetLastError();
 }

@@ -1,0 +1,120 @@
+// Dispatch: per-expert histogram, exclusive scan, stable permutation and its
+// inverse (Perplexity, "GPT-OSS el dia 0", section "Nuclis per a GPT-OSS / MoE":
+// dispatch selects each expert's tokens).
+//
+// Shared by permute.hip and the fused decode front end (front.hip). One
+// kernel, no inter-block communication. Block b owns the pairs
+// [b*kChunk, (b+1)*kChunk). Every block first histograms the whole routing table
+// in LDS (the table is tiny: 4*T int32, L2-resident), counting separately the
+// pairs before its chunk; from that it knows the exclusive scan of the totals
+// and where its own pairs of each expert start. It then ranks its pairs 256 at a
+// time: inside a wavefront, lanes holding the same expert are found with one
+// ballot per expert-index bit and ranked by popcount of the lower lanes; per-
+// wave counts in LDS give the offset across the block's four wavefronts. The
+// result is the unique stable counting sort by expert (pairs of an expert in
+// ascending pair order = ascending token order). Only integer LDS atomics are
+// used, so the output is deterministic.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+namespace pm {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 2048;
+constexpr int kMaxE = 256;
+
+// Pairs [start, min(P, start + kChunk)) of the stable counting sort, by one
+// workgroup of kThreads; the workgroup that owns pair 0 also writes counts and
+// offsets (write_totals).
+__device__ __forceinline__ void permute_chunk(const int32_t* __restrict__ idx, int P, int E,
+                                              int start, bool write_totals,
+                                              int32_t* __restrict__ counts,
+                                              int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ sorted_pair,
+                                              int32_t* __restrict__ pair_row) {
+  __shared__ int total[kMaxE];
+  __shared__ int before[kMaxE];
+  __shared__ int scan[kMaxE];
+  __shared__ int run[kMaxE];
+  __shared__ int wcnt[kThreads / kWave][kMaxE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int end = min(P, start + kChunk);
+
+  for (int e = tid; e < kMaxE; e += kThreads) {
+    total[e] = 0;
+    before[e] = 0;
+    run[e] = 0;
+    for (int w = 0; w < kThreads / kWave; ++w) wcnt[w][e] = 0;
+  }
+  __syncthreads();
+
+  for (int q = tid; q < P; q += kThreads) {
+    const int e = idx[q];
+    atomicAdd(&total[e], 1);
+    if (q < start) atomicAdd(&before[e], 1);
+  }
+  __syncthreads();
+
+  // exclusive scan of total[0..E) (Hillis-Steele over 256 entries)
+  int val = (tid < E) ? total[tid] : 0;
+  scan[tid] = val;
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    int add = (tid >= off) ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int excl = scan[tid] - val;
+  __syncthreads();
+  scan[tid] = excl;
+  if (write_totals && tid < E) {
+    counts[tid] = val;
+    offsets[tid] = excl;
+    if (tid == E - 1) offsets[E] = excl + val;
+  }
+  __syncthreads();
+
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+
+  for (int s = start; s < end; s += kThreads) {
+    const int q = s + tid;
+    const bool valid = q < end;
+    const int e = valid ? idx[q] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t set = __ballot(valid && bit);
+      same &= bit ? set : ~set;
+    }
+    const int rank = __popcll(same & lower);
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int pos = scan[e] + before[e] + run[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      sorted_pair[pos] = q;
+      pair_row[q] = pos;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int add = 0;
+      for (int w = 0; w < kThreads / kWave; ++w) {
+        add += wcnt[w][tid];
+        wcnt[w][tid] = 0;
+      }
+      run[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace pm
+}  // namespace moe

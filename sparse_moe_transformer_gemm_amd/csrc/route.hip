@@ -22,6 +22,7 @@
 //                 asc) order picks the top k, and the softmax over the picked
 //                 logits is taken in float64.
 #include "common.hpp"
+#include "route_dev.hpp"
 
 namespace moe {
 namespace {
@@ -29,7 +30,6 @@ namespace {
 constexpr int kTok = 256;     // tokens per logits block (4 wavefronts, one lane per token)
 constexpr int kEG = 32;       // experts per group (accumulators per lane)
 constexpr int kKC = 64;       // K depth of one LDS stage
-constexpr int kMaxE = 256;
 constexpr int kTargetBlocks = 480;
 
 struct RoutePlan {
@@ -141,130 +141,18 @@ __global__ __launch_bounds__(256) void route_logits(const uint16_t* __restrict__
   }
 }
 
-__device__ __forceinline__ bool better(double va, int ea, double vb, int eb) {
-  return va > vb || (va == vb && ea < eb);
-}
-
-// Top-k of the E logits in `logit` (LDS, float64) for token t, by the whole
-// workgroup: the rank of expert e is the number of experts that come before it
-// in the order (larger logit first, lower index on equal logits). Ranks are
-// distinct, so the experts of rank < k are the top k in order; a NaN logit has
-// been stored as -inf. Then the softmax over the picked logits in float64, each
-// of the k lanes summing the k exponentials in rank order, stored as fp32.
-__device__ __forceinline__ void select_topk(const double* logit, int t, int E, int k,
-                                            double* sel_v, int* sel_e,
-                                            int32_t* __restrict__ topk_idx,
-                                            float* __restrict__ topk_w) {
-  const int tid = threadIdx.x;
-  if (tid < E) {
-    const double v = logit[tid];
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < E; ++j) rank += better(logit[j], j, v, tid) ? 1 : 0;
-    if (rank < k) {
-      sel_v[rank] = v;
-      sel_e[rank] = tid;
-    }
-  }
-  __syncthreads();
-  if (tid < k) {
-    const double m = sel_v[0];
-    double den = 0.0;
-    for (int j = 0; j < k; ++j) den += exp(sel_v[j] - m);
-    topk_idx[(size_t)t * k + tid] = sel_e[tid];
-    topk_w[(size_t)t * k + tid] = static_cast<float>(exp(sel_v[tid] - m) / den);
-  }
-}
-
 __global__ __launch_bounds__(256) void route_select(const double* __restrict__ partial, int KS,
                                                     const float* __restrict__ bias, int T, int E,
                                                     int k, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
-  __shared__ double part[256];
-  __shared__ double logit[kMaxE];
-  __shared__ double sel_v[8];
-  __shared__ int sel_e[8];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int G = 256 / E;
-  if (tid < G * E) {
-    const int e = tid % E, g = tid / E;
-    double s = 0.0;
-#pragma unroll 4
-    for (int ks = g; ks < KS; ks += G) s += partial[((size_t)ks * T + t) * E + e];
-    part[g * E + e] = s;
-  }
-  __syncthreads();
-  if (tid < E) {
-    double v = 0.0;
-    for (int g = 0; g < G; ++g) v += part[g * E + tid];
-    if (bias) v += static_cast<double>(bias[tid]);
-    logit[tid] = v == v ? v : -INFINITY;
-  }
-  __syncthreads();
-  select_topk(logit, t, E, k, sel_v, sel_e, topk_idx, topk_w);
+  rt::select_token(partial, KS, bias, T, E, k, blockIdx.x, topk_idx, topk_w);
 }
-
-// Few tokens (decode): one workgroup per 64-deep K slice computes every (token,
-// expert) partial dot product of its slice in float64, with the slice of W_r
-// (read once, coalesced) and of x held in LDS; route_select then reduces the
-// d/64 slices in order. No widened copy of W_r is needed.
-constexpr int kSmallT = 64;
 
 __global__ __launch_bounds__(256) void route_partial_small(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ w, int T,
                                                            int d, int E,
                                                            double* __restrict__ partial) {
-  __shared__ float ws[64 * kMaxE];      // W_r rows k0..k0+63, all experts (fp32 is exact)
-  __shared__ float xs[kSmallT * 65];    // x[t][k0..k0+63] as fp32 (bf16 is exact in fp32)
-  const int k0 = blockIdx.x * 64;
-  const int tid = threadIdx.x;
-  // all loads of the slice are issued before any is used: W rows k0..k0+63 are
-  // 16*E float4 (E is a multiple of 4 here or handled by the scalar tail),
-  // x[t][k0..k0+63] is 8 uint4 per token
-  const int nw4 = (64 * E) / 4;
-  float4 wv[kMaxE / 16];
-#pragma unroll
-  for (int i = 0; i < kMaxE / 16; ++i) {
-    const int c = tid + 256 * i;
-    wv[i] = c < nw4 ? reinterpret_cast<const float4*>(w + (size_t)k0 * E)[c] : make_float4(0, 0, 0, 0);
-  }
-  uint4 xv[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;        // (token, 8-element chunk)
-    const int t = c >> 3, ch = c & 7;
-    xv[i] = t < T ? reinterpret_cast<const uint4*>(x + (size_t)t * d + k0)[ch] : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxE / 16; ++i) {
-    const int c = tid + 256 * i;
-    if (c < nw4) reinterpret_cast<float4*>(ws)[c] = wv[i];
-  }
-  for (int i = nw4 * 4 + tid; i < 64 * E; i += 256) ws[i] = w[(size_t)k0 * E + i];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
-    const int t = c >> 3, ch = c & 7;
-    if (t < T) {
-      const uint32_t u[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        xs[t * 65 + ch * 8 + 2 * h] = bf16_to_f32(u[h] & 0xffffu);
-        xs[t * 65 + ch * 8 + 2 * h + 1] = bf16_to_f32(u[h] >> 16);
-      }
-    }
-  }
-  __syncthreads();
-  for (int p = tid; p < T * E; p += 256) {
-    const int t = p / E, e = p - t * E;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};   // four chains (kk mod 4), summed in a fixed order
-#pragma unroll
-    for (int kk = 0; kk < 64; ++kk)
-      acc[kk & 3] = fma(static_cast<double>(xs[t * 65 + kk]), static_cast<double>(ws[kk * E + e]),
-                        acc[kk & 3]);
-    partial[((size_t)blockIdx.x * T + t) * E + e] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  }
+  rt::partial_slice(x, w, T, d, E, blockIdx.x, partial);
 }
 
 size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -272,7 +160,7 @@ size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
 size_t route_workspace_bytes(int T, int d, int E) {
-  if (T <= kSmallT) return al256((size_t)(d / 64) * T * E * sizeof(double));
+  if (T <= rt::kSmallT) return al256((size_t)(d / 64) * T * E * sizeof(double));
   const RoutePlan p = route_plan(T, d, E);
   return al256((size_t)d * p.Epad * sizeof(double)) +
          al256((size_t)p.nslices * T * E * sizeof(double));
@@ -282,7 +170,7 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
                         int d, int E, int k, int32_t* topk_idx, float* topk_w, void* ws,
                         hipStream_t stream) {
   hipError_t err;
-  if (T <= kSmallT) {
+  if (T <= rt::kSmallT) {
     double* partial = static_cast<double*>(ws);
     hipLaunchKernelGGL(route_partial_small, dim3(d / 64), dim3(256), 0, stream, x, w_router, T, d,
                        E, partial);

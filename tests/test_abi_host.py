@@ -122,6 +122,41 @@ def test_pack_sizes_and_validation(moe):
     assert L.moe_pack_mxfp4(32, 20000, 2880, src, FAKE, FAKE, None) == -1
 
 
+def test_forward_validation(moe):
+    L = moe.lib()
+    D = moe.Dims
+    ok = D(16, 512, 512, 32, 4)
+    ws = L.moe_workspace_bytes(ok)
+    m = moe.MXFP4(FAKE, FAKE)
+    # x, w_router, b_router, w_gate, w_up, w_down, b_gate, b_up, b_down, topk_idx,
+    # topk_w, counts, offsets, sorted_pair, pair_row, y_sorted, out, ws, ws_bytes, stream
+    args = [FAKE, FAKE, None, m, m, m, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE, ws, None]
+    for i in (0, 1, 6, 9, 11, 14, 16, 17):
+        a = list(args); a[i] = None
+        assert L.moe_forward(ok, *a) == -1, i
+    a = list(args); a[4] = moe.MXFP4(None, FAKE)
+    assert L.moe_forward(ok, *a) == -1
+    a = list(args); a[2] = FAKE + 4                          # misaligned b_router
+    assert L.moe_forward(ok, *a) == -1
+    a = list(args); a[18] = ws - 256
+    assert L.moe_forward(ok, *a) == -3
+    assert L.moe_forward(D(16, 512, 512, 300, 4), *args) == -2
+
+
+def test_workspace_covers_the_fused_call(moe):
+    """The whole-block call's scratch (router partials and an arrival counter
+    after the FFN regions) is part of moe_workspace_bytes at decode sizes."""
+    L = moe.lib()
+    D = moe.Dims
+    for T, d, F, E, k in [(16, 2880, 2880, 32, 4), (64, 4096, 4096, 256, 8), (1, 64, 64, 4, 4)]:
+        ws = L.moe_workspace_bytes(D(T, d, F, E, k))
+        P = T * k
+        steps = lambda K: (K + 127) // 128
+        enc = T * steps(d) * 208 + P * steps(F) * 208
+        assert ws >= enc + (d // 64) * T * E * 8 + 256, (T, d, F, E, k)
+
+
 def test_combine_norm_validation(moe):
     L = moe.lib()
     D = moe.Dims
