@@ -46,16 +46,20 @@ __global__ __launch_bounds__(256) void front_select_permute(
     int32_t* __restrict__ pair_row, int4* __restrict__ passes, int* __restrict__ counter) {
   __shared__ int last;
   __shared__ int s[257];
+  __shared__ int offs[rt::kMaxE + 1];
   rt::select_token(partial, nslices, b_router, T, E, k, blockIdx.x, topk_idx, topk_w);
-  __threadfence();  // release this token's top-k to the whole device
-  __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(counter, 1) == static_cast<int>(gridDim.x) - 1;
+  // the token's top-k was stored by lanes of the first wavefront: it releases
+  // them to the whole device, then counts the workgroup in
+  if (threadIdx.x < kWave) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (threadIdx.x == 0) last = atomicAdd(counter, 1) == static_cast<int>(gridDim.x) - 1;
+  }
   __syncthreads();
   if (!last) return;
-  __threadfence();  // acquire every other token's top-k
-  pm::permute_chunk(topk_idx, T * k, E, 0, true, counts, offsets, sorted_pair, pair_row);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every other token's top-k
+  pm::permute_chunk(topk_idx, T * k, E, 0, true, counts, offsets, sorted_pair, pair_row, offs);
   __syncthreads();
-  build_tile_table<kDecRows>(offsets, E, passes, s);
+  build_tile_table<kDecRows>(offs, E, passes, s);
 }
 
 struct FrontLayout {

@@ -27,13 +27,15 @@ constexpr int kMaxE = 256;
 
 // Pairs [start, min(P, start + kChunk)) of the stable counting sort, by one
 // workgroup of kThreads; the workgroup that owns pair 0 also writes counts and
-// offsets (write_totals).
+// offsets (write_totals). offsets_lds, if given, receives the offsets as well
+// (visible to the workgroup when the call returns).
 __device__ __forceinline__ void permute_chunk(const int32_t* __restrict__ idx, int P, int E,
                                               int start, bool write_totals,
                                               int32_t* __restrict__ counts,
                                               int32_t* __restrict__ offsets,
                                               int32_t* __restrict__ sorted_pair,
-                                              int32_t* __restrict__ pair_row) {
+                                              int32_t* __restrict__ pair_row,
+                                              int* offsets_lds = nullptr) {
   __shared__ int total[kMaxE];
   __shared__ int before[kMaxE];
   __shared__ int scan[kMaxE];
@@ -77,6 +79,10 @@ __device__ __forceinline__ void permute_chunk(const int32_t* __restrict__ idx, i
     counts[tid] = val;
     offsets[tid] = excl;
     if (tid == E - 1) offsets[E] = excl + val;
+  }
+  if (offsets_lds && tid < E) {  // the offsets also to the caller's LDS [E + 1]
+    offsets_lds[tid] = excl;
+    if (tid == E - 1) offsets_lds[E] = excl + val;
   }
   __syncthreads();
 
