@@ -824,7 +824,7 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
         if (jj < nst) {
           const uint8_t* rowp = wbuf + l16 * kDecAPitch + u * kChunk;
           v8i ahi, alo;
-          load_block_terms(rowp + q * kEncBytes, ahi, alo);
+          load_block_terms3(rowp + q * kEncBytes, ahi, alo);
           int as = *reinterpret_cast<const uint16_t*>(rowp + kChunkScales + 2 * q);
           if (4 * jj + 2 >= nblkK && q >= 2) as = 0;  // blocks past K: zero codes, finite scales
           const int bs = bsrow[jj * 64] >> (8 * (q & 1));

@@ -61,6 +61,19 @@ __device__ __forceinline__ void load_block_terms(const uint8_t* p, v8i& hi, v8i&
   lo = fp6_operand(*(lds_v2i*)(size_t)b, *(lds_v4i*)(size_t)(b + 8));
 }
 
+// The same two terms from three 16-byte LDS reads of the block's 48 bytes (no
+// 8-byte reads: with the decode window's row pitch, 16-byte reads by 16 lanes of
+// different rows and one K sub-block cover distinct banks, while 8-byte reads of
+// two sub-blocks at once collide).
+__device__ __forceinline__ void load_block_terms3(const uint8_t* p, v8i& hi, v8i& lo) {
+  const uint32_t a = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint8_t*)p;
+  const v4i r0 = *(lds_v4i*)(size_t)a;
+  const v4i r1 = *(lds_v4i*)(size_t)(a + 16);
+  const v4i r2 = *(lds_v4i*)(size_t)(a + 32);
+  hi = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, -1, -1);
+  lo = __builtin_shufflevector(r1, r2, 2, 3, 4, 5, 6, 7, -1, -1);
+}
+
 // 2^n for n in [-127, 127] as an fp32 (2^-127 is subnormal).
 __device__ __forceinline__ float pow2i(int n) {
   return n >= -126 ? __uint_as_float(static_cast<uint32_t>(n + 127) << 23)
