@@ -58,9 +58,36 @@ def test_decode_workload(gu):
     dict(T=8, d=4608, F=256, E=4, k=2, seed=38),         # decode path, K beyond the unrolled stage counts
     dict(T=96, d=320, F=4160, E=6, k=3, seed=39),        # prefill path, F not a multiple of 128
     dict(T=300, d=128, F=64, E=8, k=1, seed=43),         # prefill path, switch routing, K = 64
+    dict(T=5, d=64, F=64, E=1, k=1, seed=45),            # a single expert (E = k = 1)
 ])
 def test_edge_shapes(gu, shape):
     _full_check(gu, synth.tiny_workload(**shape))
+
+
+def test_max_tokens(gu):
+    """The largest T the calls accept (65536 tokens, 131072 pairs): routing and the
+    permutation on every token; y's mean relative error on every row; the
+    maximum-error bars on 256 sampled tokens, a sample of the size the other
+    cases check (the largest of 33M errors is a tail statistic that grows with
+    the sample, while a misplaced row would be off by O(1))."""
+    w = synth.tiny_workload(T=65536, d=256, F=256, E=8, k=2, seed=46)
+    L = w.layers[0]
+    print(f"[parity] {w.name}", flush=True)
+    g = gu.run_layer(w.x, L, w.k)
+    ref = oracle.moe_layer(w.x, L, w.k)
+    stats = gu.check_routing(g["idx"], g["w"], ref["logits"], w.k)
+    gu.check_permute(g, w.E)
+    y_ref = oracle.ffn_sorted(oracle.bf16_to_f64(w.x), g["sorted_pair"], g["offsets"], w.k, L)
+    err = np.abs(g["y_sorted"] - y_ref)
+    mean_rel_all = float(err.sum() / np.abs(y_ref).sum())
+    assert mean_rel_all <= 5e-3, mean_rel_all   # every row: a misplaced row would be O(1)
+    tok = np.sort(np.random.default_rng(47).choice(w.T, 256, replace=False))
+    rows = g["pair_row"].reshape(w.T, w.k)[tok].ravel()
+    parity.assert_close(g["y_sorted"][rows], y_ref[rows], "y_sorted", bf16_out=False)
+    out_ref = gu.oracle_tokens(w.x, L, w.k, tok, g["idx"])
+    m = parity.assert_close(parity.bf16_out_to_f64(g["out"][tok]), out_ref, "out")
+    print(f"[parity] {w.name} routing {stats} y mean rel (all rows) {mean_rel_all:.3g} sampled out {m}",
+          flush=True)
 
 
 def test_all_tokens_to_one_expert_set(gu):
