@@ -65,9 +65,11 @@ size_t workspace_for(const moe_dims& m) {
   size_t a = moe::route_workspace_bytes(m.T, m.d, m.E);
   size_t b = moe::ffn_workspace_bytes(m.T, m.d, m.F, m.E, m.k);
   size_t r = a > b ? a : b;
+  const size_t c = moe::permute_workspace_bytes(m.T, m.E, m.k);
+  r = r > c ? r : c;
   if (moe::forward_front_fits(m.T, m.d, m.F, m.k)) {
-    const size_t c = moe::forward_front_bytes(m.T, m.d, m.F, m.E, m.k);
-    r = r > c ? r : c;
+    const size_t f = moe::forward_front_bytes(m.T, m.d, m.F, m.E, m.k);
+    r = r > f ? r : f;
   }
   return (r + 255) & ~static_cast<size_t>(255);
 }
@@ -123,7 +125,7 @@ moe_status moe_permute(moe_dims dims, const int32_t* topk_idx, int32_t* counts,
   MOE_TRY(check_ptrs({topk_idx, counts, offsets, sorted_pair, pair_row}, "moe_permute"));
   MOE_TRY(check_ws(dims, ws, ws_bytes));
   return hip_status(moe::launch_permute(topk_idx, dims.T, dims.E, dims.k, counts, offsets,
-                                        sorted_pair, pair_row,
+                                        sorted_pair, pair_row, ws,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -231,7 +233,7 @@ moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
     MOE_TRY(hip_status(moe::launch_route(x, w_router, b_router, dims.T, dims.d, dims.E, dims.k,
                                          topk_idx, topk_w, ws, s)));
     MOE_TRY(hip_status(moe::launch_permute(topk_idx, dims.T, dims.E, dims.k, counts, offsets,
-                                           sorted_pair, pair_row, s)));
+                                           sorted_pair, pair_row, ws, s)));
   }
   MOE_TRY(hip_status(moe::launch_expert_ffn(a, s, front)));
   return hip_status(moe::launch_combine(y_sorted, pair_row, topk_w, dims.T, dims.d, dims.k, out, s));

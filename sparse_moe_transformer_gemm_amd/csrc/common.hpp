@@ -39,8 +39,11 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
                         int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
                         void* ws, hipStream_t stream);
 
+// Several chunks of pairs (T * k > 2048): per-chunk histograms in the workspace
+// (permute_workspace_bytes), then the ranks.
+size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
+                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row, void* ws,
                           hipStream_t stream);
 
 // Repack one [E][N][K] MXFP4 tensor from the OCP layout into the packed

@@ -19,24 +19,42 @@
 namespace moe {
 namespace {
 
+__global__ __launch_bounds__(pm::kThreads) void permute_hist(const int32_t* __restrict__ idx, int P,
+                                                             int E, int32_t* __restrict__ chist) {
+  pm::chunk_histogram(idx, P, E, blockIdx.x, chist);
+}
+
 __global__ __launch_bounds__(pm::kThreads) void permute_kernel(const int32_t* __restrict__ idx, int P,
                                                                int E, int32_t* __restrict__ counts,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_pair,
-                                                               int32_t* __restrict__ pair_row) {
+                                                               int32_t* __restrict__ pair_row,
+                                                               const int32_t* __restrict__ chist) {
   pm::permute_chunk(idx, P, E, blockIdx.x * pm::kChunk, blockIdx.x == 0, counts, offsets, sorted_pair,
-                    pair_row);
+                    pair_row, nullptr, chist, gridDim.x);
 }
 
 }  // namespace
 
+size_t permute_workspace_bytes(int T, int E, int k) {
+  const size_t blocks = ((size_t)T * k + pm::kChunk - 1) / pm::kChunk;
+  return blocks > 1 ? blocks * E * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
+                          int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row, void* ws,
                           hipStream_t stream) {
   const int P = T * k;
   const int blocks = (P + pm::kChunk - 1) / pm::kChunk;
+  int32_t* chist = nullptr;
+  if (blocks > 1) {
+    chist = static_cast<int32_t*>(ws);
+    hipLaunchKernelGGL(permute_hist, dim3(blocks), dim3(pm::kThreads), 0, stream, topk_idx, P, E, chist);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(pm::kThreads), 0, stream, topk_idx, P, E,
-                     counts, offsets, sorted_pair, pair_row);
+                     counts, offsets, sorted_pair, pair_row, chist);
   return hipGetLastError();
 }
 

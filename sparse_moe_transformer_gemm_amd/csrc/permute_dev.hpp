@@ -2,12 +2,12 @@
 // inverse (Perplexity, "GPT-OSS el dia 0", section "Nuclis per a GPT-OSS / MoE":
 // dispatch selects each expert's tokens).
 //
-// Shared by permute.hip and the fused decode front end (front.hip). One
-// kernel, no inter-block communication. Block b owns the pairs
-// [b*kChunk, (b+1)*kChunk). Every block first histograms the whole routing table
-// in LDS (the table is tiny: 4*T int32, L2-resident), counting separately the
-// pairs before its chunk; from that it knows the exclusive scan of the totals
-// and where its own pairs of each expert start. It then ranks its pairs 256 at a
+// Shared by permute.hip and the fused decode front end (front.hip). Block b
+// owns the pairs [b*kChunk, (b+1)*kChunk). With one chunk, the block histograms
+// the routing table itself; with several, a first launch writes one histogram
+// per chunk and each block of the second sums them (totals, and the counts of
+// the chunks before its own). From that it knows the exclusive scan of the
+// totals and where its own pairs of each expert start. It then ranks its pairs 256 at a
 // time: inside a wavefront, lanes holding the same expert are found with one
 // ballot per expert-index bit and ranked by popcount of the lower lanes; per-
 // wave counts in LDS give the offset across the block's four wavefronts. The
@@ -25,17 +25,42 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 2048;
 constexpr int kMaxE = 256;
 
+// Per-chunk expert histograms: chunk c's counts of its pairs [c*kChunk,
+// (c+1)*kChunk) into chist[c][0..E), by one workgroup (one counter set per
+// wavefront, so that the LDS atomics of the four wavefronts do not collide).
+__device__ __forceinline__ void chunk_histogram(const int32_t* __restrict__ idx, int P, int E,
+                                                int chunk, int32_t* __restrict__ chist) {
+  __shared__ int wh[kThreads / kWave][kMaxE];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  for (int e = tid; e < kMaxE; e += kThreads)
+    for (int w = 0; w < kThreads / kWave; ++w) wh[w][e] = 0;
+  __syncthreads();
+  const int start = chunk * kChunk, end = min(P, start + kChunk);
+  for (int q = start + tid; q < end; q += kThreads) atomicAdd(&wh[wave][idx[q]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    int c = 0;
+    for (int w = 0; w < kThreads / kWave; ++w) c += wh[w][e];
+    chist[(size_t)chunk * E + e] = c;
+  }
+}
+
 // Pairs [start, min(P, start + kChunk)) of the stable counting sort, by one
 // workgroup of kThreads; the workgroup that owns pair 0 also writes counts and
 // offsets (write_totals). offsets_lds, if given, receives the offsets as well
-// (visible to the workgroup when the call returns).
+// (visible to the workgroup when the call returns). With chist (the nchunks
+// chunk histograms of chunk_histogram) the totals and the counts before this
+// chunk come from there instead of from a pass over every pair.
 __device__ __forceinline__ void permute_chunk(const int32_t* __restrict__ idx, int P, int E,
                                               int start, bool write_totals,
                                               int32_t* __restrict__ counts,
                                               int32_t* __restrict__ offsets,
                                               int32_t* __restrict__ sorted_pair,
                                               int32_t* __restrict__ pair_row,
-                                              int* offsets_lds = nullptr) {
+                                              int* offsets_lds = nullptr,
+                                              const int32_t* __restrict__ chist = nullptr,
+                                              int nchunks = 0) {
   __shared__ int total[kMaxE];
   __shared__ int before[kMaxE];
   __shared__ int scan[kMaxE];
@@ -55,10 +80,25 @@ __device__ __forceinline__ void permute_chunk(const int32_t* __restrict__ idx, i
   }
   __syncthreads();
 
-  for (int q = tid; q < P; q += kThreads) {
-    const int e = idx[q];
-    atomicAdd(&total[e], 1);
-    if (q < start) atomicAdd(&before[e], 1);
+  if (chist) {
+    const int mine = start / kChunk;
+    for (int e = tid; e < E; e += kThreads) {
+      int t = 0, b = 0;
+#pragma unroll 8
+      for (int c = 0; c < nchunks; ++c) {
+        const int h = chist[(size_t)c * E + e];
+        t += h;
+        b += c < mine ? h : 0;
+      }
+      total[e] = t;
+      before[e] = b;
+    }
+  } else {
+    for (int q = tid; q < P; q += kThreads) {
+      const int e = idx[q];
+      atomicAdd(&total[e], 1);
+      if (q < start) atomicAdd(&before[e], 1);
+    }
   }
   __syncthreads();
 
