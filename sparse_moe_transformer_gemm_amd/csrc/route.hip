@@ -9,7 +9,7 @@
 // summation order makes it deterministic.
 //
 // Few tokens (T <= 64): route_partial_small + route_select (below). Otherwise
-// three kernels:
+// three kernels (route_select_many in place of route_select):
 //   route_widen   W_r (fp32 [d][E]) -> float64 [d][Epad] in the workspace
 //                 (Epad = E rounded up to 32, zero padded).
 //   route_logits  grid (256-token blocks, K slices, 32-expert groups). One lane
@@ -148,6 +148,53 @@ __global__ __launch_bounds__(256) void route_select(const double* __restrict__ p
   rt::select_token(partial, KS, bias, T, E, k, blockIdx.x, topk_idx, topk_w);
 }
 
+// Many tokens: 256 / Ep tokens per workgroup (Ep = E rounded up to a power of
+// two), one thread per (token, expert): the logit sums the token's K-slice
+// partials in slice order (+ bias), the expert's rank among the token's E
+// logits picks the top k, and the k picked lanes' softmax is taken in float64
+// as in rt::select_topk.
+__global__ __launch_bounds__(256) void route_select_many(const double* __restrict__ partial, int KS,
+                                                         const float* __restrict__ bias, int T,
+                                                         int E, int Ep, int k,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w) {
+  __shared__ double logit[256];
+  __shared__ double sel_v[256 * 8];   // [token slot][rank]: up to 256 slots (E = 1), k <= 8
+  __shared__ int sel_e[256 * 8];
+  const int tid = threadIdx.x;
+  const int j = tid / Ep, e = tid - j * Ep;     // token slot in the workgroup, expert
+  const int tpw = 256 / Ep;
+  const int t = blockIdx.x * tpw + j;
+  const bool live = t < T && e < E;
+  if (live) {
+    double v = 0.0;
+    const double* p = partial + (size_t)t * E + e;
+#pragma unroll 8
+    for (int ks = 0; ks < KS; ++ks) v += p[(size_t)ks * T * E];
+    if (bias) v += static_cast<double>(bias[e]);
+    logit[tid] = v == v ? v : -INFINITY;
+  }
+  __syncthreads();
+  if (live) {
+    const double* row = logit + j * Ep;
+    const double v = row[e];
+    int rank = 0;
+    for (int i = 0; i < E; ++i) rank += rt::better(row[i], i, v, e) ? 1 : 0;
+    if (rank < k) {
+      sel_v[j * 8 + rank] = v;
+      sel_e[j * 8 + rank] = e;
+    }
+  }
+  __syncthreads();
+  if (t < T && e < k) {
+    const double m = sel_v[j * 8];
+    double den = 0.0;
+    for (int i = 0; i < k; ++i) den += exp(sel_v[j * 8 + i] - m);
+    topk_idx[(size_t)t * k + e] = sel_e[j * 8 + e];
+    topk_w[(size_t)t * k + e] = static_cast<float>(exp(sel_v[j * 8 + e] - m) / den);
+  }
+}
+
 __global__ __launch_bounds__(256) void route_partial_small(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ w, int T,
                                                            int d, int E,
@@ -191,8 +238,11 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
   hipLaunchKernelGGL(route_logits, dim3(p.tblocks, p.nslices, p.ngroups), dim3(256), 0, stream, x,
                      w64, T, d, E, p.Epad, p.kslice, partial);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(route_select, dim3(T), dim3(256), 0, stream, partial, p.nslices, b_router, T,
-                     E, k, topk_idx, topk_w);
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;
+  const int tpw = 256 / Ep;
+  hipLaunchKernelGGL(route_select_many, dim3((T + tpw - 1) / tpw), dim3(256), 0, stream, partial,
+                     p.nslices, b_router, T, E, Ep, k, topk_idx, topk_w);
   return hipGetLastError();
 }
 
