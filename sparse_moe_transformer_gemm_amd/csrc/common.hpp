@@ -21,6 +21,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Inclusive prefix sum of one int per thread over a workgroup of 256 threads:
+// a shuffle scan inside each wavefront, then the totals of the wavefronts before
+// it (two barriers instead of the sixteen of a Hillis-Steele scan through LDS).
+// `tmp` is 4 ints of LDS; every thread of the workgroup must call it.
+__device__ __forceinline__ int block_inclusive_scan256(int v, int* tmp) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == kWave - 1) tmp[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += tmp[w];
+  __syncthreads();  // tmp is free again for the caller's next scan
+  return v + add;
+}
+
 // Expert owning dispatch row p: the e with offsets[e] <= p < offsets[e+1].
 __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int p) {
   int lo = 0, hi = E;  // invariant: offsets[lo] <= p < offsets[hi]

@@ -31,17 +31,12 @@ __device__ __forceinline__ uint32_t enc_scale_at(int b) { return (b >> 2) * kChu
 template <int BM>
 __device__ __forceinline__ void build_tile_table(const int32_t* __restrict__ offsets, int E,
                                                  int4* __restrict__ table, int* s) {
+  __shared__ int tmp[4];
   const int t = threadIdx.x;
   const int v = t < E ? (offsets[t + 1] - offsets[t] + BM - 1) / BM : 0;
-  s[t + 1] = v;
+  s[t + 1] = block_inclusive_scan256(v, tmp);  // s[1 + e] = tiles of experts 0..e
   if (t == 0) s[0] = 0;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of s[1..256]
-    const int add = t >= off ? s[t + 1 - off] : 0;
-    __syncthreads();
-    s[t + 1] += add;
-    __syncthreads();
-  }
   const int total = s[E];
   if (t == 0) table[0] = make_int4(total, 0, 0, 0);
   for (int mt = t; mt < total; mt += 256) {

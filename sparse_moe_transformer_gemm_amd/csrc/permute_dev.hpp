@@ -66,6 +66,7 @@ __device__ __forceinline__ void permute_chunk(const int32_t* __restrict__ idx, i
   __shared__ int scan[kMaxE];
   __shared__ int run[kMaxE];
   __shared__ int wcnt[kThreads / kWave][kMaxE];
+  __shared__ int scantmp[kThreads / kWave];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -102,18 +103,10 @@ __device__ __forceinline__ void permute_chunk(const int32_t* __restrict__ idx, i
   }
   __syncthreads();
 
-  // exclusive scan of total[0..E) (Hillis-Steele over 256 entries)
-  int val = (tid < E) ? total[tid] : 0;
-  scan[tid] = val;
-  __syncthreads();
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    int add = (tid >= off) ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  const int excl = scan[tid] - val;
-  __syncthreads();
+  // exclusive scan of total[0..E)
+  static_assert(kThreads == 256 && kMaxE == 256, "one scan entry per thread");
+  const int val = (tid < E) ? total[tid] : 0;
+  const int excl = block_inclusive_scan256(val, scantmp) - val;
   scan[tid] = excl;
   if (write_totals && tid < E) {
     counts[tid] = val;
