@@ -179,3 +179,39 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("MOE_MI355X_LIB", str(tmp_path / "missing.so"))
     with pytest.raises(m.MoeError):
         m.lib()
+
+
+def test_header_is_c99_and_usable_from_c(moe, tmp_path):
+    """include/moe.h compiles as strict C99 (gcc -std=c99 -pedantic -Werror), and
+    a C program linked against the library gets the same host-side answers as the
+    Python binding (workspace and packed sizes, validation before any launch)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "client.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "moe.h"
+int main(void) {
+  moe_dims d = {16, 2880, 2880, 32, 4};
+  moe_dims bad = {16, 2880, 2880, 3, 4};   /* k > E */
+  moe_status st = moe_route(d, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL);
+  printf("%zu %zu %zu %d\n", moe_workspace_bytes(d), moe_workspace_bytes(bad),
+         moe_mxfp4_packed_bytes(32, 2880, 2880, 0), (int)st);
+  return 0;
+}
+''')
+    exe = tmp_path / "client"
+    lib = moe.library_path()
+    libdir = os.path.dirname(lib)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", f"-I{ROOT}/include",
+           str(src), "-o", str(exe), f"-L{libdir}", f"-l:{os.path.basename(lib)}",
+           f"-Wl,-rpath,{libdir}"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    L = moe.lib()
+    assert int(out[0]) == L.moe_workspace_bytes(moe.Dims(16, 2880, 2880, 32, 4))
+    assert int(out[1]) == 0
+    assert int(out[2]) == 32 * 90 * 23 * 2048
+    assert int(out[3]) == -1   # MOE_ERR_INVALID_ARG: null pointers, nothing launched
