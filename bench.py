@@ -42,6 +42,10 @@ MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4/MXFP6 matrix throughput, pub
 METRIC = "MoE layer tokens/s; % HBM peak (T=16) and % MXFP4 MFMA peak (T=8192)"
 
 
+# the sources of the expert-FFN call's kernels, hashed into the traffic summary
+TRAFFIC_SOURCES = ("ffn.hip", "ffn_dev.hpp", "mx6.hpp", "layout.hpp", "common.hpp")
+
+
 def measured_traffic(name: str):
     """HBM bytes per launch of the expert-FFN call, from the committed rocprofv3
     counter summary for this workload, or None when there is none or when the
@@ -56,7 +60,7 @@ def measured_traffic(name: str):
             key, _, val = line.strip().partition(":")
             fields[key.strip()] = val.strip()
     h = hashlib.sha256()
-    for f in ("ffn.hip", "mx6.hpp", "common.hpp"):
+    for f in TRAFFIC_SOURCES:
         h.update(open(os.path.join(ROOT, "sparse_moe_transformer_gemm_amd", "csrc", f), "rb").read())
     if h.hexdigest()[:16] != fields.get("sources_sha256_16"):
         return None
