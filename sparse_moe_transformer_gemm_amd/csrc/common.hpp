@@ -40,16 +40,6 @@ __device__ __forceinline__ int block_inclusive_scan256(int v, int* tmp) {
   return v + add;
 }
 
-// Expert owning dispatch row p: the e with offsets[e] <= p < offsets[e+1].
-__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int p) {
-  int lo = 0, hi = E;  // invariant: offsets[lo] <= p < offsets[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= p) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error; arguments are validated by the caller.
 

@@ -103,13 +103,6 @@ __device__ __forceinline__ uint32_t div_by(uint32_t x, uint64_t m) {
   return static_cast<uint32_t>((static_cast<uint64_t>(x) * m) >> 32);
 }
 
-// Workgroup id -> logical tile such that XCD x (ids = x mod 8) owns the
-// contiguous logical range [x*G/8, (x+1)*G/8) (a bijection on [0, G)).
-__device__ __forceinline__ int xcd_remap(int bid, int G) {
-  const int per = G >> 3, rem = G & 7, x = bid & 7, i = bid >> 3;
-  return x * per + (x < rem ? x : rem) + i;
-}
-
 // ------------------------------------------------------------------ prefill
 
 // One workgroup = 128 dispatch rows x 64*NF weight rows, 2x2 wavefronts; wave

@@ -166,46 +166,6 @@ __device__ __forceinline__ void encode_block(const float (&v)[32], uint32_t (&hi
   scales = static_cast<uint32_t>(s1 + 127) | (static_cast<uint32_t>(s2 + 127) << 8);
 }
 
-// Same encoding for 32 floats held in LDS (or any memory) at v[0..31]; the
-// buffer is overwritten with the residuals. Uses few registers: the values are
-// re-read in three passes (max, hi term + residual, lo term).
-__device__ __forceinline__ void encode_block_mem(float* v, uint32_t (&hi)[6], uint32_t (&lo)[6],
-                                                 uint32_t& scales) {
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  const int s1 = block_exp(amax);
-  const float inv1 = pow2i(-s1), sc1 = pow2i(s1);
-#pragma unroll
-  for (int i = 0; i < 6; ++i) hi[i] = lo[i] = 0u;
-  float ramax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float x = v[j];
-    const uint32_t m = e2m3_code(fabsf(x) * inv1);
-    const uint32_t sign = __float_as_uint(x) >> 31;
-    const uint32_t c = (sign << 5) | m;
-    const int bit = 6 * j, word = bit >> 5, off = bit & 31;
-    hi[word] |= c << off;
-    if (off > 26) hi[word + 1] |= c >> (32 - off);
-    const float back = e2m3_value(m) * sc1;
-    const float r = x - (sign ? -back : back);
-    v[j] = r;
-    ramax = fmaxf(ramax, fabsf(r));
-  }
-  const int s2 = block_exp(ramax);
-  const float inv2 = pow2i(-s2);
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float r = v[j];
-    const uint32_t c = ((__float_as_uint(r) >> 31) << 5) | e2m3_code(fabsf(r) * inv2);
-    const int bit = 6 * j, word = bit >> 5, off = bit & 31;
-    lo[word] |= c << off;
-    if (off > 26) lo[word + 1] |= c >> (32 - off);
-  }
-  scales = static_cast<uint32_t>(s1 + 127) | (static_cast<uint32_t>(s2 + 127) << 8);
-}
-
 // The same encoding done by a group of 32 lanes (a half wavefront), one element
 // per lane: j = lane & 31 holds element j of the block. The block maxima are
 // shuffle reductions inside the half wavefront; the 6-bit codes are packed
