@@ -12,8 +12,8 @@
 //
 // Two kernel shapes, chosen on the host from T (expert row counts stay on the
 // device):
-//   prefill  128 dispatch rows x 64*NF weight rows per workgroup, 2x2 wavefronts,
-//            K in 128-deep steps copied from global memory straight into LDS
+//   prefill  128 dispatch rows x 64*NF weight rows per workgroup, 4x2 wavefronts
+//            (two per SIMD), K in 128-deep steps copied from global memory straight into LDS
 //            (three steps in flight). Every copy instruction moves 1 KB: a packed
 //            B fragment is one contiguous kilobyte, and A rows are copied as
 //            whole 208-byte chunks. The grid is an upper bound on the number of
@@ -105,53 +105,67 @@ __device__ __forceinline__ uint32_t div_by(uint32_t x, uint64_t m) {
 
 // ------------------------------------------------------------------ prefill
 
-// One workgroup = 128 dispatch rows x 64*NF weight rows, 2x2 wavefronts; wave
-// (wm, wn) owns rows 64wm..64wm+63 (two 32-row fragments) and NF 32-row weight
-// groups (for gate/up: NF/2 gate and NF/2 up groups of the same h-columns, so
-// SwiGLU can be applied to the tile).
+// One workgroup = 128 dispatch rows x 64*NF weight rows, eight wavefronts, two
+// per SIMD: while one waits (for its LDS reads, its copies, the barrier) the
+// other's MFMAs keep the matrix unit busy. Wave (wm, wn), wm = 0..3, wn = 0..1,
+// owns rows 32wm..32wm+31 (one 32-row fragment) and NF 32-row weight groups (for
+// gate/up: NF/2 gate and NF/2 up groups of the same h-columns, so SwiGLU can be
+// applied to the tile).
 //
 // Each K step is copied from global memory straight into LDS by buffer-to-LDS
 // loads (lane i of a copy writes LDS bytes [16i, 16i+16) for 16-byte copies and
-// the dword 4i, zero-extended, for 2-byte ones), three steps in flight: the copy
-// of step t+2 is issued when step t is computed. LDS layout of one step:
+// [4i, 4i+4) for 4-byte ones), three step buffers: step st+3 is copied while step
+// st+1 is read and computed. LDS layout of one step:
 //   A   [128 rows][208 B]  the rows' encoded chunks as stored (copy q of 16 B:
 //                          row q/13, piece q%13; lanes of one row read one run)
 //   B   [group][half][lane][16 B]  packed fragments, 1 KB per copy
-//   BS  [group][lane][4 B]         packed scales (2 bytes used)
-// MFMA half s of a step takes, in lane half h, block 2h + s of A and of B. Rows
-// past the tile's count, blocks past K and steps past the end are read as zero
-// through the resource's range check.
+//   BS  [matrix][group of the matrix][lane][2 B]  packed scales; one 4-byte copy
+//                          covers two groups of one matrix (lanes 0-31, 32-63)
+// The copies of a step are dealt out over the eight waves in equal numbers (a
+// wave whose share is short issues the rest into a junk area, reading nothing),
+// and each wave spreads its copies among its MFMAs: the texture addresser takes
+// about 16 cycles per 64-lane copy, so copies issued back to back would hold the
+// wave. MFMA half s of a step takes, in lane half h, block 2h + s of A and of B.
+// Rows past the tile's count, blocks past K and steps past the end are read as
+// zero through the resource's range check.
+constexpr int kPrefWaves = 8;
+
 template <int NF, bool GATEUP>
 struct Prefill {
+  static constexpr int W = kPrefWaves;
   static constexpr int BN = 64 * NF;                   // weight rows per workgroup
   static constexpr int NFR = 2 * NF;                   // 32-row weight groups per workgroup
   static constexpr int MROWS = GATEUP ? BN / 2 : BN;   // output columns per workgroup
   static constexpr int FM = GATEUP ? NF / 2 : NF;      // groups per matrix per wave
+  static constexpr int NMAT = GATEUP ? 2 : 1;
+  static constexpr int GPM = NFR / NMAT;               // groups per matrix
   static constexpr int A_COPIES = kBM * kChunkPieces / 64;
+  static constexpr int B_COPIES = 2 * NFR;
+  static constexpr int S_COPIES = NFR / 2;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = A_OFF + kBM * kChunk;
   static constexpr int BS_OFF = B_OFF + NFR * 2 * 1024;
   static constexpr int EP_PITCH = 36;                  // floats per row of the SwiGLU staging tile
-  static constexpr int EP_BYTES = 4 * 64 * EP_PITCH * 4;  // staging of all four waves (gate/up)
-  static constexpr int STAGE_DATA = BS_OFF + NFR * 256;
+  static constexpr int EP_BYTES = W * 32 * EP_PITCH * 4;  // staging of all eight waves (gate/up)
+  static constexpr int STAGE_DATA = BS_OFF + NFR * 128;
   // one step's copies, or (gate/up) the epilogue's staging, which reuses a step buffer
   static constexpr int STAGE = GATEUP && EP_BYTES > STAGE_DATA ? EP_BYTES : STAGE_DATA;
-  static constexpr int NA = (A_COPIES + 3) / 4;        // A copies per wave (at most)
-  // Weight copies are dealt out per matrix (gate and up for gate/up, the single
-  // down matrix otherwise), so the matrix of every copy is known at compile time.
-  static constexpr int NMAT = GATEUP ? 2 : 1;
-  static constexpr int GPM = NFR / NMAT;               // groups per matrix
-  static constexpr int NBM = 2 * GPM / 4;              // code copies per wave and matrix
-  static constexpr int NSM = (GPM + 3) / 4;            // scale copies per wave and matrix (at most)
-  static constexpr int cnt_lt(int n, int w) { return n > w ? (n - w + 3) / 4 : 0; }  // #t: 4t + w < n
-  // copies wave w issues per step
-  static constexpr int copies(int w) { return cnt_lt(A_COPIES, w) + NMAT * (NBM + cnt_lt(GPM, w)); }
+  // copy slots per wave: A copies i = wave + 8t, code copies c = wave + 8t, scale
+  // copies p = wave + 8t (t = 0, 1, ...); slot k numbers them A, code, scale
+  static constexpr int NA = (A_COPIES + W - 1) / W;
+  static constexpr int NB = (B_COPIES + W - 1) / W;
+  static constexpr int NS = (S_COPIES + W - 1) / W;
+  static constexpr int KB0 = NA, KS0 = NA + NB, KMAX = NA + NB + NS;  // copies per wave per step
+  // slots k < KSPLIT go among the MFMAs of half 1 of one step, the rest among
+  // those of half 0 of the next
+  static constexpr int KSPLIT = (KMAX + 1) / 2;
   static_assert(kBM * kChunkPieces % 64 == 0, "A copies are whole instructions");
+  static_assert(kBM == 4 * 32, "one 32-row fragment per wave row");
   static_assert(!GATEUP || NF % 2 == 0, "gate/up tiles pair gate and up groups");
-  static_assert(2 * GPM % 4 == 0, "code copies split evenly over the four waves");
-  static_assert(2 * copies(0) <= 63 && 2 * copies(1) <= 63, "two steps of copies must fit the vector memory counter");
-  static_assert(3 * STAGE <= 160 * 1024, "three step buffers must fit the 160 KB of LDS");
-  static_assert(!GATEUP || EP_BYTES <= STAGE, "SwiGLU staging of the four waves must fit one step buffer");
+  static_assert(GPM % 2 == 0, "scale copies take two groups of one matrix");
+  static_assert(2 * KMAX <= 63, "two steps of copies must fit the vector memory counter");
+  static_assert(3 * STAGE + 1024 <= 160 * 1024, "three step buffers and the junk area must fit the 160 KB of LDS");
+  static_assert(!GATEUP || EP_BYTES <= STAGE, "SwiGLU staging of the eight waves must fit one step buffer");
 };
 
 // s_waitcnt with only the vector memory counter bounded (gfx9 encoding:
@@ -172,7 +186,7 @@ __device__ __forceinline__ v4i rsrc4(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_void_ptr)p);
 }
-// Buffer-to-LDS copy of SIZE bytes per lane (16 or 2) to the LDS address `lds`
+// Buffer-to-LDS copy of SIZE bytes per lane (16 or 4) to the LDS address `lds`
 // (wave-uniform); out-of-range lanes write zeros. Written as inline asm so that
 // the compiler does not guard every LDS read with a wait for all copies in flight
 // (it cannot tell which buffer a copy writes); the kernel bounds the vector
@@ -180,7 +194,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // register outputs.
 template <int SIZE>
 __device__ __forceinline__ void lds_copy(v4i r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  static_assert(SIZE == 16 || SIZE == 2, "copy sizes used here");
+  static_assert(SIZE == 16 || SIZE == 4, "copy sizes used here");
   // the resource, M0 and the uniform offset live in SGPRs (no-ops when the
   // compiler already knows the values are uniform)
   r = v4i{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
@@ -191,7 +205,7 @@ __device__ __forceinline__ void lds_copy(v4i r, uint32_t lds, uint32_t voff, uin
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
 
@@ -200,16 +214,28 @@ struct IC {
   static constexpr int v = V;
 };
 
+// f(IC<I>{}) for I = B .. E-1, in order
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <int NF, bool GATEUP>
-__global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const uint8_t* __restrict__ ain,
-                                                       uint8_t* __restrict__ hout,
-                                                       const int4* __restrict__ tiles, int ntn) {
+__global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs a, const uint8_t* __restrict__ ain,
+                                                                   uint8_t* __restrict__ hout,
+                                                                   const int4* __restrict__ tiles, int ntn) {
   using C = Prefill<NF, GATEUP>;
+  constexpr int W = C::W;
   // three step buffers as separate objects, so the compiler can tell the copy
   // into one from the reads of another
   __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[C::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st2[C::STAGE];
+  // destination of the copy slots a wave has no copy for (they read nothing)
+  __shared__ __attribute__((aligned(16))) uint8_t junk[1024];
   const int K = GATEUP ? a.d : a.F;
   const int N = GATEUP ? a.F : a.d;
   const int nblkK = K / 32;
@@ -231,30 +257,22 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
   if (logical >= xend) return;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (W - 1);
   const int lane = tid & 63, lr = lane & 31, half = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const uint32_t apitch = (uint32_t)nst * kChunk;
   const uint64_t kmagic = div_magic((uint32_t)a.k);  // token of dispatch pair q: q / k
   const uint32_t gstride = (uint32_t)nst * kWStep;    // packed code bytes per 32-row group
   const uint32_t sstride = (uint32_t)nst * kWSStep;   // packed scale bytes per 32-row group
-  const uint32_t lane16 = lane * 16, lane2 = lane * 2;
+  const uint32_t lane16 = lane * 16;
 
-  // Copy i = wave + 4t of A covers 16-byte pieces 64i + lane: row (64i + lane) / 13,
-  // piece (64i + lane) % 13 (the same for every tile and step). Bit t of a_pad:
-  // the piece holds blocks 2, 3 of the step (pieces 6..11).
-  int a_row[C::NA];
-  uint32_t a_pad = 0, a_piece16[C::NA];
-#pragma unroll
-  for (int t = 0; t < C::NA; ++t) {
-    const int q = (wave + 4 * t) * 64 + lane;
-    a_row[t] = q / kChunkPieces;
-    const int piece = q - a_row[t] * kChunkPieces;
-    a_piece16[t] = piece * 16;
-    a_pad |= (piece >= 6 && piece < 12) ? 1u << t : 0u;
-  }
-  // Weight copies of matrix m: code copy t covers matrix-local copy c = 4t + wave,
-  // i.e. half c & 1 of group c >> 1; scale copy t covers group 4t + wave.
+  // A copy t of this wave is copy i = wave + 8t: 16-byte pieces 64i + lane, i.e.
+  // row (64i + lane) / 13, piece (64i + lane) % 13, the same for every tile and
+  // step (recomputed where used). Pieces 6..11 hold blocks 2, 3 of the step.
+  auto a_row = [&](int t) -> int { return ((wave + W * t) * 64 + lane) / kChunkPieces; };
+  auto a_piece = [&](int t) -> int { return ((wave + W * t) * 64 + lane) % kChunkPieces; };
+  // Group gg of matrix m is workgroup group phi (gate/up: wave column w holds
+  // NF/2 gate groups, then the NF/2 up groups of the same columns).
   auto group_of = [&](int m, int gg) -> int {
     if (GATEUP) return (gg / (NF / 2)) * NF + m * (NF / 2) + gg % (NF / 2);
     return gg;
@@ -266,6 +284,12 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
       return w * C::FM * 32 + (f < NF / 2 ? f : f - NF / 2) * 32;
     }
     return phi * 32;
+  };
+  // Scale copy p covers groups 2p', 2p'+1 of matrix p / (GPM/2), p' = p % (GPM/2):
+  // lane half h takes group 2p' + h; its LDS bytes sit at BS_OFF + 128 (m GPM + gg).
+  auto scale_voff = [&](int p) -> uint32_t {
+    const int m = p / (C::GPM / 2), gg = 2 * (p % (C::GPM / 2)) + half;
+    return (uint32_t)(group_row(group_of(m, gg)) / 32) * sstride + lr * 4;
   };
 
   // ---- per-tile state (all wave-uniform)
@@ -287,14 +311,14 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
     uint32_t src[C::NA];
     uint32_t bias[NF];  // raw bf16 (never combined before use: that would wait for the loads)
   };
-  auto fetch_entry = [&](int lg, Pre& P) {
+  auto fetch_entry = [&](int lg, Pre& P) __attribute__((always_inline)) {
     const int grp = lg / (kPrefGM * ntn);
     const int gm = min(kPrefGM, total_mt - grp * kPrefGM);
     const int r = lg - grp * kPrefGM * ntn;
     P.nt = r / gm;
     P.ent = tiles[1 + grp * kPrefGM + (r - P.nt * gm)];
   };
-  auto fetch_rest = [&](const Pre& Ein, Pre& P) {
+  auto fetch_rest = [&](const Pre& Ein, Pre& P) __attribute__((always_inline)) {
     P.ent = Ein.ent;
     P.nt = Ein.nt;
     const int pe = __builtin_amdgcn_readfirstlane(P.ent.x);
@@ -302,7 +326,7 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
     const int rv = min(kBM, __builtin_amdgcn_readfirstlane(P.ent.w) - pm0);
 #pragma unroll
     for (int t = 0; t < C::NA; ++t) {
-      const int row = min(a_row[t], rv - 1);
+      const int row = min(a_row(t), rv - 1);
       P.src[t] = GATEUP ? (uint32_t)a.sorted_pair[poff + pm0 + row] : (uint32_t)row;
     }
 #pragma unroll
@@ -313,7 +337,7 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
       P.bias[f] = bsrc[(size_t)pe * N + P.nt * C::MROWS + group_row(phi) + lr];
     }
   };
-  auto setup = [&](const Pre& P) {
+  auto setup = [&](const Pre& P) __attribute__((always_inline)) {
     e = __builtin_amdgcn_readfirstlane(P.ent.x);
     m0 = __builtin_amdgcn_readfirstlane(P.ent.y);
     off = __builtin_amdgcn_readfirstlane(P.ent.z);
@@ -330,108 +354,104 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
 #pragma unroll
     for (int t = 0; t < C::NA; ++t) {
       const uint32_t tok = GATEUP ? div_by(P.src[t], kmagic) : P.src[t];
-      const bool ok = wave + 4 * t < C::A_COPIES && a_row[t] < rows_valid;
-      a_off[t] = ok ? tok * apitch + a_piece16[t] : kOutOfRange;
+      const bool ok = wave + W * t < C::A_COPIES && a_row(t) < rows_valid;
+      a_off[t] = ok ? tok * apitch + a_piece(t) * 16 : kOutOfRange;
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) bias[f] = bf16_to_f32((uint16_t)P.bias[f]);
   };
 
-  // Copy step st of the current tile into LDS buffer `buf`. Weight copies read
-  // one contiguous kilobyte: the lane offset is lane*16, the group and step go
-  // into the uniform offset.
-  auto issue = [&](int st, uint8_t* buf) {
-    const bool live = st < nst;
-    const bool halfst = 4 * st + 2 >= nblkK;  // blocks 2, 3 of this step are past K
+  // Copy slot k (see Prefill) of step st of the current tile into the LDS buffer
+  // at `base`. Weight copies read one contiguous kilobyte: the lane offset is
+  // lane*16, the group and step go into the uniform offset. A slot this wave has
+  // no copy for, and every copy of a step past K, read nothing; the former write
+  // (zeros) to the junk area.
+  auto issue_copy = [&](auto Kc, int st, uint32_t base) __attribute__((always_inline)) {
+    constexpr int k = decltype(Kc)::v;
+    const bool dead = st >= nst;
+    if constexpr (k < C::KB0) {
+      constexpr int t = k;
+      const bool have = wave + W * t < C::A_COPIES;  // otherwise a_off[t] is out of range
+      // the step is past K, or this piece holds its blocks 2, 3 and they are
+      const bool pad = dead || (4 * st + 2 >= nblkK && a_piece(t) >= 6 && a_piece(t) < 12);
+      lds_copy<16>(ar, have ? base + C::A_OFF + (wave + W * t) * 1024 : lds_addr(junk),
+                   pad ? kOutOfRange : a_off[t], (uint32_t)st * kChunk);
+    } else if constexpr (k < C::KS0) {
+      constexpr int t = k - C::KB0;
+      const int c = wave + W * t;  // code copy: half c & 1 of group (c >> 1) % GPM of matrix c / (2 GPM)
+      const bool have = c < C::B_COPIES;
+      const int m = have ? c / (2 * C::GPM) : 0, lc = have ? c % (2 * C::GPM) : 0;
+      const int phi = group_of(m, lc >> 1), sh = lc & 1;
+      const uint32_t so = (uint32_t)((col0 + group_row(phi)) / 32) * gstride + sh * 1024 + (uint32_t)st * kWStep;
+      lds_copy<16>(m ? br1 : br0, have ? base + C::B_OFF + (phi * 2 + sh) * 1024 : lds_addr(junk),
+                   have && !dead ? lane16 : kOutOfRange, so);
+    } else {
+      constexpr int t = k - C::KS0;
+      const int p = wave + W * t;
+      const bool have = p < C::S_COPIES;
+      const int m = have ? p / (C::GPM / 2) : 0;
+      const uint32_t so = (uint32_t)(col0 / 32) * sstride + (uint32_t)st * kWSStep;
+      lds_copy<4>(m ? bsr1 : bsr0, have ? base + C::BS_OFF + p * 256 : lds_addr(junk),
+                  have && !dead ? scale_voff(have ? p : 0) : kOutOfRange, so);
+    }
+  };
+  // Copy slots K0 <= k < K1 of step st into `buf`, back to back. Every wave
+  // issues every slot of every step (those past K read nothing), so the number
+  // of copies in flight behind a step is the same at every wait.
+  auto issue = [&](int st, uint8_t* buf, auto K0c, auto K1c) __attribute__((always_inline)) {
     const uint32_t base = lds_addr(buf);
-#pragma unroll
-    for (int t = 0; t < C::NA; ++t) {
-      if (wave + 4 * t < C::A_COPIES) {
-        const bool pad = halfst && ((a_pad >> t) & 1u);
-        lds_copy<16>(ar, base + (wave + 4 * t) * 1024, live && !pad ? a_off[t] : kOutOfRange,
-                     (uint32_t)st * kChunk);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < C::NMAT; ++m) {
-#pragma unroll
-      for (int t = 0; t < C::NBM; ++t) {
-        const int c = 4 * t + wave, phi = group_of(m, c >> 1), s = c & 1;
-        const uint32_t so = (uint32_t)((col0 + group_row(phi)) / 32) * gstride + s * 1024 + (uint32_t)st * kWStep;
-        lds_copy<16>(m ? br1 : br0, base + C::B_OFF + (phi * 2 + s) * 1024, live ? lane16 : kOutOfRange, so);
-      }
-#pragma unroll
-      for (int t = 0; t < C::NSM; ++t) {
-        const int gg = 4 * t + wave;
-        if (gg < C::GPM) {
-          const int phi = group_of(m, gg);
-          const uint32_t so = (uint32_t)((col0 + group_row(phi)) / 32) * sstride + (uint32_t)st * kWSStep;
-          lds_copy<2>(m ? bsr1 : bsr0, base + C::BS_OFF + phi * 256, live ? lane2 : kOutOfRange, so);
-        }
-      }
-    }
+    static_for<decltype(K0c)::v, decltype(K1c)::v>([&](auto Kc) __attribute__((always_inline)) { issue_copy(Kc, st, base); });
   };
 
-  // Wait until at most `nb` steps of this wave's copies are still in flight.
-  auto wait_copies = [&](auto NB) {
-    constexpr int nb = decltype(NB)::v;
-    if (wave == 0) MOE_WAIT_VMCNT(nb * C::copies(0));
-    else if (wave == 1) MOE_WAIT_VMCNT(nb * C::copies(1));
-    else if (wave == 2) MOE_WAIT_VMCNT(nb * C::copies(2));
-    else MOE_WAIT_VMCNT(nb * C::copies(3));
-  };
-
-  v16f acc[2][NF];
+  v16f acc[NF];
 
   // The fragments of one MFMA half of a step: in lane half h, block 2h + s of A
-  // (both terms and their scales) and of B.
-  struct Half {
-    v8i ahi[2], alo[2];
-    int sa[2];
-    v8i b[NF];
-    int sb[NF];
-    bool halfst;  // the step's blocks 2, 3 are past K
-  };
-  // The scale dwords of a step serve both halves: half 0 reads them, half 1
-  // takes them from `from` (half 0 of the same step) without touching LDS.
-  auto read_half = [&](const uint8_t* buf, int st, auto S, Half& h, const Half& from) {
+  // (both terms) and of B; the scale dwords, read with half 0, serve both halves.
+  v8i ahi, alo, bf[NF];
+  int sa, sb[NF];
+  bool halfst;  // the step's blocks 2, 3 are past K
+  auto read_half = [&](const uint8_t* buf, int st, auto S) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::v;
-    h.halfst = 4 * st + 2 >= nblkK;
-#pragma unroll
-    for (int mf = 0; mf < 2; ++mf) {
-      const uint8_t* rowp = buf + C::A_OFF + (wm * 64 + mf * 32 + lr) * kChunk;
-      load_block_terms(rowp + half * 96 + s * kEncBytes, h.ahi[mf], h.alo[mf]);
-      h.sa[mf] = s == 0 ? *reinterpret_cast<const int*>(rowp + kChunkScales + 4 * half) : from.sa[mf];
-    }
+    const uint8_t* rowp = buf + C::A_OFF + (wm * 32 + lr) * kChunk;
+    load_block_terms(rowp + half * 96 + s * kEncBytes, ahi, alo);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int phi = wn * NF + f;
-      h.b[f] = fp4_operand(reinterpret_cast<const v4i*>(buf + C::B_OFF + (phi * 2 + s) * 1024)[lane]);
-      h.sb[f] = s == 0 ? reinterpret_cast<const int*>(buf + C::BS_OFF + phi * 256)[lane] : from.sb[f];
+      bf[f] = fp4_operand(reinterpret_cast<const v4i*>(buf + C::B_OFF + (phi * 2 + s) * 1024)[lane]);
+    }
+    if (s == 0) {
+      halfst = 4 * st + 2 >= nblkK;
+      sa = *reinterpret_cast<const int*>(rowp + kChunkScales + 4 * half);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int m = GATEUP && f >= NF / 2 ? 1 : 0;
+        const int gg = GATEUP ? wn * (NF / 2) + f % (NF / 2) : wn * NF + f;
+        sb[f] = reinterpret_cast<const uint16_t*>(buf + C::BS_OFF + (m * C::GPM + gg) * 128)[lane];
+      }
     }
   };
-  // 2 x NF x 2 scaled MFMAs: the hi terms of all tiles, then the lo terms, so
-  // that no MFMA waits on the accumulator of the one just before it. Scale
-  // bytes: A hi 2s, A lo 2s+1, B s. A half step at the end of K (K % 128 == 64)
-  // still takes both MFMA halves: lane half 0 holds blocks 0, 1 (valid), lane
-  // half 1 zero codes whose scale bytes (never written) are forced finite.
-  auto mma_half = [&](const Half& h, auto S) {
+  // 2 x NF scaled MFMAs: the hi terms of all tiles, then the lo terms, so that no
+  // MFMA waits on the accumulator of the one just before it. Scale bytes: A hi
+  // 2s, A lo 2s+1, B s. A half step at the end of K (K % 128 == 64) still takes
+  // both MFMA halves: lane half 0 holds blocks 0, 1 (valid), lane half 1 zero
+  // codes whose scale bytes (never written) are forced finite. Copy slots
+  // K0 <= k < K1 of step cst (into the buffer at cbase) go evenly among them.
+  auto mma_half = [&](auto S, auto K0c, auto K1c, int cst, uint32_t cbase) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::v;
-    int sa[2];
-#pragma unroll
-    for (int mf = 0; mf < 2; ++mf) sa[mf] = h.halfst && half ? 0 : h.sa[mf];
-#pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(h.ahi[mf], h.b[f], acc[mf][f], 2, 4,
-                                                                    2 * s, sa[mf], s, h.sb[f]);
-#pragma unroll
-    for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        acc[mf][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(h.alo[mf], h.b[f], acc[mf][f], 2, 4,
-                                                                    2 * s + 1, sa[mf], s, h.sb[f]);
+    constexpr int k0 = decltype(K0c)::v, k1 = decltype(K1c)::v, nk = k1 - k0;
+    constexpr int NM = 2 * NF;
+    const int sav = halfst && half ? 0 : sa;
+    static_for<0, NM>([&](auto Jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(Jc)::v;
+      constexpr int term = j / NF, f = j % NF;
+      acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(term ? alo : ahi, bf[f], acc[f], 2, 4, 2 * s + term,
+                                                              sav, s, sb[f]);
+      static_for<k0, k1>([&](auto Kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(Kc)::v;
+        if constexpr (nk > 0 && (k - k0) * NM / nk == j) issue_copy(Kc, cst, cbase);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   // ---- first tile (its fetches wait; later tiles' do not)
@@ -446,56 +466,54 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
     if (more) fetch_rest(e1, R);
     setup(p0);
   }
-  issue(0, st0);
-  issue(1, st1);
-  issue(2, st2);
+  issue(0, st0, IC<0>{}, IC<C::KMAX>{});
+  issue(1, st1, IC<0>{}, IC<C::KMAX>{});
+  issue(2, st2, IC<0>{}, IC<C::KSPLIT>{});
 
   for (;;) {
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mf][f][i] = bias[f];
+      for (int i = 0; i < 16; ++i) acc[f][i] = bias[f];
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- main loop, software-pipelined: the LDS reads of one MFMA half overlap
-    // the MFMAs of the other. Per step st (its data in `c0`, half 0 already in
-    // registers): read half 1, compute half 0; then, once every wave has read
-    // `c0` and step st+1 has landed (barrier), copy step st+3 into `c0`, read
-    // half 0 of step st+1 from `c1` and compute half 1. Three steps of copies
-    // are in flight ahead of the one being read.
-    Half h0, h1;
-    wait_copies(IC<2>{});
+    // ---- main loop. Per step st (its data in `c0`): read half 0, compute it
+    // while copying the second part of step st+2 into `c2`; read half 1; then,
+    // once step st+1 has landed and every wave has read `c0` (barrier), compute
+    // half 1 of step st while copying the first part of step st+3 into `c0`. The
+    // other wavefront on the SIMD computes while this one waits for its reads.
+    // step 0 has landed (step 1 and the first part of step 2 may be in flight)
+    MOE_WAIT_VMCNT(C::KMAX + C::KSPLIT);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    read_half(st0, 0, IC<0>{}, h0, h0);
-    auto body = [&](int st, uint8_t* c0, const uint8_t* c1) {
-      if (st < nst) {
-        read_half(c0, st, IC<1>{}, h1, h0);
-        __builtin_amdgcn_sched_barrier(0);  // the reads go out before the MFMAs they overlap
-        mma_half(h0, IC<0>{});
-      }
+    // Straight-line code per step (a branch inside would let the compiler move
+    // MFMAs across the barrier).
+    auto body = [&](int st, uint8_t* c0, uint8_t* c2) __attribute__((always_inline)) {
+      read_half(c0, st, IC<0>{});
       __builtin_amdgcn_sched_barrier(0);
-      MOE_WAIT_LGKM0();      // this wave's reads of `c0` are complete
-      wait_copies(IC<1>{});  // its copies of step st+1 have landed
+      MOE_WAIT_LGKM0();
+      mma_half(IC<0>{}, IC<C::KSPLIT>{}, IC<C::KMAX>{}, st + 2, lds_addr(c2));
+      __builtin_amdgcn_sched_barrier(0);
+      read_half(c0, st, IC<1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_WAIT_LGKM0();            // this wave's reads of `c0` are complete
+      MOE_WAIT_VMCNT(C::KMAX);     // step st+1 has landed (step st+2 may be in flight)
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");  // no LDS access moves across the barrier
       __builtin_amdgcn_sched_barrier(0);
-      issue(st + 3, c0);
-      if (st + 1 < nst) read_half(c1, st + 1, IC<0>{}, h0, h0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (st < nst) mma_half(h1, IC<1>{});
+      mma_half(IC<1>{}, IC<0>{}, IC<C::KSPLIT>{}, st + 3, lds_addr(c0));
       __builtin_amdgcn_sched_barrier(0);
     };
-    // Steps go in threes (one per buffer); steps past the end copy zeros and
-    // compute nothing.
-    for (int t = 0; t < nst; t += 3) {
-      body(t, st0, st1);
-      body(t + 1, st1, st2);
-      body(t + 2, st2, st0);
+    // Steps go in threes (one per buffer), then the one or two left.
+    int t = 0;
+    for (; t + 3 <= nst; t += 3) {
+      body(t, st0, st2);
+      body(t + 1, st1, st0);
+      body(t + 2, st2, st1);
     }
+    if (t < nst) body(t, st0, st2);
+    if (t + 1 < nst) body(t + 1, st1, st0);
     MOE_WAIT_VMCNT(0);
     __syncthreads();
 
@@ -507,68 +525,66 @@ __global__ __launch_bounds__(256) void grouped_prefill(const FfnArgs a, const ui
     const bool more3 = logical + 3 * nslot < xend;
     if (more) {
       setup(R);
-      issue(0, st0);
-      issue(1, st1);
-      if (!GATEUP) issue(2, st2);
+      issue(0, st0, IC<0>{}, IC<C::KMAX>{});
+      issue(1, st1, IC<0>{}, IC<C::KMAX>{});
+      if (!GATEUP) issue(2, st2, IC<0>{}, IC<C::KSPLIT>{});
     }
 
     if constexpr (GATEUP) {
-      // h = silu(g) * u; per gate group f, the wave's two 32x32 tiles go to LDS as
-      // 64 rows x 32 columns and each lane encodes one row's 32-column block as
-      // two-term MXFP6 into the row's step chunk.
-      float* ep = reinterpret_cast<float*>(st2) + wave * 64 * C::EP_PITCH;
+      // h = silu(g) * u; per gate group f, the wave's 32x32 tile goes to LDS as
+      // 32 rows x 32 columns and lanes 0..31 each encode one row's 32-column
+      // block as two-term MXFP6 into the row's step chunk.
+      float* ep = reinterpret_cast<float*>(st2) + wave * 32 * C::EP_PITCH;
       const uint32_t hpitch = (uint32_t)nsteps_of(a.F) * kChunk;
-      const int grow = c_m0 + wm * 64 + lane;
+      const int grow = c_m0 + wm * 32 + lane;
 #pragma unroll
       for (int f = 0; f < C::FM; ++f) {
 #pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
+        for (int i = 0; i < 16; ++i) {
+          const int rr = 8 * (i >> 2) + 4 * half + (i & 3);
+          const float g = acc[f][i], u = acc[f + C::FM][i];
+          ep[rr * C::EP_PITCH + lr] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane < 32) {
+          float v[32];
+          const float4* src = reinterpret_cast<const float4*>(ep + lane * C::EP_PITCH);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rr = mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const float g = acc[mf][f][i], u = acc[mf][f + C::FM][i];
-            ep[rr * C::EP_PITCH + lr] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+          for (int q = 0; q < 8; ++q) {
+            const float4 t4 = src[q];
+            v[4 * q] = t4.x;
+            v[4 * q + 1] = t4.y;
+            v[4 * q + 2] = t4.z;
+            v[4 * q + 3] = t4.w;
           }
-        __builtin_amdgcn_wave_barrier();
-        float v[32];
-        const float4* src = reinterpret_cast<const float4*>(ep + lane * C::EP_PITCH);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 t4 = src[q];
-          v[4 * q] = t4.x;
-          v[4 * q + 1] = t4.y;
-          v[4 * q + 2] = t4.z;
-          v[4 * q + 3] = t4.w;
+          uint32_t hw[6], lw[6], sc;
+          encode_block(v, hw, lw, sc);
+          if (grow < c_cnt) {
+            const int b = (c_col0 + wn * C::FM * 32 + f * 32) / 32;
+            uint8_t* hrow = hout + (size_t)(c_off + grow) * hpitch;
+            store_enc(hrow + enc_codes_at(b), hw, lw);
+            *reinterpret_cast<uint16_t*>(hrow + enc_scale_at(b)) = static_cast<uint16_t>(sc);
+          }
         }
         __builtin_amdgcn_wave_barrier();
-        uint32_t hw[6], lw[6], sc;
-        encode_block(v, hw, lw, sc);
-        if (grow < c_cnt) {
-          const int b = (c_col0 + wn * C::FM * 32 + f * 32) / 32;
-          uint8_t* hrow = hout + (size_t)(c_off + grow) * hpitch;
-          store_enc(hrow + enc_codes_at(b), hw, lw);
-          *reinterpret_cast<uint16_t*>(hrow + enc_scale_at(b)) = static_cast<uint16_t>(sc);
-        }
       }
     } else {
 #pragma unroll
-      for (int mf = 0; mf < 2; ++mf)
+      for (int i = 0; i < 16; ++i) {
+        const int rr = wm * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (rr < c_rows) {
+          float* yr = a.y_sorted + (size_t)(c_off + c_m0 + rr) * N + c_col0 + wn * NF * 32 + lr;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rr = wm * 64 + mf * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (rr < c_rows) {
-            float* yr = a.y_sorted + (size_t)(c_off + c_m0 + rr) * N + c_col0 + wn * NF * 32 + lr;
-#pragma unroll
-            for (int f = 0; f < NF; ++f) yr[f * 32] = acc[mf][f][i];
-          }
+          for (int f = 0; f < NF; ++f) yr[f * 32] = acc[f][i];
         }
+      }
     }
     if (!more) break;
     if (more2) fetch_rest(E, R);
     if (more3) fetch_entry(logical + 3 * nslot, E);
     if (GATEUP) {
       __syncthreads();  // every wave is done with st2
-      issue(2, st2);
+      issue(2, st2, IC<0>{}, IC<C::KSPLIT>{});
     }
     logical += nslot;
     more = more2;
@@ -888,11 +904,11 @@ hipError_t launch_prefill(const FfnArgs& a, const uint8_t* ain, uint8_t* hout, c
                           int ncu, hipStream_t stream) {
   const int N = GATEUP ? a.F : a.d;
   const int ntn = N / Prefill<NF, GATEUP>::MROWS;
-  // persistent: one workgroup per CU (the LDS holds one), 8 per XCD at least
+  // persistent: one workgroup of eight waves per CU (the LDS holds one), 8 per XCD at least
   const long long tiles_max = (long long)max_row_tiles(a.T, a.E, a.k, kBM) * ntn;
   long long grid = ncu < tiles_max ? ncu : tiles_max;
   grid = grid < 8 ? 8 : grid & ~7LL;
-  hipLaunchKernelGGL((grouped_prefill<NF, GATEUP>), dim3((unsigned)grid), dim3(256), 0, stream, a,
+  hipLaunchKernelGGL((grouped_prefill<NF, GATEUP>), dim3((unsigned)grid), dim3(kPrefWaves * 64), 0, stream, a,
                      ain, hout, tp, ntn);
   return hipGetLastError();
 }
