@@ -122,7 +122,8 @@ __device__ __forceinline__ uint32_t div_by(uint32_t x, uint64_t m) {
 //   BS  [matrix][group of the matrix][lane][2 B]  packed scales; one 4-byte copy
 //                          covers two groups of one matrix (lanes 0-31, 32-63)
 // The copies of a step are dealt out over the eight waves in equal numbers (a
-// wave whose share is short issues the rest into a junk area, reading nothing),
+// wave whose share is short issues the rest into a junk area, reading nothing;
+// the weight copies of one matrix go to the same waves, gate/up: 0-3 and 4-7),
 // and each wave spreads its copies among its MFMAs: the texture addresser takes
 // about 16 cycles per 64-lane copy, so copies issued back to back would hold the
 // wave. MFMA half s of a step takes, in lane half h, block 2h + s of A and of B.
@@ -140,8 +141,9 @@ struct Prefill {
   static constexpr int NMAT = GATEUP ? 2 : 1;
   static constexpr int GPM = NFR / NMAT;               // groups per matrix
   static constexpr int A_COPIES = kBM * kChunkPieces / 64;
-  static constexpr int B_COPIES = 2 * NFR;
-  static constexpr int S_COPIES = NFR / 2;
+  static constexpr int WPM = W / NMAT;                 // waves copying the weights of one matrix
+  static constexpr int B_COPIES = 2 * GPM;             // code copies per matrix
+  static constexpr int S_COPIES = GPM / 2;             // scale copies per matrix
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = A_OFF + kBM * kChunk;
   static constexpr int BS_OFF = B_OFF + NFR * 2 * 1024;
@@ -150,11 +152,13 @@ struct Prefill {
   static constexpr int STAGE_DATA = BS_OFF + NFR * 128;
   // one step's copies, or (gate/up) the epilogue's staging, which reuses a step buffer
   static constexpr int STAGE = GATEUP && EP_BYTES > STAGE_DATA ? EP_BYTES : STAGE_DATA;
-  // copy slots per wave: A copies i = wave + 8t, code copies c = wave + 8t, scale
-  // copies p = wave + 8t (t = 0, 1, ...); slot k numbers them A, code, scale
+  // copy slots per wave: A copies i = wave + 8t, then, for the matrix of the
+  // wave (gate/up: waves 0-3 gate, 4-7 up), code copies c = r + WPM t and scale
+  // copies p = r + WPM t, r the wave's rank among that matrix's waves (t = 0, 1,
+  // ...); slot k numbers them A, code, scale
   static constexpr int NA = (A_COPIES + W - 1) / W;
-  static constexpr int NB = (B_COPIES + W - 1) / W;
-  static constexpr int NS = (S_COPIES + W - 1) / W;
+  static constexpr int NB = (B_COPIES + WPM - 1) / WPM;
+  static constexpr int NS = (S_COPIES + WPM - 1) / WPM;
   static constexpr int KB0 = NA, KS0 = NA + NB, KMAX = NA + NB + NS;  // copies per wave per step
   // slots k < KSPLIT go among the MFMAs of half 1 of one step, the rest among
   // those of half 0 of the next
@@ -260,6 +264,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (W - 1);
   const int lane = tid & 63, lr = lane & 31, half = lane >> 5;
   const int wm = wave & 3, wn = wave >> 2;
+  const int mw = wave / C::WPM, rw = wave % C::WPM;  // matrix this wave copies, its rank among the copiers
   const uint32_t apitch = (uint32_t)nst * kChunk;
   const uint64_t kmagic = div_magic((uint32_t)a.k);  // token of dispatch pair q: q / k
   const uint32_t gstride = (uint32_t)nst * kWStep;    // packed code bytes per 32-row group
@@ -285,16 +290,15 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     }
     return phi * 32;
   };
-  // Scale copy p covers groups 2p', 2p'+1 of matrix p / (GPM/2), p' = p % (GPM/2):
-  // lane half h takes group 2p' + h; its LDS bytes sit at BS_OFF + 128 (m GPM + gg).
+  // Scale copy p of matrix mw covers its groups 2p, 2p+1: lane half h takes
+  // group 2p + h; its LDS bytes sit at BS_OFF + 128 (mw GPM + gg).
   auto scale_voff = [&](int p) -> uint32_t {
-    const int m = p / (C::GPM / 2), gg = 2 * (p % (C::GPM / 2)) + half;
-    return (uint32_t)(group_row(group_of(m, gg)) / 32) * sstride + lr * 4;
+    return (uint32_t)(group_row(group_of(mw, 2 * p + half)) / 32) * sstride + lr * 4;
   };
 
   // ---- per-tile state (all wave-uniform)
   int e, m0, off, cnt, rows_valid, col0;
-  v4i ar, br0, br1, bsr0, bsr1;
+  v4i ar, br, bsr;  // A rows; this wave's matrix: codes, scales
   uint32_t a_off[C::NA];  // per-lane A source offsets (step 0)
   float bias[NF];
 
@@ -316,7 +320,9 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     const int gm = min(kPrefGM, total_mt - grp * kPrefGM);
     const int r = lg - grp * kPrefGM * ntn;
     P.nt = r / gm;
-    P.ent = tiles[1 + grp * kPrefGM + (r - P.nt * gm)];
+    // through the constant address space: one scalar load into SGPRs
+    const __attribute__((address_space(4))) int4* ct = (const __attribute__((address_space(4))) int4*)tiles;
+    P.ent = ct[1 + grp * kPrefGM + (r - P.nt * gm)];
   };
   auto fetch_rest = [&](const Pre& Ein, Pre& P) __attribute__((always_inline)) {
     P.ent = Ein.ent;
@@ -347,10 +353,8 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     ar = GATEUP ? rsrc4(ain, (uint32_t)a.T * apitch)
                 : rsrc4(ain + (size_t)(off + m0) * apitch, (uint32_t)rows_valid * apitch);
     const size_t eb = (size_t)e * (N / 32) * gstride, es = (size_t)e * (N / 32) * sstride;
-    br0 = rsrc4((GATEUP ? a.wg_codes : a.wd_codes) + eb, (uint32_t)(N / 32) * gstride);
-    br1 = rsrc4((GATEUP ? a.wu_codes : a.wd_codes) + eb, (uint32_t)(N / 32) * gstride);
-    bsr0 = rsrc4((GATEUP ? a.wg_scales : a.wd_scales) + es, (uint32_t)(N / 32) * sstride);
-    bsr1 = rsrc4((GATEUP ? a.wu_scales : a.wd_scales) + es, (uint32_t)(N / 32) * sstride);
+    br = rsrc4((GATEUP ? (mw ? a.wu_codes : a.wg_codes) : a.wd_codes) + eb, (uint32_t)(N / 32) * gstride);
+    bsr = rsrc4((GATEUP ? (mw ? a.wu_scales : a.wg_scales) : a.wd_scales) + es, (uint32_t)(N / 32) * sstride);
 #pragma unroll
     for (int t = 0; t < C::NA; ++t) {
       const uint32_t tok = GATEUP ? div_by(P.src[t], kmagic) : P.src[t];
@@ -378,20 +382,18 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
                    pad ? kOutOfRange : a_off[t], (uint32_t)st * kChunk);
     } else if constexpr (k < C::KS0) {
       constexpr int t = k - C::KB0;
-      const int c = wave + W * t;  // code copy: half c & 1 of group (c >> 1) % GPM of matrix c / (2 GPM)
+      const int c = rw + C::WPM * t;  // code copy: half c & 1 of group c >> 1 of matrix mw
       const bool have = c < C::B_COPIES;
-      const int m = have ? c / (2 * C::GPM) : 0, lc = have ? c % (2 * C::GPM) : 0;
-      const int phi = group_of(m, lc >> 1), sh = lc & 1;
+      const int phi = group_of(mw, have ? c >> 1 : 0), sh = c & 1;
       const uint32_t so = (uint32_t)((col0 + group_row(phi)) / 32) * gstride + sh * 1024 + (uint32_t)st * kWStep;
-      lds_copy<16>(m ? br1 : br0, have ? base + C::B_OFF + (phi * 2 + sh) * 1024 : lds_addr(junk),
+      lds_copy<16>(br, have ? base + C::B_OFF + (phi * 2 + sh) * 1024 : lds_addr(junk),
                    have && !dead ? lane16 : kOutOfRange, so);
     } else {
       constexpr int t = k - C::KS0;
-      const int p = wave + W * t;
+      const int p = rw + C::WPM * t;
       const bool have = p < C::S_COPIES;
-      const int m = have ? p / (C::GPM / 2) : 0;
       const uint32_t so = (uint32_t)(col0 / 32) * sstride + (uint32_t)st * kWSStep;
-      lds_copy<4>(m ? bsr1 : bsr0, have ? base + C::BS_OFF + p * 256 : lds_addr(junk),
+      lds_copy<4>(bsr, have ? base + C::BS_OFF + (mw * C::GPM + 2 * p) * 128 : lds_addr(junk),
                   have && !dead ? scale_voff(have ? p : 0) : kOutOfRange, so);
     }
   };
