@@ -14,9 +14,11 @@ torch.cuda.synchronize(); the weights rotate over R identical copies (R * layer
 bytes >= 1.5 GB) so the 256 MB last-level cache cannot hold them. A second timed
 loop runs the same steps as the four separate calls (moe_route, moe_permute,
 moe_expert_ffn_mxfp4, moe_combine) with HIP events on the launch stream around
-the expert-FFN call; its average duration gives the roofline figure. The timed output is checked against
-the CPU oracle in the same run, and the oracle is timed on the host cores as
-the CPU baseline.
+the expert-FFN call. The roofline figure is the dominant kernel's, the gate/up
+GEMM (moe_expert_ffn_mxfp4_stage 1), whose average launch duration comes from
+a third loop that launches it back to back over the weight copies with events
+around the loop; the whole expert-FFN call's figure is reported beside it. The timed output is checked against the CPU oracle in the same run, and the
+oracle is timed on the host cores as the CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
                        [--no-stack] [--no-cpu-baseline] [--workload 1]
@@ -46,10 +48,11 @@ METRIC = "MoE layer tokens/s; % HBM peak (T=16) and % MXFP4 MFMA peak (T=8192)"
 TRAFFIC_SOURCES = ("ffn.hip", "ffn_dev.hpp", "mx6.hpp", "layout.hpp", "common.hpp")
 
 
-def measured_traffic(name: str):
-    """HBM bytes per launch of the expert-FFN call, from the committed rocprofv3
-    counter summary for this workload, or None when there is none or when the
-    kernel sources have changed since the counters were taken."""
+def measured_traffic(name: str, key: str = "traffic_bytes_per_launch"):
+    """HBM bytes per launch (of the gate/up GEMM, or with key
+    traffic_bytes_per_call of the whole expert-FFN call) from the committed
+    rocprofv3 counter summary for this workload, or None when there is none or
+    when the kernel sources have changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_expert_ffn_{name}.txt")
     if not os.path.exists(path):
@@ -57,14 +60,26 @@ def measured_traffic(name: str):
     fields = {}
     for line in open(path):
         if ":" in line:
-            key, _, val = line.strip().partition(":")
-            fields[key.strip()] = val.strip()
+            name_, _, val = line.strip().partition(":")
+            fields[name_.strip()] = val.strip()
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
         h.update(open(os.path.join(ROOT, "sparse_moe_transformer_gemm_amd", "csrc", f), "rb").read())
-    if h.hexdigest()[:16] != fields.get("sources_sha256_16"):
+    if h.hexdigest()[:16] != fields.get("sources_sha256_16") or key not in fields:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return int(fields[key])
+
+
+def enc_bytes(rows: int, K: int) -> int:
+    """Bytes of `rows` activation rows encoded for the matrix cores (208 per
+    128-deep step)."""
+    return rows * ((K + 127) // 128) * 208
+
+
+def gateup_bytes(d: int, F: int) -> int:
+    """Algorithmic bytes of one expert in the gate/up GEMM: the gate and up
+    MXFP4 matrices and their bf16 biases."""
+    return 2 * (d * F // 2 + d * F // 32) + 2 * 2 * F
 
 
 def expert_bytes(d: int, F: int) -> int:
@@ -160,8 +175,33 @@ def run_gpu(cfg: int, steps: int, warmup: int, log) -> dict:
         return (time.perf_counter() - t0) * 1e3 / steps
 
     ms_step = timed(step)                 # the headline: whole-block calls
-    ms_step_calls = timed(step_calls)     # the FFN call's duration for the roofline
+    ms_step_calls = timed(step_calls)     # the FFN call's duration
     ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # The GEMMs' average launch durations: the gate/up GEMM (stage 1, the
+    # dominant kernel) and then the down GEMM (stage 2) launched back to back
+    # over the rotating weight copies, on what the earlier stages left in the
+    # workspace (every launch rewrites the same h or y), one event pair around
+    # each timed run.
+    wt0 = copies[0]
+    idx, _ = moe.route(x, wt0.w_router, wt0.b_router, k, ws, bufs["topk_idx"], bufs["topk_w"])
+    perm = moe.permute(idx, E, ws, bufs["perm"])
+    moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], wt0, k, ws, bufs["y_sorted"], 0)
+
+    def stage_ms(stage):
+        for i in range(warmup):
+            moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], copies[i % R], k, ws, bufs["y_sorted"], stage)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record()
+        for i in range(steps):
+            moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], copies[i % R], k, ws, bufs["y_sorted"], stage)
+        g1.record()
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) / steps
+
+    gu_ms = stage_ms(1)
+    dn_ms = stage_ms(2)
     # the checked output is the whole-block call's
     step(0)
     torch.cuda.synchronize()
@@ -171,6 +211,9 @@ def run_gpu(cfg: int, steps: int, warmup: int, log) -> dict:
     idx_gpu = bufs["topk_idx"].cpu().numpy()
 
     ffn_bytes = U * expert_bytes(d, F) + 2 * T * d
+    # gate/up GEMM: its weights and biases, the encoded x it reads, the encoded h it writes
+    gu_bytes = U * gateup_bytes(d, F) + enc_bytes(T, d) + enc_bytes(T * k, F)
+    gu_flops = 2.0 * T * k * 2 * d * F
     layer_alg_bytes = ffn_bytes + 4 * d * E + (4 * E if L.b_router is not None else 0) + 2 * T * d
     flops = 2.0 * T * k * 3 * d * F
     res = dict(
@@ -178,13 +221,16 @@ def run_gpu(cfg: int, steps: int, warmup: int, log) -> dict:
         experts_touched=U, ms_per_step=ms_step, ms_per_step_calls=ms_step_calls,
         tokens_per_s=T / (ms_step / 1e3),
         ffn_ms=ffn_ms, ffn_alg_bytes=ffn_bytes, layer_alg_bytes=layer_alg_bytes,
+        gu_ms=gu_ms, dn_ms=dn_ms, gu_alg_bytes=gu_bytes, gu_flops=gu_flops,
+        gu_gbs=gu_bytes / (gu_ms / 1e3) / 1e9, gu_tflops=gu_flops / (gu_ms / 1e3) / 1e12,
         ffn_gbs=ffn_bytes / (ffn_ms / 1e3) / 1e9, ffn_tflops=flops / (ffn_ms / 1e3) / 1e12,
         layer_gbs=layer_alg_bytes / (ms_step / 1e3) / 1e9,
         layer_tflops=flops / (ms_step / 1e3) / 1e12, flops=flops,
         _out_bits=out_bits, _idx=idx_gpu, _workload=w)
     log(f"[bench] {w.name}: {ms_step * 1e3:.1f} us/step ({ms_step_calls * 1e3:.1f} as four calls), "
-        f"ffn {ffn_ms * 1e3:.1f} us, "
-        f"{res['tokens_per_s']:.4g} tok/s, ffn {res['ffn_gbs']:.0f} GB/s / {res['ffn_tflops']:.0f} TFLOP/s")
+        f"ffn {ffn_ms * 1e3:.1f} us (back to back: gate/up {gu_ms * 1e3:.1f}, down {dn_ms * 1e3:.1f}), "
+        f"{res['tokens_per_s']:.4g} tok/s, ffn {res['ffn_gbs']:.0f} GB/s / {res['ffn_tflops']:.0f} TFLOP/s, "
+        f"gate/up {res['gu_gbs']:.0f} GB/s / {res['gu_tflops']:.0f} TFLOP/s")
     del copies, ws, bufs
     torch.cuda.empty_cache()
     return res
@@ -343,10 +389,14 @@ def main():
         sec = {
             "workload": s["workload"], "T": s["T"], "tokens_per_s": s["tokens_per_s"],
             "ms_per_step": s["ms_per_step"], "experts_touched": s["experts_touched"],
-            "roofline": {"bound": "mfma", "kernel": "moe_expert_ffn_mxfp4",
-                         "achieved": s["ffn_tflops"], "peak": MXFP4_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": s["ffn_tflops"] / MXFP4_PEAK_TFLOPS,
-                         "traffic": None},
+            "roofline": {"bound": "mfma", "kernel": "grouped_prefill<6, true>: the gate/up GEMM with "
+                                                     "SwiGLU (moe_expert_ffn_mxfp4 stage 1)",
+                         "achieved": s["gu_tflops"], "peak": MXFP4_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": s["gu_tflops"] / MXFP4_PEAK_TFLOPS,
+                         "traffic": None, "flops_per_launch": s["gu_flops"], "avg_launch_ms": s["gu_ms"],
+                         "down_gemm_ms": s["dn_ms"],
+                         "ffn_call": {"achieved": s["ffn_tflops"], "frac": s["ffn_tflops"] / MXFP4_PEAK_TFLOPS,
+                                      "avg_ms": s["ffn_ms"], "flops": s["flops"]}},
             "layer_frac_mxfp4_peak": s["layer_tflops"] / MXFP4_PEAK_TFLOPS,
             "ffn_ms": s["ffn_ms"],
         }
@@ -375,13 +425,24 @@ def main():
                                f"top-{r['k']}, seed {r['seed']}",
                    "global_batch": r["T"], "weight_copies": r["weight_copies"],
                    "experts_touched": r["experts_touched"]},
-        "roofline": {"bound": "hbm", "kernel": "moe_expert_ffn_mxfp4",
-                     "achieved": r["ffn_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": r["ffn_gbs"] / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "grouped_decode<true, 6>: the gate/up GEMM with SwiGLU "
+                                               "(moe_expert_ffn_mxfp4 stage 1)",
+                     "achieved": r["gu_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["gu_gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"{r['workload']}_T{r['T']}"),
-                     "alg_bytes_per_launch": r["ffn_alg_bytes"], "avg_launch_ms": r["ffn_ms"],
-                     "timing": "HIP events around moe_expert_ffn_mxfp4 in a second timed loop "
-                               "of the same steps run as the four separate calls"},
+                     "alg_bytes_per_launch": r["gu_alg_bytes"], "avg_launch_ms": r["gu_ms"],
+                     "timing": "gate/up GEMM (moe_expert_ffn_mxfp4_stage 1) launched back to back "
+                               "over the rotating weight copies, HIP events on the launch stream "
+                               "around the timed launches",
+                     "down_gemm_ms": r["dn_ms"],
+                     "ffn_call": {"kernels": "encode + gate/up GEMM + down GEMM",
+                                  "achieved": r["ffn_gbs"], "frac": r["ffn_gbs"] / HBM_PEAK_GBS,
+                                  "avg_ms": r["ffn_ms"], "alg_bytes": r["ffn_alg_bytes"],
+                                  "timing": "HIP events around moe_expert_ffn_mxfp4 in a second "
+                                            "timed loop of the same steps run as the four "
+                                            "separate calls",
+                                  "traffic": measured_traffic(f"{r['workload']}_T{r['T']}",
+                                                              "traffic_bytes_per_call")}},
         "ms_per_step_four_calls": r["ms_per_step_calls"],
         "layer_frac_hbm_peak": r["layer_gbs"] / HBM_PEAK_GBS,
         "cpu_baseline": cpu,

@@ -170,6 +170,26 @@ moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x,
                                 const moe_bf16* b_down, float* y_sorted,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* moe_expert_ffn_mxfp4 as three separately enqueued stages, for callers that
+ * time or schedule the two GEMMs on their own (same arguments, plus `stage`):
+ *   stage 0  encodes x for the matrix cores and builds the expert tile tables
+ *            (into ws)
+ *   stage 1  the gate/up GEMM with its biases and SwiGLU: h, encoded, into ws
+ *   stage 2  the down GEMM with its bias: y_sorted
+ * Stages 0, 1, 2 enqueued in that order on one stream with the same arguments
+ * and workspace write exactly the bytes moe_expert_ffn_mxfp4 writes. Stage 1
+ * reads what stage 0 left in ws and stage 2 what stage 1 left: running a stage
+ * without the earlier ones of the same call (same dims, inputs and ws, nothing
+ * else using ws in between) is undefined. Errors: MOE_ERR_INVALID_ARG for a
+ * stage outside 0..2, otherwise as moe_expert_ffn_mxfp4. */
+moe_status moe_expert_ffn_mxfp4_stage(moe_dims dims, const moe_bf16* x,
+                                      const int32_t* sorted_pair, const int32_t* offsets,
+                                      moe_mxfp4_packed w_gate, moe_mxfp4_packed w_up,
+                                      moe_mxfp4_packed w_down,
+                                      const moe_bf16* b_gate, const moe_bf16* b_up,
+                                      const moe_bf16* b_down, float* y_sorted, int32_t stage,
+                                      void* ws, size_t ws_bytes, void* stream);
+
 /* Atomic-free weighted combine back to token order:
  *   out[t] = bf16( sum_{j=0..k-1} topk_w[t][j] * y_sorted[pair_row[t*k+j]] ),
  * summed in fp32 in fixed j order, rounded once to nearest even.

@@ -21,7 +21,7 @@ __all__ = [
     "MoeError", "Dims", "MXFP4", "library_path", "lib", "workspace_bytes", "route",
     "permute", "expert_ffn_mxfp4", "combine", "rmsnorm", "residual_add", "forward",
     "ExpertWeights", "EXPORTED", "pack_mxfp4", "packed_bytes", "load_expert_weights",
-    "forward_calls",
+    "forward_calls", "expert_ffn_mxfp4_stage",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,7 @@ _LIB_NAME = "libmoe_mi355x.so"
 EXPORTED = (
     "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine",
     "moe_rmsnorm", "moe_residual_add", "moe_status_string", "moe_last_error",
-    "moe_mxfp4_packed_bytes", "moe_pack_mxfp4", "moe_forward",
+    "moe_mxfp4_packed_bytes", "moe_pack_mxfp4", "moe_forward", "moe_expert_ffn_mxfp4_stage",
 )
 
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.moe_permute.argtypes = [Dims, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_ffn_mxfp4.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp,
                                        vp, sz, vp]
+    L.moe_expert_ffn_mxfp4_stage.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp,
+                                             i32, vp, sz, vp]
     L.moe_combine.argtypes = [Dims, vp, vp, vp, vp, vp]
     L.moe_forward.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, vp, sz, vp]
@@ -78,7 +80,8 @@ def lib() -> ctypes.CDLL:
     L.moe_pack_mxfp4.argtypes = [i32, i32, i32, MXFP4, vp, vp, vp]
     L.moe_rmsnorm.argtypes = [i32, i32, vp, vp, ctypes.c_float, vp, vp]
     L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp]
-    for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine", "moe_rmsnorm",
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_expert_ffn_mxfp4_stage",
+              "moe_combine", "moe_rmsnorm",
               "moe_residual_add", "moe_pack_mxfp4", "moe_forward"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
@@ -254,6 +257,28 @@ def expert_ffn_mxfp4(x, sorted_pair, offsets, w: ExpertWeights, k: int, ws, y_so
         _dev(w.b_down, torch.bfloat16, (E, d), "b_down"),
         _dev(y_sorted, torch.float32, (P, d), "y_sorted"),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream()), "moe_expert_ffn_mxfp4")
+    return y_sorted
+
+
+def expert_ffn_mxfp4_stage(x, sorted_pair, offsets, w: ExpertWeights, k: int, ws, y_sorted, stage: int):
+    """One stage of expert_ffn_mxfp4 (0: encode x and build the tile tables,
+    1: gate/up GEMM + SwiGLU, 2: down GEMM into y_sorted); the three in order
+    with the same arguments are expert_ffn_mxfp4."""
+    T, d = x.shape
+    dw, F, E = w.dims
+    if dw != d:
+        raise ValueError("x width does not match the router weight")
+    P = T * k
+    mg, mu, md = _packed_args(w)
+    _check(lib().moe_expert_ffn_mxfp4_stage(
+        _dims(T, d, F, E, k), _dev(x, torch.bfloat16, (T, d), "x"),
+        _dev(sorted_pair, torch.int32, (P,), "sorted_pair"),
+        _dev(offsets, torch.int32, (E + 1,), "offsets"), mg, mu, md,
+        _dev(w.b_gate, torch.bfloat16, (E, F), "b_gate"),
+        _dev(w.b_up, torch.bfloat16, (E, F), "b_up"),
+        _dev(w.b_down, torch.bfloat16, (E, d), "b_down"),
+        _dev(y_sorted, torch.float32, (P, d), "y_sorted"), int(stage),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream()), "moe_expert_ffn_mxfp4_stage")
     return y_sorted
 
 

@@ -151,19 +151,16 @@ moe_status moe_pack_mxfp4(int32_t E, int32_t N, int32_t K, moe_mxfp4 src, uint8_
                                            static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x, const int32_t* sorted_pair,
-                                const int32_t* offsets, moe_mxfp4_packed w_gate,
-                                moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
-                                const moe_bf16* b_gate, const moe_bf16* b_up,
-                                const moe_bf16* b_down, float* y_sorted, void* ws,
-                                size_t ws_bytes, void* stream) {
-  g_last_error[0] = 0;
+static moe_status ffn_args(moe_dims dims, const moe_bf16* x, const int32_t* sorted_pair,
+                           const int32_t* offsets, moe_mxfp4_packed w_gate, moe_mxfp4_packed w_up,
+                           moe_mxfp4_packed w_down, const moe_bf16* b_gate, const moe_bf16* b_up,
+                           const moe_bf16* b_down, float* y_sorted, void* ws, size_t ws_bytes,
+                           const char* who, moe::FfnArgs& a) {
   MOE_TRY(check_dims(dims));
   MOE_TRY(check_ptrs({x, sorted_pair, offsets, w_gate.codes, w_gate.scales, w_up.codes,
                       w_up.scales, w_down.codes, w_down.scales, b_gate, b_up, b_down, y_sorted},
-                     "moe_expert_ffn_mxfp4"));
+                     who));
   MOE_TRY(check_ws(dims, ws, ws_bytes));
-  moe::FfnArgs a;
   a.T = dims.T;
   a.d = dims.d;
   a.F = dims.F;
@@ -183,7 +180,37 @@ moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x, const int32_t*
   a.b_down = b_down;
   a.y_sorted = y_sorted;
   a.ws = ws;
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x, const int32_t* sorted_pair,
+                                const int32_t* offsets, moe_mxfp4_packed w_gate,
+                                moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                                const moe_bf16* b_gate, const moe_bf16* b_up,
+                                const moe_bf16* b_down, float* y_sorted, void* ws,
+                                size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  moe::FfnArgs a;
+  MOE_TRY(ffn_args(dims, x, sorted_pair, offsets, w_gate, w_up, w_down, b_gate, b_up, b_down,
+                   y_sorted, ws, ws_bytes, "moe_expert_ffn_mxfp4", a));
   return hip_status(moe::launch_expert_ffn(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_ffn_mxfp4_stage(moe_dims dims, const moe_bf16* x, const int32_t* sorted_pair,
+                                      const int32_t* offsets, moe_mxfp4_packed w_gate,
+                                      moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                                      const moe_bf16* b_gate, const moe_bf16* b_up,
+                                      const moe_bf16* b_down, float* y_sorted, int32_t stage,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (stage < 0 || stage > 2) {
+    set_error("%s", "moe_expert_ffn_mxfp4_stage: stage not in 0..2");
+    return MOE_ERR_INVALID_ARG;
+  }
+  moe::FfnArgs a;
+  MOE_TRY(ffn_args(dims, x, sorted_pair, offsets, w_gate, w_up, w_down, b_gate, b_up, b_down,
+                   y_sorted, ws, ws_bytes, "moe_expert_ffn_mxfp4_stage", a));
+  return hip_status(moe::launch_expert_ffn_stage(a, static_cast<hipStream_t>(stream), (int)stage));
 }
 
 moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,

@@ -77,6 +77,10 @@ bool ffn_decode_shape(int T, int d, int F);
 // front_done: x is already encoded and the pass table built in the workspace
 // (by launch_forward_front); decode shape only.
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_done = false);
+// One stage of it: 0 encodes x and builds the tile tables (nothing when
+// front_done), 1 runs the gate/up GEMM with SwiGLU into the encoded h, 2 the
+// down GEMM into y_sorted; the three in order are launch_expert_ffn.
+hipError_t launch_expert_ffn_stage(const FfnArgs& a, hipStream_t stream, int stage, bool front_done = false);
 
 // Fused route + permute + activation encode of the whole-block call, for the
 // shapes where forward_front_fits; its scratch follows the FFN workspace and

@@ -320,9 +320,10 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     const int gm = min(kPrefGM, total_mt - grp * kPrefGM);
     const int r = lg - grp * kPrefGM * ntn;
     P.nt = r / gm;
-    // through the constant address space: one scalar load into SGPRs
-    const __attribute__((address_space(4))) int4* ct = (const __attribute__((address_space(4))) int4*)tiles;
-    P.ent = ct[1 + grp * kPrefGM + (r - P.nt * gm)];
+    // through the constant address space: scalar loads into SGPRs
+    const __attribute__((address_space(4))) int* ct = (const __attribute__((address_space(4))) int*)tiles;
+    const int q = 4 * (1 + grp * kPrefGM + (r - P.nt * gm));
+    P.ent = make_int4(ct[q], ct[q + 1], ct[q + 2], ct[q + 3]);
   };
   auto fetch_rest = [&](const Pre& Ein, Pre& P) __attribute__((always_inline)) {
     P.ent = Ein.ent;
@@ -969,7 +970,7 @@ bool ffn_decode_shape(int T, int d, int F) {
   return T <= kDecodeMaxT && decode_fits(d) && decode_fits(F);
 }
 
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_done) {
+hipError_t launch_expert_ffn_stage(const FfnArgs& a, hipStream_t stream, int stage, bool front_done) {
   const WsLayout L = ws_layout(a.T, a.d, a.F, a.E, a.k);
   int dev = 0, ncu = 0;
   hipError_t qerr = hipGetDevice(&dev);
@@ -988,38 +989,42 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_do
   int4* pp = reinterpret_cast<int4*>(ws + L.passes);
   const TableJob tj{a.offsets, a.E, (!dec_gu || !dec_dn) ? tp : nullptr, (dec_gu || dec_dn) ? pp : nullptr};
 
-  // x is encoded once; one extra workgroup of the same launch builds the tables
-  // (or the fused front end has done both: decode shape only)
-  hipError_t err = hipSuccess;
-  if (front_done) {
-    if (!dec_gu || !dec_dn) return hipErrorInvalidValue;
-  } else {
+  if (stage == 0) {
+    // x is encoded once; one extra workgroup of the same launch builds the tables
+    // (or the fused front end has done both: decode shape only)
+    if (front_done) return (dec_gu && dec_dn) ? hipSuccess : hipErrorInvalidValue;
     const int nx = a.T * (a.d / 32);
     if (nx <= 16384)
       hipLaunchKernelGGL(encode_rows, dim3((nx + 7) / 8 + 1), dim3(256), 0, stream, a.x, a.T, a.d, xenc, tj);
     else
       hipLaunchKernelGGL(encode_rows_thread, dim3((nx + 255) / 256 + 1), dim3(256), 0, stream, a.x, a.T,
                          a.d, xenc, tj);
-    err = hipGetLastError();
+    return hipGetLastError();
+  }
+  if (stage == 1) {
+    // Column tiles: the widest that divides N (gate/up: 32*NF h-columns, down:
+    // 64*NF output columns per workgroup).
+    if (dec_gu) return launch_decode<true>(a, xenc, henc, pp, ncu, stream);
+    if (a.F % 192 == 0) return launch_prefill<6, true>(a, xenc, henc, tp, ncu, stream);
+    if (a.F % 128 == 0) return launch_prefill<4, true>(a, xenc, henc, tp, ncu, stream);
+    return launch_prefill<2, true>(a, xenc, henc, tp, ncu, stream);
+  }
+  if (stage == 2) {
+    if (dec_dn) return launch_decode<false>(a, henc, henc, pp, ncu, stream);
+    if (a.d % 320 == 0) return launch_prefill<5, false>(a, henc, henc, tp, ncu, stream);
+    if (a.d % 192 == 0) return launch_prefill<3, false>(a, henc, henc, tp, ncu, stream);
+    if (a.d % 128 == 0) return launch_prefill<2, false>(a, henc, henc, tp, ncu, stream);
+    return launch_prefill<1, false>(a, henc, henc, tp, ncu, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_done) {
+  for (int stage = 0; stage < 3; ++stage) {
+    const hipError_t err = launch_expert_ffn_stage(a, stream, stage, front_done);
     if (err != hipSuccess) return err;
   }
-  // Column tiles: the widest that divides N (gate/up: 32*NF h-columns, down:
-  // 64*NF output columns per workgroup).
-  if (dec_gu) {
-    err = launch_decode<true>(a, xenc, henc, pp, ncu, stream);
-  } else if (a.F % 192 == 0) {
-    err = launch_prefill<6, true>(a, xenc, henc, tp, ncu, stream);
-  } else if (a.F % 128 == 0) {
-    err = launch_prefill<4, true>(a, xenc, henc, tp, ncu, stream);
-  } else {
-    err = launch_prefill<2, true>(a, xenc, henc, tp, ncu, stream);
-  }
-  if (err != hipSuccess) return err;
-  if (dec_dn) return launch_decode<false>(a, henc, henc, pp, ncu, stream);
-  if (a.d % 320 == 0) return launch_prefill<5, false>(a, henc, henc, tp, ncu, stream);
-  if (a.d % 192 == 0) return launch_prefill<3, false>(a, henc, henc, tp, ncu, stream);
-  if (a.d % 128 == 0) return launch_prefill<2, false>(a, henc, henc, tp, ncu, stream);
-  return launch_prefill<1, false>(a, henc, henc, tp, ncu, stream);
+  return hipSuccess;
 }
 
 }  // namespace moe

@@ -144,6 +144,29 @@ def test_forward_validation(moe):
     assert L.moe_forward(D(16, 512, 512, 300, 4), *args) == -2
 
 
+def test_ffn_stage_validation(moe):
+    """The staged FFN call rejects a stage outside 0..2 and checks the rest of
+    its arguments as moe_expert_ffn_mxfp4 does, before any launch."""
+    L = moe.lib()
+    D = moe.Dims
+    ok = D(16, 512, 512, 32, 4)
+    ws = L.moe_workspace_bytes(ok)
+    m = moe.MXFP4(FAKE, FAKE)
+    # x, sorted_pair, offsets, w_gate, w_up, w_down, b_gate, b_up, b_down, y_sorted,
+    # stage, ws, ws_bytes, stream
+    args = [FAKE, FAKE, FAKE, m, m, m, FAKE, FAKE, FAKE, FAKE, 1, FAKE, ws, None]
+    for stage in (-1, 3):
+        a = list(args); a[10] = stage
+        assert L.moe_expert_ffn_mxfp4_stage(ok, *a) == -1, stage
+        assert b"stage" in L.moe_last_error()
+    for i in (0, 1, 2, 6, 9, 11):
+        a = list(args); a[i] = None
+        assert L.moe_expert_ffn_mxfp4_stage(ok, *a) == -1, i
+    a = list(args); a[12] = ws - 256
+    assert L.moe_expert_ffn_mxfp4_stage(ok, *a) == -3
+    assert L.moe_expert_ffn_mxfp4_stage(D(16, 512, 512, 300, 4), *args) == -2
+
+
 def test_workspace_covers_the_fused_call(moe):
     """The whole-block call's scratch (router partials and an arrival counter
     after the FFN regions) is part of moe_workspace_bytes at decode sizes."""

@@ -81,3 +81,31 @@ def test_forward_reuses_workspace(gu, E):
         a = _host(moe.forward(x, wt, w.k, ws))
         b = _host(moe.forward_calls(x, wt, w.k, ws_ref))
         _same(a, b, f"T={T}")
+
+
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[2], SHAPES[6], SHAPES[7],
+                                   dict(T=300, d=320, F=384, E=12, k=4, seed=47)],
+                         ids=["decode", "ragged", "wide-K", "prefill-path", "prefill-ragged"])
+def test_ffn_stages_equal_the_call(gu, shape):
+    """moe_expert_ffn_mxfp4_stage 0, 1, 2 in order write y_sorted byte for byte
+    as moe_expert_ffn_mxfp4 does (decode and prefill kernels, ragged shapes)."""
+    import torch
+
+    import sparse_moe_transformer_gemm_amd as moe
+    w = synth.tiny_workload(**shape)
+    L = w.layers[0]
+    print(f"[stages] {w.name}", flush=True)
+    wt = gu.weights_dev(L)
+    ws = gu.workspace(w.T, w.d, w.F, w.E, w.k)
+    x = gu.bf16_dev(w.x)
+    idx, _ = moe.route(x, wt.w_router, wt.b_router, w.k, ws)
+    perm = moe.permute(idx, w.E, ws)
+    P = w.T * w.k
+    y_call = moe.expert_ffn_mxfp4(x, perm[2], perm[1], wt, w.k, ws,
+                                  torch.full((P, w.d), float("nan"), device=x.device))
+    ws2 = gu.workspace(w.T, w.d, w.F, w.E, w.k)
+    y_st = torch.full((P, w.d), float("nan"), device=x.device)
+    for stage in range(3):
+        moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], wt, w.k, ws2, y_st, stage)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_call.cpu().numpy().view(np.uint32), y_st.cpu().numpy().view(np.uint32))
