@@ -114,8 +114,8 @@ __device__ __forceinline__ uint32_t div_by(uint32_t x, uint64_t m) {
 //
 // Each K step is copied from global memory straight into LDS by buffer-to-LDS
 // loads (lane i of a copy writes LDS bytes [16i, 16i+16) for 16-byte copies and
-// [4i, 4i+4) for 4-byte ones), three step buffers: step st+3 is copied while step
-// st+1 is read and computed. LDS layout of one step:
+// [4i, 4i+4) for 4-byte ones), three step buffers: step st+2 is copied while step
+// st is read and computed. LDS layout of one step:
 //   A   [128 rows][208 B]  the rows' encoded chunks as stored (copy q of 16 B:
 //                          row q/13, piece q%13; lanes of one row read one run)
 //   B   [group][half][lane][16 B]  packed fragments, 1 KB per copy
@@ -160,14 +160,15 @@ struct Prefill {
   static constexpr int NB = (B_COPIES + WPM - 1) / WPM;
   static constexpr int NS = (S_COPIES + WPM - 1) / WPM;
   static constexpr int KB0 = NA, KS0 = NA + NB, KMAX = NA + NB + NS;  // copies per wave per step
-  // slots k < KSPLIT go among the MFMAs of half 1 of one step, the rest among
-  // those of half 0 of the next
+  // slots k < KSPLIT go among the MFMAs of half 0 of a step, the rest among
+  // those of half 1
   static constexpr int KSPLIT = (KMAX + 1) / 2;
   static_assert(kBM * kChunkPieces % 64 == 0, "A copies are whole instructions");
   static_assert(kBM == 4 * 32, "one 32-row fragment per wave row");
   static_assert(!GATEUP || NF % 2 == 0, "gate/up tiles pair gate and up groups");
   static_assert(GPM % 2 == 0, "scale copies take two groups of one matrix");
   static_assert(2 * KMAX <= 63, "two steps of copies must fit the vector memory counter");
+  static_assert(KSPLIT > 0 && KSPLIT < KMAX, "each half step carries copies");
   static_assert(3 * STAGE + 1024 <= 160 * 1024, "three step buffers and the junk area must fit the 160 KB of LDS");
   static_assert(!GATEUP || EP_BYTES <= STAGE, "SwiGLU staging of the eight waves must fit one step buffer");
 };
@@ -471,7 +472,6 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
   }
   issue(0, st0, IC<0>{}, IC<C::KMAX>{});
   issue(1, st1, IC<0>{}, IC<C::KMAX>{});
-  issue(2, st2, IC<0>{}, IC<C::KSPLIT>{});
 
   for (;;) {
 #pragma unroll
@@ -480,13 +480,14 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       for (int i = 0; i < 16; ++i) acc[f][i] = bias[f];
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- main loop. Per step st (its data in `c0`): read half 0, compute it
-    // while copying the second part of step st+2 into `c2`; read half 1; then,
-    // once step st+1 has landed and every wave has read `c0` (barrier), compute
-    // half 1 of step st while copying the first part of step st+3 into `c0`. The
-    // other wavefront on the SIMD computes while this one waits for its reads.
-    // step 0 has landed (step 1 and the first part of step 2 may be in flight)
-    MOE_WAIT_VMCNT(C::KMAX + C::KSPLIT);
+    // ---- main loop. Per step st (its data in `c0`): read half 0 and compute it,
+    // read half 1 and compute it, copying step st+2 into `c2` (the buffer step
+    // st-1 left) among the MFMAs of both halves; then wait until step st+1 has
+    // landed and every wave has read `c0` (barrier). The barrier comes after all
+    // of the step's MFMAs, so the wavefront that reaches it first waits while the
+    // other one on its SIMD is still computing.
+    // step 0 has landed (step 1 may be in flight)
+    MOE_WAIT_VMCNT(C::KMAX);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -496,16 +497,16 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       read_half(c0, st, IC<0>{});
       __builtin_amdgcn_sched_barrier(0);
       MOE_WAIT_LGKM0();
-      mma_half(IC<0>{}, IC<C::KSPLIT>{}, IC<C::KMAX>{}, st + 2, lds_addr(c2));
+      mma_half(IC<0>{}, IC<0>{}, IC<C::KSPLIT>{}, st + 2, lds_addr(c2));
       __builtin_amdgcn_sched_barrier(0);
       read_half(c0, st, IC<1>{});
       __builtin_amdgcn_sched_barrier(0);
       MOE_WAIT_LGKM0();            // this wave's reads of `c0` are complete
+      mma_half(IC<1>{}, IC<C::KSPLIT>{}, IC<C::KMAX>{}, st + 2, lds_addr(c2));
+      __builtin_amdgcn_sched_barrier(0);
       MOE_WAIT_VMCNT(C::KMAX);     // step st+1 has landed (step st+2 may be in flight)
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");  // no LDS access moves across the barrier
-      __builtin_amdgcn_sched_barrier(0);
-      mma_half(IC<1>{}, IC<0>{}, IC<C::KSPLIT>{}, st + 3, lds_addr(c0));
       __builtin_amdgcn_sched_barrier(0);
     };
     // Steps go in threes (one per buffer), then the one or two left.
@@ -520,17 +521,17 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     MOE_WAIT_VMCNT(0);
     __syncthreads();
 
-    // ---- this tile's output coordinates; the next tile's first steps are copied
-    // while this tile's epilogue runs (gate/up stages through st2, so its third
-    // step waits for the epilogue); the fetches for the tiles after it are
-    // issued after the epilogue and complete while the next tile is computed
+    // ---- this tile's output coordinates; the next tile's first two steps are
+    // copied while this tile's epilogue runs (gate/up stages through st2, which
+    // the next tile's first step copies into); the fetches for the tiles after
+    // it are issued after the epilogue and complete while the next tile is
+    // computed
     const int c_off = off, c_m0 = m0, c_cnt = cnt, c_rows = rows_valid, c_col0 = col0;
     const bool more3 = logical + 3 * nslot < xend;
     if (more) {
       setup(R);
       issue(0, st0, IC<0>{}, IC<C::KMAX>{});
       issue(1, st1, IC<0>{}, IC<C::KMAX>{});
-      if (!GATEUP) issue(2, st2, IC<0>{}, IC<C::KSPLIT>{});
     }
 
     if constexpr (GATEUP) {
@@ -585,10 +586,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     if (!more) break;
     if (more2) fetch_rest(E, R);
     if (more3) fetch_entry(logical + 3 * nslot, E);
-    if (GATEUP) {
-      __syncthreads();  // every wave is done with st2
-      issue(2, st2, IC<0>{}, IC<C::KSPLIT>{});
-    }
+    if (GATEUP) __syncthreads();  // every wave is done with st2 before step 2 is copied into it
     logical += nslot;
     more = more2;
     more2 = more3;
