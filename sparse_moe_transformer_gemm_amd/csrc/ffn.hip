@@ -148,10 +148,10 @@ struct Prefill {
   static constexpr int B_OFF = A_OFF + kBM * kChunk;
   static constexpr int BS_OFF = B_OFF + NFR * 2 * 1024;
   static constexpr int EP_PITCH = 36;                  // floats per row of the SwiGLU staging tile
-  static constexpr int EP_BYTES = W * 32 * EP_PITCH * 4;  // staging of all eight waves (gate/up)
+  static constexpr int EP_BYTES = W * 32 * EP_PITCH * 4;  // epilogue staging of all eight waves
   static constexpr int STAGE_DATA = BS_OFF + NFR * 128;
-  // one step's copies, or (gate/up) the epilogue's staging, which reuses a step buffer
-  static constexpr int STAGE = GATEUP && EP_BYTES > STAGE_DATA ? EP_BYTES : STAGE_DATA;
+  // one step's copies, or the epilogue's staging, which reuses a step buffer
+  static constexpr int STAGE = EP_BYTES > STAGE_DATA ? EP_BYTES : STAGE_DATA;
   // copy slots per wave: A copies i = wave + 8t, then, for the matrix of the
   // wave (gate/up: waves 0-3 gate, 4-7 up), code copies c = r + WPM t and scale
   // copies p = r + WPM t, r the wave's rank among that matrix's waves (t = 0, 1,
@@ -170,7 +170,7 @@ struct Prefill {
   static_assert(2 * KMAX <= 63, "two steps of copies must fit the vector memory counter");
   static_assert(KSPLIT > 0 && KSPLIT < KMAX, "each half step carries copies");
   static_assert(3 * STAGE + 1024 <= 160 * 1024, "three step buffers and the junk area must fit the 160 KB of LDS");
-  static_assert(!GATEUP || EP_BYTES <= STAGE, "SwiGLU staging of the eight waves must fit one step buffer");
+  static_assert(EP_BYTES <= STAGE, "epilogue staging of the eight waves must fit one step buffer");
 };
 
 // s_waitcnt with only the vector memory counter bounded (gfx9 encoding:
@@ -522,9 +522,9 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     __syncthreads();
 
     // ---- this tile's output coordinates; the next tile's first two steps are
-    // copied while this tile's epilogue runs (gate/up stages through st2, which
-    // the next tile's first step copies into); the fetches for the tiles after
-    // it are issued after the epilogue and complete while the next tile is
+    // copied while this tile's epilogue runs (the epilogue stages through st2,
+    // which the next tile's first step copies into); the fetches for the tiles
+    // after it are issued after the epilogue and complete while the next tile is
     // computed
     const int c_off = off, c_m0 = m0, c_cnt = cnt, c_rows = rows_valid, c_col0 = col0;
     const bool more3 = logical + 3 * nslot < xend;
@@ -573,20 +573,35 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
         __builtin_amdgcn_wave_barrier();
       }
     } else {
+      // y = the fp32 accumulators, staged per 32-column group through LDS (st2,
+      // which no copy targets until the next tile's first step) so that each lane
+      // stores 16 contiguous bytes: store q of a wave writes 8 whole rows of the
+      // group (8 lanes x 16 B per row) instead of 64 single floats.
+      float* ep = reinterpret_cast<float*>(st2) + wave * 32 * C::EP_PITCH;
+      const int srow = lane >> 3, scol = (lane & 7) * 4;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rr = wm * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (rr < c_rows) {
-          float* yr = a.y_sorted + (size_t)(c_off + c_m0 + rr) * N + c_col0 + wn * NF * 32 + lr;
+      for (int f = 0; f < NF; ++f) {
 #pragma unroll
-          for (int f = 0; f < NF; ++f) yr[f * 32] = acc[f][i];
+        for (int i = 0; i < 16; ++i) {
+          const int rr = 8 * (i >> 2) + 4 * half + (i & 3);
+          ep[rr * C::EP_PITCH + lr] = acc[f][i];
         }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 8 * q + srow;  // row within the wave's 32
+          const float4 v = *reinterpret_cast<const float4*>(ep + r * C::EP_PITCH + scol);
+          if (wm * 32 + r < c_rows)
+            *reinterpret_cast<float4*>(a.y_sorted + (size_t)(c_off + c_m0 + wm * 32 + r) * N + c_col0 +
+                                       wn * NF * 32 + f * 32 + scol) = v;
+        }
+        __builtin_amdgcn_wave_barrier();
       }
     }
     if (!more) break;
     if (more2) fetch_rest(E, R);
     if (more3) fetch_entry(logical + 3 * nslot, E);
-    if (GATEUP) __syncthreads();  // every wave is done with st2 before step 2 is copied into it
+    __syncthreads();  // every wave is done with st2 before step 2 is copied into it
     logical += nslot;
     more = more2;
     more2 = more3;
