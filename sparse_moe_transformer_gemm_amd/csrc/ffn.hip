@@ -363,8 +363,17 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       const bool ok = wave + W * t < C::A_COPIES && a_row(t) < rows_valid;
       a_off[t] = ok ? tok * apitch + a_piece(t) * 16 : kOutOfRange;
     }
+  };
+  // the biases of the tile P describes, added to its accumulators at the end.
+  // The empty asm keeps the conversion ahead of P's refill: sunk past it, the old
+  // and the new raw values would overlap and the refilled ones would be copied
+  // into place, a copy that waits for every load and copy in flight.
+  auto take_bias = [&](const Pre& P) __attribute__((always_inline)) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) bias[f] = bf16_to_f32((uint16_t)P.bias[f]);
+    for (int f = 0; f < NF; ++f) {
+      bias[f] = bf16_to_f32((uint16_t)P.bias[f]);
+      asm volatile("" : "+v"(bias[f]));
+    }
   };
 
   // Copy slot k (see Prefill) of step st of the current tile into the LDS buffer
@@ -411,45 +420,65 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
 
   // The fragments of one MFMA half of a step: in lane half h, block 2h + s of A
   // (both terms) and of B; the scale dwords, read with half 0, serve both halves.
+  // They are read piece by piece among the MFMAs of the half before, each piece
+  // right after the last MFMA that reads the registers it overwrites.
   v8i ahi, alo, bf[NF];
   int sa, sb[NF];
   bool halfst;  // the step's blocks 2, 3 are past K
-  auto read_half = [&](const uint8_t* buf, int st, auto S) __attribute__((always_inline)) {
-    constexpr int s = decltype(S)::v;
-    const uint8_t* rowp = buf + C::A_OFF + (wm * 32 + lr) * kChunk;
-    load_block_terms(rowp + half * 96 + s * kEncBytes, ahi, alo);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int phi = wn * NF + f;
-      bf[f] = fp4_operand(reinterpret_cast<const v4i*>(buf + C::B_OFF + (phi * 2 + s) * 1024)[lane]);
-    }
+  auto arow = [&](const uint8_t* buf, int s) __attribute__((always_inline)) {
+    return buf + C::A_OFF + (wm * 32 + lr) * kChunk + half * 96 + s * kEncBytes;
+  };
+  auto rd_b = [&](const uint8_t* buf, int s, int f) __attribute__((always_inline)) {
+    const int phi = wn * NF + f;
+    bf[f] = fp4_operand(reinterpret_cast<const v4i*>(buf + C::B_OFF + (phi * 2 + s) * 1024)[lane]);
     if (s == 0) {
-      halfst = 4 * st + 2 >= nblkK;
-      sa = *reinterpret_cast<const int*>(rowp + kChunkScales + 4 * half);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int m = GATEUP && f >= NF / 2 ? 1 : 0;
-        const int gg = GATEUP ? wn * (NF / 2) + f % (NF / 2) : wn * NF + f;
-        sb[f] = reinterpret_cast<const uint16_t*>(buf + C::BS_OFF + (m * C::GPM + gg) * 128)[lane];
-      }
+      const int m = GATEUP && f >= NF / 2 ? 1 : 0;
+      const int gg = GATEUP ? wn * (NF / 2) + f % (NF / 2) : wn * NF + f;
+      sb[f] = reinterpret_cast<const uint16_t*>(buf + C::BS_OFF + (m * C::GPM + gg) * 128)[lane];
     }
   };
-  // 2 x NF scaled MFMAs: the hi terms of all tiles, then the lo terms, so that no
-  // MFMA waits on the accumulator of the one just before it. Scale bytes: A hi
-  // 2s, A lo 2s+1, B s. A half step at the end of K (K % 128 == 64) still takes
-  // both MFMA halves: lane half 0 holds blocks 0, 1 (valid), lane half 1 zero
-  // codes whose scale bytes (never written) are forced finite. Copy slots
-  // K0 <= k < K1 of step cst (into the buffer at cbase) go evenly among them.
-  auto mma_half = [&](auto S, auto K0c, auto K1c, int cst, uint32_t cbase) __attribute__((always_inline)) {
-    constexpr int s = decltype(S)::v;
+  auto rd_sa = [&](const uint8_t* buf, int st) __attribute__((always_inline)) {
+    halfst = 4 * st + 2 >= nblkK;
+    sa = *reinterpret_cast<const int*>(buf + C::A_OFF + (wm * 32 + lr) * kChunk + kChunkScales + 4 * half);
+  };
+  auto read_all = [&](const uint8_t* buf, int st, int s) __attribute__((always_inline)) {
+    ahi = load_term_hi(arow(buf, s));
+    alo = load_term_lo(arow(buf, s));
+#pragma unroll
+    for (int f = 0; f < NF; ++f) rd_b(buf, s, f);
+    if (s == 0) rd_sa(buf, st);
+  };
+  // 2 x NF scaled MFMAs of half S of a step: the hi terms of all tiles, then the
+  // lo terms, so that no MFMA waits on the accumulator of the one just before it.
+  // With Z (the tile's first half) the hi MFMAs start from zero.
+  // Scale bytes: A hi 2s, A lo 2s+1, B s. A half step at the end of K
+  // (K % 128 == 64) still takes both MFMA halves: lane half 0 holds blocks 0, 1
+  // (valid), lane half 1 zero codes whose scale bytes (never written) are forced
+  // finite. Copy slots K0 <= k < K1 of step cst (into the buffer at cbase) go
+  // evenly among them. With RD, half RS of step rst is read from rbuf meanwhile:
+  // the A hi term after the last hi MFMA, B group f (and its scales) after the
+  // lo MFMA of group f, the A lo term (and the A scales) after the last MFMA.
+  auto mma_half = [&](auto S, auto K0c, auto K1c, int cst, uint32_t cbase, auto RD, const uint8_t* rbuf, int rst,
+                      auto RS, auto Z) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::v, rs = decltype(RS)::v;
+    constexpr bool zero = decltype(Z)::v != 0;
+    constexpr bool rd = decltype(RD)::v != 0;
     constexpr int k0 = decltype(K0c)::v, k1 = decltype(K1c)::v, nk = k1 - k0;
     constexpr int NM = 2 * NF;
     const int sav = halfst && half ? 0 : sa;
     static_for<0, NM>([&](auto Jc) __attribute__((always_inline)) {
       constexpr int j = decltype(Jc)::v;
       constexpr int term = j / NF, f = j % NF;
-      acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(term ? alo : ahi, bf[f], acc[f], 2, 4, 2 * s + term,
-                                                              sav, s, sb[f]);
+      acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(term ? alo : ahi, bf[f], zero && !term ? v16f{} : acc[f],
+                                                              2, 4, 2 * s + term, sav, s, sb[f]);
+      if constexpr (rd) {
+        if constexpr (j == NF - 1) ahi = load_term_hi(arow(rbuf, rs));
+        if constexpr (term == 1) rd_b(rbuf, rs, f);
+        if constexpr (j == NM - 1) {
+          alo = load_term_lo(arow(rbuf, rs));
+          if constexpr (rs == 0) rd_sa(rbuf, rst);
+        }
+      }
       static_for<k0, k1>([&](auto Kc) __attribute__((always_inline)) {
         constexpr int k = decltype(Kc)::v;
         if constexpr (nk > 0 && (k - k0) * NM / nk == j) issue_copy(Kc, cst, cbase);
@@ -469,55 +498,68 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     fetch_rest(e0, p0);
     if (more) fetch_rest(e1, R);
     setup(p0);
+    take_bias(p0);
   }
   issue(0, st0, IC<0>{}, IC<C::KMAX>{});
   issue(1, st1, IC<0>{}, IC<C::KMAX>{});
 
-  for (;;) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[f][i] = bias[f];
+  // Wait until step st+1 has landed (step st+2 may be in flight) and every wave
+  // has completed its reads of step st (barrier).
+  auto step_barrier = [&]() __attribute__((always_inline)) {
+    MOE_WAIT_VMCNT(C::KMAX);
+    MOE_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS access moves across the barrier
     __builtin_amdgcn_sched_barrier(0);
+  };
 
-    // ---- main loop. Per step st (its data in `c0`): read half 0 and compute it,
-    // read half 1 and compute it, copying step st+2 into `c2` (the buffer step
-    // st-1 left) among the MFMAs of both halves; then wait until step st+1 has
-    // landed and every wave has read `c0` (barrier). The barrier comes after all
-    // of the step's MFMAs, so the wavefront that reaches it first waits while the
-    // other one on its SIMD is still computing.
+  for (;;) {
+    // ---- main loop. Step st lives in buffer st % 3. Barrier X_st comes between
+    // the two MFMA halves of step st: before it, the MFMAs of half 0 of step st
+    // read half 1 of st; after it, those of half 1 read half 0 of step st+1,
+    // which X_st certifies has landed. Step st+2 is copied into the buffer of
+    // step st-1 (free since X_{st-1}) among the MFMAs between X_{st-1} and X_st.
+    // The wavefront that reaches a barrier first has its next operands in
+    // registers, so the matrix unit idles only while the barrier collects the
+    // waves.
     // step 0 has landed (step 1 may be in flight)
     MOE_WAIT_VMCNT(C::KMAX);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // Straight-line code per step (a branch inside would let the compiler move
-    // MFMAs across the barrier).
-    auto body = [&](int st, uint8_t* c0, uint8_t* c2) __attribute__((always_inline)) {
-      read_half(c0, st, IC<0>{});
+    read_all(st0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // up to X_0: half 0 of step 0, all copies of step 2
+    mma_half(IC<0>{}, IC<0>{}, IC<C::KMAX>{}, 2, lds_addr(st2), IC<1>{}, st0, 0, IC<1>{}, IC<1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    step_barrier();
+    // X_{st-1} to X_st (straight-line code: a branch inside would let the
+    // compiler move MFMAs across a barrier)
+    auto period = [&](int st, uint8_t* c0, uint8_t* c2) __attribute__((always_inline)) {
+      mma_half(IC<1>{}, IC<0>{}, IC<C::KSPLIT>{}, st + 2, lds_addr(c2), IC<1>{}, c0, st, IC<0>{}, IC<0>{});
       __builtin_amdgcn_sched_barrier(0);
-      MOE_WAIT_LGKM0();
-      mma_half(IC<0>{}, IC<0>{}, IC<C::KSPLIT>{}, st + 2, lds_addr(c2));
+      mma_half(IC<0>{}, IC<C::KSPLIT>{}, IC<C::KMAX>{}, st + 2, lds_addr(c2), IC<1>{}, c0, st, IC<1>{}, IC<0>{});
       __builtin_amdgcn_sched_barrier(0);
-      read_half(c0, st, IC<1>{});
-      __builtin_amdgcn_sched_barrier(0);
-      MOE_WAIT_LGKM0();            // this wave's reads of `c0` are complete
-      mma_half(IC<1>{}, IC<C::KSPLIT>{}, IC<C::KMAX>{}, st + 2, lds_addr(c2));
-      __builtin_amdgcn_sched_barrier(0);
-      MOE_WAIT_VMCNT(C::KMAX);     // step st+1 has landed (step st+2 may be in flight)
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");  // no LDS access moves across the barrier
-      __builtin_amdgcn_sched_barrier(0);
+      step_barrier();
     };
-    // Steps go in threes (one per buffer), then the one or two left.
-    int t = 0;
-    for (; t + 3 <= nst; t += 3) {
-      body(t, st0, st2);
-      body(t + 1, st1, st0);
-      body(t + 2, st2, st1);
+    // Steps 1.. with the buffers rotated (one copy of the code, so the operands
+    // carried from one step to the next keep their registers): bx, by, bz hold
+    // steps st, st+1, st+2.
+    uint8_t *bx = st1, *by = st2, *bz = st0;
+    for (int t = 1; t < nst; ++t) {
+      period(t, bx, bz);
+      uint8_t* const tmp = bx;
+      bx = by;
+      by = bz;
+      bz = tmp;
     }
-    if (t < nst) body(t, st0, st2);
-    if (t + 1 < nst) body(t + 1, st1, st0);
+    // half 1 of the last step; the empty asm keeps its MFMAs here (left alone,
+    // the compiler sinks them past the next tile's copies, where their operands
+    // would take registers the copies' setup needs)
+    mma_half(IC<1>{}, IC<0>{}, IC<0>{}, 0, 0u, IC<0>{}, st0, 0, IC<0>{}, IC<0>{});
+#pragma unroll
+    for (int f = 0; f < NF; ++f) asm volatile("" : "+v"(acc[f]));
+    __builtin_amdgcn_sched_barrier(0);
     MOE_WAIT_VMCNT(0);
     __syncthreads();
 
@@ -546,7 +588,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int rr = 8 * (i >> 2) + 4 * half + (i & 3);
-          const float g = acc[f][i], u = acc[f + C::FM][i];
+          const float g = acc[f][i] + bias[f], u = acc[f + C::FM][i] + bias[f + C::FM];
           ep[rr * C::EP_PITCH + lr] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
         }
         __builtin_amdgcn_wave_barrier();
@@ -584,7 +626,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int rr = 8 * (i >> 2) + 4 * half + (i & 3);
-          ep[rr * C::EP_PITCH + lr] = acc[f][i];
+          ep[rr * C::EP_PITCH + lr] = acc[f][i] + bias[f];
         }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -599,6 +641,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       }
     }
     if (!more) break;
+    take_bias(R);
     if (more2) fetch_rest(E, R);
     if (more3) fetch_entry(logical + 3 * nslot, E);
     __syncthreads();  // every wave is done with st2 before step 2 is copied into it

@@ -61,6 +61,17 @@ __device__ __forceinline__ void load_block_terms(const uint8_t* p, v8i& hi, v8i&
   lo = fp6_operand(*(lds_v2i*)(size_t)b, *(lds_v4i*)(size_t)(b + 8));
 }
 
+// The hi and the lo term of that block separately (for reads spread among MFMAs).
+__device__ __forceinline__ v8i load_term_hi(const uint8_t* p) {
+  const uint32_t a = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint8_t*)p;
+  return fp6_operand(*(lds_v4i*)(size_t)a, *(lds_v2i*)(size_t)(a + 16));
+}
+__device__ __forceinline__ v8i load_term_lo(const uint8_t* p) {
+  uint32_t b = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint8_t*)p + 24;
+  asm volatile("" : "+v"(b));
+  return fp6_operand(*(lds_v2i*)(size_t)b, *(lds_v4i*)(size_t)(b + 8));
+}
+
 // The same two terms from three 16-byte LDS reads of the block's 48 bytes (no
 // 8-byte reads: with the decode window's row pitch, 16-byte reads by 16 lanes of
 // different rows and one K sub-block cover distinct banks, while 8-byte reads of
