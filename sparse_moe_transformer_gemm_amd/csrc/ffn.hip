@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
   int e, m0, off, cnt, rows_valid, col0;
   v4i ar, br, bsr;  // A rows; this wave's matrix: codes, scales
   uint32_t a_off[C::NA];  // per-lane A source offsets (step 0)
-  float bias[NF];
+  float bias[NF], nbias[NF];  // of the tile being computed; of the tile set up last
 
   // A tile's table entry, column tile, dispatch entries (gate/up: the token of
   // each A copy's row) and raw bf16 biases are fetched ahead of time: the entry
@@ -364,26 +364,20 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       a_off[t] = ok ? tok * apitch + a_piece(t) * 16 : kOutOfRange;
     }
   };
-  // the biases of the tile P describes, added to its accumulators at the end.
-  // The empty asm keeps the conversion ahead of P's refill: sunk past it, the old
-  // and the new raw values would overlap and the refilled ones would be copied
-  // into place, a copy that waits for every load and copy in flight.
+  // the biases of the tile P describes (taken with its setup, so P can be
+  // refilled right after), added to its accumulators at its end
   auto take_bias = [&](const Pre& P) __attribute__((always_inline)) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      bias[f] = bf16_to_f32((uint16_t)P.bias[f]);
-      asm volatile("" : "+v"(bias[f]));
-    }
+    for (int f = 0; f < NF; ++f) nbias[f] = bf16_to_f32((uint16_t)P.bias[f]);
   };
 
-  // Copy slot k (see Prefill) of step st of the current tile into the LDS buffer
-  // at `base`. Weight copies read one contiguous kilobyte: the lane offset is
-  // lane*16, the group and step go into the uniform offset. A slot this wave has
-  // no copy for, and every copy of a step past K, read nothing; the former write
-  // (zeros) to the junk area.
-  auto issue_copy = [&](auto Kc, int st, uint32_t base) __attribute__((always_inline)) {
+  // Copy slot k (see Prefill) of step st of the tile set up last into the LDS
+  // buffer at `base`. Weight copies read one contiguous kilobyte: the lane offset
+  // is lane*16, the group and step go into the uniform offset. A slot this wave
+  // has no copy for, and every copy of a dead step (past K, or after the last
+  // tile), read nothing; the former write (zeros) to the junk area.
+  auto issue_copy = [&](auto Kc, int st, bool dead, uint32_t base) __attribute__((always_inline)) {
     constexpr int k = decltype(Kc)::v;
-    const bool dead = st >= nst;
     if constexpr (k < C::KB0) {
       constexpr int t = k;
       const bool have = wave + W * t < C::A_COPIES;  // otherwise a_off[t] is out of range
@@ -413,7 +407,8 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
   // of copies in flight behind a step is the same at every wait.
   auto issue = [&](int st, uint8_t* buf, auto K0c, auto K1c) __attribute__((always_inline)) {
     const uint32_t base = lds_addr(buf);
-    static_for<decltype(K0c)::v, decltype(K1c)::v>([&](auto Kc) __attribute__((always_inline)) { issue_copy(Kc, st, base); });
+    static_for<decltype(K0c)::v, decltype(K1c)::v>(
+        [&](auto Kc) __attribute__((always_inline)) { issue_copy(Kc, st, st >= nst, base); });
   };
 
   v16f acc[NF];
@@ -454,12 +449,12 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
   // Scale bytes: A hi 2s, A lo 2s+1, B s. A half step at the end of K
   // (K % 128 == 64) still takes both MFMA halves: lane half 0 holds blocks 0, 1
   // (valid), lane half 1 zero codes whose scale bytes (never written) are forced
-  // finite. Copy slots K0 <= k < K1 of step cst (into the buffer at cbase) go
-  // evenly among them. With RD, half RS of step rst is read from rbuf meanwhile:
+  // finite. Copy slots K0 <= k < K1 of step cst (into the buffer at cbase; dead
+  // with cdead) go evenly among them. With RD, half RS of step rst is read from rbuf meanwhile:
   // the A hi term after the last hi MFMA, B group f (and its scales) after the
   // lo MFMA of group f, the A lo term (and the A scales) after the last MFMA.
-  auto mma_half = [&](auto S, auto K0c, auto K1c, int cst, uint32_t cbase, auto RD, const uint8_t* rbuf, int rst,
-                      auto RS, auto Z) __attribute__((always_inline)) {
+  auto mma_half = [&](auto S, auto K0c, auto K1c, int cst, bool cdead, uint32_t cbase, auto RD, const uint8_t* rbuf,
+                      int rst, auto RS, auto Z) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::v, rs = decltype(RS)::v;
     constexpr bool zero = decltype(Z)::v != 0;
     constexpr bool rd = decltype(RD)::v != 0;
@@ -481,7 +476,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       }
       static_for<k0, k1>([&](auto Kc) __attribute__((always_inline)) {
         constexpr int k = decltype(Kc)::v;
-        if constexpr (nk > 0 && (k - k0) * NM / nk == j) issue_copy(Kc, cst, cbase);
+        if constexpr (nk > 0 && (k - k0) * NM / nk == j) issue_copy(Kc, cst, cdead, cbase);
       });
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -499,6 +494,8 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     if (more) fetch_rest(e1, R);
     setup(p0);
     take_bias(p0);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) bias[f] = nbias[f];
   }
   issue(0, st0, IC<0>{}, IC<C::KMAX>{});
   issue(1, st1, IC<0>{}, IC<C::KMAX>{});
@@ -512,75 +509,114 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     asm volatile("" ::: "memory");  // no LDS access moves across the barrier
     __builtin_amdgcn_sched_barrier(0);
   };
+  // X_{st-1} to X_st (straight-line code: a branch inside would let the
+  // compiler move MFMAs across a barrier), copying step cst (dead with cdead)
+  // into c2
+  auto period = [&](int st, uint8_t* c0, uint8_t* c2, int cst, bool cdead) __attribute__((always_inline)) {
+    const uint32_t cb = lds_addr(c2);
+    mma_half(IC<1>{}, IC<0>{}, IC<C::KSPLIT>{}, cst, cdead, cb, IC<1>{}, c0, st, IC<0>{}, IC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mma_half(IC<0>{}, IC<C::KSPLIT>{}, IC<C::KMAX>{}, cst, cdead, cb, IC<1>{}, c0, st, IC<1>{}, IC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    step_barrier();
+  };
+
+  // The three step buffers rotate: at a tile's start bx, by, bz hold its steps
+  // 0, 1, 2, and each step moves them on by one, so after the tile they hold
+  // steps nst, nst+1, nst+2, i.e. the next tile's 0, 1, 2.
+  uint8_t *bx = st0, *by = st1, *bz = st2;
+  auto rot = [&]() __attribute__((always_inline)) {
+    uint8_t* const tmp = bx;
+    bx = by;
+    by = bz;
+    bz = tmp;
+  };
+  // With three or more steps per tile the next tile's first two steps are
+  // copied among the MFMAs of this tile's last two (hand-over), so their first
+  // round trip is hidden; otherwise they are copied after the tile.
+  const bool handover = nst >= 3;
+  int c_off, c_m0, c_cnt, c_rows, c_col0;  // the output coordinates of the tile being computed
+  auto save_coords = [&]() __attribute__((always_inline)) {
+    c_off = off;
+    c_m0 = m0;
+    c_cnt = cnt;
+    c_rows = rows_valid;
+    c_col0 = col0;
+  };
 
   for (;;) {
-    // ---- main loop. Step st lives in buffer st % 3. Barrier X_st comes between
-    // the two MFMA halves of step st: before it, the MFMAs of half 0 of step st
-    // read half 1 of st; after it, those of half 1 read half 0 of step st+1,
-    // which X_st certifies has landed. Step st+2 is copied into the buffer of
-    // step st-1 (free since X_{st-1}) among the MFMAs between X_{st-1} and X_st.
-    // The wavefront that reaches a barrier first has its next operands in
-    // registers, so the matrix unit idles only while the barrier collects the
+    // ---- main loop. Step st lives in buffer st % 3 of the rotation. Barrier
+    // X_st comes between the two MFMA halves of step st: before it, the MFMAs of
+    // half 0 of step st read half 1 of st; after it, those of half 1 read half 0
+    // of step st+1, which X_st certifies has landed. Step st+2 is copied into the
+    // buffer of step st-1 (free since X_{st-1}) among the MFMAs between X_{st-1}
+    // and X_st. The wavefront that reaches a barrier first has its next operands
+    // in registers, so the matrix unit idles only while the barrier collects the
     // waves.
-    // step 0 has landed (step 1 may be in flight)
+    save_coords();
+    // step 0 has landed (step 1 may be in flight); every wave is done with the
+    // previous tile's epilogue staging in bz
     MOE_WAIT_VMCNT(C::KMAX);
+    MOE_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    read_all(st0, 0, 0);
+    read_all(bx, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     // up to X_0: half 0 of step 0, all copies of step 2
-    mma_half(IC<0>{}, IC<0>{}, IC<C::KMAX>{}, 2, lds_addr(st2), IC<1>{}, st0, 0, IC<1>{}, IC<1>{});
+    mma_half(IC<0>{}, IC<0>{}, IC<C::KMAX>{}, 2, nst <= 2, lds_addr(bz), IC<1>{}, bx, 0, IC<1>{}, IC<1>{});
+    // (the empty asm keeps these MFMAs ahead of the barrier)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) asm volatile("" : "+v"(acc[f]));
     __builtin_amdgcn_sched_barrier(0);
     step_barrier();
-    // X_{st-1} to X_st (straight-line code: a branch inside would let the
-    // compiler move MFMAs across a barrier)
-    auto period = [&](int st, uint8_t* c0, uint8_t* c2) __attribute__((always_inline)) {
-      mma_half(IC<1>{}, IC<0>{}, IC<C::KSPLIT>{}, st + 2, lds_addr(c2), IC<1>{}, c0, st, IC<0>{}, IC<0>{});
-      __builtin_amdgcn_sched_barrier(0);
-      mma_half(IC<0>{}, IC<C::KSPLIT>{}, IC<C::KMAX>{}, st + 2, lds_addr(c2), IC<1>{}, c0, st, IC<1>{}, IC<0>{});
-      __builtin_amdgcn_sched_barrier(0);
-      step_barrier();
-    };
-    // Steps 1.. with the buffers rotated (one copy of the code, so the operands
-    // carried from one step to the next keep their registers): bx, by, bz hold
-    // steps st, st+1, st+2.
-    uint8_t *bx = st1, *by = st2, *bz = st0;
-    for (int t = 1; t < nst; ++t) {
-      period(t, bx, bz);
-      uint8_t* const tmp = bx;
-      bx = by;
-      by = bz;
-      bz = tmp;
+    rot();
+    // steps 1 .. nst-3, copying steps 3 .. nst-1; then steps nst-2, nst-1,
+    // which with the hand-over copy the next tile's steps 0 and 1 (set up
+    // first), otherwise nothing. Loops, so that the operands carried from one
+    // step to the next keep their registers.
+    for (int t = 1; t + 2 < nst; ++t) {
+      period(t, bx, bz, t + 2, false);
+      rot();
+    }
+    if (handover && more) {
+      setup(R);
+      take_bias(R);
+    }
+    for (int t = max(1, nst - 2); t < nst; ++t) {
+      period(t, bx, bz, t + 2 - nst, !(handover && more));
+      rot();
     }
     // half 1 of the last step; the empty asm keeps its MFMAs here (left alone,
     // the compiler sinks them past the next tile's copies, where their operands
     // would take registers the copies' setup needs)
-    mma_half(IC<1>{}, IC<0>{}, IC<0>{}, 0, 0u, IC<0>{}, st0, 0, IC<0>{}, IC<0>{});
+    mma_half(IC<1>{}, IC<0>{}, IC<0>{}, 0, true, 0u, IC<0>{}, bx, 0, IC<0>{}, IC<0>{});
 #pragma unroll
     for (int f = 0; f < NF; ++f) asm volatile("" : "+v"(acc[f]));
     __builtin_amdgcn_sched_barrier(0);
-    MOE_WAIT_VMCNT(0);
-    __syncthreads();
 
-    // ---- this tile's output coordinates; the next tile's first two steps are
-    // copied while this tile's epilogue runs (the epilogue stages through st2,
-    // which the next tile's first step copies into); the fetches for the tiles
-    // after it are issued after the epilogue and complete while the next tile is
-    // computed
-    const int c_off = off, c_m0 = m0, c_cnt = cnt, c_rows = rows_valid, c_col0 = col0;
-    const bool more3 = logical + 3 * nslot < xend;
-    if (more) {
-      setup(R);
-      issue(0, st0, IC<0>{}, IC<C::KMAX>{});
-      issue(1, st1, IC<0>{}, IC<C::KMAX>{});
+    // ---- without the hand-over, the next tile's first two steps are copied
+    // now, while this tile's epilogue runs. The epilogue stages through bz, the
+    // buffer of this tile's last step, which no copy targets before the next
+    // tile's barrier. The fetches for the tiles after the next are issued after
+    // the epilogue and complete while the next tile is computed.
+    if (!handover) {
+      MOE_WAIT_VMCNT(0);
+      __syncthreads();
+      if (more) {
+        setup(R);
+        take_bias(R);
+        issue(0, bx, IC<0>{}, IC<C::KMAX>{});
+        issue(1, by, IC<0>{}, IC<C::KMAX>{});
+      }
     }
+    const bool more3 = logical + 3 * nslot < xend;
 
     if constexpr (GATEUP) {
       // h = silu(g) * u; per gate group f, the wave's 32x32 tile goes to LDS as
       // 32 rows x 32 columns and lanes 0..31 each encode one row's 32-column
       // block as two-term MXFP6 into the row's step chunk.
-      float* ep = reinterpret_cast<float*>(st2) + wave * 32 * C::EP_PITCH;
+      float* ep = reinterpret_cast<float*>(bz) + wave * 32 * C::EP_PITCH;
       const uint32_t hpitch = (uint32_t)nsteps_of(a.F) * kChunk;
       const int grow = c_m0 + wm * 32 + lane;
 #pragma unroll
@@ -615,11 +651,11 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
         __builtin_amdgcn_wave_barrier();
       }
     } else {
-      // y = the fp32 accumulators, staged per 32-column group through LDS (st2,
-      // which no copy targets until the next tile's first step) so that each lane
+      // y = the fp32 accumulators plus bias, staged per 32-column group through
+      // LDS (bz) so that each lane
       // stores 16 contiguous bytes: store q of a wave writes 8 whole rows of the
       // group (8 lanes x 16 B per row) instead of 64 single floats.
-      float* ep = reinterpret_cast<float*>(st2) + wave * 32 * C::EP_PITCH;
+      float* ep = reinterpret_cast<float*>(bz) + wave * 32 * C::EP_PITCH;
       const int srow = lane >> 3, scol = (lane & 7) * 4;
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -641,10 +677,10 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       }
     }
     if (!more) break;
-    take_bias(R);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) bias[f] = nbias[f];
     if (more2) fetch_rest(E, R);
     if (more3) fetch_entry(logical + 3 * nslot, E);
-    __syncthreads();  // every wave is done with st2 before step 2 is copied into it
     logical += nslot;
     more = more2;
     more2 = more3;
