@@ -415,33 +415,42 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
 
   // The fragments of one MFMA half of a step: in lane half h, block 2h + s of A
   // (both terms) and of B; the scale dwords, read with half 0, serve both halves.
-  // They are read piece by piece among the MFMAs of the half before, each piece
-  // right after the last MFMA that reads the registers it overwrites.
-  v8i ahi, alo, bf[NF];
+  // While one half is computed the other is read: the A terms and the last NSP
+  // B groups into the set of registers the half being computed does not use
+  // (read first), the other B groups (and with half 0 all B scales) each right
+  // after the last MFMA of the running half that reads the registers it
+  // overwrites. So the last read of a half is issued a few MFMAs before its end.
+  constexpr int NSP = NF < 2 ? NF : 2;  // B groups with a register set per half
+  constexpr int FR = NF - NSP;          // B groups read in place
+  v8i ah[2], al[2], bf[NF > NSP ? NF - NSP : 1], bsp[2][NSP];
   int sa, sb[NF];
   bool halfst;  // the step's blocks 2, 3 are past K
   auto arow = [&](const uint8_t* buf, int s) __attribute__((always_inline)) {
     return buf + C::A_OFF + (wm * 32 + lr) * kChunk + half * 96 + s * kEncBytes;
   };
-  auto rd_b = [&](const uint8_t* buf, int s, int f) __attribute__((always_inline)) {
-    const int phi = wn * NF + f;
-    bf[f] = fp4_operand(reinterpret_cast<const v4i*>(buf + C::B_OFF + (phi * 2 + s) * 1024)[lane]);
-    if (s == 0) {
-      const int m = GATEUP && f >= NF / 2 ? 1 : 0;
-      const int gg = GATEUP ? wn * (NF / 2) + f % (NF / 2) : wn * NF + f;
-      sb[f] = reinterpret_cast<const uint16_t*>(buf + C::BS_OFF + (m * C::GPM + gg) * 128)[lane];
-    }
+  auto ld_b = [&](const uint8_t* buf, int s, int f) __attribute__((always_inline)) {
+    return fp4_operand(reinterpret_cast<const v4i*>(buf + C::B_OFF + ((wn * NF + f) * 2 + s) * 1024)[lane]);
+  };
+  auto ld_sb = [&](const uint8_t* buf, int f) __attribute__((always_inline)) {
+    const int m = GATEUP && f >= NF / 2 ? 1 : 0;
+    const int gg = GATEUP ? wn * (NF / 2) + f % (NF / 2) : wn * NF + f;
+    return (int)reinterpret_cast<const uint16_t*>(buf + C::BS_OFF + (m * C::GPM + gg) * 128)[lane];
   };
   auto rd_sa = [&](const uint8_t* buf, int st) __attribute__((always_inline)) {
     halfst = 4 * st + 2 >= nblkK;
     sa = *reinterpret_cast<const int*>(buf + C::A_OFF + (wm * 32 + lr) * kChunk + kChunkScales + 4 * half);
   };
-  auto read_all = [&](const uint8_t* buf, int st, int s) __attribute__((always_inline)) {
-    ahi = load_term_hi(arow(buf, s));
-    alo = load_term_lo(arow(buf, s));
+  // everything of half 0 of step st
+  auto read_all = [&](const uint8_t* buf, int st) __attribute__((always_inline)) {
+    ah[0] = load_term_hi(arow(buf, 0));
+    al[0] = load_term_lo(arow(buf, 0));
 #pragma unroll
-    for (int f = 0; f < NF; ++f) rd_b(buf, s, f);
-    if (s == 0) rd_sa(buf, st);
+    for (int f = 0; f < NF; ++f) {
+      if (f < FR) bf[f] = ld_b(buf, 0, f);
+      else bsp[0][f - FR] = ld_b(buf, 0, f);
+      sb[f] = ld_sb(buf, f);
+    }
+    rd_sa(buf, st);
   };
   // 2 x NF scaled MFMAs of half S of a step: the hi terms of all tiles, then the
   // lo terms, so that no MFMA waits on the accumulator of the one just before it.
@@ -450,9 +459,8 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
   // (K % 128 == 64) still takes both MFMA halves: lane half 0 holds blocks 0, 1
   // (valid), lane half 1 zero codes whose scale bytes (never written) are forced
   // finite. Copy slots K0 <= k < K1 of step cst (into the buffer at cbase; dead
-  // with cdead) go evenly among them. With RD, half RS of step rst is read from rbuf meanwhile:
-  // the A hi term after the last hi MFMA, B group f (and its scales) after the
-  // lo MFMA of group f, the A lo term (and the A scales) after the last MFMA.
+  // with cdead) go evenly among them. With RD, half RS (the other one) of step
+  // rst is read from rbuf meanwhile, as described above.
   auto mma_half = [&](auto S, auto K0c, auto K1c, int cst, bool cdead, uint32_t cbase, auto RD, const uint8_t* rbuf,
                       int rst, auto RS, auto Z) __attribute__((always_inline)) {
     constexpr int s = decltype(S)::v, rs = decltype(RS)::v;
@@ -460,19 +468,29 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     constexpr bool rd = decltype(RD)::v != 0;
     constexpr int k0 = decltype(K0c)::v, k1 = decltype(K1c)::v, nk = k1 - k0;
     constexpr int NM = 2 * NF;
+    static_assert(!rd || rs != s, "the other half is read");
     const int sav = halfst && half ? 0 : sa;
     static_for<0, NM>([&](auto Jc) __attribute__((always_inline)) {
       constexpr int j = decltype(Jc)::v;
       constexpr int term = j / NF, f = j % NF;
-      acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(term ? alo : ahi, bf[f], zero && !term ? v16f{} : acc[f],
+      const v8i& bop = [&]() -> const v8i& {
+        if constexpr (f < FR) return bf[f < FR ? f : 0];
+        else return bsp[s][f - FR];
+      }();
+      acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(term ? al[s] : ah[s], bop, zero && !term ? v16f{} : acc[f],
                                                               2, 4, 2 * s + term, sav, s, sb[f]);
       if constexpr (rd) {
-        if constexpr (j == NF - 1) ahi = load_term_hi(arow(rbuf, rs));
-        if constexpr (term == 1) rd_b(rbuf, rs, f);
-        if constexpr (j == NM - 1) {
-          alo = load_term_lo(arow(rbuf, rs));
+        if constexpr (j == 0) {
+          ah[rs] = load_term_hi(arow(rbuf, rs));
           if constexpr (rs == 0) rd_sa(rbuf, rst);
         }
+        if constexpr (j == (NM > 1 ? 1 : 0)) al[rs] = load_term_lo(arow(rbuf, rs));
+        static_for<0, NSP>([&](auto Ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(Ic)::v;
+          if constexpr (j == (2 + i < NM ? 2 + i : NM - 1)) bsp[rs][i] = ld_b(rbuf, rs, FR + i);
+        });
+        if constexpr (term == 1 && f < FR) bf[f < FR ? f : 0] = ld_b(rbuf, rs, f);
+        if constexpr (term == 1 && rs == 0) sb[f] = ld_sb(rbuf, f);
       }
       static_for<k0, k1>([&](auto Kc) __attribute__((always_inline)) {
         constexpr int k = decltype(Kc)::v;
@@ -561,7 +579,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    read_all(bx, 0, 0);
+    read_all(bx, 0);
     __builtin_amdgcn_sched_barrier(0);
     // up to X_0: half 0 of step 0, all copies of step 2
     mma_half(IC<0>{}, IC<0>{}, IC<C::KMAX>{}, 2, nst <= 2, lds_addr(bz), IC<1>{}, bx, 0, IC<1>{}, IC<1>{});
