@@ -297,6 +297,8 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     return (uint32_t)(group_row(group_of(mw, 2 * p + half)) / 32) * sstride + lr * 4;
   };
 
+  const uint32_t junk_lds = lds_addr(junk);
+
   // ---- per-tile state (all wave-uniform)
   int e, m0, off, cnt, rows_valid, col0;
   v4i ar, br, bsr;  // A rows; this wave's matrix: codes, scales
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       const bool have = wave + W * t < C::A_COPIES;  // otherwise a_off[t] is out of range
       // the step is past K, or this piece holds its blocks 2, 3 and they are
       const bool pad = dead || (4 * st + 2 >= nblkK && a_piece(t) >= 6 && a_piece(t) < 12);
-      lds_copy<16>(ar, have ? base + C::A_OFF + (wave + W * t) * 1024 : lds_addr(junk),
+      lds_copy<16>(ar, have ? base + C::A_OFF + (wave + W * t) * 1024 : junk_lds,
                    pad ? kOutOfRange : a_off[t], (uint32_t)st * kChunk);
     } else if constexpr (k < C::KS0) {
       constexpr int t = k - C::KB0;
@@ -391,14 +393,14 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
       const bool have = c < C::B_COPIES;
       const int phi = group_of(mw, have ? c >> 1 : 0), sh = c & 1;
       const uint32_t so = (uint32_t)((col0 + group_row(phi)) / 32) * gstride + sh * 1024 + (uint32_t)st * kWStep;
-      lds_copy<16>(br, have ? base + C::B_OFF + (phi * 2 + sh) * 1024 : lds_addr(junk),
+      lds_copy<16>(br, have ? base + C::B_OFF + (phi * 2 + sh) * 1024 : junk_lds,
                    have && !dead ? lane16 : kOutOfRange, so);
     } else {
       constexpr int t = k - C::KS0;
       const int p = rw + C::WPM * t;
       const bool have = p < C::S_COPIES;
       const uint32_t so = (uint32_t)(col0 / 32) * sstride + (uint32_t)st * kWSStep;
-      lds_copy<4>(bsr, have ? base + C::BS_OFF + (mw * C::GPM + 2 * p) * 128 : lds_addr(junk),
+      lds_copy<4>(bsr, have ? base + C::BS_OFF + (mw * C::GPM + 2 * p) * 128 : junk_lds,
                   have && !dead ? scale_voff(have ? p : 0) : kOutOfRange, so);
     }
   };
