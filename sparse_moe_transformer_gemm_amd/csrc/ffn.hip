@@ -634,8 +634,9 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
 
     if constexpr (GATEUP) {
       // h = silu(g) * u; per gate group f, the wave's 32x32 tile goes to LDS as
-      // 32 rows x 32 columns and lanes 0..31 each encode one row's 32-column
-      // block as two-term MXFP6 into the row's step chunk.
+      // 32 rows x 32 columns, the even columns of a row first and then the odd
+      // ones (the conversions' operand order), and lanes 0..31 each encode one
+      // row's 32-column block as two-term MXFP6 into the row's step chunk.
       float* ep = reinterpret_cast<float*>(bz) + wave * 32 * C::EP_PITCH;
       const uint32_t hpitch = (uint32_t)nsteps_of(a.F) * kChunk;
       const int grow = c_m0 + wm * 32 + lane;
@@ -645,22 +646,13 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
         for (int i = 0; i < 16; ++i) {
           const int rr = 8 * (i >> 2) + 4 * half + (i & 3);
           const float g = acc[f][i] + bias[f], u = acc[f + C::FM][i] + bias[f + C::FM];
-          ep[rr * C::EP_PITCH + lr] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+          ep[rr * C::EP_PITCH + (lr & 1) * 16 + (lr >> 1)] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
         }
         __builtin_amdgcn_wave_barrier();
         if (lane < 32) {
-          float v[32];
-          const float4* src = reinterpret_cast<const float4*>(ep + lane * C::EP_PITCH);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float4 t4 = src[q];
-            v[4 * q] = t4.x;
-            v[4 * q + 1] = t4.y;
-            v[4 * q + 2] = t4.z;
-            v[4 * q + 3] = t4.w;
-          }
+          const v16f* src = reinterpret_cast<const v16f*>(ep + lane * C::EP_PITCH);
           uint32_t hw[6], lw[6], sc;
-          encode_block(v, hw, lw, sc);
+          encode_block_eo(src[0], src[1], hw, lw, sc);
           if (grow < c_cnt) {
             const int b = (c_col0 + wn * C::FM * 32 + f * 32) / 32;
             uint8_t* hrow = hout + (size_t)(c_off + grow) * hpitch;

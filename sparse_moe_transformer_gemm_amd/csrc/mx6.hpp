@@ -177,6 +177,40 @@ __device__ __forceinline__ void encode_block(const float (&v)[32], uint32_t (&hi
   scales = static_cast<uint32_t>(s1 + 127) | (static_cast<uint32_t>(s2 + 127) << 8);
 }
 
+// The same encoding from the block's even-indexed elements (ev[i] = element 2i)
+// and odd-indexed ones (od[i] = element 2i+1), the operand order of the
+// conversions, so that no register copies are needed to form them.
+__device__ __forceinline__ void encode_block_eo(const v16f& ev, const v16f& od, uint32_t (&hi)[6],
+                                                uint32_t (&lo)[6], uint32_t& scales) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    amax = fmaxf(amax, fabsf(ev[i]));
+    amax = fmaxf(amax, fabsf(od[i]));
+  }
+  const int s1 = block_exp(amax);
+  const float sc1 = pow2i(s1);
+  const v6u h = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, sc1);
+  const v32f back = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(h, sc1);
+  v16f re, ro;
+  float ramax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    re[i] = ev[i] - back[2 * i];
+    ro[i] = od[i] - back[2 * i + 1];
+    ramax = fmaxf(ramax, fabsf(re[i]));
+    ramax = fmaxf(ramax, fabsf(ro[i]));
+  }
+  const int s2 = block_exp(ramax);
+  const v6u l = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(re, ro, pow2i(s2));
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    hi[i] = h[i];
+    lo[i] = l[i];
+  }
+  scales = static_cast<uint32_t>(s1 + 127) | (static_cast<uint32_t>(s2 + 127) << 8);
+}
+
 // The same encoding done by a group of 32 lanes (a half wavefront), one element
 // per lane: j = lane & 31 holds element j of the block. The block maxima are
 // shuffle reductions inside the half wavefront; the 6-bit codes are packed
