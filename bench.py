@@ -48,12 +48,29 @@ METRIC = "MoE layer tokens/s; % HBM peak (T=16) and % MXFP4 MFMA peak (T=8192)"
 TRAFFIC_SOURCES = ("ffn.hip", "ffn_dev.hpp", "mx6.hpp", "layout.hpp", "common.hpp")
 
 
+def traffic_sources_hash(read=None) -> str:
+    """First 16 hex digits of the sha256 of TRAFFIC_SOURCES concatenated, each
+    with its comments removed and every run of white space made one blank, so
+    that an edit of comments alone does not void a counter summary. `read`
+    (file name -> text) defaults to the working tree."""
+    import hashlib
+    import re
+    if read is None:
+        def read(f):
+            return open(os.path.join(ROOT, "sparse_moe_transformer_gemm_amd", "csrc", f)).read()
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        t = re.sub(r"/\*.*?\*/", " ", read(f), flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(" ".join(t.split()).encode())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(name: str, key: str = "traffic_bytes_per_launch"):
     """HBM bytes per launch (of the gate/up GEMM, or with key
     traffic_bytes_per_call of the whole expert-FFN call) from the committed
     rocprofv3 counter summary for this workload, or None when there is none or
     when the kernel sources have changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_expert_ffn_{name}.txt")
     if not os.path.exists(path):
         return None
@@ -62,10 +79,7 @@ def measured_traffic(name: str, key: str = "traffic_bytes_per_launch"):
         if ":" in line:
             name_, _, val = line.strip().partition(":")
             fields[name_.strip()] = val.strip()
-    h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        h.update(open(os.path.join(ROOT, "sparse_moe_transformer_gemm_amd", "csrc", f), "rb").read())
-    if h.hexdigest()[:16] != fields.get("sources_sha256_16") or key not in fields:
+    if traffic_sources_hash() != fields.get("sources_sha256_16") or key not in fields:
         return None
     return int(fields[key])
 

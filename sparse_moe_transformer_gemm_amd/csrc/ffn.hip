@@ -114,8 +114,9 @@ __device__ __forceinline__ uint32_t div_by(uint32_t x, uint64_t m) {
 //
 // Each K step is copied from global memory straight into LDS by buffer-to-LDS
 // loads (lane i of a copy writes LDS bytes [16i, 16i+16) for 16-byte copies and
-// [4i, 4i+4) for 4-byte ones), three step buffers: step st+2 is copied while step
-// st is read and computed. LDS layout of one step:
+// [4i, 4i+4) for 4-byte ones) into three step buffers that rotate from step to
+// step and from tile to tile: step st+2 is copied while step st is computed.
+// LDS layout of one step:
 //   A   [128 rows][208 B]  the rows' encoded chunks as stored (copy q of 16 B:
 //                          row q/13, piece q%13; lanes of one row read one run)
 //   B   [group][half][lane][16 B]  packed fragments, 1 KB per copy
@@ -160,8 +161,8 @@ struct Prefill {
   static constexpr int NB = (B_COPIES + WPM - 1) / WPM;
   static constexpr int NS = (S_COPIES + WPM - 1) / WPM;
   static constexpr int KB0 = NA, KS0 = NA + NB, KMAX = NA + NB + NS;  // copies per wave per step
-  // slots k < KSPLIT go among the MFMAs of half 0 of a step, the rest among
-  // those of half 1
+  // slots k < KSPLIT go among the 2 NF MFMAs that follow a step barrier (half 1
+  // of the step before), the rest among the next 2 NF (half 0 of the step)
   static constexpr int KSPLIT = (KMAX + 1) / 2;
   static_assert(kBM * kChunkPieces % 64 == 0, "A copies are whole instructions");
   static_assert(kBM == 4 * 32, "one 32-row fragment per wave row");
@@ -234,8 +235,7 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
                                                                    const int4* __restrict__ tiles, int ntn) {
   using C = Prefill<NF, GATEUP>;
   constexpr int W = C::W;
-  // three step buffers as separate objects, so the compiler can tell the copy
-  // into one from the reads of another
+  // the three step buffers (rotated through pointers below)
   __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[C::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st2[C::STAGE];
