@@ -22,6 +22,7 @@ __device__ __forceinline__ bool better(double va, int ea, double vb, int eb) {
 // distinct, so the experts of rank < k are the top k in order; a NaN logit has
 // been stored as -inf. Then the softmax over the picked logits in float64, each
 // of the k lanes summing the k exponentials in rank order, stored as fp32.
+// Every thread of the workgroup must call it (it contains barriers).
 __device__ __forceinline__ void select_topk(const double* logit, int t, int E, int k,
                                             double* sel_v, int* sel_e,
                                             int32_t* __restrict__ topk_idx,
@@ -38,12 +39,16 @@ __device__ __forceinline__ void select_topk(const double* logit, int t, int E, i
     }
   }
   __syncthreads();
+  // each of the k lanes takes one exponential (float64 exp is long), then each
+  // sums all k in rank order
+  __shared__ double sel_x[8];
+  if (tid < k) sel_x[tid] = exp(sel_v[tid] - sel_v[0]);
+  __syncthreads();
   if (tid < k) {
-    const double m = sel_v[0];
     double den = 0.0;
-    for (int j = 0; j < k; ++j) den += exp(sel_v[j] - m);
+    for (int j = 0; j < k; ++j) den += sel_x[j];
     topk_idx[(size_t)t * k + tid] = sel_e[tid];
-    topk_w[(size_t)t * k + tid] = static_cast<float>(exp(sel_v[tid] - m) / den);
+    topk_w[(size_t)t * k + tid] = static_cast<float>(sel_x[tid] / den);
   }
 }
 
