@@ -407,10 +407,13 @@ def main():
                                                      "SwiGLU (moe_expert_ffn_mxfp4 stage 1)",
                          "achieved": s["gu_tflops"], "peak": MXFP4_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": s["gu_tflops"] / MXFP4_PEAK_TFLOPS,
-                         "traffic": None, "flops_per_launch": s["gu_flops"], "avg_launch_ms": s["gu_ms"],
+                         "traffic": measured_traffic(f"{s['workload']}_T{s['T']}"),
+                         "flops_per_launch": s["gu_flops"], "avg_launch_ms": s["gu_ms"],
                          "down_gemm_ms": s["dn_ms"],
                          "ffn_call": {"achieved": s["ffn_tflops"], "frac": s["ffn_tflops"] / MXFP4_PEAK_TFLOPS,
-                                      "avg_ms": s["ffn_ms"], "flops": s["flops"]}},
+                                      "avg_ms": s["ffn_ms"], "flops": s["flops"],
+                                      "traffic": measured_traffic(f"{s['workload']}_T{s['T']}",
+                                                                  "traffic_bytes_per_call")}},
             "layer_frac_mxfp4_peak": s["layer_tflops"] / MXFP4_PEAK_TFLOPS,
             "ffn_ms": s["ffn_ms"],
         }

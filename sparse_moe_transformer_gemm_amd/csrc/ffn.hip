@@ -33,7 +33,11 @@
 namespace moe {
 namespace {
 
-constexpr int kPrefGM = 8;      // row tiles per raster group of the prefill grid
+// row tiles per raster group of the prefill grid (gate/up, down): chosen by
+// measurement; the 32 workgroups of an XCD then share GM row tiles of A and
+// 32/GM column tiles of the weights
+template <bool GATEUP>
+constexpr int kPrefGM = GATEUP ? 8 : 4;
 constexpr int kDecodeMaxT = 64; // decode kernels when T <= this
 
 // The tables the GEMMs of this call need, built by one extra workgroup of the
@@ -319,13 +323,13 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
     uint32_t bias[NF];  // raw bf16 (never combined before use: that would wait for the loads)
   };
   auto fetch_entry = [&](int lg, Pre& P) __attribute__((always_inline)) {
-    const int grp = lg / (kPrefGM * ntn);
-    const int gm = min(kPrefGM, total_mt - grp * kPrefGM);
-    const int r = lg - grp * kPrefGM * ntn;
+    const int grp = lg / (kPrefGM<GATEUP> * ntn);
+    const int gm = min(kPrefGM<GATEUP>, total_mt - grp * kPrefGM<GATEUP>);
+    const int r = lg - grp * kPrefGM<GATEUP> * ntn;
     P.nt = r / gm;
     // through the constant address space: scalar loads into SGPRs
     const __attribute__((address_space(4))) int* ct = (const __attribute__((address_space(4))) int*)tiles;
-    const int q = 4 * (1 + grp * kPrefGM + (r - P.nt * gm));
+    const int q = 4 * (1 + grp * kPrefGM<GATEUP> + (r - P.nt * gm));
     P.ent = make_int4(ct[q], ct[q + 1], ct[q + 2], ct[q + 3]);
   };
   auto fetch_rest = [&](const Pre& Ein, Pre& P) __attribute__((always_inline)) {
