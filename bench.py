@@ -374,7 +374,7 @@ def main():
     log = lambda s: print(s, file=sys.stderr, flush=True)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              f"(this build has no multi-GPU path)", file=sys.stderr)
+              f"(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
