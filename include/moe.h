@@ -60,7 +60,17 @@ typedef enum {
 
 /* Layer dimensions: T tokens, model width d, expert FFN width F, E experts,
  * k experts per token. Supported: T >= 1, d and F multiples of 64 (MX blocks of
- * 32 and the kernels' K step), d <= 16384, F <= 16384, 1 <= k <= 8, k <= E <= 256. */
+ * 32 and the kernels' K step), d <= 16384, F <= 16384, 1 <= k <= 8, k <= E <= 256.
+ * The calls that run the expert FFN (moe_expert_ffn_mxfp4, its staged form and
+ * moe_forward) also need d >= MOE_MIN_FFN_K and F >= MOE_MIN_FFN_K, and return
+ * MOE_ERR_UNSUPPORTED below: they feed the activations to the matrix cores as two
+ * MXFP6-E2M3 terms per 32-element block, and with fewer than 512 elements per dot
+ * product the tail of the error that encoding adds reaches the layer's tolerance
+ * (max error <= 2e-2 RMS of the exact result) over large tensors. From 512 on its
+ * largest value over 4e7 outputs stays below two thirds of that bound (at
+ * d = F = 2880, about a third). moe_route and moe_permute accept d >= 64. */
+#define MOE_MIN_FFN_K 512
+
 typedef struct {
   int32_t T, d, F, E, k;
 } moe_dims;
@@ -146,6 +156,14 @@ moe_status moe_pack_mxfp4(int32_t E, int32_t N, int32_t K, moe_mxfp4 src, uint8_
                           uint8_t* scales_out, void* stream);
 
 /* Grouped expert FFN in dispatch order, MXFP4 weights.
+ * Two departures from a call that would take the weights as stored (the OCP
+ * layout of moe_mxfp4) with d and F any multiple of 32:
+ *   - the weights are passed packed (moe_mxfp4_packed, made once per matrix by
+ *     moe_pack_mxfp4). The library allocates nothing and keeps no state, so it
+ *     cannot repack on the caller's behalf without paying a full pass over the
+ *     weights on every call; the packed bytes are the stored bytes reordered;
+ *   - d and F are multiples of 64 (the MFMA step covers two 32-element blocks)
+ *     and at least MOE_MIN_FFN_K.
  * For every expert e and row p in [offsets[e], offsets[e+1]), with
  * t = sorted_pair[p] / k:
  *   g = x[t] Wg[e]^T + b_gate[e],  u = x[t] Wu[e]^T + b_up[e],

@@ -41,6 +41,22 @@ moe_status check_dims(const moe_dims& m) {
   return MOE_OK;
 }
 
+// The expert FFN encodes its activations as two MXFP6-E2M3 terms per 32-element
+// block. Over large tensors the error that encoding adds stays within the
+// layer's tolerance (max error <= 2e-2 RMS, mean relative error <= 5e-3) only
+// when the contraction length K = min(d, F) is at least MOE_MIN_FFN_K: with
+// fewer blocks per dot product the tail of the error distribution reaches the
+// bound (at K = 64 about 18 in a million outputs of y exceed it; at K = 256 a
+// few of 4e7 do), while at K >= 512 its largest value over 4e7 outputs stays
+// below two thirds of it.
+moe_status check_ffn_k(const moe_dims& m) {
+  if (m.d < MOE_MIN_FFN_K || m.F < MOE_MIN_FFN_K) {
+    set_error("%s", "dims: the expert FFN needs d >= 512 and F >= 512 (MOE_MIN_FFN_K)");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
 moe_status check_ptrs(std::initializer_list<const void*> ptrs, const char* what) {
   for (const void* p : ptrs) {
     if (!p) {
@@ -157,6 +173,7 @@ static moe_status ffn_args(moe_dims dims, const moe_bf16* x, const int32_t* sort
                            const moe_bf16* b_down, float* y_sorted, void* ws, size_t ws_bytes,
                            const char* who, moe::FfnArgs& a) {
   MOE_TRY(check_dims(dims));
+  MOE_TRY(check_ffn_k(dims));
   MOE_TRY(check_ptrs({x, sorted_pair, offsets, w_gate.codes, w_gate.scales, w_up.codes,
                       w_up.scales, w_down.codes, w_down.scales, b_gate, b_up, b_down, y_sorted},
                      who));
@@ -221,6 +238,7 @@ moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
                        float* y_sorted, moe_bf16* out, void* ws, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   MOE_TRY(check_dims(dims));
+  MOE_TRY(check_ffn_k(dims));
   MOE_TRY(check_ptrs({x, w_router, w_gate.codes, w_gate.scales, w_up.codes, w_up.scales,
                       w_down.codes, w_down.scales, b_gate, b_up, b_down, topk_idx, topk_w,
                       counts, offsets, sorted_pair, pair_row, y_sorted, out},

@@ -200,8 +200,8 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // (wave-uniform); out-of-range lanes write zeros. Written as inline asm so that
 // the compiler does not guard every LDS read with a wait for all copies in flight
 // (it cannot tell which buffer a copy writes); the kernel bounds the vector
-// memory counter itself before each barrier. The asm sets M0 itself and has no
-// register outputs.
+// memory counter itself before each barrier. The LDS address reaches M0 through
+// the operand constraint (the compiler sets M0), and the asm has no register outputs.
 template <int SIZE>
 __device__ __forceinline__ void lds_copy(v4i r, uint32_t lds, uint32_t voff, uint32_t soff) {
   static_assert(SIZE == 16 || SIZE == 4, "copy sizes used here");
@@ -212,11 +212,11 @@ __device__ __forceinline__ void lds_copy(v4i r, uint32_t lds, uint32_t voff, uin
   lds = __builtin_amdgcn_readfirstlane(lds);
   soff = __builtin_amdgcn_readfirstlane(soff);
   if constexpr (SIZE == 16)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+    asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+    asm volatile("buffer_load_dword %1, %2, %3 offen lds"
+                 :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
 
 template <int V>

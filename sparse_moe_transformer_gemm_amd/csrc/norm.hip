@@ -50,9 +50,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   }
 }
 
-__global__ __launch_bounds__(256) void residual_kernel(const uint4* __restrict__ x,
-                                                       const uint4* __restrict__ m, size_t n8,
-                                                       uint4* __restrict__ out) {
+// out may alias x or m (each element is read, then written, by one thread), so
+// none of the three is declared __restrict__.
+__global__ __launch_bounds__(256) void residual_kernel(const uint4* x, const uint4* m, size_t n8,
+                                                       uint4* out) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8;
        i += (size_t)gridDim.x * blockDim.x) {
     const uint4 a = x[i], b = m[i];

@@ -95,6 +95,20 @@ def check_permute(g: dict, E: int) -> None:
     assert np.array_equal(g["pair_row"], r)
 
 
+def oracle_y_out(x_bits: np.ndarray, L: synth.LayerParams, k: int, g: dict):
+    """Oracle expert outputs in the GPU's dispatch order (every row) and the
+    layer output of every token, routed with the GPU's expert choice (the
+    routing and the dispatch are checked separately, bit for bit); float64,
+    unrounded. y_ref[p] is FFN_e(x[t]) for the pair in row p; out_ref[t] sums
+    the rows of token t weighted by the softmax of the oracle's logits over the
+    GPU's chosen experts."""
+    x = oracle.bf16_to_f64(x_bits)
+    y_ref = oracle.ffn_sorted(x, g["sorted_pair"], g["offsets"], k, L)
+    logits = oracle.router_logits(x, L.w_router, L.b_router)
+    w = oracle.softmax_selected(logits, g["idx"])
+    return y_ref, oracle.combine(y_ref, g["pair_row"], w)
+
+
 def oracle_tokens(x_bits: np.ndarray, L: synth.LayerParams, k: int, tokens: np.ndarray,
                   idx_gpu: np.ndarray) -> np.ndarray:
     """Oracle output for selected tokens, routed with the GPU's expert choice (the

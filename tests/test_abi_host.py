@@ -102,6 +102,13 @@ def test_ffn_validation(moe):
     assert L.moe_expert_ffn_mxfp4(ok, *a) == -3
     assert L.moe_expert_ffn_mxfp4(D(16, 512, 544, 32, 4), *args) == -1  # F % 64
     assert L.moe_expert_ffn_mxfp4(D(70000, 512, 512, 32, 4), *args) == -2  # T too big
+    # contraction lengths below MOE_MIN_FFN_K: the encoding's error tail
+    for dd, ff in ((448, 512), (512, 448), (64, 64)):
+        small = D(16, dd, ff, 32, 4)
+        a = list(args); a[11] = L.moe_workspace_bytes(small)
+        assert a[11] > 0  # routing and dispatch still accept the widths
+        assert L.moe_expert_ffn_mxfp4(small, *a) == -2, (dd, ff)
+        assert b"512" in L.moe_last_error()
 
 
 def test_pack_sizes_and_validation(moe):
@@ -142,6 +149,8 @@ def test_forward_validation(moe):
     a = list(args); a[18] = ws - 256
     assert L.moe_forward(ok, *a) == -3
     assert L.moe_forward(D(16, 512, 512, 300, 4), *args) == -2
+    a = list(args); a[18] = L.moe_workspace_bytes(D(16, 256, 512, 32, 4))
+    assert L.moe_forward(D(16, 256, 512, 32, 4), *a) == -2  # d below MOE_MIN_FFN_K
 
 
 def test_ffn_stage_validation(moe):
@@ -165,6 +174,8 @@ def test_ffn_stage_validation(moe):
     a = list(args); a[12] = ws - 256
     assert L.moe_expert_ffn_mxfp4_stage(ok, *a) == -3
     assert L.moe_expert_ffn_mxfp4_stage(D(16, 512, 512, 300, 4), *args) == -2
+    a = list(args); a[12] = L.moe_workspace_bytes(D(16, 512, 384, 32, 4))
+    assert L.moe_expert_ffn_mxfp4_stage(D(16, 512, 384, 32, 4), *a) == -2  # F below the minimum
 
 
 def test_workspace_covers_the_fused_call(moe):

@@ -14,13 +14,13 @@ import synth  # noqa: E402
 
 SHAPES = [
     dict(T=16, d=2880, F=2880, E=32, k=4, seed=1),   # decode-20b shape (fused front end)
-    dict(T=1, d=64, F=64, E=4, k=4, seed=30),        # one token, E = k
-    dict(T=37, d=128, F=192, E=8, k=2, seed=31),     # ragged T, d != F
-    dict(T=50, d=64, F=128, E=16, k=1, seed=32),     # switch routing
-    dict(T=64, d=192, F=320, E=256, k=8, seed=34),   # largest fused T, E and k
-    dict(T=40, d=256, F=128, E=64, k=4, seed=44),    # F < d
-    dict(T=8, d=4608, F=256, E=4, k=2, seed=38),     # K beyond the decode kernels: separate launches
-    dict(T=128, d=256, F=256, E=32, k=4, seed=40),   # T above the decode limit: separate launches
+    dict(T=1, d=512, F=512, E=4, k=4, seed=30),      # one token, E = k
+    dict(T=37, d=512, F=704, E=8, k=2, seed=31),     # ragged T, d != F
+    dict(T=50, d=512, F=640, E=16, k=1, seed=32),    # switch routing
+    dict(T=64, d=576, F=640, E=256, k=8, seed=34),   # largest fused T, E and k
+    dict(T=40, d=768, F=512, E=64, k=4, seed=44),    # F < d
+    dict(T=8, d=4608, F=512, E=4, k=2, seed=38),     # K beyond the decode kernels: separate launches
+    dict(T=128, d=512, F=512, E=32, k=4, seed=40),   # T above the decode limit: separate launches
 ]
 
 
@@ -68,7 +68,7 @@ def test_forward_reuses_workspace(gu, E):
     """Consecutive calls on one workspace with different tokens and batch sizes
     (the fused front end's arrival counter is cleared on every call)."""
     import sparse_moe_transformer_gemm_amd as moe
-    w = synth.tiny_workload(T=48, d=256, F=256, E=E, k=4, seed=41)
+    w = synth.tiny_workload(T=48, d=512, F=512, E=E, k=4, seed=41)
     L = w.layers[0]
     wt = gu.weights_dev(L)
     ws = gu.workspace(w.T, w.d, w.F, w.E, w.k)
@@ -84,7 +84,7 @@ def test_forward_reuses_workspace(gu, E):
 
 
 @pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[2], SHAPES[6], SHAPES[7],
-                                   dict(T=300, d=320, F=384, E=12, k=4, seed=47)],
+                                   dict(T=300, d=576, F=640, E=12, k=4, seed=47)],
                          ids=["decode", "ragged", "wide-K", "prefill-path", "prefill-ragged"])
 def test_ffn_stages_equal_the_call(gu, shape):
     """moe_expert_ffn_mxfp4_stage 0, 1, 2 in order write y_sorted byte for byte

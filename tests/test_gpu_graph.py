@@ -32,7 +32,7 @@ def _snapshot(r: dict) -> dict:
 
 @pytest.mark.parametrize("shape", [
     dict(T=16, d=2880, F=2880, E=32, k=4, seed=1),   # decode-20b shape: the fused front end
-    dict(T=200, d=256, F=192, E=16, k=4, seed=48),   # separate launches (T > 64)
+    dict(T=200, d=512, F=576, E=16, k=4, seed=48),   # separate launches (T > 64)
 ], ids=["decode", "prefill-path"])
 def test_forward_graph_replays(gu, shape):
     import torch
