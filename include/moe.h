@@ -240,6 +240,33 @@ moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
                        float* y_sorted, moe_bf16* out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, checks, launches and output bytes as
+ * moe_forward, minus ws and ws_bytes: the scratch those calls need lives in a
+ * fixed device array inside the library, moe_forward_noalloc_max_bytes() bytes
+ * (32 MiB) per GPU, which each GPU the library runs on holds until the process
+ * ends. The call itself allocates nothing and frees nothing; its first call on
+ * a device looks up that device's copy of the array.
+ *   Limit: dims whose moe_workspace_bytes(dims) exceeds the array return
+ *   MOE_ERR_UNSUPPORTED (at d = F = 2880, E = 32 that is T above ~1400 tokens;
+ *   decode batches need well under 5 MiB).
+ *   Sharing: every call on one GPU uses the same array and leaves its
+ *   contents behind (what must start at zero is cleared by the call's own
+ *   kernels). Calls that may overlap on one GPU -- on different streams, or
+ *   from several threads without ordering -- race on it and give undefined
+ *   results; order them on one stream. */
+moe_status moe_forward_noalloc(moe_dims dims, const moe_bf16* x, const float* w_router,
+                               const float* b_router, moe_mxfp4_packed w_gate,
+                               moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                               const moe_bf16* b_gate, const moe_bf16* b_up,
+                               const moe_bf16* b_down, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                               int32_t* pair_row, float* y_sorted, moe_bf16* out, void* stream);
+
+/* Bytes of the scratch array moe_forward_noalloc uses (per GPU). */
+size_t moe_forward_noalloc_max_bytes(void);
+
 /* RMSNorm of each row (the pre-norm of a transformer block; rms_norm_eps = 1e-5
  * per CSDN "GPT-OSS-120B 4-bit 量化技术深度解析", section "推理优化"):
  *   out[t] = bf16( x[t] / sqrt(mean_i x[t][i]^2 + eps) * gain ), fp32 arithmetic.

@@ -21,7 +21,7 @@ __all__ = [
     "MoeError", "Dims", "MXFP4", "library_path", "lib", "workspace_bytes", "route",
     "permute", "expert_ffn_mxfp4", "combine", "rmsnorm", "residual_add", "forward",
     "ExpertWeights", "EXPORTED", "pack_mxfp4", "packed_bytes", "load_expert_weights",
-    "forward_calls", "expert_ffn_mxfp4_stage",
+    "forward_calls", "expert_ffn_mxfp4_stage", "forward_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +30,7 @@ EXPORTED = (
     "moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_combine",
     "moe_rmsnorm", "moe_residual_add", "moe_status_string", "moe_last_error",
     "moe_mxfp4_packed_bytes", "moe_pack_mxfp4", "moe_forward", "moe_expert_ffn_mxfp4_stage",
+    "moe_forward_noalloc", "moe_forward_noalloc_max_bytes",
 )
 
 
@@ -75,6 +76,10 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.argtypes = [Dims, vp, vp, vp, vp, vp]
     L.moe_forward.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward_noalloc.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, vp, vp, vp, vp]
+    L.moe_forward_noalloc_max_bytes.argtypes = []
+    L.moe_forward_noalloc_max_bytes.restype = sz
     L.moe_mxfp4_packed_bytes.argtypes = [i32, i32, i32, i32]
     L.moe_mxfp4_packed_bytes.restype = sz
     L.moe_pack_mxfp4.argtypes = [i32, i32, i32, MXFP4, vp, vp, vp]
@@ -82,7 +87,7 @@ def lib() -> ctypes.CDLL:
     L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_expert_ffn_mxfp4_stage",
               "moe_combine", "moe_rmsnorm",
-              "moe_residual_add", "moe_pack_mxfp4", "moe_forward"):
+              "moe_residual_add", "moe_pack_mxfp4", "moe_forward", "moe_forward_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -338,6 +343,17 @@ def _outputs(T, d, E, k, dev, bufs: Optional[dict]) -> dict:
 def forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict] = None) -> dict:
     """The whole block in one call (moe_forward) on the current stream. `bufs`, if
     given, supplies preallocated outputs (keys as in the returned dict)."""
+    return _forward(x, w, k, ws, bufs)
+
+
+def forward_noalloc(x, w: ExpertWeights, k: int, bufs: Optional[dict] = None) -> dict:
+    """moe_forward_noalloc: the whole block with the library's own scratch array
+    instead of a workspace (the outputs are still the caller's: pass them in
+    `bufs` to allocate nothing at all)."""
+    return _forward(x, w, k, None, bufs)
+
+
+def _forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict]) -> dict:
     T, d = x.shape
     dw, F, E = w.dims
     if dw != d:
@@ -347,7 +363,7 @@ def forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict] = None) -> dic
     counts, offsets, sorted_pair, pair_row = b["perm"]
     mg, mu, md = _packed_args(w)
     br = None if w.b_router is None else _dev(w.b_router, torch.float32, (E,), "b_router")
-    _check(lib().moe_forward(
+    args = [
         _dims(T, d, F, E, k), _dev(x, torch.bfloat16, (T, d), "x"),
         _dev(w.w_router, torch.float32, (d, E), "w_router"), br, mg, mu, md,
         _dev(w.b_gate, torch.bfloat16, (E, F), "b_gate"),
@@ -360,8 +376,12 @@ def forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict] = None) -> dic
         _dev(sorted_pair, torch.int32, (P,), "sorted_pair"),
         _dev(pair_row, torch.int32, (P,), "pair_row"),
         _dev(b["y_sorted"], torch.float32, (P, d), "y_sorted"),
-        _dev(b["out"], torch.bfloat16, (T, d), "out"),
-        ws.data_ptr(), ws.numel() * ws.element_size(), _stream()), "moe_forward")
+        _dev(b["out"], torch.bfloat16, (T, d), "out")]
+    if ws is None:
+        _check(lib().moe_forward_noalloc(*args, _stream()), "moe_forward_noalloc")
+    else:
+        _check(lib().moe_forward(*args, ws.data_ptr(), ws.numel() * ws.element_size(), _stream()),
+               "moe_forward")
     return dict(topk_idx=b["topk_idx"], topk_w=b["topk_w"], perm=b["perm"],
                 y_sorted=b["y_sorted"], out=b["out"])
 

@@ -230,25 +230,37 @@ moe_status moe_expert_ffn_mxfp4_stage(moe_dims dims, const moe_bf16* x, const in
   return hip_status(moe::launch_expert_ffn_stage(a, static_cast<hipStream_t>(stream), (int)stage));
 }
 
-moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
-                       const float* b_router, moe_mxfp4_packed w_gate, moe_mxfp4_packed w_up,
-                       moe_mxfp4_packed w_down, const moe_bf16* b_gate, const moe_bf16* b_up,
-                       const moe_bf16* b_down, int32_t* topk_idx, float* topk_w, int32_t* counts,
-                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
-                       float* y_sorted, moe_bf16* out, void* ws, size_t ws_bytes, void* stream) {
-  g_last_error[0] = 0;
+// moe_forward and moe_forward_noalloc: argument checks other than the
+// workspace's, then the launches on `ws`.
+static moe_status forward_checks(const moe_dims& dims, const moe_bf16* x, const float* w_router,
+                                 const float* b_router, moe_mxfp4_packed w_gate,
+                                 moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                                 const moe_bf16* b_gate, const moe_bf16* b_up,
+                                 const moe_bf16* b_down, int32_t* topk_idx, float* topk_w,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                 int32_t* pair_row, float* y_sorted, moe_bf16* out,
+                                 const char* who) {
   MOE_TRY(check_dims(dims));
   MOE_TRY(check_ffn_k(dims));
   MOE_TRY(check_ptrs({x, w_router, w_gate.codes, w_gate.scales, w_up.codes, w_up.scales,
                       w_down.codes, w_down.scales, b_gate, b_up, b_down, topk_idx, topk_w,
                       counts, offsets, sorted_pair, pair_row, y_sorted, out},
-                     "moe_forward"));
+                     who));
   if (b_router && !aligned16(b_router)) {
     set_error("%s", "b_router not 16-byte aligned");
     return MOE_ERR_INVALID_ARG;
   }
-  MOE_TRY(check_ws(dims, ws, ws_bytes));
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+static moe_status forward_launch(const moe_dims& dims, const moe_bf16* x, const float* w_router,
+                                 const float* b_router, moe_mxfp4_packed w_gate,
+                                 moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                                 const moe_bf16* b_gate, const moe_bf16* b_up,
+                                 const moe_bf16* b_down, int32_t* topk_idx, float* topk_w,
+                                 int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                 int32_t* pair_row, float* y_sorted, moe_bf16* out, void* ws,
+                                 hipStream_t s) {
   moe::FfnArgs a;
   a.T = dims.T;
   a.d = dims.d;
@@ -282,6 +294,49 @@ moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
   }
   MOE_TRY(hip_status(moe::launch_expert_ffn(a, s, front)));
   return hip_status(moe::launch_combine(y_sorted, pair_row, topk_w, dims.T, dims.d, dims.k, out, s));
+}
+
+moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
+                       const float* b_router, moe_mxfp4_packed w_gate, moe_mxfp4_packed w_up,
+                       moe_mxfp4_packed w_down, const moe_bf16* b_gate, const moe_bf16* b_up,
+                       const moe_bf16* b_down, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
+                       float* y_sorted, moe_bf16* out, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  MOE_TRY(forward_checks(dims, x, w_router, b_router, w_gate, w_up, w_down, b_gate, b_up, b_down,
+                         topk_idx, topk_w, counts, offsets, sorted_pair, pair_row, y_sorted, out,
+                         "moe_forward"));
+  MOE_TRY(check_ws(dims, ws, ws_bytes));
+  return forward_launch(dims, x, w_router, b_router, w_gate, w_up, w_down, b_gate, b_up, b_down,
+                        topk_idx, topk_w, counts, offsets, sorted_pair, pair_row, y_sorted, out,
+                        ws, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_forward_noalloc_max_bytes(void) { return moe::kNoAllocScratchBytes; }
+
+moe_status moe_forward_noalloc(moe_dims dims, const moe_bf16* x, const float* w_router,
+                               const float* b_router, moe_mxfp4_packed w_gate,
+                               moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                               const moe_bf16* b_gate, const moe_bf16* b_up,
+                               const moe_bf16* b_down, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                               int32_t* pair_row, float* y_sorted, moe_bf16* out, void* stream) {
+  g_last_error[0] = 0;
+  MOE_TRY(forward_checks(dims, x, w_router, b_router, w_gate, w_up, w_down, b_gate, b_up, b_down,
+                         topk_idx, topk_w, counts, offsets, sorted_pair, pair_row, y_sorted, out,
+                         "moe_forward_noalloc"));
+  if (workspace_for(dims) > moe::kNoAllocScratchBytes) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "moe_forward_noalloc: these dims need %zu bytes of scratch, more than the %zu "
+             "bytes the library holds per GPU (use moe_forward with a workspace)",
+             workspace_for(dims), moe::kNoAllocScratchBytes);
+    return MOE_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  MOE_TRY(hip_status(moe::noalloc_scratch(&ws)));
+  return forward_launch(dims, x, w_router, b_router, w_gate, w_up, w_down, b_gate, b_up, b_down,
+                        topk_idx, topk_w, counts, offsets, sorted_pair, pair_row, y_sorted, out,
+                        ws, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(moe_dims dims, const float* y_sorted, const int32_t* pair_row,

@@ -93,6 +93,11 @@ hipError_t launch_forward_front(const uint16_t* x, const float* w_router, const 
                                 int32_t* sorted_pair, int32_t* pair_row, void* ws,
                                 hipStream_t stream);
 
+// The allocation-free whole-block call's scratch: a device array of this many
+// bytes per GPU (noalloc.hip); *ptr receives its address on the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_row, const float* topk_w,
                           int T, int d, int k, uint16_t* out, hipStream_t stream);
 
