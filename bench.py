@@ -1,27 +1,32 @@
 #!/usr/bin/env python3
 """Throughput of the MXFP4 sparse-MoE block on one MI355X.
 
-One step = one pass of the whole block (moe_forward: route -> permute ->
-expert FFN -> combine) over one batch of T tokens whose inputs are already
-resident in HBM. The headline workload is the decode-shaped gpt-oss-20b
-layer (T=16, d=F=2880, E=32, top-4), which is bound by streaming the MXFP4
-weights from HBM; the prefill-shaped layer (T=8192) is reported beside it
-against the MXFP4 matrix-core peak, and the 24-block pre-norm stack (T=2048 per
-block) as tokens/s of the whole stack.
+One step = one pass of the whole block (moe_forward: route -> permute -> expert
+FFN -> combine) over one batch of T tokens whose inputs are already resident in
+HBM. The headline workload is the decode-shaped gpt-oss-20b layer (T=16,
+d=F=2880, E=32, top-4), bound by streaming the MXFP4 weights from HBM. Every
+other workload gets a line beside it: tiny (T=128, d=F=512), prefill-20b
+(T=8192, against the MXFP4 matrix-core peak), wide-120b (T=4096, E=128, skewed
+router) and the 24-block pre-norm stack (T=2048 per block).
 
-Timing: W untimed warmup steps, then K timed steps bracketed by
-torch.cuda.synchronize(); the weights rotate over R identical copies (R * layer
-bytes >= 1.5 GB) so the 256 MB last-level cache cannot hold them. A second timed
-loop runs the same steps as the four separate calls (moe_route, moe_permute,
-moe_expert_ffn_mxfp4, moe_combine) with HIP events on the launch stream around
-the expert-FFN call. The roofline figure is the dominant kernel's, the gate/up
-GEMM (moe_expert_ffn_mxfp4_stage 1), whose average launch duration comes from
-a third loop that launches it back to back over the weight copies with events
-around the loop; the whole expert-FFN call's figure is reported beside it. The timed output is checked against the CPU oracle in the same run, and the
-oracle is timed on the host cores as the CPU baseline.
+Timing protocol, per workload:
+  * the weights rotate over R identical copies (R * layer bytes >= 1.5 GB) so
+    the 256 MB last-level cache cannot hold them (the stack's 24 layers already
+    exceed it; the tiny layer is cache-resident by nature);
+  * W untimed warmup steps, then `repeats` runs of exactly K timed steps, each
+    bracketed by torch.cuda.synchronize(); the line reports the median run
+    (and the best), eager calls on torch's current stream;
+  * beside it the same steps captured once as a HIP graph and replayed;
+  * one timed step's output is checked against the CPU oracle (tiny and
+    decode-20b; the larger workloads are checked element by element in the
+    GPU tests).
+The roofline object is the dominant kernel's, the decode gate/up GEMM
+(moe_expert_ffn_mxfp4_stage 1), whose average launch duration comes from HIP
+events on its launch stream around a loop of back-to-back launches over the
+weight copies. The oracle is timed on the host cores as the CPU baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
-                       [--no-stack] [--no-cpu-baseline] [--workload 1]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats 5]
+                       [--workloads 1,0,2,3,4] [--no-cpu-baseline]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -29,6 +34,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -84,22 +90,28 @@ def measured_traffic(name: str, key: str = "traffic_bytes_per_launch"):
     return int(fields[key])
 
 
-def enc_bytes(rows: int, K: int) -> int:
-    """Bytes of `rows` activation rows encoded for the matrix cores (208 per
-    128-deep step)."""
-    return rows * ((K + 127) // 128) * 208
-
-
 def gateup_bytes(d: int, F: int) -> int:
     """Algorithmic bytes of one expert in the gate/up GEMM: the gate and up
-    MXFP4 matrices and their bf16 biases."""
+    MXFP4 matrices (0.5 B per element + 1 B per 32) and their bf16 biases."""
     return 2 * (d * F // 2 + d * F // 32) + 2 * 2 * F
 
 
+def down_bytes(d: int, F: int) -> int:
+    """Algorithmic bytes of one expert in the down GEMM: W_down and its bias."""
+    return (d * F // 2 + d * F // 32) + 2 * d
+
+
 def expert_bytes(d: int, F: int) -> int:
-    """Algorithmic bytes of one expert: 3 MXFP4 matrices (0.5 B/elt + 1 B per 32)
-    and its bf16 biases (2F + d)."""
-    return 3 * (d * F // 2 + d * F // 32) + 2 * (2 * F + d)
+    """Algorithmic bytes of one expert: 3 MXFP4 matrices and its bf16 biases."""
+    return gateup_bytes(d, F) + down_bytes(d, F)
+
+
+def layer_alg(T, d, F, E, k, U, has_bias) -> tuple:
+    """The layer's algorithmic bytes (touched experts' weights and biases, the
+    router weight and bias, x in, out back) and flops (the three expert
+    contractions); traffic the implementation adds is not credited."""
+    b = U * expert_bytes(d, F) + 4 * d * E + (4 * E if has_bias else 0) + 2 * T * d + 2 * T * d
+    return b, 2.0 * T * k * 3 * d * F
 
 
 def parse():
@@ -107,12 +119,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1)
-    ap.add_argument("--secondary", type=int, default=2, help="second workload (-1: none)")
-    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--repeats", type=int, default=5)
+    ap.add_argument("--workloads", default="1,0,2,3,4",
+                    help="comma list; the first is the headline (default: decode-20b)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-stack", action="store_true", help="skip the 24-block stack workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 passes of the library's streaming residual-add kernel "
                          "over MIB MiB per operand (reads 2 x MIB, writes MIB: a known byte "
@@ -120,7 +132,105 @@ def parse():
     return ap.parse_args()
 
 
-def run_gpu(cfg: int, steps: int, warmup: int, log) -> dict:
+def clocks() -> dict:
+    """Current GPU clocks as rocm-smi reports them (not locked)."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [l.strip() for l in r.stdout.splitlines() if "sclk" in l or "mclk" in l]
+        return {"rocm_smi": lines[:4]}
+    except Exception as e:  # rocm-smi missing or failing: say so
+        return {"rocm_smi": f"unavailable ({type(e).__name__})"}
+
+
+def _dev_inputs(L, dev):
+    import torch
+
+    import sparse_moe_transformer_gemm_amd as moe
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    return moe.load_expert_weights(
+        w_router=torch.from_numpy(L.w_router).to(dev),
+        b_router=None if L.b_router is None else torch.from_numpy(L.b_router).to(dev),
+        gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales),
+        up_codes=u8(L.up.codes), up_scales=u8(L.up.scales),
+        down_codes=u8(L.down.codes), down_scales=u8(L.down.scales),
+        b_gate=bf16(L.b_gate), b_up=bf16(L.b_up), b_down=bf16(L.b_down)), bf16
+
+
+def timed_runs(step, steps, warmup, repeats) -> list:
+    """ms per step of `repeats` runs of exactly `steps` calls of step(i), each
+    run between torch.cuda.synchronize() calls, after `warmup` untimed calls."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        out.append((time.perf_counter() - t0) * 1e3 / steps)
+    return out
+
+
+def graph_runs(step, per_graph, steps, repeats) -> list:
+    """The same steps captured once as a HIP graph of `per_graph` calls
+    (step(0) .. step(per_graph - 1)) and replayed: ms per step of `repeats` runs
+    of steps // per_graph replays."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(per_graph):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            step(i)
+    n = max(1, steps // per_graph)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            g.replay()
+        torch.cuda.synchronize()
+        out.append((time.perf_counter() - t0) * 1e3 / (n * per_graph))
+    del g
+    return out
+
+
+def stage_ms(moe, x, perm, copies, k, ws, y, stage, steps, warmup) -> float:
+    """Average launch duration of one expert-FFN stage launched back to back over
+    the weight copies, from HIP events on the launching stream around the loop
+    (each launch rewrites the same h or y from what the earlier stages left)."""
+    import torch
+    R = len(copies)
+    for i in range(warmup):
+        moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], copies[i % R], k, ws, y, stage)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record()
+    for i in range(steps):
+        moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], copies[i % R], k, ws, y, stage)
+    g1.record()
+    torch.cuda.synchronize()
+    return g0.elapsed_time(g1) / steps
+
+
+def run_layer(cfg: int, steps: int, warmup: int, repeats: int, graph: bool, log) -> dict:
     import torch
 
     import sparse_moe_transformer_gemm_amd as moe
@@ -130,127 +240,67 @@ def run_gpu(cfg: int, steps: int, warmup: int, log) -> dict:
     L = w.layers[0]
     T, d, F, E, k = w.T, w.d, w.F, w.E, w.k
     layer_bytes = E * expert_bytes(d, F) + 4 * d * E
-    R = max(1, int(np.ceil(1.5e9 / layer_bytes)))
-    log(f"[bench] workload {w.name}: T={T} d={d} F={F} E={E} k={k}; {R} weight copies")
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    def u8(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
+    R = 1 if cfg == 0 else max(1, int(np.ceil(1.5e9 / layer_bytes)))
+    log(f"[bench] {w.name}: T={T} d={d} F={F} E={E} k={k}; {R} weight copies")
     copies = []
     for _ in range(R):
-        copies.append(moe.load_expert_weights(
-            w_router=torch.from_numpy(L.w_router).to(dev),
-            b_router=None if L.b_router is None else torch.from_numpy(L.b_router).to(dev),
-            gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales),
-            up_codes=u8(L.up.codes), up_scales=u8(L.up.scales),
-            down_codes=u8(L.down.codes), down_scales=u8(L.down.scales),
-            b_gate=bf16(L.b_gate), b_up=bf16(L.b_up), b_down=bf16(L.b_down)))
+        wt, bf16 = _dev_inputs(L, dev)
+        copies.append(wt)
     x = bf16(w.x)
     ws = torch.empty(moe.workspace_bytes(T, d, F, E, k), dtype=torch.uint8, device=dev)
-    P = T * k
-    bufs = dict(
-        topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
-        topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
-        perm=(torch.empty(E, dtype=torch.int32, device=dev),
-              torch.empty(E + 1, dtype=torch.int32, device=dev),
-              torch.empty(P, dtype=torch.int32, device=dev),
-              torch.empty(P, dtype=torch.int32, device=dev)),
-        y_sorted=torch.empty((P, d), dtype=torch.float32, device=dev),
-        out=torch.empty((T, d), dtype=torch.bfloat16, device=dev))
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    bufs = moe._outputs(T, d, E, k, x.device, None)
 
     def step(i):
         moe.forward(x, copies[i % R], k, ws, bufs)
 
-    def step_calls(i):
-        # the same block as the four separate calls, with HIP events on the
-        # launch stream around the expert-FFN call
-        wt = copies[i % R]
-        idx, tw = moe.route(x, wt.w_router, wt.b_router, k, ws, bufs["topk_idx"], bufs["topk_w"])
-        perm = moe.permute(idx, E, ws, bufs["perm"])
-        ev[i][0].record()
-        y = moe.expert_ffn_mxfp4(x, perm[2], perm[1], wt, k, ws, bufs["y_sorted"])
-        ev[i][1].record()
-        moe.combine(y, perm[3], tw, bufs["out"])
+    eager = timed_runs(step, steps, warmup, repeats)
+    per_graph = max(R, min(steps, 8 * R))
+    gr = graph_runs(step, per_graph, steps, repeats) if graph else None
 
-    def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            fn(i)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
-
-    ms_step = timed(step)                 # the headline: whole-block calls
-    ms_step_calls = timed(step_calls)     # the FFN call's duration
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-
-    # The GEMMs' average launch durations: the gate/up GEMM (stage 1, the
-    # dominant kernel) and then the down GEMM (stage 2) launched back to back
-    # over the rotating weight copies, on what the earlier stages left in the
-    # workspace (every launch rewrites the same h or y), one event pair around
-    # each timed run.
+    # the GEMM stages back to back, on what the earlier stages left in ws
     wt0 = copies[0]
     idx, _ = moe.route(x, wt0.w_router, wt0.b_router, k, ws, bufs["topk_idx"], bufs["topk_w"])
     perm = moe.permute(idx, E, ws, bufs["perm"])
     moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], wt0, k, ws, bufs["y_sorted"], 0)
+    kst = max(10, steps // 4)
+    gu_ms = stage_ms(moe, x, perm, copies, k, ws, bufs["y_sorted"], 1, kst, max(3, warmup // 4))
+    dn_ms = stage_ms(moe, x, perm, copies, k, ws, bufs["y_sorted"], 2, kst, max(3, warmup // 4))
 
-    def stage_ms(stage):
-        for i in range(warmup):
-            moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], copies[i % R], k, ws, bufs["y_sorted"], stage)
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        g0.record()
-        for i in range(steps):
-            moe.expert_ffn_mxfp4_stage(x, perm[2], perm[1], copies[i % R], k, ws, bufs["y_sorted"], stage)
-        g1.record()
-        torch.cuda.synchronize()
-        return g0.elapsed_time(g1) / steps
-
-    gu_ms = stage_ms(1)
-    dn_ms = stage_ms(2)
-    # the checked output is the whole-block call's
     step(0)
     torch.cuda.synchronize()
     counts = bufs["perm"][0].cpu().numpy()
     U = int((counts > 0).sum())
     out_bits = bufs["out"].view(torch.int16).cpu().numpy().view(np.uint16)
     idx_gpu = bufs["topk_idx"].cpu().numpy()
-
-    ffn_bytes = U * expert_bytes(d, F) + 2 * T * d
-    # gate/up GEMM: its weights and biases, the encoded x it reads, the encoded h it writes
-    gu_bytes = U * gateup_bytes(d, F) + enc_bytes(T, d) + enc_bytes(T * k, F)
-    gu_flops = 2.0 * T * k * 2 * d * F
-    layer_alg_bytes = ffn_bytes + 4 * d * E + (4 * E if L.b_router is not None else 0) + 2 * T * d
-    flops = 2.0 * T * k * 3 * d * F
+    ms = float(np.median(eager))
+    b_alg, f_alg = layer_alg(T, d, F, E, k, U, L.b_router is not None)
+    gu_b, dn_b = U * gateup_bytes(d, F), U * down_bytes(d, F)
+    gu_f = 2.0 * T * k * 2 * d * F
     res = dict(
-        workload=w.name, T=T, d=d, F=F, E=E, k=k, seed=w.seed, weight_copies=R,
-        experts_touched=U, ms_per_step=ms_step, ms_per_step_calls=ms_step_calls,
-        tokens_per_s=T / (ms_step / 1e3),
-        ffn_ms=ffn_ms, ffn_alg_bytes=ffn_bytes, layer_alg_bytes=layer_alg_bytes,
-        gu_ms=gu_ms, dn_ms=dn_ms, gu_alg_bytes=gu_bytes, gu_flops=gu_flops,
-        gu_gbs=gu_bytes / (gu_ms / 1e3) / 1e9, gu_tflops=gu_flops / (gu_ms / 1e3) / 1e12,
-        ffn_gbs=ffn_bytes / (ffn_ms / 1e3) / 1e9, ffn_tflops=flops / (ffn_ms / 1e3) / 1e12,
-        layer_gbs=layer_alg_bytes / (ms_step / 1e3) / 1e9,
-        layer_tflops=flops / (ms_step / 1e3) / 1e12, flops=flops,
+        workload=w.name, T=T, d=d, F=F, E=E, k=k, seed=w.seed, weight_copies=R, experts_touched=U,
+        rows_per_expert=[int(counts.min()), int(counts.max())],
+        ms_per_step=ms, ms_per_step_best=float(min(eager)), ms_per_step_runs=eager,
+        ms_per_step_graph=None if gr is None else float(np.median(gr)),
+        ms_per_step_graph_best=None if gr is None else float(min(gr)),
+        tokens_per_s=T / (ms / 1e3),
+        alg_bytes=b_alg, alg_flops=f_alg,
+        frac_hbm_peak=b_alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        frac_mxfp4_peak=f_alg / (ms / 1e3) / 1e12 / MXFP4_PEAK_TFLOPS,
+        gate_up_gemm=dict(avg_launch_ms=gu_ms, alg_bytes=gu_b, flops=gu_f,
+                          gbs=gu_b / (gu_ms / 1e3) / 1e9, tflops=gu_f / (gu_ms / 1e3) / 1e12),
+        down_gemm=dict(avg_launch_ms=dn_ms, alg_bytes=dn_b, flops=gu_f / 2,
+                       gbs=dn_b / (dn_ms / 1e3) / 1e9, tflops=gu_f / 2 / (dn_ms / 1e3) / 1e12),
         _out_bits=out_bits, _idx=idx_gpu, _workload=w)
-    log(f"[bench] {w.name}: {ms_step * 1e3:.1f} us/step ({ms_step_calls * 1e3:.1f} as four calls), "
-        f"ffn {ffn_ms * 1e3:.1f} us (back to back: gate/up {gu_ms * 1e3:.1f}, down {dn_ms * 1e3:.1f}), "
-        f"{res['tokens_per_s']:.4g} tok/s, ffn {res['ffn_gbs']:.0f} GB/s / {res['ffn_tflops']:.0f} TFLOP/s, "
-        f"gate/up {res['gu_gbs']:.0f} GB/s / {res['gu_tflops']:.0f} TFLOP/s")
+    log(f"[bench] {w.name}: {ms * 1e3:.1f} us/step median of {repeats} (best {min(eager) * 1e3:.1f}"
+        + ("" if gr is None else f", graph {np.median(gr) * 1e3:.1f}") + f"), {res['tokens_per_s']:.4g} tok/s, "
+        f"{100 * res['frac_hbm_peak']:.1f}% HBM / {100 * res['frac_mxfp4_peak']:.1f}% MXFP4; "
+        f"gate/up {gu_ms * 1e3:.1f} us, down {dn_ms * 1e3:.1f} us, U={U}")
     del copies, ws, bufs
     torch.cuda.empty_cache()
     return res
 
 
-def run_stack(cfg: int, steps: int, warmup: int, log) -> dict:
+def run_stack(cfg: int, steps: int, warmup: int, repeats: int, log) -> dict:
     """The pre-norm stack workload: per step, every block does
     x <- x + MoE(RMSNorm(x)) through the C ABI, all layers' weights resident."""
     import torch
@@ -260,39 +310,19 @@ def run_stack(cfg: int, steps: int, warmup: int, log) -> dict:
     dev = "cuda:0"
     w = synth.workload(cfg, with_layers=False)
     T, d, F, E, k = w.T, w.d, w.F, w.E, w.k
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    def u8(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
     layers = []
     for l in range(w.n_layers):
         L = synth.stack_layer(cfg, l)
-        layers.append((bf16(L.gain), moe.load_expert_weights(
-            w_router=torch.from_numpy(L.w_router).to(dev), b_router=None,
-            gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales),
-            up_codes=u8(L.up.codes), up_scales=u8(L.up.scales),
-            down_codes=u8(L.down.codes), down_scales=u8(L.down.scales),
-            b_gate=bf16(L.b_gate), b_up=bf16(L.b_up), b_down=bf16(L.b_down))))
-    log(f"[bench] workload {w.name}: T={T} d={d} F={F} E={E} k={k}, {w.n_layers} blocks")
+        wt, bf16 = _dev_inputs(L, dev)
+        layers.append((bf16(L.gain), wt))
+    log(f"[bench] {w.name}: T={T} d={d} F={F} E={E} k={k}, {w.n_layers} blocks")
     x0 = bf16(w.x)
     xa, xb = x0.clone(), torch.empty_like(x0)
     nrm = torch.empty_like(x0)
     ws = torch.empty(moe.workspace_bytes(T, d, F, E, k), dtype=torch.uint8, device=dev)
-    P = T * k
-    bufs = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
-                topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
-                perm=(torch.empty(E, dtype=torch.int32, device=dev),
-                      torch.empty(E + 1, dtype=torch.int32, device=dev),
-                      torch.empty(P, dtype=torch.int32, device=dev),
-                      torch.empty(P, dtype=torch.int32, device=dev)),
-                y_sorted=torch.empty((P, d), dtype=torch.float32, device=dev),
-                out=torch.empty((T, d), dtype=torch.bfloat16, device=dev))
-    touched = []
+    bufs = moe._outputs(T, d, E, k, x0.device, None)
 
-    def stack_pass():
+    def stack_pass(i):
         xa.copy_(x0)
         cur, nxt = xa, xb
         for gain, wt in layers:
@@ -301,30 +331,25 @@ def run_stack(cfg: int, steps: int, warmup: int, log) -> dict:
             moe.residual_add(cur, r["out"], nxt)
             cur, nxt = nxt, cur
 
-    for _ in range(warmup):
-        stack_pass()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        stack_pass()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    # experts touched by the last block (every block touches all 32 at T=2048)
+    runs = timed_runs(stack_pass, steps, warmup, repeats)
+    ms = float(np.median(runs))
     U = int((bufs["perm"][0].cpu().numpy() > 0).sum())
-    per_layer_bytes = U * expert_bytes(d, F) + 4 * d * E + 4 * T * d + 10 * T * d
-    flops = w.n_layers * 2.0 * T * k * 3 * d * F
-    res = dict(workload=w.name, T=T, blocks=w.n_layers, ms_per_step=ms, tokens_per_s=T / (ms / 1e3),
-               frac_hbm_peak=w.n_layers * per_layer_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-               frac_mxfp4_peak=flops / (ms / 1e3) / 1e12 / MXFP4_PEAK_TFLOPS,
-               note="x copied in at the start of every step (0.02% of the step)")
-    log(f"[bench] {w.name}: {ms:.2f} ms per {w.n_layers}-block pass, {res['tokens_per_s']:.4g} tok/s")
+    b, f = layer_alg(T, d, F, E, k, U, False)
+    b += 10 * T * d  # norm and residual per block
+    res = dict(workload=w.name, T=T, blocks=w.n_layers, ms_per_step=ms, ms_per_step_best=float(min(runs)),
+               ms_per_step_runs=runs, ms_per_block=ms / w.n_layers, tokens_per_s=T / (ms / 1e3),
+               frac_hbm_peak=w.n_layers * b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+               frac_mxfp4_peak=w.n_layers * f / (ms / 1e3) / 1e12 / MXFP4_PEAK_TFLOPS,
+               note="one step = one pass of all 24 blocks; x copied in at its start (0.02%)")
+    log(f"[bench] {w.name}: {ms:.2f} ms per {w.n_layers}-block pass ({ms / w.n_layers * 1e3:.0f} us per block), "
+        f"{res['tokens_per_s']:.4g} tok/s")
     del layers, ws, bufs
     torch.cuda.empty_cache()
     return res
 
 
 def oracle_check(res: dict, log) -> dict:
-    """Compare the timed run's output with the CPU oracle (tolerance of the parity tests)."""
+    """Compare the timed run's output with the CPU oracle (the parity tests' bars)."""
     import oracle
     w = res["_workload"]
     L = w.layers[0]
@@ -337,9 +362,10 @@ def oracle_check(res: dict, log) -> dict:
     _, e2 = np.frexp(np.abs(ref["out"]))
     excess = float(np.maximum(err - np.ldexp(1.0, e2 - 9), 0).max() / rms)
     mean_rel = float(err.sum() / np.abs(ref["out"]).sum())
-    ok = bool(np.array_equal(res["_idx"], ref["idx"]) and excess <= 2e-2 and mean_rel <= 5e-3)
-    log(f"[bench] oracle check: routing equal {np.array_equal(res['_idx'], ref['idx'])}, "
-        f"excess {excess:.3g}, mean rel {mean_rel:.3g} -> {'ok' if ok else 'FAIL'}")
+    same = bool(np.array_equal(res["_idx"], ref["idx"]))
+    ok = bool(same and excess <= 2e-2 and mean_rel <= 5e-3)
+    log(f"[bench] oracle check {w.name}: routing equal {same}, excess {excess:.3g}, "
+        f"mean rel {mean_rel:.3g} -> {'ok' if ok else 'FAIL'}")
     return dict(ok=ok, excess_over_rms=excess, mean_rel=mean_rel,
                 literal_over_rms=float(err.max() / rms), oracle_seconds=dt)
 
@@ -369,6 +395,10 @@ def cpu_baseline(res: dict, seconds: float, log) -> dict:
                 sample=f"{n} full passes of the {w.name} workload ({w.T} tokens each), numpy float64")
 
 
+def _public(r: dict) -> dict:
+    return {k: v for k, v in r.items() if not k.startswith("_")}
+
+
 def main():
     args = parse()
     log = lambda s: print(s, file=sys.stderr, flush=True)
@@ -395,36 +425,47 @@ def main():
             f"(read {2 * a.numel() * 2} B, write {a.numel() * 2} B per pass)")
         return
 
-    main_res = run_gpu(args.workload, args.steps, args.warmup, log)
-    check = oracle_check(main_res, log) if args.workload in (0, 1) else None
-    sec = None
-    if not args.no_secondary and args.secondary >= 0:
-        s = run_gpu(args.secondary, max(10, args.steps // 4), max(3, args.warmup // 4), log)
-        sec = {
-            "workload": s["workload"], "T": s["T"], "tokens_per_s": s["tokens_per_s"],
-            "ms_per_step": s["ms_per_step"], "experts_touched": s["experts_touched"],
-            "roofline": {"bound": "mfma", "kernel": "grouped_prefill<6, true>: the gate/up GEMM with "
-                                                     "SwiGLU (moe_expert_ffn_mxfp4 stage 1)",
-                         "achieved": s["gu_tflops"], "peak": MXFP4_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": s["gu_tflops"] / MXFP4_PEAK_TFLOPS,
-                         "traffic": measured_traffic(f"{s['workload']}_T{s['T']}"),
-                         "flops_per_launch": s["gu_flops"], "avg_launch_ms": s["gu_ms"],
-                         "down_gemm_ms": s["dn_ms"],
-                         "ffn_call": {"achieved": s["ffn_tflops"], "frac": s["ffn_tflops"] / MXFP4_PEAK_TFLOPS,
-                                      "avg_ms": s["ffn_ms"], "flops": s["flops"],
-                                      "traffic": measured_traffic(f"{s['workload']}_T{s['T']}",
-                                                                  "traffic_bytes_per_call")}},
-            "layer_frac_mxfp4_peak": s["layer_tflops"] / MXFP4_PEAK_TFLOPS,
-            "ffn_ms": s["ffn_ms"],
-        }
-    stack = None
-    if not args.no_stack:
-        stack = run_stack(4, 3, 1, log)
+    clk0 = clocks()
+    order = [int(c) for c in args.workloads.split(",") if c.strip()]
+    results, checks = {}, {}
+    for cfg in order:
+        if synth.WORKLOADS[cfg]["n_layers"] > 1:
+            results[cfg] = run_stack(cfg, max(3, args.steps // 40), max(2, args.warmup // 10),
+                                     max(3, args.repeats), log)
+        else:
+            # the prefill-sized layers take ~1 ms per step: fewer steps
+            big = synth.WORKLOADS[cfg]["T"] > 1024
+            st = max(20, args.steps // 5) if big else args.steps
+            results[cfg] = run_layer(cfg, st, args.warmup, args.repeats, not args.no_graph, log)
+            if cfg in (0, 1):
+                checks[cfg] = oracle_check(results[cfg], log)
+    head = results[order[0]]
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(main_res, args.cpu_seconds, log)
+    if not args.no_cpu_baseline and "_workload" in head:
+        cpu = cpu_baseline(head, args.cpu_seconds, log)
+    clk1 = clocks()
 
-    r = main_res
+    r = head
+    gu = r.get("gate_up_gemm", {})
+    decode = r.get("T", 0) <= 64
+    if decode:
+        roof = {"bound": "hbm", "achieved": gu["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gu["gbs"] / HBM_PEAK_GBS,
+                "traffic": measured_traffic(f"{r['workload']}_T{r['T']}"),
+                "kernel": "grouped_decode<true, 6>: the gate/up GEMM with SwiGLU "
+                          "(moe_expert_ffn_mxfp4 stage 1)",
+                "alg_bytes_per_launch": gu["alg_bytes"], "avg_launch_ms": gu["avg_launch_ms"],
+                "units": f"{r['experts_touched']} touched experts x {gateup_bytes(r['d'], r['F'])} B "
+                         f"(gate and up MXFP4 codes, E8M0 scales, bf16 biases)"}
+    else:
+        roof = {"bound": "mfma", "achieved": gu["tflops"], "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": gu["tflops"] / MXFP4_PEAK_TFLOPS,
+                "traffic": measured_traffic(f"{r['workload']}_T{r['T']}"),
+                "kernel": "grouped_prefill<6, true>: the gate/up GEMM with SwiGLU (stage 1)",
+                "flops_per_launch": gu["flops"], "avg_launch_ms": gu["avg_launch_ms"]}
+    roof["timing"] = ("stage launched back to back over the rotating weight copies, HIP events "
+                      "on the launch stream around the timed launches")
+    roof["layer_frac"] = r["frac_hbm_peak"] if decode else r["frac_mxfp4_peak"]
     line = {
         "metric": METRIC,
         "value": r["tokens_per_s"],
@@ -440,32 +481,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{r['workload']}: T={r['T']} d={r['d']} F={r['F']} E={r['E']} "
                                f"top-{r['k']}, seed {r['seed']}",
-                   "global_batch": r["T"], "weight_copies": r["weight_copies"],
-                   "experts_touched": r["experts_touched"]},
-        "roofline": {"bound": "hbm", "kernel": "grouped_decode<true, 6>: the gate/up GEMM with SwiGLU "
-                                               "(moe_expert_ffn_mxfp4 stage 1)",
-                     "achieved": r["gu_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": r["gu_gbs"] / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(f"{r['workload']}_T{r['T']}"),
-                     "alg_bytes_per_launch": r["gu_alg_bytes"], "avg_launch_ms": r["gu_ms"],
-                     "timing": "gate/up GEMM (moe_expert_ffn_mxfp4_stage 1) launched back to back "
-                               "over the rotating weight copies, HIP events on the launch stream "
-                               "around the timed launches",
-                     "down_gemm_ms": r["dn_ms"],
-                     "ffn_call": {"kernels": "encode + gate/up GEMM + down GEMM",
-                                  "achieved": r["ffn_gbs"], "frac": r["ffn_gbs"] / HBM_PEAK_GBS,
-                                  "avg_ms": r["ffn_ms"], "alg_bytes": r["ffn_alg_bytes"],
-                                  "timing": "HIP events around moe_expert_ffn_mxfp4 in a second "
-                                            "timed loop of the same steps run as the four "
-                                            "separate calls",
-                                  "traffic": measured_traffic(f"{r['workload']}_T{r['T']}",
-                                                              "traffic_bytes_per_call")}},
-        "ms_per_step_four_calls": r["ms_per_step_calls"],
-        "layer_frac_hbm_peak": r["layer_gbs"] / HBM_PEAK_GBS,
+                   "global_batch": r["T"], "weight_copies": r.get("weight_copies"),
+                   "experts_touched": r.get("experts_touched")},
+        "timing": f"median of {args.repeats} runs of {args.steps} eager moe_forward steps after "
+                  f"{args.warmup} warmup steps; graph replay and best run beside it",
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "parity": check,
-        "secondary": sec,
-        "stack": stack,
+        "parity": {("tiny" if c == 0 else "decode-20b"): v for c, v in checks.items()},
+        "workloads": {results[c]["workload"]: _public(results[c]) for c in order},
+        "clocks": {"before": clk0, "after": clk1},
     }
     print(json.dumps(line), flush=True)
 
