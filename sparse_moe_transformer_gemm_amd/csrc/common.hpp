@@ -48,7 +48,7 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
                         int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
                         void* ws, hipStream_t stream);
 
-// Several chunks of pairs (T * k > 2048): per-chunk histograms in the workspace
+// Several chunks of pairs (T * k > 512): per-chunk histograms in the workspace
 // (permute_workspace_bytes), then the ranks.
 size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,

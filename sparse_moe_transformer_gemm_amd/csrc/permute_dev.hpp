@@ -22,7 +22,7 @@ namespace moe {
 namespace pm {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 2048;
+constexpr int kChunk = 512;
 constexpr int kMaxE = 256;
 
 // Per-chunk expert histograms: chunk c's counts of its pairs [c*kChunk,
