@@ -86,6 +86,10 @@ size_t workspace_for(const moe_dims& m) {
   if (moe::forward_front_fits(m.T, m.d, m.F, m.k)) {
     const size_t f = moe::forward_front_bytes(m.T, m.d, m.F, m.E, m.k);
     r = r > f ? r : f;
+  } else if (m.T > 64) {
+    // the whole-block call keeps the permutation's histograms past the FFN's regions
+    const size_t f = b + c;
+    r = r > f ? r : f;
   }
   return (r + 255) & ~static_cast<size_t>(255);
 }
@@ -281,18 +285,28 @@ static moe_status forward_launch(const moe_dims& dims, const moe_bf16* x, const 
   a.b_down = b_down;
   a.y_sorted = y_sorted;
   a.ws = ws;
+  // decode sizes: route + encode, then select + permute + pass table (two
+  // launches); many tokens: route + select + encode (one launch), then the
+  // permutation with the GEMMs' tile table; otherwise the separate calls' launches
   const bool front = moe::forward_front_fits(dims.T, dims.d, dims.F, dims.k);
+  const bool many = !front && !moe::ffn_decode_shape(dims.T, dims.d, dims.F) && dims.T > 64;
   if (front) {
     MOE_TRY(hip_status(moe::launch_forward_front(x, w_router, b_router, dims.T, dims.d, dims.F,
                                                  dims.E, dims.k, topk_idx, topk_w, counts, offsets,
                                                  sorted_pair, pair_row, ws, s)));
+  } else if (many) {
+    MOE_TRY(hip_status(moe::launch_route_encode(x, w_router, b_router, dims.T, dims.d, dims.E,
+                                                dims.k, topk_idx, topk_w, moe::ffn_xenc(a), s)));
+    MOE_TRY(hip_status(moe::launch_permute(topk_idx, dims.T, dims.E, dims.k, counts, offsets,
+                                           sorted_pair, pair_row, moe::ffn_ws_end(a), s,
+                                           moe::ffn_tiles(a))));
   } else {
     MOE_TRY(hip_status(moe::launch_route(x, w_router, b_router, dims.T, dims.d, dims.E, dims.k,
                                          topk_idx, topk_w, ws, s)));
     MOE_TRY(hip_status(moe::launch_permute(topk_idx, dims.T, dims.E, dims.k, counts, offsets,
                                            sorted_pair, pair_row, ws, s)));
   }
-  MOE_TRY(hip_status(moe::launch_expert_ffn(a, s, front)));
+  MOE_TRY(hip_status(moe::launch_expert_ffn(a, s, front || many)));
   return hip_status(moe::launch_combine(y_sorted, pair_row, topk_w, dims.T, dims.d, dims.k, out, s));
 }
 

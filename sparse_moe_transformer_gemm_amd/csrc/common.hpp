@@ -48,12 +48,20 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
                         int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
                         void* ws, hipStream_t stream);
 
+// The many-token routing (T > 64) that also writes x encoded for the expert
+// GEMMs into xenc (rows of nsteps(d) * 208 bytes), as the FFN's own encode would.
+hipError_t launch_route_encode(const uint16_t* x, const float* w_router, const float* b_router,
+                               int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
+                               uint8_t* xenc, hipStream_t stream);
+
 // Several chunks of pairs (T * k > 512): per-chunk histograms in the workspace
 // (permute_workspace_bytes), then the ranks.
 size_t permute_workspace_bytes(int T, int E, int k);
+// With tiles non-null, the workgroup that writes the offsets also builds the
+// expert GEMMs' 128-row tile table there (as the FFN's encode launch would).
 hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row, void* ws,
-                          hipStream_t stream);
+                          hipStream_t stream, int4* tiles = nullptr);
 
 // Repack one [E][N][K] MXFP4 tensor from the OCP layout into the packed
 // fragment layout (layout.hpp).
@@ -74,9 +82,18 @@ struct FfnArgs {
 size_t ffn_workspace_bytes(int T, int d, int F, int E, int k);
 // Both expert GEMMs take the weight-streaming decode kernels at this shape.
 bool ffn_decode_shape(int T, int d, int F);
-// front_done: x is already encoded and the pass table built in the workspace
-// (by launch_forward_front); decode shape only.
+// front_done: x is already encoded and the tile tables the GEMMs need are
+// built in the workspace (by launch_forward_front at decode sizes, by
+// launch_route_encode and launch_permute with the tile table otherwise).
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_done = false);
+// Where launch_expert_ffn keeps the encoded x and the 128-row tile table in the
+// workspace (for callers that fill them themselves).
+uint8_t* ffn_xenc(const FfnArgs& a);
+int4* ffn_tiles(const FfnArgs& a);
+// The workspace past the FFN's regions (ffn_workspace_bytes from the start):
+// where the whole-block call keeps the permutation's chunk histograms while the
+// encoded x already sits in the FFN's region.
+void* ffn_ws_end(const FfnArgs& a);
 // One stage of it: 0 encodes x and builds the tile tables (nothing when
 // front_done), 1 runs the gate/up GEMM with SwiGLU into the encoded h, 2 the
 // down GEMM into y_sorted; the three in order are launch_expert_ffn.

@@ -1099,10 +1099,12 @@ hipError_t launch_expert_ffn_stage(const FfnArgs& a, hipStream_t stream, int sta
 
   if (stage == 0) {
     // x is encoded once; one extra workgroup of the same launch builds the tables
-    // (or the fused front end has done both: decode shape only)
-    if (front_done) return (dec_gu && dec_dn) ? hipSuccess : hipErrorInvalidValue;
+    // (or the whole-block call's front end has done both)
+    if (front_done) return hipSuccess;
+    // the decode-sized encoder (cooperative, short latency) for T <= 64, the
+    // one-block-per-thread encoder (the many-token router's) otherwise
     const int nx = a.T * (a.d / 32);
-    if (nx <= 16384)
+    if (a.T <= kDecodeMaxT)
       hipLaunchKernelGGL(encode_rows, dim3((nx + 7) / 8 + 1), dim3(256), 0, stream, a.x, a.T, a.d, xenc, tj);
     else
       hipLaunchKernelGGL(encode_rows_thread, dim3((nx + 255) / 256 + 1), dim3(256), 0, stream, a.x, a.T,
@@ -1125,6 +1127,18 @@ hipError_t launch_expert_ffn_stage(const FfnArgs& a, hipStream_t stream, int sta
     return launch_prefill<1, false>(a, henc, henc, tp, ncu, stream);
   }
   return hipErrorInvalidValue;
+}
+
+uint8_t* ffn_xenc(const FfnArgs& a) {
+  return static_cast<uint8_t*>(a.ws) + ws_layout(a.T, a.d, a.F, a.E, a.k).x;
+}
+
+int4* ffn_tiles(const FfnArgs& a) {
+  return reinterpret_cast<int4*>(static_cast<uint8_t*>(a.ws) + ws_layout(a.T, a.d, a.F, a.E, a.k).tiles);
+}
+
+void* ffn_ws_end(const FfnArgs& a) {
+  return static_cast<uint8_t*>(a.ws) + ws_layout(a.T, a.d, a.F, a.E, a.k).total;
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_done) {

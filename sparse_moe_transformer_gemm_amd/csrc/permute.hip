@@ -14,6 +14,7 @@
 // ascending pair order = ascending token order). Only integer LDS atomics are
 // used, so the output is deterministic.
 #include "common.hpp"
+#include "ffn_dev.hpp"
 #include "permute_dev.hpp"
 
 namespace moe {
@@ -29,9 +30,17 @@ __global__ __launch_bounds__(pm::kThreads) void permute_kernel(const int32_t* __
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_pair,
                                                                int32_t* __restrict__ pair_row,
-                                                               const int32_t* __restrict__ chist) {
+                                                               const int32_t* __restrict__ chist,
+                                                               int4* __restrict__ tiles) {
+  __shared__ int offs[pm::kMaxE + 1];
+  __shared__ int s[257];
   pm::permute_chunk(idx, P, E, blockIdx.x * pm::kChunk, blockIdx.x == 0, counts, offsets, sorted_pair,
-                    pair_row, nullptr, chist, gridDim.x);
+                    pair_row, offs, chist, gridDim.x);
+  // workgroup 0 also lays out the expert GEMMs' row tiles from the offsets it holds
+  if (tiles && blockIdx.x == 0) {
+    __syncthreads();
+    build_tile_table<kBM>(offs, E, tiles, s);
+  }
 }
 
 }  // namespace
@@ -43,7 +52,7 @@ size_t permute_workspace_bytes(int T, int E, int k) {
 
 hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row, void* ws,
-                          hipStream_t stream) {
+                          hipStream_t stream, int4* tiles) {
   const int P = T * k;
   const int blocks = (P + pm::kChunk - 1) / pm::kChunk;
   int32_t* chist = nullptr;
@@ -54,7 +63,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t*
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(pm::kThreads), 0, stream, topk_idx, P, E,
-                     counts, offsets, sorted_pair, pair_row, chist);
+                     counts, offsets, sorted_pair, pair_row, chist, tiles);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@
 // (In each pass the ranges' sums are added in wavefront order, so the result
 // does not depend on timing.)
 #include "common.hpp"
+#include "mx6.hpp"
 #include "route_dev.hpp"
 
 namespace moe {
@@ -40,24 +41,28 @@ __global__ __launch_bounds__(256) void route_select(const double* __restrict__ p
 //
 // V_MFMA_F64_16X16X4_F64 multiplies a 16x4 A by a 4x16 B into 16x16 float64
 // accumulators: lane l supplies A[l%16][l/16] and B[l/16][l%16], and holds
-// D[l/16 + 4j][l%16] in register pair j (checked on gfx950 with one-hot B). Here A[m][q] is x of token t0+m and
-// B[q][n] is W_r of expert 16b+n, both at K index k = 32c + 8q + s: in step s of
-// 32-deep chunk c the lanes of quad q cover K elements 32c+8q+s, so that a lane
-// reads its token's 8 consecutive bf16 of the chunk with one 16-byte load. The
-// chunk's 8 steps cover its 32 K elements once each. The W_r reads are fp32
-// (exact in float64), 16 experts = 64 contiguous bytes per quad.
+// D[l/16 + 4j][l%16] in register pair j (checked on gfx950 with one-hot B).
+// Here A[m][q] is x of token t0+m and B[q][n] is W_r of expert 16b+n, both at K
+// index k = 128c + 32q + s: in step s of 128-deep chunk c the lanes of quad q
+// cover 32-element block 4c+q, so a lane holds one whole block of its token's
+// x (four 16-byte loads) and the chunk's 32 steps cover its 128 K elements once
+// each. The W_r reads are fp32 (exact in float64), 16 experts = 64 contiguous
+// bytes per quad. A lane holding a whole block can also encode it for the
+// expert GEMMs (two MXFP6-E2M3 terms, the encoding of encode_block), which the
+// whole-block call uses to skip a separate pass over x.
 typedef double v4d __attribute__((ext_vector_type(4)));
 constexpr int kRtTok = 16;    // tokens per workgroup
 constexpr int kRtWaves = 8;   // wavefronts per workgroup, one K range each
-constexpr int kRtMaxNB = 4;   // 16-expert blocks per pass over K (more: further passes)
+constexpr int kRtHalf = 16;   // K steps per half chunk (the unit of the load pipeline)
 
-template <int NB>
+template <int NB, bool ENC>
 __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias, int T,
                                                             int d, int E, int k,
                                                             int32_t* __restrict__ topk_idx,
-                                                            float* __restrict__ topk_w) {
+                                                            float* __restrict__ topk_w,
+                                                            uint8_t* __restrict__ xenc) {
   __shared__ double red[kRtTok][16 * NB + 1];     // one pass: the K ranges, added in order
   __shared__ double logit[kRtTok][rt::kMaxE + 1];
   __shared__ double sel_v[kRtTok][8], sel_x[kRtTok][8];
@@ -67,11 +72,14 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int t0 = blockIdx.x * kRtTok;
   const bool tv = t0 + r < T;
-  const int nchunk = d / 32;
+  const int nblk = d / 32;
+  const int nchunk = (nblk + 3) / 4;               // the last one may hold two blocks
   const int c0 = wave * nchunk / kRtWaves, c1 = (wave + 1) * nchunk / kRtWaves;
-  // rows past T read the last token (and count as zero); columns past E read the last expert
-  const uint4* xrow = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + r, T - 1) * d + 8 * q);
+  // rows past T read the last token (and count as zero); columns past E read the
+  // last expert, blocks past K the last block (both count as zero)
+  const uint16_t* xrow = x + (size_t)min(t0 + r, T - 1) * d;
   const int nbt = (E + 15) / 16;
+  const uint32_t pitch = (uint32_t)nsteps_of(d) * kChunk;
 
   for (int eb0 = 0; eb0 < nbt; eb0 += NB) {
     // two accumulator chains per block (even and odd steps), added at the end
@@ -85,38 +93,78 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
       live[b] = 16 * (eb0 + b) + r < E;
       col[b] = min(16 * (eb0 + b) + r, E - 1);
     }
-    auto load = [&](int c, uint4& xv, float (&wv)[8][NB]) __attribute__((always_inline)) {
-      xv = xrow[c * 4];
-      const float* wr = w + (size_t)(32 * c + 8 * q) * E;
+    auto load_x = [&](int c, uint4 (&xv)[4]) __attribute__((always_inline)) {
+      const int blk = min(4 * c + q, nblk - 1);
+      const uint4* p = reinterpret_cast<const uint4*>(xrow + 32 * blk);
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2)
+      for (int i = 0; i < 4; ++i) xv[i] = p[i];
+    };
+    auto load_w = [&](int hc, float (&wv)[kRtHalf][NB]) __attribute__((always_inline)) {
+      const int c = hc >> 1, h = hc & 1;
+      const int blk = min(4 * c + q, nblk - 1);
+      const float* wr = w + (size_t)(32 * blk + kRtHalf * h) * E;
+#pragma unroll
+      for (int s2 = 0; s2 < kRtHalf; ++s2)
 #pragma unroll
         for (int b = 0; b < NB; ++b) wv[s2][b] = wr[(size_t)s2 * E + col[b]];
     };
-    auto compute = [&](const uint4& xv, const float (&wv)[8][NB]) __attribute__((always_inline)) {
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    auto compute = [&](int hc, const uint4 (&xv)[4], const float (&wv)[kRtHalf][NB])
+                       __attribute__((always_inline)) {
+      const bool ok = tv && 4 * (hc >> 1) + q < nblk;
+      const int h = hc & 1;
+      const uint32_t xw[8] = {xv[2 * h].x, xv[2 * h].y, xv[2 * h].z, xv[2 * h].w,
+                              xv[2 * h + 1].x, xv[2 * h + 1].y, xv[2 * h + 1].z, xv[2 * h + 1].w};
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) {
+      for (int s2 = 0; s2 < kRtHalf; ++s2) {
         const float xf = bf16_to_f32(s2 & 1 ? (xw[s2 >> 1] >> 16) : (xw[s2 >> 1] & 0xffffu));
-        const double a = static_cast<double>(tv ? xf : 0.0f);
+        const double a = static_cast<double>(ok ? xf : 0.0f);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
           acc[s2 & 1][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(
               a, static_cast<double>(live[b] ? wv[s2][b] : 0.0f), acc[s2 & 1][b], 0, 0, 0);
       }
     };
-    // two chunks in flight: the loads of chunk c+1 are issued before chunk c is computed
-    uint4 xa, xb;
-    float wa[8][NB], wb[8][NB];
-    int c = c0;
-    if (c < c1) load(c, xa, wa);
-    for (; c + 1 < c1; c += 2) {
-      load(c + 1, xb, wb);
-      compute(xa, wa);
-      if (c + 2 < c1) load(c + 2, xa, wa);
-      compute(xb, wb);
+    auto encode = [&](int c, const uint4 (&xv)[4]) __attribute__((always_inline)) {
+      const int blk = 4 * c + q;
+      if (!tv || blk >= nblk) return;
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+        for (int h2 = 0; h2 < 4; ++h2) {
+          v[8 * i + 2 * h2] = bf16_to_f32(u[h2] & 0xffffu);
+          v[8 * i + 2 * h2 + 1] = bf16_to_f32(u[h2] >> 16);
+        }
+      }
+      uint32_t hi[6], lo[6], sc;
+      encode_block(v, hi, lo, sc);
+      uint8_t* rowp = xenc + (size_t)(t0 + r) * pitch;
+      store_enc(rowp + (uint32_t)(blk >> 2) * kChunk + (blk & 3) * kEncBytes, hi, lo);
+      *reinterpret_cast<uint16_t*>(rowp + (uint32_t)(blk >> 2) * kChunk + kChunkScales + (blk & 3) * 2) =
+          static_cast<uint16_t>(sc);
+    };
+    // half chunks hc = 2c + h; the W_r loads of the next half and the x loads of
+    // the next chunk are issued before the current half is computed
+    const int h0 = 2 * c0, h1 = 2 * c1;
+    uint4 xa[4], xb[4];
+    float wa[kRtHalf][NB], wb[kRtHalf][NB];
+    if (h0 < h1) {
+      load_x(c0, xa);
+      load_w(h0, wa);
     }
-    if (c < c1) compute(xa, wa);
+    for (int hc = h0; hc < h1; hc += 2) {
+      // half 0 of chunk c (x in xa): prefetch half 1's weights and the next chunk's x
+      const int c = hc >> 1;
+      load_w(hc + 1, wb);
+      if (c + 1 < c1) load_x(c + 1, xb);
+      compute(hc, xa, wa);
+      if (ENC && eb0 == 0) encode(c, xa);
+      if (hc + 2 < h1) load_w(hc + 2, wa);
+      compute(hc + 1, xa, wb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xa[i] = xb[i];
+    }
 
     // the K ranges, added in wavefront order
     for (int wv2 = 0; wv2 < kRtWaves; ++wv2) {
@@ -170,6 +218,20 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
   }
 }
 
+template <bool ENC>
+hipError_t launch_route_mfma(const uint16_t* x, const float* w_router, const float* b_router, int T,
+                             int d, int E, int k, int32_t* topk_idx, float* topk_w, uint8_t* xenc,
+                             hipStream_t stream) {
+  const dim3 grid((T + kRtTok - 1) / kRtTok), block(kRtWaves * 64);
+  if (E <= 16)
+    hipLaunchKernelGGL((route_mfma<1, ENC>), grid, block, 0, stream, x, w_router, b_router, T, d, E, k,
+                       topk_idx, topk_w, xenc);
+  else
+    hipLaunchKernelGGL((route_mfma<2, ENC>), grid, block, 0, stream, x, w_router, b_router, T, d, E, k,
+                       topk_idx, topk_w, xenc);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void route_partial_small(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ w, int T,
                                                            int d, int E,
@@ -200,15 +262,13 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
                        E, k, topk_idx, topk_w);
     return hipGetLastError();
   }
-  const dim3 grid((T + kRtTok - 1) / kRtTok);
-  const int nbt = (E + 15) / 16;
-  if (nbt <= 1)
-    hipLaunchKernelGGL(route_mfma<1>, grid, dim3(kRtWaves * 64), 0, stream, x, w_router, b_router, T, d, E, k, topk_idx, topk_w);
-  else if (nbt <= 2)
-    hipLaunchKernelGGL(route_mfma<2>, grid, dim3(kRtWaves * 64), 0, stream, x, w_router, b_router, T, d, E, k, topk_idx, topk_w);
-  else
-    hipLaunchKernelGGL(route_mfma<kRtMaxNB>, grid, dim3(kRtWaves * 64), 0, stream, x, w_router, b_router, T, d, E, k, topk_idx, topk_w);
-  return hipGetLastError();
+  return launch_route_mfma<false>(x, w_router, b_router, T, d, E, k, topk_idx, topk_w, nullptr, stream);
+}
+
+hipError_t launch_route_encode(const uint16_t* x, const float* w_router, const float* b_router,
+                               int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
+                               uint8_t* xenc, hipStream_t stream) {
+  return launch_route_mfma<true>(x, w_router, b_router, T, d, E, k, topk_idx, topk_w, xenc, stream);
 }
 
 }  // namespace moe
