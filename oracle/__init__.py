@@ -25,18 +25,25 @@ experts, MoE weights in MXFP4). The MXFP4 bit format itself is not on the pages:
 it is the OCP Microscaling Formats (MX) v1.0 encoding (E2M1 elements, one E8M0
 scale per 32 consecutive elements).
 
+A second weight format, FP8-E4M3 with one float32 scale per 128x128 block
+(oracle/fp8.py), serves the same expert FFN (ffn_sorted_fp8); and routing
+weights may be rounded to bf16 before the combine (round_bf16).
+
 Every function here is pinned by `-m "not gpu"` tests against closed forms, exact
 rational arithmetic, published format tables or invariants; none is "parity
 unpinned".
 """
 from .mx import E2M1, E8M0, e2m1_value, e8m0_value, unpack_codes, dequant
+from .fp8 import E4M3, e4m3_value, dequant_fp8
 from .moe import (
     bf16_to_f64, router_logits, topk_select, softmax_selected, route, permute,
     silu, swiglu, gate_up, down, expert_ffn, ffn_sorted, combine, moe_layer, dense_moe, rmsnorm,
+    expert_ffn_fp8, ffn_sorted_fp8, round_bf16,
 )
 
 __all__ = [
     "E2M1", "E8M0", "e2m1_value", "e8m0_value", "unpack_codes", "dequant",
+    "E4M3", "e4m3_value", "dequant_fp8", "expert_ffn_fp8", "ffn_sorted_fp8", "round_bf16",
     "bf16_to_f64", "router_logits", "topk_select", "softmax_selected", "route",
     "permute", "silu", "swiglu", "gate_up", "down", "expert_ffn", "ffn_sorted", "combine", "moe_layer",
     "dense_moe", "rmsnorm",

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .fp8 import dequant_fp8
 from .mx import dequant
 
 
@@ -151,6 +152,47 @@ def ffn_sorted(x: np.ndarray, sorted_pair: np.ndarray, offsets: np.ndarray, k: i
         rows = x[np.asarray(sorted_pair[a:b], np.int64) // k]
         y[a:b] = expert_ffn(rows, *_expert_weights(layer, e))
     return y
+
+
+def expert_ffn_fp8(xr, layer8, e: int, b_gate, b_up, b_down) -> np.ndarray:
+    """One expert on rows xr with FP8 block-scaled weights (layer8: gate/up/down
+    each (codes [E][N][K], scales [E][ceil(N/128)][ceil(K/128)])); the biases
+    as bf16 bits [E][N]. The FFN itself is the same as expert_ffn.
+
+    [P3] section "GPT-OSS a Hopper": the experts run as FP8 with 128x128 block
+    scales; section "Nuclis per a GPT-OSS / MoE": biases in the accumulators."""
+    wg = dequant_fp8(*[a[e] for a in layer8["gate"]])
+    wu = dequant_fp8(*[a[e] for a in layer8["up"]])
+    wd = dequant_fp8(*[a[e] for a in layer8["down"]])
+    return expert_ffn(xr, wg, wu, wd, bf16_to_f64(b_gate[e]), bf16_to_f64(b_up[e]),
+                      bf16_to_f64(b_down[e]))
+
+
+def ffn_sorted_fp8(x, sorted_pair, offsets, k: int, layer8, b_gate, b_up, b_down) -> np.ndarray:
+    """ffn_sorted with FP8 block-scaled expert weights."""
+    x = np.asarray(x, np.float64)
+    E = offsets.size - 1
+    d_out = layer8["down"][0].shape[1]
+    y = np.zeros((sorted_pair.size, d_out), np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        y[a:b] = expert_ffn_fp8(x[np.asarray(sorted_pair[a:b], np.int64) // k], layer8, e,
+                                b_gate, b_up, b_down)
+    return y
+
+
+def round_bf16(w: np.ndarray) -> np.ndarray:
+    """Routing weights as the GPU holds them (float32), rounded to the nearest
+    bf16 (ties to even), as float64.
+
+    [P3] section "Nuclis per a GPT-OSS / MoE": computing the expert (routing)
+    weights in bfloat16 was critical for matching the reference numerics."""
+    f = np.ascontiguousarray(np.asarray(w, np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def combine(y_sorted: np.ndarray, pair_row: np.ndarray, w: np.ndarray) -> np.ndarray:

@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits", "MX4", "LayerParams", "Workload", "WORKLOADS", "draw_layer",
-    "workload", "stack_layer", "tiny_workload",
+    "workload", "stack_layer", "tiny_workload", "fp8_weights",
 ]
 
 
@@ -159,6 +159,23 @@ def stack_layer(i: int, l: int) -> LayerParams:
 def stack_layers(i: int) -> Iterator[LayerParams]:
     for l in range(WORKLOADS[i]["n_layers"]):
         yield stack_layer(i, l)
+
+
+def fp8_weights(rng: np.random.Generator, E: int, N: int, K: int):
+    """Random FP8-E4M3 block-scaled weights for one [E][N][K] tensor: codes with a
+    uniform sign, a uniform exponent field in 4..11 and a uniform mantissa (no
+    NaN codes), and one float32 scale per 128x128 block drawn as 2^u * (1 + v),
+    u uniform in -9..-7, v uniform in [0, 1). Returns (codes uint8 [E][N][K],
+    scales float32 [E][ceil(N/128)][ceil(K/128)])."""
+    sign = rng.integers(0, 2, (E, N, K), dtype=np.uint8)
+    expf = rng.integers(4, 12, (E, N, K), dtype=np.uint8)
+    man = rng.integers(0, 8, (E, N, K), dtype=np.uint8)
+    codes = (sign << 7) | (expf << 3) | man
+    nb, kb = (N + 127) // 128, (K + 127) // 128
+    u = rng.integers(-9, -6, (E, nb, kb))
+    v = rng.random((E, nb, kb))
+    scales = (np.exp2(u) * (1.0 + v)).astype(np.float32)
+    return codes.astype(np.uint8), scales
 
 
 def tiny_workload(T: int, d: int, F: int, E: int, k: int, seed: int, zipf: bool = False,

@@ -461,4 +461,130 @@ def pin_rmsnorm_scale_invariance():
     assert np.allclose(rms, 1.0, rtol=1e-15)
 
 
+
+
+# ------------------------------------------------------------------ FP8 block-scaled weights
+
+import oracle.fp8 as of8  # noqa: E402
+
+
+def golden_e4m3():
+    vals = {}
+    with open(os.path.join(GOLDEN, "e4m3_values.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            c, v = line.split()
+            vals[int(c, 16)] = float(v)
+    return vals
+
+
+def pin_e4m3_table():
+    """The OCP E4M3 values of selected codes (golden file), sign symmetry over all
+    256 codes, exactly two NaN codes, and strictly increasing finite magnitudes
+    0x00 .. 0x7E (each step a fixed fraction of its binade)."""
+    for c, v in golden_e4m3().items():
+        got = of8.e4m3_value(c)
+        assert (math.isnan(v) and math.isnan(got)) or got == v, (hex(c), got, v)
+        assert (math.isnan(v) and math.isnan(of8.E4M3[c])) or of8.E4M3[c] == v
+    t = of8.E4M3
+    assert np.isnan(t).sum() == 2 and np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0) and pos[-1] == 448.0
+    for c in range(0x7F):
+        assert t[c | 0x80] == -t[c]
+        if c >= 8:
+            _, e = math.frexp(t[c])   # within a binade [2^(e-1), 2^e) the step is 2^(e-1)/8
+            assert t[c + 1] - t[c] == math.ldexp(1.0, e - 1 - 3) if c + 1 < 0x7F else True
+
+
+def pin_fp8_block_dequant():
+    """Element (n, k) of a block-scaled FP8 matrix is E4M3[code] times the scale
+    of block (n // 128, k // 128), including partial edge blocks: checked one
+    element at a time against a loop, on a non-square shape with partial blocks
+    in both directions."""
+    rng = np.random.default_rng(60)
+    N, K = 200, 300
+    codes = rng.integers(0, 0x7F, (N, K), dtype=np.uint8)
+    codes[rng.random((N, K)) < 0.5] |= 0x80
+    scales = (2.0 ** rng.integers(-9, 3, (2, 3)) * (1 + rng.random((2, 3)))).astype(np.float32)
+    got = of8.dequant_fp8(codes, scales)
+    for _ in range(400):
+        n, k = int(rng.integers(N)), int(rng.integers(K))
+        want = of8.e4m3_value(int(codes[n, k])) * float(scales[n // 128][k // 128])
+        assert got[n, k] == want, (n, k)
+    assert got.shape == (N, K)
+
+
+def _mx4_to_fp8_bruteforce(packed, scales):
+    """Convert one MXFP4 matrix [N][K] to FP8 with 128x128 block scales by brute
+    force: block scale = 2^(largest E8M0 exponent in the block), and each element's
+    code is the E4M3 code whose value equals element / block scale exactly
+    (searched in the table); returns (codes, scales)."""
+    vals = omx.dequant(packed, scales)
+    N, K = vals.shape
+    nb, kb = (N + 127) // 128, (K + 127) // 128
+    bs = np.zeros((nb, kb), np.float32)
+    codes = np.zeros((N, K), np.uint8)
+    lookup = {}
+    for c in range(256):
+        v = of8.E4M3[c]
+        if not np.isnan(v) and v not in lookup and not (v == 0 and c == 0x80):
+            lookup[v] = c
+    for i in range(nb):
+        for j in range(kb):
+            smax = int(scales[128 * i:128 * (i + 1), 4 * j:4 * (j + 1)].max())
+            bs[i, j] = np.float32(math.ldexp(1.0, smax - 127))
+            blk = vals[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)] / float(bs[i, j])
+            codes[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)] = np.vectorize(lookup.__getitem__)(blk)
+    return codes, bs
+
+
+def pin_mxfp4_to_fp8_exact():
+    """MXFP4 weights whose E8M0 exponents within a 128x128 block differ by at most
+    8 are exactly FP8 block-scaled weights (the conversion the pages' Hopper
+    engine made once): the brute-force conversion exists and its FP8 dequant
+    equals the MXFP4 dequant exactly. Shape with partial blocks."""
+    rng = np.random.default_rng(61)
+    N, K = 160, 192
+    packed = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.integers(121, 125, (N, K // 32), dtype=np.uint8)
+    codes, bs = _mx4_to_fp8_bruteforce(packed, scales)
+    assert np.array_equal(of8.dequant_fp8(codes, bs), omx.dequant(packed, scales))
+
+
+def pin_ffn_fp8_matches_mxfp4():
+    """The FP8 expert FFN on exactly converted weights is the MXFP4 expert FFN
+    (the same float64 values give the same result bit for bit), and on weights
+    scaled by 2 in one block the output changes (the block scale is used)."""
+    w = synth.tiny_workload(T=24, d=128, F=192, E=3, k=2, seed=62)
+    L = w.layers[0]
+    conv = {}
+    for name in ("gate", "up", "down"):
+        m = getattr(L, name)
+        cs = [_mx4_to_fp8_bruteforce(m.codes[e], m.scales[e]) for e in range(3)]
+        conv[name] = (np.stack([c for c, _ in cs]), np.stack([s for _, s in cs]))
+    x = om.bf16_to_f64(w.x)
+    idx, _, _ = om.route(x, L.w_router, L.b_router, 2)
+    _, off, sp, _ = om.permute(idx, 3)
+    y4 = om.ffn_sorted(x, sp, off, 2, L)
+    y8 = om.ffn_sorted_fp8(x, sp, off, 2, conv, L.b_gate, L.b_up, L.b_down)
+    assert np.array_equal(y4, y8)
+    conv["down"][1][0, 0, 0] *= 2
+    y8b = om.ffn_sorted_fp8(x, sp, off, 2, conv, L.b_gate, L.b_up, L.b_down)
+    assert not np.array_equal(y4, y8b)
+
+
+def pin_round_bf16():
+    """Routing weights rounded to bf16: ties to even at 1 + 2^-8 and 1 + 3 2^-8,
+    and equal to torch's float32 -> bfloat16 cast on random weights."""
+    import torch
+    r = om.round_bf16(np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 0.3]))
+    assert r[0] == 1.0 and r[1] == 1.0 and r[2] == 1 + 2.0 ** -6
+    w = np.random.default_rng(63).random(1000)
+    want = torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(om.round_bf16(w), want)
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -123,7 +123,38 @@ def _rmsnorm_no_mean(x, gain, eps=1e-5):
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * gain
 
 
+import oracle.fp8 as of8  # noqa: E402
+
+
+def _e4m3_bias8(code):
+    sign, exp, man = (code >> 7) & 1, (code >> 3) & 15, code & 7
+    if exp == 15 and man == 7:
+        return float("nan")
+    mag = (man / 8.0) * 2.0 ** -7 if exp == 0 else 2.0 ** (exp - 8) * (1.0 + man / 8.0)
+    return -mag if sign else mag
+
+
+def _dequant_fp8_blocks_transposed(codes, scales):
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape[-2:]
+    sc = np.asarray(scales, np.float32).astype(np.float64)
+    # wrong: block (i, j) scale taken from the transposed grid (reshaped to fit)
+    sc = np.swapaxes(sc, -1, -2).reshape(sc.shape)
+    full = np.repeat(np.repeat(sc, 128, axis=-2), 128, axis=-1)[..., :N, :K]
+    return of8.E4M3[codes] * full
+
+
+def _round_bf16_truncate(w):
+    f = np.ascontiguousarray(np.asarray(w, np.float64).astype(np.float32))
+    u = (f.view(np.uint32) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 MUTATIONS = {
+    "e4m3_bias_8": (of8, "e4m3_value", _e4m3_bias8),
+    "e4m3_table_bias_8": (of8, "E4M3", np.array([_e4m3_bias8(c) for c in range(256)])),
+    "fp8_block_scales_transposed": (of8, "dequant_fp8", _dequant_fp8_blocks_transposed),
+    "routing_weights_truncated_to_bf16": (om, "round_bf16", _round_bf16_truncate),
     "nibble_order_swapped": (omx, "unpack_codes", _unpack_swapped),
     "e2m1_sign_dropped": (omx, "E2M1", np.abs(omx.E2M1)),
     "e2m1_subnormal_as_normal": (omx, "E2M1", np.array([1.0, 1.5, 1, 1.5, 2, 3, 4, 6] * 2) * np.repeat([1, -1], 8)),
