@@ -240,6 +240,61 @@ moe_status moe_forward(moe_dims dims, const moe_bf16* x, const float* w_router,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row,
                        float* y_sorted, moe_bf16* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 expert weights: the pages' serving variant ("GPT-OSS el dia 0", section
+ * "GPT-OSS a Hopper": the MXFP4 experts converted once to FP8 with 128x128
+ * block scales and run on FP8 GEMMs extended with a bias term; section "Nuclis
+ * per a GPT-OSS / MoE": the bias goes into the GEMM accumulators).
+ * A matrix W[N][K] is stored as codes[N][K], one OCP FP8 E4M3 byte per element
+ * (bias 7, subnormals, no infinities, 0x7F/0xFF NaN), and scales
+ * [ceil(N/128)][ceil(K/128)] float32, one per 128 x 128 block:
+ *   W[n][k] = E4M3(codes[n][k]) * scales[n/128][k/128].
+ * For all E experts: codes [E][N][K], scales [E][ceil(N/128)][ceil(K/128)]. */
+typedef struct {
+  const uint8_t* codes;  /* [E][N][K] (moe_convert_mxfp4_to_fp8), or packed (moe_pack_fp8) */
+  const float* scales;   /* [E][ceil(N/128)][ceil(K/128)] */
+} moe_fp8;
+
+/* Convert MXFP4 weights (OCP layout, [device]) to FP8 with 128x128 block
+ * scales, once, as the pages' engine did: each block's scale is 2^(its largest
+ * E8M0 exponent - 127) and each element is rounded to the nearest E4M3 value
+ * (ties to even) of element / block scale. When the E8M0 exponents inside a
+ * 128x128 block differ by at most 8 (the gpt-oss-like weights here differ by 3)
+ * every element is exact, so the FP8 layer computes the same function.
+ *   codes_out  [device] E * N * K bytes;  scales_out [device] float32
+ *   E * ceil(N/128) * ceil(K/128). N, K positive multiples of 64, <= 16384. */
+moe_status moe_convert_mxfp4_to_fp8(int32_t E, int32_t N, int32_t K, moe_mxfp4 src,
+                                    uint8_t* codes_out, float* scales_out, void* stream);
+
+/* Bytes of the packed form of [E][N][K] FP8 codes (0 for unusable sizes). */
+size_t moe_fp8_packed_bytes(int32_t E, int32_t N, int32_t K);
+
+/* Repack FP8 codes [E][N][K] into the B-operand order of gfx950's scaled MFMA
+ * with an FP8 operand (a byte permutation, once at load time):
+ *   [E][N/32][ceil(K/128)][2][64][32 B]: entry (e,g,j,s,l), row 32g + l%32,
+ *   h = l/32, holds in bytes 0..15 the codes of elements 16h..16h+15 of the
+ *   32-element block 4j + s and in bytes 16..31 those of block 4j + 2 + s
+ *   (the instruction takes an 8-bit operand in 16-element pieces); zero past K.
+ * The block scales are used as stored. Output must not overlap the input. */
+moe_status moe_pack_fp8(int32_t E, int32_t N, int32_t K, const uint8_t* codes,
+                        uint8_t* packed_out, void* stream);
+
+/* moe_expert_ffn_mxfp4 with FP8 block-scaled expert weights: the same
+ * arguments, dims checks and outputs, with each moe_fp8 holding codes packed by
+ * moe_pack_fp8 and the float32 block scales. Accumulators start at the bias;
+ * each 128-deep K step is scaled by its block scale as it is added. */
+moe_status moe_expert_ffn_fp8(moe_dims dims, const moe_bf16* x, const int32_t* sorted_pair,
+                              const int32_t* offsets, moe_fp8 w_gate, moe_fp8 w_up,
+                              moe_fp8 w_down, const moe_bf16* b_gate, const moe_bf16* b_up,
+                              const moe_bf16* b_down, float* y_sorted, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Routing weights in bfloat16 ("GPT-OSS el dia 0", section "Nuclis per a
+ * GPT-OSS / MoE": computing the expert weights in bf16 was critical to match
+ * the reference numerics): rounds topk_w [device] fp32 [T][k] in place to the
+ * nearest bf16 value (ties to even), still stored as fp32, for moe_combine. */
+moe_status moe_round_weights_bf16(int32_t T, int32_t k, float* topk_w, void* stream);
+
 /* moe_forward without a workspace, for callers that cannot allocate device
  * memory (code under graph capture, tight serving loops, harnesses that forbid
  * allocation). Same arguments, checks, launches and output bytes as

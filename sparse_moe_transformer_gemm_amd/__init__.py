@@ -21,7 +21,9 @@ __all__ = [
     "MoeError", "Dims", "MXFP4", "library_path", "lib", "workspace_bytes", "route",
     "permute", "expert_ffn_mxfp4", "combine", "rmsnorm", "residual_add", "forward",
     "ExpertWeights", "EXPORTED", "pack_mxfp4", "packed_bytes", "load_expert_weights",
-    "forward_calls", "expert_ffn_mxfp4_stage", "forward_noalloc",
+    "forward_calls", "expert_ffn_mxfp4_stage", "forward_noalloc", "Fp8Weights",
+    "convert_mxfp4_to_fp8", "pack_fp8", "load_fp8_weights", "fp8_from_mxfp4", "expert_ffn_fp8",
+    "round_weights_bf16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +33,8 @@ EXPORTED = (
     "moe_rmsnorm", "moe_residual_add", "moe_status_string", "moe_last_error",
     "moe_mxfp4_packed_bytes", "moe_pack_mxfp4", "moe_forward", "moe_expert_ffn_mxfp4_stage",
     "moe_forward_noalloc", "moe_forward_noalloc_max_bytes",
+    "moe_convert_mxfp4_to_fp8", "moe_fp8_packed_bytes", "moe_pack_fp8", "moe_expert_ffn_fp8",
+    "moe_round_weights_bf16",
 )
 
 
@@ -80,6 +84,12 @@ def lib() -> ctypes.CDLL:
                                       vp, vp, vp, vp, vp, vp, vp]
     L.moe_forward_noalloc_max_bytes.argtypes = []
     L.moe_forward_noalloc_max_bytes.restype = sz
+    L.moe_convert_mxfp4_to_fp8.argtypes = [i32, i32, i32, MXFP4, vp, vp, vp]
+    L.moe_fp8_packed_bytes.argtypes = [i32, i32, i32]
+    L.moe_fp8_packed_bytes.restype = sz
+    L.moe_pack_fp8.argtypes = [i32, i32, i32, vp, vp, vp]
+    L.moe_expert_ffn_fp8.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_round_weights_bf16.argtypes = [i32, i32, vp, vp]
     L.moe_mxfp4_packed_bytes.argtypes = [i32, i32, i32, i32]
     L.moe_mxfp4_packed_bytes.restype = sz
     L.moe_pack_mxfp4.argtypes = [i32, i32, i32, MXFP4, vp, vp, vp]
@@ -87,7 +97,8 @@ def lib() -> ctypes.CDLL:
     L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_expert_ffn_mxfp4_stage",
               "moe_combine", "moe_rmsnorm",
-              "moe_residual_add", "moe_pack_mxfp4", "moe_forward", "moe_forward_noalloc"):
+              "moe_residual_add", "moe_pack_mxfp4", "moe_forward", "moe_forward_noalloc",
+              "moe_convert_mxfp4_to_fp8", "moe_pack_fp8", "moe_expert_ffn_fp8", "moe_round_weights_bf16"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -285,6 +296,122 @@ def expert_ffn_mxfp4_stage(x, sorted_pair, offsets, w: ExpertWeights, k: int, ws
         _dev(y_sorted, torch.float32, (P, d), "y_sorted"), int(stage),
         ws.data_ptr(), ws.numel() * ws.element_size(), _stream()), "moe_expert_ffn_mxfp4_stage")
     return y_sorted
+
+
+# --------------------------------------------------------------------------- FP8 weights
+# moe_fp8 has the same two pointers as moe_mxfp4 (codes, then float32 scales),
+# so the MXFP4 ctypes structure carries it.
+
+@dataclass
+class Fp8Weights:
+    """Device tensors of one MoE layer with FP8-E4M3 expert weights: the three
+    expert tensors as packed codes (moe_pack_fp8, flat uint8) and float32
+    128x128 block scales, the bf16 biases, and the fp32 router."""
+    d: int
+    F: int
+    E: int
+    w_router: torch.Tensor
+    b_router: Optional[torch.Tensor]
+    gate_codes: torch.Tensor          # packed, from codes [E][F][d]
+    gate_scales: torch.Tensor         # float32 [E][ceil(F/128)][ceil(d/128)]
+    up_codes: torch.Tensor
+    up_scales: torch.Tensor
+    down_codes: torch.Tensor          # packed, from codes [E][d][F]
+    down_scales: torch.Tensor         # float32 [E][ceil(d/128)][ceil(F/128)]
+    b_gate: torch.Tensor
+    b_up: torch.Tensor
+    b_down: torch.Tensor
+
+    @property
+    def dims(self):
+        return self.d, self.F, self.E
+
+
+def _nb(n: int) -> int:
+    return (n + 127) // 128
+
+
+def convert_mxfp4_to_fp8(codes: torch.Tensor, scales: torch.Tensor):
+    """MXFP4 tensor (OCP layout: codes uint8 [E][N][K/2], scales uint8 [E][N][K/32])
+    -> FP8 codes uint8 [E][N][K] and float32 block scales [E][ceil(N/128)][ceil(K/128)]."""
+    E, N, Kh = codes.shape
+    K = 2 * Kh
+    c8 = torch.empty((E, N, K), dtype=torch.uint8, device=codes.device)
+    s8 = torch.empty((E, _nb(N), _nb(K)), dtype=torch.float32, device=codes.device)
+    src = MXFP4(_dev(codes, torch.uint8, (E, N, K // 2), "codes"),
+                _dev(scales, torch.uint8, (E, N, K // 32), "scales"))
+    _check(lib().moe_convert_mxfp4_to_fp8(E, N, K, src, c8.data_ptr(), s8.data_ptr(), _stream()),
+           "moe_convert_mxfp4_to_fp8")
+    return c8, s8
+
+
+def pack_fp8(codes: torch.Tensor) -> torch.Tensor:
+    """Repack FP8 codes uint8 [E][N][K] into the layout moe_expert_ffn_fp8 streams."""
+    E, N, K = codes.shape
+    n = lib().moe_fp8_packed_bytes(E, N, K)
+    if n == 0:
+        raise MoeError(f"unsupported FP8 tensor shape E={E} N={N} K={K}")
+    out = torch.empty(n, dtype=torch.uint8, device=codes.device)
+    _check(lib().moe_pack_fp8(E, N, K, _dev(codes, torch.uint8, (E, N, K), "codes"), out.data_ptr(),
+                              _stream()), "moe_pack_fp8")
+    return out
+
+
+def load_fp8_weights(w_router, b_router, gate, up, down, b_gate, b_up, b_down) -> Fp8Weights:
+    """Fp8Weights from device tensors: gate, up, down are (codes uint8 [E][N][K],
+    scales float32 [E][ceil(N/128)][ceil(K/128)]); the codes are packed here."""
+    d, E = w_router.shape
+    F = gate[0].shape[1]
+    return Fp8Weights(d=int(d), F=int(F), E=int(E), w_router=w_router, b_router=b_router,
+                      gate_codes=pack_fp8(gate[0]), gate_scales=gate[1],
+                      up_codes=pack_fp8(up[0]), up_scales=up[1],
+                      down_codes=pack_fp8(down[0]), down_scales=down[1],
+                      b_gate=b_gate, b_up=b_up, b_down=b_down)
+
+
+def fp8_from_mxfp4(w_router, b_router, gate_codes, gate_scales, up_codes, up_scales, down_codes,
+                   down_scales, b_gate, b_up, b_down) -> Fp8Weights:
+    """The same layer as load_expert_weights, converted once to FP8 with 128x128
+    block scales (moe_convert_mxfp4_to_fp8) and packed."""
+    return load_fp8_weights(w_router, b_router, convert_mxfp4_to_fp8(gate_codes, gate_scales),
+                            convert_mxfp4_to_fp8(up_codes, up_scales),
+                            convert_mxfp4_to_fp8(down_codes, down_scales), b_gate, b_up, b_down)
+
+
+def expert_ffn_fp8(x, sorted_pair, offsets, w: Fp8Weights, k: int, ws, y_sorted=None):
+    T, d = x.shape
+    dw, F, E = w.dims
+    if dw != d:
+        raise ValueError("x width does not match the router weight")
+    P = T * k
+    if y_sorted is None:
+        y_sorted = torch.empty((P, d), dtype=torch.float32, device=x.device)
+    u8, f32 = torch.uint8, torch.float32
+    gb, db = lib().moe_fp8_packed_bytes(E, F, d), lib().moe_fp8_packed_bytes(E, d, F)
+    mg = MXFP4(_dev(w.gate_codes, u8, (gb,), "gate_codes"),
+               _dev(w.gate_scales, f32, (E, _nb(F), _nb(d)), "gate_scales"))
+    mu = MXFP4(_dev(w.up_codes, u8, (gb,), "up_codes"),
+               _dev(w.up_scales, f32, (E, _nb(F), _nb(d)), "up_scales"))
+    md = MXFP4(_dev(w.down_codes, u8, (db,), "down_codes"),
+               _dev(w.down_scales, f32, (E, _nb(d), _nb(F)), "down_scales"))
+    _check(lib().moe_expert_ffn_fp8(
+        _dims(T, d, F, E, k), _dev(x, torch.bfloat16, (T, d), "x"),
+        _dev(sorted_pair, torch.int32, (P,), "sorted_pair"),
+        _dev(offsets, torch.int32, (E + 1,), "offsets"), mg, mu, md,
+        _dev(w.b_gate, torch.bfloat16, (E, F), "b_gate"),
+        _dev(w.b_up, torch.bfloat16, (E, F), "b_up"),
+        _dev(w.b_down, torch.bfloat16, (E, d), "b_down"),
+        _dev(y_sorted, torch.float32, (P, d), "y_sorted"),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream()), "moe_expert_ffn_fp8")
+    return y_sorted
+
+
+def round_weights_bf16(topk_w):
+    """moe_round_weights_bf16: the routing weights rounded to bf16 in place."""
+    T, k = topk_w.shape
+    _check(lib().moe_round_weights_bf16(T, k, _dev(topk_w, torch.float32, (T, k), "topk_w"), _stream()),
+           "moe_round_weights_bf16")
+    return topk_w
 
 
 def combine(y_sorted, pair_row, topk_w, out=None):

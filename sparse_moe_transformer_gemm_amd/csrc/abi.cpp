@@ -353,6 +353,57 @@ moe_status moe_forward_noalloc(moe_dims dims, const moe_bf16* x, const float* w_
                         ws, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_convert_mxfp4_to_fp8(int32_t E, int32_t N, int32_t K, moe_mxfp4 src,
+                                    uint8_t* codes_out, float* scales_out, void* stream) {
+  g_last_error[0] = 0;
+  if (!packable(E, N, K)) {
+    set_error("%s", "moe_convert_mxfp4_to_fp8: need 1 <= E <= 256 and N, K positive multiples of 64, <= 16384");
+    return MOE_ERR_INVALID_ARG;
+  }
+  MOE_TRY(check_ptrs({src.codes, src.scales, codes_out, scales_out}, "moe_convert_mxfp4_to_fp8"));
+  return hip_status(moe::launch_convert_mxfp4_to_fp8(src.codes, src.scales, E, N, K, codes_out,
+                                                     scales_out, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_fp8_packed_bytes(int32_t E, int32_t N, int32_t K) {
+  return packable(E, N, K) ? moe::fp8_packed_bytes(E, N, K) : 0;
+}
+
+moe_status moe_pack_fp8(int32_t E, int32_t N, int32_t K, const uint8_t* codes, uint8_t* packed_out,
+                        void* stream) {
+  g_last_error[0] = 0;
+  if (!packable(E, N, K)) {
+    set_error("%s", "moe_pack_fp8: need 1 <= E <= 256 and N, K positive multiples of 64, <= 16384");
+    return MOE_ERR_INVALID_ARG;
+  }
+  MOE_TRY(check_ptrs({codes, packed_out}, "moe_pack_fp8"));
+  return hip_status(moe::launch_pack_fp8(codes, E, N, K, packed_out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_ffn_fp8(moe_dims dims, const moe_bf16* x, const int32_t* sorted_pair,
+                              const int32_t* offsets, moe_fp8 w_gate, moe_fp8 w_up, moe_fp8 w_down,
+                              const moe_bf16* b_gate, const moe_bf16* b_up, const moe_bf16* b_down,
+                              float* y_sorted, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  moe::FfnArgs a;
+  const moe_mxfp4_packed g{w_gate.codes, reinterpret_cast<const uint8_t*>(w_gate.scales)};
+  const moe_mxfp4_packed u{w_up.codes, reinterpret_cast<const uint8_t*>(w_up.scales)};
+  const moe_mxfp4_packed dn{w_down.codes, reinterpret_cast<const uint8_t*>(w_down.scales)};
+  MOE_TRY(ffn_args(dims, x, sorted_pair, offsets, g, u, dn, b_gate, b_up, b_down, y_sorted, ws,
+                   ws_bytes, "moe_expert_ffn_fp8", a));
+  return hip_status(moe::launch_expert_ffn_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_round_weights_bf16(int32_t T, int32_t k, float* topk_w, void* stream) {
+  g_last_error[0] = 0;
+  if (T < 1 || k < 1 || k > 8 || T > kMaxT) {
+    set_error("%s", "moe_round_weights_bf16: need 1 <= T <= 65536, 1 <= k <= 8");
+    return MOE_ERR_INVALID_ARG;
+  }
+  MOE_TRY(check_ptrs({topk_w}, "moe_round_weights_bf16"));
+  return hip_status(moe::launch_round_bf16(topk_w, T * k, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_combine(moe_dims dims, const float* y_sorted, const int32_t* pair_row,
                        const float* topk_w, moe_bf16* out, void* stream) {
   g_last_error[0] = 0;

@@ -110,6 +110,17 @@ hipError_t launch_forward_front(const uint16_t* x, const float* w_router, const 
                                 int32_t* sorted_pair, int32_t* pair_row, void* ws,
                                 hipStream_t stream);
 
+// FP8-E4M3 expert weights with float32 128x128 block scales (fp8.hip). In FfnArgs
+// the w*_codes point at packed FP8 codes and the w*_scales at the float32 block
+// scales [E][ceil(N/128)][ceil(K/128)].
+size_t fp8_packed_bytes(int E, int N, int K);
+hipError_t launch_convert_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, int E, int N, int K,
+                                       uint8_t* out, float* bscale, hipStream_t stream);
+hipError_t launch_pack_fp8(const uint8_t* codes, int E, int N, int K, uint8_t* out, hipStream_t stream);
+hipError_t launch_expert_ffn_fp8(const FfnArgs& a, hipStream_t stream);
+// Round n float32 values to the nearest bf16 (ties to even), in place.
+hipError_t launch_round_bf16(float* w, int n, hipStream_t stream);
+
 // The allocation-free whole-block call's scratch: a device array of this many
 // bytes per GPU (noalloc.hip); *ptr receives its address on the current device.
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
