@@ -122,6 +122,7 @@ def parse():
     ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--workloads", default="1,0,2,3,4",
                     help="comma list; the first is the headline (default: decode-20b)")
+    ap.add_argument("--fp8", default="1,2", help="workloads also run with FP8 expert weights ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -300,6 +301,78 @@ def run_layer(cfg: int, steps: int, warmup: int, repeats: int, graph: bool, log)
     return res
 
 
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix throughput, published
+
+
+def fp8_expert_bytes(d: int, F: int) -> int:
+    """Algorithmic bytes of one expert in FP8: 3 matrices of 1 B per element, their
+    float32 128x128 block scales, and the bf16 biases."""
+    nb = lambda n: (n + 127) // 128
+    return 3 * d * F + 4 * 3 * nb(d) * nb(F) + 2 * (2 * F + d)
+
+
+def run_fp8(cfg: int, steps: int, warmup: int, repeats: int, log) -> dict:
+    """The same layer with its experts converted once to FP8 with 128x128 block
+    scales (moe_convert_mxfp4_to_fp8), run as the four calls moe_route,
+    moe_permute, moe_expert_ffn_fp8 and moe_combine."""
+    import torch
+
+    import sparse_moe_transformer_gemm_amd as moe
+
+    dev = "cuda:0"
+    w = synth.workload(cfg)
+    L = w.layers[0]
+    T, d, F, E, k = w.T, w.d, w.F, w.E, w.k
+    R = max(1, int(np.ceil(1.5e9 / (E * fp8_expert_bytes(d, F)))))
+    log(f"[bench] {w.name} fp8: T={T} d={d} F={F} E={E} k={k}; {R} weight copies")
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    copies = [moe.fp8_from_mxfp4(
+        w_router=u8(L.w_router), b_router=None if L.b_router is None else u8(L.b_router),
+        gate_codes=u8(L.gate.codes), gate_scales=u8(L.gate.scales), up_codes=u8(L.up.codes),
+        up_scales=u8(L.up.scales), down_codes=u8(L.down.codes), down_scales=u8(L.down.scales),
+        b_gate=bf16(L.b_gate), b_up=bf16(L.b_up), b_down=bf16(L.b_down)) for _ in range(R)]
+    x = bf16(w.x)
+    ws = torch.empty(moe.workspace_bytes(T, d, F, E, k), dtype=torch.uint8, device=dev)
+    b = moe._outputs(T, d, E, k, x.device, None)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def step(i):
+        wt = copies[i % R]
+        idx, tw = moe.route(x, wt.w_router, wt.b_router, k, ws, b["topk_idx"], b["topk_w"])
+        perm = moe.permute(idx, E, ws, b["perm"])
+        if i < steps:
+            ev[i][0].record()
+        y = moe.expert_ffn_fp8(x, perm[2], perm[1], wt, k, ws, b["y_sorted"])
+        if i < steps:
+            ev[i][1].record()
+        moe.combine(y, perm[3], tw, b["out"])
+
+    runs = timed_runs(step, steps, warmup, repeats)
+    ffn_ms = float(np.median([a.elapsed_time(c) for a, c in ev]))
+    ms = float(np.median(runs))
+    U = int((b["perm"][0].cpu().numpy() > 0).sum())
+    ffn_bytes = U * fp8_expert_bytes(d, F) + 2 * T * d
+    lay_bytes = ffn_bytes + 4 * d * E + 2 * T * d
+    flops = 2.0 * T * k * 3 * d * F
+    res = dict(workload=f"{w.name}-fp8", T=T, weight_copies=R, experts_touched=U, ms_per_step=ms,
+               ms_per_step_best=float(min(runs)), tokens_per_s=T / (ms / 1e3),
+               frac_hbm_peak=lay_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+               frac_fp8_peak=flops / (ms / 1e3) / 1e12 / FP8_PEAK_TFLOPS,
+               ffn_call=dict(avg_ms=ffn_ms, alg_bytes=ffn_bytes,
+                             gbs=ffn_bytes / (ffn_ms / 1e3) / 1e9,
+                             tflops=flops / (ffn_ms / 1e3) / 1e12),
+               note="four calls (route, permute, FP8 expert FFN, combine); weights converted once "
+                    "from the MXFP4 layer, exactly")
+    log(f"[bench] {w.name} fp8: {ms * 1e3:.1f} us/step, {res['tokens_per_s']:.4g} tok/s, "
+        f"{100 * res['frac_hbm_peak']:.1f}% HBM / {100 * res['frac_fp8_peak']:.1f}% FP8; "
+        f"ffn {ffn_ms * 1e3:.1f} us = {res['ffn_call']['gbs']:.0f} GB/s")
+    del copies, ws, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_stack(cfg: int, steps: int, warmup: int, repeats: int, log) -> dict:
     """The pre-norm stack workload: per step, every block does
     x <- x + MoE(RMSNorm(x)) through the C ABI, all layers' weights resident."""
@@ -439,6 +512,11 @@ def main():
             results[cfg] = run_layer(cfg, st, args.warmup, args.repeats, not args.no_graph, log)
             if cfg in (0, 1):
                 checks[cfg] = oracle_check(results[cfg], log)
+    fp8 = {}
+    for cfg in [int(c) for c in args.fp8.split(",") if c.strip()]:
+        big = synth.WORKLOADS[cfg]["T"] > 1024
+        r8 = run_fp8(cfg, max(20, args.steps // 5) if big else args.steps, args.warmup, args.repeats, log)
+        fp8[r8["workload"]] = r8
     head = results[order[0]]
     cpu = None
     if not args.no_cpu_baseline and "_workload" in head:
@@ -489,6 +567,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": {("tiny" if c == 0 else "decode-20b"): v for c, v in checks.items()},
         "workloads": {results[c]["workload"]: _public(results[c]) for c in order},
+        "fp8_weights": fp8,
         "clocks": {"before": clk0, "after": clk1},
     }
     print(json.dumps(line), flush=True)
