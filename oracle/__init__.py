@@ -27,7 +27,9 @@ scale per 32 consecutive elements).
 
 A second weight format, FP8-E4M3 with one float32 scale per 128x128 block
 (oracle/fp8.py), serves the same expert FFN (ffn_sorted_fp8); and routing
-weights may be rounded to bf16 before the combine (round_bf16).
+weights may be rounded to bf16 before the combine (round_bf16). The other
+kernel the pages build for gpt-oss, attention whose softmax includes a
+per-head sink logit, is in oracle/attention.py.
 
 Every function here is pinned by `-m "not gpu"` tests against closed forms, exact
 rational arithmetic, published format tables or invariants; none is "parity
@@ -35,6 +37,7 @@ unpinned".
 """
 from .mx import E2M1, E8M0, e2m1_value, e8m0_value, unpack_codes, dequant
 from .fp8 import E4M3, e4m3_value, dequant_fp8
+from .attention import visible, attention_sink, attention_sink_chunked
 from .moe import (
     bf16_to_f64, router_logits, topk_select, softmax_selected, route, permute,
     silu, swiglu, gate_up, down, expert_ffn, ffn_sorted, combine, moe_layer, dense_moe, rmsnorm,
@@ -44,6 +47,7 @@ from .moe import (
 __all__ = [
     "E2M1", "E8M0", "e2m1_value", "e8m0_value", "unpack_codes", "dequant",
     "E4M3", "e4m3_value", "dequant_fp8", "expert_ffn_fp8", "ffn_sorted_fp8", "round_bf16",
+    "visible", "attention_sink", "attention_sink_chunked",
     "bf16_to_f64", "router_logits", "topk_select", "softmax_selected", "route",
     "permute", "silu", "swiglu", "gate_up", "down", "expert_ffn", "ffn_sorted", "combine", "moe_layer",
     "dense_moe", "rmsnorm",

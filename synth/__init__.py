@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits", "MX4", "LayerParams", "Workload", "WORKLOADS", "draw_layer",
-    "workload", "stack_layer", "tiny_workload", "fp8_weights",
+    "workload", "stack_layer", "tiny_workload", "fp8_weights", "attention_inputs", "ATTN_WORKLOADS",
 ]
 
 
@@ -176,6 +176,27 @@ def fp8_weights(rng: np.random.Generator, E: int, N: int, K: int):
     v = rng.random((E, nb, kb))
     scales = (np.exp2(u) * (1.0 + v)).astype(np.float32)
     return codes.astype(np.uint8), scales
+
+
+def attention_inputs(seed: int, B: int, Tq: int, S: int, Hq: int, Hkv: int, D: int):
+    """Seeded inputs of one attention call: q [B][Tq][Hq][D], k and v [B][S][Hkv][D]
+    as bf16 bits, each element ~ N(0, 1); sinks [Hq] float32 ~ N(1, 1) (one per
+    query head). Drawn in that order from default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    q = bf16_bits(rng.standard_normal((B, Tq, Hq, D)))
+    k = bf16_bits(rng.standard_normal((B, S, Hkv, D)))
+    v = bf16_bits(rng.standard_normal((B, S, Hkv, D)))
+    sinks = (1.0 + rng.standard_normal(Hq)).astype(np.float32)
+    return q, k, v, sinks
+
+
+# Attention workloads of the gpt-oss-20b shape (64 query heads, 8 KV heads,
+# head size 64): an 8192-token prefill (causal; the full-attention layers) and
+# a decode step of 16 sequences against 8192-token KV caches.
+ATTN_WORKLOADS = {
+    "attn-prefill": dict(B=1, Tq=8192, S=8192, Hq=64, Hkv=8, D=64, window=0, seed=80),
+    "attn-decode": dict(B=16, Tq=1, S=8192, Hq=64, Hkv=8, D=64, window=0, seed=81),
+}
 
 
 def tiny_workload(T: int, d: int, F: int, E: int, k: int, seed: int, zipf: bool = False,

@@ -587,4 +587,92 @@ def pin_round_bf16():
     assert np.array_equal(om.round_bf16(w), want)
 
 
+# ------------------------------------------------------------------ attention with sinks
+
+import oracle.attention as oat  # noqa: E402
+
+
+def _attn_inputs(seed, B, Tq, S, Hq, Hkv, D):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Tq, Hq, D))
+    k = rng.standard_normal((B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    s = rng.standard_normal(Hq)
+    return q, k, v, s
+
+
+def pin_attention_without_sink_is_sdpa():
+    """A sink of -inf takes no part: the result is torch's scaled dot-product
+    attention (float64, CPU) with the same causal and sliding-window mask and the
+    KV heads repeated for grouped queries."""
+    import torch
+    q, k, v, _ = _attn_inputs(70, 2, 6, 11, 4, 2, 8)
+    for window in (0, 4):
+        got = oat.attention_sink(q, k, v, np.full(4, -np.inf), 0.35, window)
+        mask = torch.from_numpy(oat.visible(6, 11, window))
+        for b in range(2):
+            Q = torch.from_numpy(q[b]).permute(1, 0, 2)            # [H][Tq][D]
+            K = torch.from_numpy(k[b]).permute(1, 0, 2).repeat_interleave(2, dim=0)
+            V = torch.from_numpy(v[b]).permute(1, 0, 2).repeat_interleave(2, dim=0)
+            want = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=0.35)
+            assert np.allclose(got[b], want.permute(1, 0, 2).numpy(), rtol=0, atol=1e-13)
+
+
+def pin_attention_single_key():
+    """One visible key: out = v * sigmoid(z - s), z = scale <q, k> (a two-way
+    softmax with the sink); a window of 1 reduces every query to that case."""
+    q, k, v, s = _attn_inputs(71, 1, 3, 3, 2, 1, 4)
+    out = oat.attention_sink(q, k, v, s, 0.5, window=1)
+    for i in range(3):
+        for h in range(2):
+            z = 0.5 * float(q[0, i, h] @ k[0, i, 0])
+            assert np.allclose(out[0, i, h], v[0, i, 0] / (1 + math.exp(s[h] - z)), rtol=1e-14, atol=0)
+
+
+def pin_attention_brute_force():
+    """Every output element against a plain loop over keys with math.exp, on a
+    ragged shape (Tq < S, grouped heads, a window)."""
+    q, k, v, s = _attn_inputs(72, 1, 3, 7, 4, 2, 3)
+    out = oat.attention_sink(q, k, v, s, 0.7, window=5)
+    for i in range(3):
+        pos = 7 - 3 + i
+        for h in range(4):
+            g = h // 2
+            keys = [j for j in range(7) if j <= pos and j > pos - 5]
+            w = [math.exp(0.7 * sum(q[0, i, h, c] * k[0, j, g, c] for c in range(3))) for j in keys]
+            den = math.exp(s[h]) + sum(w)
+            for c in range(3):
+                want = sum(wj * v[0, j, g, c] for wj, j in zip(w, keys)) / den
+                assert abs(out[0, i, h, c] - want) <= 1e-13 * (1 + abs(want))
+
+
+def pin_attention_chunks_take_the_sink_once():
+    """The split-KV form (online-softmax partials merged in chunk order, the sink
+    in the first chunk only) equals the direct form; counting the sink in every
+    chunk instead does not."""
+    q, k, v, s = _attn_inputs(73, 2, 4, 13, 4, 1, 8)
+    direct = oat.attention_sink(q, k, v, s, 0.3, 0)
+    for chunk in (1, 4, 5, 13):
+        assert np.allclose(oat.attention_sink_chunked(q, k, v, s, 0.3, 0, chunk), direct, rtol=1e-12, atol=1e-14)
+    # the sink counted once per chunk: a larger denominator, outputs shrink
+    K = 13
+    twice = oat.attention_sink(q, k, v, s + math.log(math.ceil(K / 4)), 0.3, 0)
+    assert not np.allclose(twice, direct)
+
+
+def pin_attention_sink_limits():
+    """A very large sink absorbs the softmax (outputs -> 0); the output is a
+    convex combination of the visible values scaled by 1 - p_sink."""
+    q, k, v, s = _attn_inputs(74, 1, 4, 6, 2, 2, 4)
+    big = oat.attention_sink(q, k, v, np.full(2, 80.0), 0.2, 0)
+    assert np.abs(big).max() < 1e-20
+    out = oat.attention_sink(q, k, v, s, 0.2, 0)
+    for i in range(4):
+        pos = 6 - 4 + i
+        for h in range(2):
+            vis = v[0, :pos + 1, h, :]
+            assert np.all(out[0, i, h] <= np.maximum(vis.max(axis=0), 0) + 1e-12)
+            assert np.all(out[0, i, h] >= np.minimum(vis.min(axis=0), 0) - 1e-12)
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

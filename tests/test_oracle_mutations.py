@@ -150,7 +150,50 @@ def _round_bf16_truncate(w):
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+import oracle.attention as oat  # noqa: E402
+
+_orig_visible = oat.visible
+_orig_attn = oat.attention_sink
+
+
+def _visible_strict(Tq, S, window=0):
+    m = _orig_visible(Tq, S, window)
+    qpos = S - Tq + np.arange(Tq)[:, None]
+    return m & (np.arange(S)[None, :] < qpos)   # wrong: a query does not see its own key
+
+
+def _attn_no_sink(q, k, v, sinks, scale, window=0):
+    return _orig_attn(q, k, v, np.full(len(sinks), -np.inf), scale, window)
+
+
+def _attn_gqa_modulo(q, k, v, sinks, scale, window=0):
+    q = np.asarray(q, np.float64)
+    Hq, Hkv = q.shape[2], np.asarray(k).shape[2]
+    # wrong: query head h reads KV head h % Hkv instead of h // (Hq / Hkv)
+    order = [h % Hkv for h in range(Hq)]
+    kk = np.asarray(k, np.float64)[:, :, order, :]
+    vv = np.asarray(v, np.float64)[:, :, order, :]
+    return _orig_attn(q, kk, vv, sinks, scale, window)
+
+
+def _attn_sink_in_numerator(q, k, v, sinks, scale, window=0):
+    # wrong: the sink also carries a value (the mean of the visible values)
+    out = _orig_attn(q, k, v, sinks, scale, window)
+    return out + 0.01
+
+
+def _chunked_sink_every_chunk(q, k, v, sinks, scale, window, chunk):
+    S = np.asarray(k).shape[1]
+    n = -(-S // chunk)
+    return _orig_attn(q, k, v, np.asarray(sinks) + np.log(n), scale, window)
+
+
 MUTATIONS = {
+    "attention_mask_excludes_own_key": (oat, "visible", _visible_strict),
+    "attention_sink_dropped": (oat, "attention_sink", _attn_no_sink),
+    "attention_gqa_modulo_heads": (oat, "attention_sink", _attn_gqa_modulo),
+    "attention_sink_with_value": (oat, "attention_sink", _attn_sink_in_numerator),
+    "attention_sink_in_every_chunk": (oat, "attention_sink_chunked", _chunked_sink_every_chunk),
     "e4m3_bias_8": (of8, "e4m3_value", _e4m3_bias8),
     "e4m3_table_bias_8": (of8, "E4M3", np.array([_e4m3_bias8(c) for c in range(256)])),
     "fp8_block_scales_transposed": (of8, "dequant_fp8", _dequant_fp8_blocks_transposed),
