@@ -123,6 +123,8 @@ def parse():
     ap.add_argument("--workloads", default="1,0,2,3,4",
                     help="comma list; the first is the headline (default: decode-20b)")
     ap.add_argument("--fp8", default="1,2", help="workloads also run with FP8 expert weights ('' for none)")
+    ap.add_argument("--attention", default="attn-decode,attn-prefill",
+                    help="attention-with-sinks workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -302,6 +304,7 @@ def run_layer(cfg: int, steps: int, warmup: int, repeats: int, graph: bool, log)
 
 
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix throughput, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix throughput, published
 
 
 def fp8_expert_bytes(d: int, F: int) -> int:
@@ -369,6 +372,70 @@ def run_fp8(cfg: int, steps: int, warmup: int, repeats: int, log) -> dict:
         f"{100 * res['frac_hbm_peak']:.1f}% HBM / {100 * res['frac_fp8_peak']:.1f}% FP8; "
         f"ffn {ffn_ms * 1e3:.1f} us = {res['ffn_call']['gbs']:.0f} GB/s")
     del copies, ws, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def attention_alg(B, Tq, S, Hq, Hkv, D, window) -> tuple:
+    """(flops, bytes) of one attention call: 4 D flops per visible (query, key)
+    pair (the score and the value product); K and V read once, q read and out
+    written once, in bf16."""
+    qpos = np.arange(Tq) + (S - Tq)
+    lo = np.zeros(Tq, np.int64) if window <= 0 else np.maximum(qpos - window + 1, 0)
+    pairs = int((qpos - lo + 1).sum())
+    flops = 4.0 * D * pairs * B * Hq
+    byts = 2 * B * S * Hkv * D * 2 + 2 * B * Tq * Hq * D * 2
+    return flops, byts
+
+
+def run_attention(name: str, steps: int, warmup: int, repeats: int, log) -> dict:
+    """moe_attention_sink on a gpt-oss-20b-shaped attention (64 query heads over
+    8 KV heads of size 64, per-head sinks): a causal prefill (bound by the bf16
+    matrix cores) or batched decode against long caches (bound by HBM; the caches
+    rotate over copies larger than the last-level cache)."""
+    import torch
+
+    import sparse_moe_transformer_gemm_amd as moe
+
+    dev = "cuda:0"
+    c = synth.ATTN_WORKLOADS[name]
+    B, Tq, S, Hq, Hkv, D, win = c["B"], c["Tq"], c["S"], c["Hq"], c["Hkv"], c["D"], c["window"]
+    q, k, v, sk = synth.attention_inputs(c["seed"], B, Tq, S, Hq, Hkv, D)
+    bf = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    flops, byts = attention_alg(B, Tq, S, Hq, Hkv, D, win)
+    decode = Tq <= 64
+    R = max(1, int(np.ceil(1.5e9 / byts))) if decode else 1
+    qd, sd = bf(q), torch.from_numpy(sk).to(dev)
+    kv = [(bf(k), bf(v)) for _ in range(R)]
+    out = torch.empty_like(qd)
+    n = moe.attention_workspace_bytes(B, Tq, S, Hq, Hkv, D, win)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    log(f"[bench] {name}: B={B} Tq={Tq} S={S} Hq={Hq} Hkv={Hkv} D={D}; {R} cache copies; "
+        f"workspace {n} B")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def step(i):
+        kk, vv = kv[i % R]
+        if i < steps:
+            ev[i][0].record()
+        moe.attention_sink(qd, kk, vv, sd, 0.125, win, out, ws)
+        if i < steps:
+            ev[i][1].record()
+
+    runs = timed_runs(step, steps, warmup, repeats)
+    call_ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    ms = float(np.median(runs))
+    res = dict(workload=name, B=B, Tq=Tq, S=S, Hq=Hq, Hkv=Hkv, D=D, window=win, cache_copies=R,
+               ms_per_call=ms, ms_per_call_best=float(min(runs)), call_event_ms=call_ms,
+               alg_flops=flops, alg_bytes=byts,
+               tflops=flops / (ms / 1e3) / 1e12, gbs=byts / (ms / 1e3) / 1e9)
+    if decode:
+        res.update(bound="hbm", frac=res["gbs"] / HBM_PEAK_GBS)
+    else:
+        res.update(bound="mfma", frac=res["tflops"] / BF16_PEAK_TFLOPS)
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/call, {res['tflops']:.1f} TFLOP/s, {res['gbs']:.0f} GB/s "
+        f"({100 * res['frac']:.1f}% of the {res['bound']} peak)")
+    del kv, ws, out
     torch.cuda.empty_cache()
     return res
 
@@ -517,6 +584,11 @@ def main():
         big = synth.WORKLOADS[cfg]["T"] > 1024
         r8 = run_fp8(cfg, max(20, args.steps // 5) if big else args.steps, args.warmup, args.repeats, log)
         fp8[r8["workload"]] = r8
+    attn = {}
+    for name in [a.strip() for a in args.attention.split(",") if a.strip()]:
+        big = synth.ATTN_WORKLOADS[name]["Tq"] > 64
+        attn[name] = run_attention(name, max(10, args.steps // 10) if big else args.steps,
+                                   max(2, args.warmup // 2) if big else args.warmup, args.repeats, log)
     head = results[order[0]]
     cpu = None
     if not args.no_cpu_baseline and "_workload" in head:
@@ -568,6 +640,7 @@ def main():
         "parity": {("tiny" if c == 0 else "decode-20b"): v for c, v in checks.items()},
         "workloads": {results[c]["workload"]: _public(results[c]) for c in order},
         "fp8_weights": fp8,
+        "attention_sink": attn,
         "clocks": {"before": clk0, "after": clk1},
     }
     print(json.dumps(line), flush=True)

@@ -295,6 +295,40 @@ moe_status moe_expert_ffn_fp8(moe_dims dims, const moe_bf16* x, const int32_t* s
  * nearest bf16 value (ties to even), still stored as fp32, for moe_combine. */
 moe_status moe_round_weights_bf16(int32_t T, int32_t k, float* topk_w, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Attention with per-head sinks, the other kernel the pages build for gpt-oss
+ * ("GPT-OSS el dia 0", section "Atenció: GQA amb Attention Sinks": every head
+ * has a pretrained sink that takes part in the softmax; section "Nuclis per a
+ * GPT-OSS / Atenció de buidatge": an online softmax starts its running maximum
+ * at the sink, in the first KV chunk only). For query q of head h:
+ *   out = sum_j exp(z_j) v_j / (exp(sinks[h]) + sum_j exp(z_j)),  z_j = scale * <q, k_j>,
+ * over the keys j the query sees, with KV head h / (Hq / Hkv) (grouped queries).
+ * Queries are the last Tq of the S positions (query i at position S - Tq + i) and
+ * see keys j <= their position; with window > 0 only keys j > position - window. */
+typedef struct {
+  int32_t B;       /* batch entries (sequences) */
+  int32_t Tq;      /* queries per entry, 1 <= Tq <= S */
+  int32_t S;       /* keys per entry */
+  int32_t Hq, Hkv; /* query and KV heads; Hq a multiple of Hkv, Hq / Hkv <= 8 */
+  int32_t D;       /* head size: 64 */
+  int32_t window;  /* sliding window, 0 for none */
+} moe_attn_dims;
+
+/* Workspace bytes of moe_attention_sink (0 when it needs none; also 0 for dims
+ * it does not support, which moe_attention_sink rejects). */
+size_t moe_attention_workspace_bytes(moe_attn_dims dims);
+
+/*   q      [device] bf16 [B][Tq][Hq][D];  k, v [device] bf16 [B][S][Hkv][D]
+ *   sinks  [device] fp32 [Hq] (in logit units)
+ *   scale  softmax scale (1/sqrt(D) for gpt-oss)
+ *   out    [device] bf16 [B][Tq][Hq][D]
+ * fp32 accumulation; the probabilities enter the P V product as bf16. When the
+ * keys are split into chunks (few queries), each chunk's partial softmax is kept
+ * in the workspace and merged in chunk order (deterministic). */
+moe_status moe_attention_sink(moe_attn_dims dims, const moe_bf16* q, const moe_bf16* k,
+                              const moe_bf16* v, const float* sinks, float scale, moe_bf16* out,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* moe_forward without a workspace, for callers that cannot allocate device
  * memory (code under graph capture, tight serving loops, harnesses that forbid
  * allocation). Same arguments, checks, launches and output bytes as

@@ -23,7 +23,7 @@ __all__ = [
     "ExpertWeights", "EXPORTED", "pack_mxfp4", "packed_bytes", "load_expert_weights",
     "forward_calls", "expert_ffn_mxfp4_stage", "forward_noalloc", "Fp8Weights",
     "convert_mxfp4_to_fp8", "pack_fp8", "load_fp8_weights", "fp8_from_mxfp4", "expert_ffn_fp8",
-    "round_weights_bf16",
+    "round_weights_bf16", "AttnDims", "attention_workspace_bytes", "attention_sink",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +34,7 @@ EXPORTED = (
     "moe_mxfp4_packed_bytes", "moe_pack_mxfp4", "moe_forward", "moe_expert_ffn_mxfp4_stage",
     "moe_forward_noalloc", "moe_forward_noalloc_max_bytes",
     "moe_convert_mxfp4_to_fp8", "moe_fp8_packed_bytes", "moe_pack_fp8", "moe_expert_ffn_fp8",
-    "moe_round_weights_bf16",
+    "moe_round_weights_bf16", "moe_attention_workspace_bytes", "moe_attention_sink",
 )
 
 
@@ -45,6 +45,12 @@ class MoeError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("F", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32)]
+
+
+class AttnDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 class MXFP4(ctypes.Structure):
@@ -90,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.moe_pack_fp8.argtypes = [i32, i32, i32, vp, vp, vp]
     L.moe_expert_ffn_fp8.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp, vp, sz, vp]
     L.moe_round_weights_bf16.argtypes = [i32, i32, vp, vp]
+    L.moe_attention_workspace_bytes.argtypes = [AttnDims]
+    L.moe_attention_workspace_bytes.restype = sz
+    L.moe_attention_sink.argtypes = [AttnDims, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     L.moe_mxfp4_packed_bytes.argtypes = [i32, i32, i32, i32]
     L.moe_mxfp4_packed_bytes.restype = sz
     L.moe_pack_mxfp4.argtypes = [i32, i32, i32, MXFP4, vp, vp, vp]
@@ -98,7 +107,8 @@ def lib() -> ctypes.CDLL:
     for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_expert_ffn_mxfp4_stage",
               "moe_combine", "moe_rmsnorm",
               "moe_residual_add", "moe_pack_mxfp4", "moe_forward", "moe_forward_noalloc",
-              "moe_convert_mxfp4_to_fp8", "moe_pack_fp8", "moe_expert_ffn_fp8", "moe_round_weights_bf16"):
+              "moe_convert_mxfp4_to_fp8", "moe_pack_fp8", "moe_expert_ffn_fp8", "moe_round_weights_bf16",
+              "moe_attention_sink"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -412,6 +422,32 @@ def round_weights_bf16(topk_w):
     _check(lib().moe_round_weights_bf16(T, k, _dev(topk_w, torch.float32, (T, k), "topk_w"), _stream()),
            "moe_round_weights_bf16")
     return topk_w
+
+
+# --------------------------------------------------------------------------- attention
+
+def attention_workspace_bytes(B, Tq, S, Hq, Hkv, D=64, window=0) -> int:
+    return lib().moe_attention_workspace_bytes(AttnDims(B, Tq, S, Hq, Hkv, D, window))
+
+
+def attention_sink(q, k, v, sinks, scale: float, window: int = 0, out=None, ws=None):
+    """moe_attention_sink: q [B][Tq][Hq][D], k and v [B][S][Hkv][D] (bf16), sinks
+    [Hq] (fp32) -> out [B][Tq][Hq][D] bf16."""
+    B, Tq, Hq, D = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    dims = AttnDims(B, Tq, S, Hq, Hkv, D, window)
+    if out is None:
+        out = torch.empty_like(q)
+    n = lib().moe_attention_workspace_bytes(dims)
+    if ws is None and n:
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(lib().moe_attention_sink(
+        dims, _dev(q, torch.bfloat16, (B, Tq, Hq, D), "q"), _dev(k, torch.bfloat16, (B, S, Hkv, D), "k"),
+        _dev(v, torch.bfloat16, (B, S, Hkv, D), "v"), _dev(sinks, torch.float32, (Hq,), "sinks"),
+        float(scale), _dev(out, torch.bfloat16, (B, Tq, Hq, D), "out"),
+        None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream()), "moe_attention_sink")
+    return out
 
 
 def combine(y_sorted, pair_row, topk_w, out=None):

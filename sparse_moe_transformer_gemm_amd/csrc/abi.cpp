@@ -404,6 +404,53 @@ moe_status moe_round_weights_bf16(int32_t T, int32_t k, float* topk_w, void* str
   return hip_status(moe::launch_round_bf16(topk_w, T * k, static_cast<hipStream_t>(stream)));
 }
 
+static moe_status check_attn(const moe_attn_dims& m) {
+  if (m.B < 1 || m.Tq < 1 || m.S < 1 || m.Tq > m.S || m.Hq < 1 || m.Hkv < 1 || m.window < 0) {
+    set_error("%s", "attention dims: need B, Tq, S, Hq, Hkv >= 1, Tq <= S, window >= 0");
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (m.Hq % m.Hkv) {
+    set_error("%s", "attention dims: Hq must be a multiple of Hkv");
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (m.D != 64 || m.Hq / m.Hkv > 8 || (size_t)m.B * m.S > ((size_t)1 << 26) || m.Hq > 1024) {
+    set_error("%s", "attention dims: supported D = 64, Hq / Hkv <= 8, B * S <= 2^26, Hq <= 1024");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+size_t moe_attention_workspace_bytes(moe_attn_dims dims) {
+  if (check_attn(dims) != MOE_OK) return 0;
+  return moe::attention_workspace_bytes(dims.B, dims.Tq, dims.S, dims.Hq, dims.Hkv);
+}
+
+moe_status moe_attention_sink(moe_attn_dims dims, const moe_bf16* q, const moe_bf16* k,
+                              const moe_bf16* v, const float* sinks, float scale, moe_bf16* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  MOE_TRY(check_attn(dims));
+  MOE_TRY(check_ptrs({q, k, v, sinks, out}, "moe_attention_sink"));
+  if (!(scale > 0.0f)) {
+    set_error("%s", "moe_attention_sink: scale must be positive");
+    return MOE_ERR_INVALID_ARG;
+  }
+  const size_t need = moe::attention_workspace_bytes(dims.B, dims.Tq, dims.S, dims.Hq, dims.Hkv);
+  if (need) {
+    if (!ws || !aligned16(ws)) {
+      set_error("%s", "workspace pointer null or not 16-byte aligned");
+      return MOE_ERR_INVALID_ARG;
+    }
+    if (ws_bytes < need) {
+      set_error("%s", "workspace smaller than moe_attention_workspace_bytes(dims)");
+      return MOE_ERR_WORKSPACE;
+    }
+  }
+  return hip_status(moe::launch_attention_sink(q, k, v, sinks, dims.B, dims.Tq, dims.S, dims.Hq,
+                                               dims.Hkv, dims.window, scale, out, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_combine(moe_dims dims, const float* y_sorted, const int32_t* pair_row,
                        const float* topk_w, moe_bf16* out, void* stream) {
   g_last_error[0] = 0;

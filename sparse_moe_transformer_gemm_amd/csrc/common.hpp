@@ -121,6 +121,13 @@ hipError_t launch_expert_ffn_fp8(const FfnArgs& a, hipStream_t stream);
 // Round n float32 values to the nearest bf16 (ties to even), in place.
 hipError_t launch_round_bf16(float* w, int n, hipStream_t stream);
 
+// Attention with per-head sinks (attention.hip): head size 64, Hq / Hkv <= 8.
+size_t attention_workspace_bytes(int B, int Tq, int S, int Hq, int Hkv);
+hipError_t launch_attention_sink(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const float* sinks, int B, int Tq, int S, int Hq, int Hkv,
+                                 int window, float scale, uint16_t* out, void* ws,
+                                 hipStream_t stream);
+
 // The allocation-free whole-block call's scratch: a device array of this many
 // bytes per GPU (noalloc.hip); *ptr receives its address on the current device.
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;

@@ -9,6 +9,20 @@ Tolerance on bf16 outputs (ref is the unrounded float64 oracle value):
     literal figure is reported beside it.
   * mean relative error: sum|out - ref| / sum|ref| <= 5e-3.
 RMS is over every element of the checked tensor.
+
+Attention outputs (assert_attention_close) carry a per-element bound instead of
+the RMS-relative one, because their magnitudes span orders of magnitude along a
+causal sequence (an early query averages a few values, a late one thousands).
+The kernel rounds each probability to bf16 (relative error <= 2^-9) before the
+probability-times-value product and sums the row total from the unrounded fp32
+probabilities, so out = sum_j p~_j v_j / l with |p~_j - p_j| <= 2^-9 p_j, and
+
+    |out - ref| <= half_ulp_bf16(out) + 2^-9 * sum_j p_j |v_j| / l + (fp32 terms).
+
+The gate is that bound with the 2^-9 term doubled (the fp32 score, exponential
+and accumulation errors are near 2^-20 of the same sum), where
+sum_j p_j |v_j| / l is the oracle's attention with |v| as the values; the mean
+relative error bar above applies as well.
 """
 from __future__ import annotations
 
@@ -49,3 +63,17 @@ def assert_close(out, ref, what: str = "", bf16_out: bool = True) -> dict:
 
 def bf16_out_to_f64(bits) -> np.ndarray:
     return bf16_to_f64(np.asarray(bits, np.uint16))
+
+
+def assert_attention_close(out, ref, abs_ref, what: str = "") -> dict:
+    """out: bf16 results as float64; ref: the oracle's attention; abs_ref: the
+    oracle's attention of the same queries and keys with |v| as the values."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    m = error_metrics(out, ref)
+    err = np.abs(out - ref)
+    bound = half_ulp_bf16(np.maximum(np.abs(out), np.abs(ref))) + 2.0 ** -8 * np.asarray(abs_ref, np.float64)
+    ratio = err / bound
+    m["bound_ratio"] = float(ratio.max()) if err.size else 0.0
+    assert m["bound_ratio"] <= 1.0 and m["mean_rel"] <= MEAN_REL_TOL, (what, m)
+    return m
