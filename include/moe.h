@@ -307,7 +307,7 @@ moe_status moe_round_weights_bf16(int32_t T, int32_t k, float* topk_w, void* str
  * see keys j <= their position; with window > 0 only keys j > position - window. */
 typedef struct {
   int32_t B;       /* batch entries (sequences) */
-  int32_t Tq;      /* queries per entry, 1 <= Tq <= S */
+  int32_t Tq;      /* queries per entry, 1 <= Tq <= S, Tq <= 2^20 */
   int32_t S;       /* keys per entry */
   int32_t Hq, Hkv; /* query and KV heads; Hq a multiple of Hkv, Hq / Hkv <= 8 */
   int32_t D;       /* head size: 64 */

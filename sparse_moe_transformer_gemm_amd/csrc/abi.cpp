@@ -413,8 +413,10 @@ static moe_status check_attn(const moe_attn_dims& m) {
     set_error("%s", "attention dims: Hq must be a multiple of Hkv");
     return MOE_ERR_INVALID_ARG;
   }
-  if (m.D != 64 || m.Hq / m.Hkv > 8 || (size_t)m.B * m.S > ((size_t)1 << 26) || m.Hq > 1024) {
-    set_error("%s", "attention dims: supported D = 64, Hq / Hkv <= 8, B * S <= 2^26, Hq <= 1024");
+  if (m.D != 64 || m.Hq / m.Hkv > 8 || (size_t)m.B * m.S > ((size_t)1 << 26) || m.Hq > 1024 ||
+      m.Tq > (1 << 20)) {
+    set_error("%s", "attention dims: supported D = 64, Hq / Hkv <= 8, B * S <= 2^26, Hq <= 1024, "
+                    "Tq <= 2^20");
     return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;
@@ -422,7 +424,7 @@ static moe_status check_attn(const moe_attn_dims& m) {
 
 size_t moe_attention_workspace_bytes(moe_attn_dims dims) {
   if (check_attn(dims) != MOE_OK) return 0;
-  return moe::attention_workspace_bytes(dims.B, dims.Tq, dims.S, dims.Hq, dims.Hkv);
+  return moe::attention_workspace_bytes(dims.B, dims.Tq, dims.S, dims.Hq, dims.Hkv, dims.window);
 }
 
 moe_status moe_attention_sink(moe_attn_dims dims, const moe_bf16* q, const moe_bf16* k,
@@ -435,7 +437,7 @@ moe_status moe_attention_sink(moe_attn_dims dims, const moe_bf16* q, const moe_b
     set_error("%s", "moe_attention_sink: scale must be positive");
     return MOE_ERR_INVALID_ARG;
   }
-  const size_t need = moe::attention_workspace_bytes(dims.B, dims.Tq, dims.S, dims.Hq, dims.Hkv);
+  const size_t need = moe::attention_workspace_bytes(dims.B, dims.Tq, dims.S, dims.Hq, dims.Hkv, dims.window);
   if (need) {
     if (!ws || !aligned16(ws)) {
       set_error("%s", "workspace pointer null or not 16-byte aligned");

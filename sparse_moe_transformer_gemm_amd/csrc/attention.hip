@@ -9,22 +9,36 @@
 // over the keys the query sees (causal; optionally a sliding window), with
 // grouped KV heads (query head h reads KV head h / (Hq / Hkv)).
 //
-// attn_fwd, in the style of FlashAttention-2 on gfx950's bf16 matrix cores. A
-// workgroup takes 32 consecutive queries of one batch entry and one KV head,
-// with one wavefront per query head of the group (up to 8; they share every K/V tile,
-// which is staged once in LDS), and one chunk of the keys. Per 32-key tile a
-// wavefront computes S^T = K Q^T (32 keys x 32 queries, four 32x32x16 bf16
-// MFMAs over the head size 64), so each lane holds one query's 16 keys and a
-// query's running max and sum need one cross-half shuffle; then the online
-// softmax update (in base 2, log2(e) folded into the scale) and O^T += V^T P^T,
-// P^T taken from the S^T accumulators as bf16. In the accumulator a lane l
-// holds query l%32 and keys 8(i/4) + 4(l/32) + i%4 (i = 0..15); the matrix
-// instruction pairs element t of A's lane half with element t of B's, so the
-// V^T operand of MFMA c (keys 16c .. 16c+15) lists, for lane half h, the keys
-// its P^T registers 8c .. 8c+7 hold: 16c + 8(t/4) + 4h + t%4.
-// A single chunk normalises and stores bf16 output; several chunks store the
-// partial (running max, denominator, unnormalised output) and attn_merge adds
-// them in chunk order.
+// Both kernels work on 32-key tiles with gfx950's bf16 matrix cores. A
+// wavefront holds 32 query slots; per tile it computes S^T = K Q^T (32 keys x
+// 32 slots, four 32x32x16 bf16 MFMAs over the head size 64), so each lane holds
+// one slot's 16 keys and a slot's running max and sum need one cross-half
+// shuffle; then the online softmax update (base 2, log2(e) folded into the
+// scale) and O^T += V^T P^T with P^T taken from the S^T accumulators as bf16.
+// In the accumulator a lane l holds slot l%32 and keys 8(i/4) + 4(l/32) + i%4
+// (i = 0..15); the matrix instruction pairs element t of A's lane half with
+// element t of B's, so the V^T operand of MFMA c (keys 16c .. 16c+15) lists,
+// for lane half h, the keys its P^T registers 8c .. 8c+7 hold:
+// 16c + 8(t/4) + 4h + t%4.
+//
+// The running maximum is raised only when a tile's maximum exceeds it by more
+// than 8 (base 2): probabilities then stay below 2^8, and the 32 output
+// rescales per lane and tile are skipped on most tiles. The result is the same
+// quantity (numerator and denominator share the stale maximum), rounded
+// differently.
+//
+// attn_fwd (many queries, FlashAttention-2 style): a workgroup takes 32
+// consecutive queries of one batch entry and KV head, one wavefront per query
+// head of the group (up to 8), all sharing each K/V tile staged once in LDS
+// (double-buffered, one barrier per tile); slot = query.
+// attn_dec (few queries: G * Tq <= 32 for G = Hq / Hkv): one wavefront packs
+// the G heads x Tq queries of a KV head into its 32 slots; the 4 wavefronts of
+// a workgroup take interleaved tiles of the workgroup's keys, loading K rows
+// straight into MFMA operand registers (the tile after next in flight) and V
+// through a per-wavefront LDS transpose, and merge their partials in wave order.
+// A single chunk of keys normalises and stores bf16 output; several chunks
+// store partials (running max, denominator, unnormalised output) that
+// attn_merge adds in chunk order.
 #include "common.hpp"
 
 namespace moe {
@@ -33,17 +47,26 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f_a __attribute__((ext_vector_type(16)));
 
-constexpr int kHD = 64;      // head size
-constexpr int kQB = 32;      // queries per workgroup
-constexpr int kKT = 32;      // keys per tile
+constexpr int kHD = 64;             // head size
+constexpr int kQB = 32;             // query slots per wavefront
+constexpr int kKT = 32;             // keys per tile
+constexpr int kKS = 72;             // K tile row stride in LDS (halves): 144 B, conflict-free 16 B reads
+constexpr int kVS = 36;             // V^T tile row stride in LDS (halves): 72 B
+constexpr int kKTile = kKT * kKS;   // halves
+constexpr int kVTile = kHD * kVS;   // halves
+constexpr int kBuf = kKTile + kVTile;
+constexpr int kDW = 4;              // wavefronts per attn_dec workgroup
+constexpr int kPS = 68;             // partial record (floats): m, l, 2 unused, o[64]
+constexpr int kPO = 4;              // offset of o in the record
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTau = 8.0f;        // lazy-rescale threshold (base 2)
 
 struct AttnArgs {
   const uint16_t *q, *k, *v;
   const float* sinks;
   uint16_t* out;
-  float* part;          // [B][Tq][Hq][nchunks][2 + 64] when nchunks > 1
-  int B, Tq, S, Hq, Hkv, window, nchunks, chunk;
+  float* part;          // [B][Tq][Hq][nchunks][kPS] when nchunks > 1
+  int B, Tq, S, Hq, Hkv, window, nchunks, chunk, kofs;   // chunk c: keys kofs + [c chunk, (c+1) chunk)
   float scale;
 };
 
@@ -56,12 +79,101 @@ __device__ __forceinline__ v8bf as_bf(uint4 u) {
   return c.b;
 }
 
+// orders LDS accesses of different lanes of one wavefront (no workgroup barrier)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One tile of the online softmax for a lane's slot. s: this lane's 16 raw
+// scores, -inf where the key is invisible. On return pf holds the bf16 P^T
+// operands 2^(sc2 s - m) (0 where invisible); m, l, o0, o1 are updated.
+__device__ __forceinline__ void softmax_tile(v16f_a& s, float& m, float& l, v16f_a& o0, v16f_a& o1,
+                                             float sc2, v8bf (&pf)[2]) {
+  float tmax = s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sc2;   // sc2 > 0: the max of the scaled scores
+  if (__builtin_amdgcn_ballot_w64(tmax > m + kTau)) {
+    const float mn = fmaxf(m, tmax);
+    const float alpha = m == mn ? 1.0f : ex2(m - mn);   // m = -inf: 0
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      o0[i] *= alpha;
+      o1[i] *= alpha;
+    }
+    m = mn;
+  }
+  // m = -inf here: no visible key so far, every s is -inf and every p 0
+  const float nb = m == -INFINITY ? 0.0f : -m;
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s[i] = ex2(fmaf(s[i], sc2, nb));
+    psum += s[i];
+  }
+  l += psum + __shfl_xor(psum, 32);
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[c2][e] = (__bf16)s[8 * c2 + e];
+}
+
+// O^T += V^T P^T over one tile; vt: the tile's V^T [dim][key] (row stride kVS)
+__device__ __forceinline__ void pv_tile(const uint16_t* vt, int lr, int hf, const v8bf (&pf)[2],
+                                        v16f_a& o0, v16f_a& o1) {
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    const int key0 = 16 * c2 + 4 * hf;   // V^T element t: key key0 + 8 (t / 4) + t % 4
+    const uint2 v0a = *reinterpret_cast<const uint2*>(&vt[lr * kVS + key0]);
+    const uint2 v0b = *reinterpret_cast<const uint2*>(&vt[lr * kVS + key0 + 8]);
+    const uint2 v1a = *reinterpret_cast<const uint2*>(&vt[(32 + lr) * kVS + key0]);
+    const uint2 v1b = *reinterpret_cast<const uint2*>(&vt[(32 + lr) * kVS + key0 + 8]);
+    o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(make_uint4(v0a.x, v0a.y, v0b.x, v0b.y)), pf[c2], o0, 0, 0, 0);
+    o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(make_uint4(v1a.x, v1a.y, v1b.x, v1b.y)), pf[c2], o1, 0, 0, 0);
+  }
+}
+
+// a slot's partial (m, l, o) into a 16-byte-aligned record of kPS floats; lane
+// half hf holds dims 8 j + 4 hf .. +3 (j = 0..3) of each 32-dim half
+__device__ __forceinline__ void store_partial(float* p, int hf, float m, float l, const v16f_a& o0,
+                                              const v16f_a& o1) {
+  if (hf == 0) {
+    p[0] = m;
+    p[1] = l;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = 8 * j + 4 * hf;
+    *reinterpret_cast<float4*>(p + kPO + d) = make_float4(o0[4 * j], o0[4 * j + 1], o0[4 * j + 2], o0[4 * j + 3]);
+    *reinterpret_cast<float4*>(p + kPO + 32 + d) = make_float4(o1[4 * j], o1[4 * j + 1], o1[4 * j + 2], o1[4 * j + 3]);
+  }
+}
+
+// normalised bf16 output of a lane's slot into row lr of st (32 x 64 halves)
+__device__ __forceinline__ void stage_out(uint16_t* st, int lr, int hf, float l, const v16f_a& o0,
+                                          const v16f_a& o1) {
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int d = 8 * (i >> 2) + 4 * hf + (i & 3);
+    st[lr * kHD + d] = f32_to_bf16(o0[i] * inv);
+    st[lr * kHD + 32 + d] = f32_to_bf16(o1[i] * inv);
+  }
+}
+
+// NP: K/V pair pieces per thread and tile (256 pieces / threads, rounded up)
+template <int NP>
 __global__ __launch_bounds__(512) void attn_fwd(const AttnArgs a) {
   const int G = a.Hq / a.Hkv;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKT * kHD];   // [key][dim]
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kHD * kKT];   // [dim][key]
-  __shared__ __attribute__((aligned(16))) uint16_t ost[8][kQB * kHD];  // output staging per wave
-  const int qb = blockIdx.x, bg = blockIdx.y, c = blockIdx.z;
+  // two K/V tile buffers; after the loop, the per-wavefront output staging
+  __shared__ __attribute__((aligned(16))) uint16_t sm[8 * kQB * kHD > 2 * kBuf ? 8 * kQB * kHD : 2 * kBuf];
+  const int bg = blockIdx.x, c = blockIdx.z;
+  const int qb = gridDim.y - 1 - blockIdx.y;    // the longest causal rows first
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int tid = threadIdx.x, nthr = G * 64;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, hf = lane >> 5;
@@ -72,7 +184,7 @@ __global__ __launch_bounds__(512) void attn_fwd(const AttnArgs a) {
   const int qpos = a.S - a.Tq + qi;             // its position
   // keys this workgroup covers: its chunk, cut to what any of its queries sees
   const int qpos_lo = a.S - a.Tq + q0, qpos_hi = a.S - a.Tq + min(q0 + kQB, a.Tq) - 1;
-  int k0 = c * a.chunk, k1 = min(a.S, k0 + a.chunk);
+  int k0 = a.kofs + c * a.chunk, k1 = min(a.S, k0 + a.chunk);
   k1 = min(k1, qpos_hi + 1);
   if (a.window > 0) k0 = max(k0, qpos_lo - a.window + 1);
   const int ntile = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
@@ -89,126 +201,87 @@ __global__ __launch_bounds__(512) void attn_fwd(const AttnArgs a) {
   float l = c == 0 ? 1.0f : 0.0f;                       // running denominator
   v16f_a o0 = {}, o1 = {};                              // O^T: dims 0..31, 32..63 x queries
 
-  // K/V tile loads: threads [0, 256) one 16-byte piece of K each, [256, 512) of V
-  const bool loader = tid < 512;
-  const int piece = tid & 255, pkey = piece >> 3, pdim = (piece & 7) * 8;
-  auto gload = [&](int t) -> uint4 {
-    const int key = min(k0 + t * kKT + pkey, a.S - 1);
-    const uint16_t* src = (tid < 256 ? a.k : a.v) + (((size_t)b * a.S + key) * a.Hkv + g) * kHD + pdim;
-    return *reinterpret_cast<const uint4*>(src);
-  };
-  auto lstore = [&](int buf, uint4 u) {
-    if (tid < 256) {
-      *reinterpret_cast<uint4*>(&ks[buf][pkey * kHD + pdim]) = u;
-    } else {
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  // Tile loads: piece p < 128 holds keys 2 (p%16) and +1 of K at dims 8 (p/16) .. +7;
+  // p in [128, 256) the same of V. Thread tid takes pieces tid + j nthr.
+  uint4 pre[NP][2];
+  auto gload = [&](int t) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) vt[buf][(pdim + t) * kKT + pkey] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
-    }
-  };
-  uint4 pre = make_uint4(0u, 0u, 0u, 0u);
-  if (ntile > 0 && loader && nthr >= 512) lstore(0, gload(0));
-  // fewer than 512 threads (G < 8): the tile is loaded in several rounds
-  if (ntile > 0 && nthr < 512) {
-    for (int p2 = tid; p2 < 512; p2 += nthr) {
-      const int pc = p2 & 255, key = min(k0 + (pc >> 3), a.S - 1), dim = (pc & 7) * 8;
-      const uint4 u = *reinterpret_cast<const uint4*>((p2 < 256 ? a.k : a.v) +
-                                                      (((size_t)b * a.S + key) * a.Hkv + g) * kHD + dim);
-      if (p2 < 256) *reinterpret_cast<uint4*>(&ks[0][(pc >> 3) * kHD + dim]) = u;
-      else {
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-        for (int t = 0; t < 8; ++t) vt[0][(dim + t) * kKT + (pc >> 3)] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+    for (int j = 0; j < NP; ++j) {
+      const int p = tid + j * nthr;
+      if (p < 256) {
+        const int pp = p & 127, dg = pp >> 4, kk = k0 + t * kKT + 2 * (pp & 15);
+        const uint16_t* base = (p < 128 ? a.k : a.v) + (size_t)b * a.S * a.Hkv * kHD + g * kHD + 8 * dg;
+        pre[j][0] = *reinterpret_cast<const uint4*>(base + (size_t)min(kk, a.S - 1) * a.Hkv * kHD);
+        pre[j][1] = *reinterpret_cast<const uint4*>(base + (size_t)min(kk + 1, a.S - 1) * a.Hkv * kHD);
       }
     }
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntile; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < ntile;
-    if (more && loader && nthr >= 512) pre = gload(t + 1);
-    // S^T = K Q^T over the head size
-    v16f_a s = {};
+  };
+  // K rows as they are; V as V^T with the key pair in one 32-bit word
+  auto lstore = [&](int buf) {
+    uint16_t* kt = sm + buf * kBuf;
+    uint16_t* vt = kt + kKTile;
 #pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2) {
-      const v8bf kf = as_bf(*reinterpret_cast<const uint4*>(&ks[buf][lr * kHD + 16 * ks2 + 8 * hf]));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks2], s, 0, 0, 0);
-    }
-    // mask, tile max, online update
-    const int kb = k0 + t * kKT;
-    float tmax = -INFINITY;
+    for (int j = 0; j < NP; ++j) {
+      const int p = tid + j * nthr;
+      if (p < 256) {
+        const int pp = p & 127, dg = pp >> 4, mm = pp & 15;
+        if (p < 128) {
+          *reinterpret_cast<uint4*>(&kt[(2 * mm) * kKS + 8 * dg]) = pre[j][0];
+          *reinterpret_cast<uint4*>(&kt[(2 * mm + 1) * kKS + 8 * dg]) = pre[j][1];
+        } else {
+          const uint32_t x[4] = {pre[j][0].x, pre[j][0].y, pre[j][0].z, pre[j][0].w};
+          const uint32_t y[4] = {pre[j][1].x, pre[j][1].y, pre[j][1].z, pre[j][1].w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kj = kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-      const bool vis = qvalid && kj < k1 && kj <= qpos && (a.window <= 0 || kj > qpos - a.window);
-      s[i] = vis ? s[i] * sc2 : -INFINITY;
-      tmax = fmaxf(tmax, s[i]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mn = fmaxf(m, tmax);
-    const float base = mn == -INFINITY ? 0.0f : mn;
-    const float alpha = exp2f(m - base);
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = exp2f(s[i] - base);
-      psum += s[i];
-    }
-    psum += __shfl_xor(psum, 32);
-    l = l * alpha + psum;
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      o0[i] *= alpha;
-      o1[i] *= alpha;
-    }
-    // O^T += V^T P^T: two 16-key MFMAs per 32-dim half
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      v8bf pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[8 * c2 + e];
-      // keys of V^T's element t: 16 c2 + 8 (t / 4) + 4 hf + t % 4 -> two runs of 4
-      const int key0 = 16 * c2 + 4 * hf;
-      const uint2 v0a = *reinterpret_cast<const uint2*>(&vt[buf][lr * kKT + key0]);
-      const uint2 v0b = *reinterpret_cast<const uint2*>(&vt[buf][lr * kKT + key0 + 8]);
-      const uint2 v1a = *reinterpret_cast<const uint2*>(&vt[buf][(32 + lr) * kKT + key0]);
-      const uint2 v1b = *reinterpret_cast<const uint2*>(&vt[buf][(32 + lr) * kKT + key0 + 8]);
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(make_uint4(v0a.x, v0a.y, v0b.x, v0b.y)), pf, o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(make_uint4(v1a.x, v1a.y, v1b.x, v1b.y)), pf, o1, 0, 0, 0);
-    }
-    __syncthreads();   // every wave is done with buffer buf^1 (read in tile t-1)
-    if (more) {
-      if (nthr >= 512) {
-        if (loader) lstore(buf ^ 1, pre);
-      } else {
-        for (int p2 = tid; p2 < 512; p2 += nthr) {
-          const int pc = p2 & 255, key = min(k0 + (t + 1) * kKT + (pc >> 3), a.S - 1), dim = (pc & 7) * 8;
-          const uint4 u = *reinterpret_cast<const uint4*>((p2 < 256 ? a.k : a.v) +
-                                                          (((size_t)b * a.S + key) * a.Hkv + g) * kHD + dim);
-          if (p2 < 256) *reinterpret_cast<uint4*>(&ks[buf ^ 1][(pc >> 3) * kHD + dim]) = u;
-          else {
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-            for (int t2 = 0; t2 < 8; ++t2)
-              vt[buf ^ 1][(dim + t2) * kKT + (pc >> 3)] = (uint16_t)(w[t2 >> 1] >> (16 * (t2 & 1)));
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t lo = (x[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+            const uint32_t hi = (y[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+            *reinterpret_cast<uint32_t*>(&vt[(8 * dg + t) * kVS + 2 * mm]) = lo | (hi << 16);
           }
         }
       }
     }
+  };
+  if (ntile > 0) {
+    gload(0);
+    lstore(0);
+  }
+  if (ntile > 1) gload(1);
+  __syncthreads();
+
+  for (int t = 0; t < ntile; ++t) {
+    const uint16_t* kt = sm + (t & 1) * kBuf;
+    // S^T = K Q^T over the head size
+    v16f_a s = {};
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2) {
+      const v8bf kf = as_bf(*reinterpret_cast<const uint4*>(&kt[lr * kKS + 16 * ks2 + 8 * hf]));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks2], s, 0, 0, 0);
+    }
+    const int kb = k0 + t * kKT;
+    v8bf pf[2];
+    // every key of the tile visible to every query of the workgroup
+    const bool full = kb + kKT <= k1 && kb + kKT - 1 <= qpos_lo && (a.window <= 0 || kb > qpos_hi - a.window);
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (!(qvalid && kj < k1 && kj <= qpos && (a.window <= 0 || kj > qpos - a.window))) s[i] = -INFINITY;
+      }
+    }
+    softmax_tile(s, m, l, o0, o1, sc2, pf);
+    pv_tile(kt + kKTile, lr, hf, pf, o0, o1);
+    // buffer (t+1)&1 was last read for tile t-1, which every wavefront finished
+    // before the barrier that ended it
+    if (t + 1 < ntile) lstore((t + 1) & 1);
+    if (t + 2 < ntile) gload(t + 2);
     __syncthreads();
   }
 
   // lane l holds query l%32, dims 8(i/4) + 4 hf + i%4 (+32 in o1)
   if (a.nchunks == 1) {
-    const float inv = 1.0f / l;
-    uint16_t* st = ost[wave];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 8 * (i >> 2) + 4 * hf + (i & 3);
-      st[lr * kHD + d] = f32_to_bf16(o0[i] * inv);
-      st[lr * kHD + 32 + d] = f32_to_bf16(o1[i] * inv);
-    }
-    __builtin_amdgcn_wave_barrier();
+    uint16_t* st = sm + wave * kQB * kHD;
+    stage_out(st, lr, hf, l, o0, o1);
+    wave_sync();
     // 32 queries x 128 B: 4 passes of 16 bytes per lane
 #pragma unroll
     for (int p2 = 0; p2 < 4; ++p2) {
@@ -218,17 +291,129 @@ __global__ __launch_bounds__(512) void attn_fwd(const AttnArgs a) {
             *reinterpret_cast<const uint4*>(&st[row * kHD + col]);
     }
   } else if (qvalid) {
-    float* p = a.part + ((((size_t)b * a.Tq + qi) * a.Hq + h) * a.nchunks + c) * (2 + kHD);
-    if (hf == 0) {
-      p[0] = m;
-      p[1] = l;
-    }
+    store_partial(a.part + ((((size_t)b * a.Tq + qi) * a.Hq + h) * a.nchunks + c) * kPS, hf, m, l, o0, o1);
+  }
+}
+
+__global__ __launch_bounds__(kDW * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_dec(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t vts[kDW][kVTile];   // per-wavefront V^T tile
+  // the 32 slots' queries [slot][dim] (row stride kKS) during the loop; then one
+  // wavefront's partials for the merge
+  __shared__ __attribute__((aligned(16))) float mrg[kQB * kPS];
+  uint16_t* qs = reinterpret_cast<uint16_t*>(mrg);
+  const int G = a.Hq / a.Hkv;
+  const int bg = blockIdx.x, c = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hf = lane >> 5;
+  // slot lr = (query tq, head hq of the group), tq = lr / G
+  const int tq = lr / G, hq = lr - tq * G;
+  const bool sval = tq < a.Tq;
+  const int tqc = min(tq, a.Tq - 1), h = g * G + hq;
+  const int qpos = a.S - a.Tq + tqc;
+  const int qpos_lo = a.S - a.Tq, qpos_hi = a.S - 1;
+  int k0 = a.kofs + c * a.chunk;
+  const int k1 = min(a.S, k0 + a.chunk);
+  if (a.window > 0) k0 = max(k0, qpos_lo - a.window + 1);
+  const int ntile = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
+
+  {
+    // thread tid: 16 bytes of slot tid / 8 (its query and head)
+    const int r = tid >> 3, rq = min(r / G, a.Tq - 1), col = (tid & 7) * 8;
+    *reinterpret_cast<uint4*>(&qs[r * kKS + col]) = *reinterpret_cast<const uint4*>(
+        a.q + (((size_t)b * a.Tq + rq) * a.Hq + g * G + (r - (r / G) * G)) * kHD + col);
+  }
+  __syncthreads();
+  const float sc2 = a.scale * kLog2e;
+  const bool sink = c == 0 && wave == 0;
+  float m = sink ? a.sinks[h] * kLog2e : -INFINITY;
+  float l = sink ? 1.0f : 0.0f;
+  v16f_a o0 = {}, o1 = {};
+
+  // lane (key lr, half hf) of tile t: K dims 16 j + 8 hf .. +7 = its A operand
+  // of MFMA j; V the same dims, written transposed into the wavefront's tile
+  const size_t rs = (size_t)a.Hkv * kHD;
+  const uint16_t* kbase = a.k + (size_t)b * a.S * rs + g * kHD + 8 * hf;
+  const uint16_t* vbase = a.v + (size_t)b * a.S * rs + g * kHD + 8 * hf;
+  // One register set: the next tile's loads go out as soon as this tile's K
+  // and V have been consumed (V^T written, scores computed) and fly during the
+  // softmax and the value product; the other wavefronts on the SIMD cover the rest.
+  uint4 kc[4], vc[4];
+  auto gload = [&](int t) {
+    const size_t row = (size_t)min(k0 + t * kKT + lr, a.S - 1) * rs;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 8 * (i >> 2) + 4 * hf + (i & 3);
-      p[2 + d] = o0[i];
-      p[2 + 32 + d] = o1[i];
+    for (int j = 0; j < 4; ++j) {
+      kc[j] = *reinterpret_cast<const uint4*>(kbase + row + 16 * j);
+      vc[j] = *reinterpret_cast<const uint4*>(vbase + row + 16 * j);
     }
+  };
+  uint16_t* vt = vts[wave];
+  if (wave < ntile) gload(wave);
+  for (int t = wave; t < ntile; t += kDW) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x[4] = {vc[j].x, vc[j].y, vc[j].z, vc[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vt[(16 * j + 8 * hf + e) * kVS + lr] = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
+    }
+    v16f_a s = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // Q^T fragment (B operand): slot lr, dims 16 j + 8 hf .. +7
+      const v8bf qf = as_bf(*reinterpret_cast<const uint4*>(&qs[lr * kKS + 16 * j + 8 * hf]));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kc[j]), qf, s, 0, 0, 0);
+    }
+    if (t + kDW < ntile) gload(t + kDW);
+    const int kb = k0 + t * kKT;
+    v8bf pf[2];
+    const bool full = kb + kKT <= k1 && kb + kKT - 1 <= qpos_lo && (a.window <= 0 || kb > qpos_hi - a.window);
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = kb + 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (!(sval && kj < k1 && kj <= qpos && (a.window <= 0 || kj > qpos - a.window))) s[i] = -INFINITY;
+      }
+    }
+    softmax_tile(s, m, l, o0, o1, sc2, pf);
+    wave_sync();   // the V^T tile written by every lane
+    pv_tile(vt, lr, hf, pf, o0, o1);
+    wave_sync();   // and read before the next tile overwrites it
+  }
+
+  // merge wavefronts 1..3 into wavefront 0, in order
+  float* mr = mrg + lr * kPS;
+  for (int w = 1; w < kDW; ++w) {
+    __syncthreads();
+    if (wave == w) store_partial(mr, hf, m, l, o0, o1);
+    __syncthreads();
+    if (wave == 0) {
+      const float m2 = mr[0], l2 = mr[1], M = fmaxf(m, m2);
+      const float a1 = m == M ? 1.0f : ex2(m - M), a2 = m2 == M ? 1.0f : ex2(m2 - M);
+      l = l * a1 + l2 * a2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 8 * (i >> 2) + 4 * hf + (i & 3);
+        o0[i] = o0[i] * a1 + mr[kPO + d] * a2;
+        o1[i] = o1[i] * a1 + mr[kPO + 32 + d] * a2;
+      }
+      m = M;
+    }
+  }
+  if (wave != 0) return;
+  if (a.nchunks == 1) {
+    uint16_t* st = reinterpret_cast<uint16_t*>(mrg);
+    wave_sync();   // the last partial read before the staging overwrites it
+    stage_out(st, lr, hf, l, o0, o1);
+    wave_sync();
+#pragma unroll
+    for (int p2 = 0; p2 < 4; ++p2) {
+      const int idx = p2 * 64 + lane, r = idx >> 3, col = (idx & 7) * 8, rq = r / G;
+      if (rq < a.Tq)
+        *reinterpret_cast<uint4*>(a.out + (((size_t)b * a.Tq + rq) * a.Hq + g * G + (r - rq * G)) * kHD + col) =
+            *reinterpret_cast<const uint4*>(&st[r * kHD + col]);
+    }
+  } else if (sval) {
+    store_partial(a.part + ((((size_t)b * a.Tq + tq) * a.Hq + h) * a.nchunks + c) * kPS, hf, m, l, o0, o1);
   }
 }
 
@@ -240,48 +425,73 @@ __global__ __launch_bounds__(256) void attn_merge(const AttnArgs a) {
   if (i >= n) return;
   const size_t row = i / kHD;
   const int d = (int)(i - row * kHD);
-  const float* p = a.part + row * a.nchunks * (2 + kHD);
+  const float* p = a.part + row * a.nchunks * kPS;
   float M = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, p[c * (2 + kHD)]);
+  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, p[c * kPS]);
   float L = 0.0f, O = 0.0f;
   for (int c = 0; c < a.nchunks; ++c) {
-    const float* pc = p + c * (2 + kHD);
+    const float* pc = p + c * kPS;
     const float w = pc[0] == -INFINITY ? 0.0f : exp2f(pc[0] - M);
     L += pc[1] * w;
-    O += pc[2 + d] * w;
+    O += pc[kPO + d] * w;
   }
   a.out[i] = f32_to_bf16(O / L);
 }
 
 struct AttnPlan {
-  int nchunks, chunk;
+  bool dec;          // attn_dec (G * Tq <= 32) or attn_fwd
+  int nchunks, chunk, kofs;
 };
 
-AttnPlan attn_plan(int B, int Tq, int S, int Hkv) {
-  const int blocks = B * Hkv * ((Tq + kQB - 1) / kQB);
-  int n = (1024 + blocks - 1) / blocks;             // aim at >= 1024 workgroups
-  const int maxn = (S + 255) / 256;                  // chunks of at least 256 keys
-  n = n < 1 ? 1 : (n > maxn ? maxn : n);
-  const int chunk = ((S + n - 1) / n + kKT - 1) / kKT * kKT;
-  return {(S + chunk - 1) / chunk, chunk};
+AttnPlan attn_plan(int B, int Tq, int S, int Hq, int Hkv, int window) {
+  const int G = Hq / Hkv;
+  const bool dec = G * Tq <= kQB;
+  // the keys any query sees start at kofs
+  const int kofs = window > 0 ? max(0, S - Tq - window + 1) : 0;
+  const int span = S - kofs, nt = (span + kKT - 1) / kKT;
+  int n, maxn;
+  if (dec) {
+    n = (1024 + B * Hkv - 1) / (B * Hkv);            // >= 1024 workgroups of 4 wavefronts
+    maxn = (nt + 2 * kDW - 1) / (2 * kDW);            // >= 2 tiles per wavefront
+  } else {
+    const int blocks = B * Hkv * ((Tq + kQB - 1) / kQB);
+    n = (1024 + blocks - 1) / blocks;
+    maxn = (span + 255) / 256;                        // chunks of at least 256 keys
+  }
+  n = n > maxn ? maxn : n;
+  n = n < 1 ? 1 : n;
+  const int chunk = ((nt + n - 1) / n) * kKT;
+  return {dec, (span + chunk - 1) / chunk, chunk, kofs};
 }
 
 }  // namespace
 
-size_t attention_workspace_bytes(int B, int Tq, int S, int Hq, int Hkv) {
-  const AttnPlan p = attn_plan(B, Tq, S, Hkv);
-  return p.nchunks > 1 ? (size_t)B * Tq * Hq * p.nchunks * (2 + kHD) * sizeof(float) : 0;
+size_t attention_workspace_bytes(int B, int Tq, int S, int Hq, int Hkv, int window) {
+  const AttnPlan p = attn_plan(B, Tq, S, Hq, Hkv, window);
+  return p.nchunks > 1 ? (size_t)B * Tq * Hq * p.nchunks * kPS * sizeof(float) : 0;
 }
 
 hipError_t launch_attention_sink(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const float* sinks, int B, int Tq, int S, int Hq, int Hkv,
                                  int window, float scale, uint16_t* out, void* ws,
                                  hipStream_t stream) {
-  const AttnPlan p = attn_plan(B, Tq, S, Hkv);
+  const AttnPlan p = attn_plan(B, Tq, S, Hq, Hkv, window);
   AttnArgs a{q, k, v, sinks, out, static_cast<float*>(ws), B, Tq, S, Hq, Hkv, window,
-             p.nchunks, p.chunk, scale};
+             p.nchunks, p.chunk, p.kofs, scale};
   const int G = Hq / Hkv;
-  hipLaunchKernelGGL(attn_fwd, dim3((Tq + kQB - 1) / kQB, B * Hkv, p.nchunks), dim3(G * 64), 0, stream, a);
+  if (p.dec) {
+    hipLaunchKernelGGL(attn_dec, dim3(B * Hkv, p.nchunks), dim3(kDW * 64), 0, stream, a);
+  } else {
+    // x: batch entry and KV head, so consecutive workgroups (dealt out over the
+    // chip's 8 L2 slices in turn) keep one KV head per slice when Hkv = 8
+    const dim3 grid(B * Hkv, (Tq + kQB - 1) / kQB, p.nchunks);
+    if (G >= 4)
+      hipLaunchKernelGGL(attn_fwd<1>, grid, dim3(G * 64), 0, stream, a);
+    else if (G >= 2)
+      hipLaunchKernelGGL(attn_fwd<2>, grid, dim3(G * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_fwd<4>, grid, dim3(G * 64), 0, stream, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.nchunks == 1) return err;
   const size_t n = (size_t)B * Tq * Hq * kHD;

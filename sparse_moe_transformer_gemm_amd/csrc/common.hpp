@@ -122,7 +122,7 @@ hipError_t launch_expert_ffn_fp8(const FfnArgs& a, hipStream_t stream);
 hipError_t launch_round_bf16(float* w, int n, hipStream_t stream);
 
 // Attention with per-head sinks (attention.hip): head size 64, Hq / Hkv <= 8.
-size_t attention_workspace_bytes(int B, int Tq, int S, int Hq, int Hkv);
+size_t attention_workspace_bytes(int B, int Tq, int S, int Hq, int Hkv, int window);
 hipError_t launch_attention_sink(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const float* sinks, int B, int Tq, int S, int Hq, int Hkv,
                                  int window, float scale, uint16_t* out, void* ws,

@@ -51,6 +51,12 @@ def _check(gu, B, Tq, S, Hq, Hkv, window, seed, sinks=None):
     dict(B=4, Tq=1, S=3000, Hq=16, Hkv=2, window=0, seed=93),     # decode: split keys, merged
     dict(B=3, Tq=5, S=777, Hq=64, Hkv=8, window=0, seed=94),      # a few queries, split keys
     dict(B=2, Tq=3, S=5, Hq=4, Hkv=1, window=2, seed=95),         # tiny, window 2, G = 4
+    dict(B=3, Tq=4, S=1000, Hq=16, Hkv=2, window=0, seed=99),     # 4 queries x 8 heads = 32 slots, causal in-tile
+    dict(B=2, Tq=2, S=900, Hq=6, Hkv=2, window=300, seed=100),    # G = 3 packed, sliding window
+    dict(B=1, Tq=1, S=8192, Hq=64, Hkv=8, window=128, seed=101),  # decode with a 128-key window
+    dict(B=1, Tq=70, S=70, Hq=6, Hkv=2, window=0, seed=102),      # G = 3: two pieces per thread
+    dict(B=2, Tq=50, S=120, Hq=2, Hkv=2, window=0, seed=103),     # G = 1: four pieces per thread
+    dict(B=1, Tq=200, S=1000, Hq=8, Hkv=1, window=100, seed=104), # queries at the end, window
 ], ids=lambda d: f"B{d['B']}-Tq{d['Tq']}-S{d['S']}-H{d['Hq']}/{d['Hkv']}-w{d['window']}")
 def test_attention_shapes(gu, shape):
     _check(gu, **shape)
