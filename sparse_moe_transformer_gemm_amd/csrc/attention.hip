@@ -32,10 +32,11 @@
 // head of the group (up to 8), all sharing each K/V tile staged once in LDS
 // (double-buffered, one barrier per tile); slot = query.
 // attn_dec (few queries: G * Tq <= 32 for G = Hq / Hkv): one wavefront packs
-// the G heads x Tq queries of a KV head into its 32 slots; the 4 wavefronts of
-// a workgroup take interleaved tiles of the workgroup's keys, loading K rows
-// straight into MFMA operand registers (the tile after next in flight) and V
-// through a per-wavefront LDS transpose, and merge their partials in wave order.
+// the G heads x Tq queries of a KV head into its 32 slots; a workgroup holds
+// one wavefront per KV head (up to 4) of one batch entry, all on the same chunk
+// of keys, so together they stream whole contiguous KV rows; each wavefront
+// loads whole 128-byte rows of its head, passes K through LDS to the MFMA
+// operand layout and V through an LDS transpose, with two tiles in flight.
 // A single chunk of keys normalises and stores bf16 output; several chunks
 // store partials (running max, denominator, unnormalised output) that
 // attn_merge adds in chunk order.
@@ -46,6 +47,9 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f_a __attribute__((ext_vector_type(16)));
+// 16 bytes as a native vector (copies of HIP's uint4 struct between address
+// spaces can leave the array behind in scratch memory)
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 constexpr int kHD = 64;             // head size
 constexpr int kQB = 32;             // query slots per wavefront
@@ -55,7 +59,7 @@ constexpr int kVS = 36;             // V^T tile row stride in LDS (halves): 72 B
 constexpr int kKTile = kKT * kKS;   // halves
 constexpr int kVTile = kHD * kVS;   // halves
 constexpr int kBuf = kKTile + kVTile;
-constexpr int kDW = 4;              // wavefronts per attn_dec workgroup
+constexpr int kDecW = 4;            // wavefronts (KV heads) per attn_dec workgroup, at most
 constexpr int kPS = 68;             // partial record (floats): m, l, 2 unused, o[64]
 constexpr int kPO = 4;              // offset of o in the record
 constexpr float kLog2e = 1.4426950408889634f;
@@ -69,6 +73,15 @@ struct AttnArgs {
   int B, Tq, S, Hq, Hkv, window, nchunks, chunk, kofs;   // chunk c: keys kofs + [c chunk, (c+1) chunk)
   float scale;
 };
+
+__device__ __forceinline__ v8bf as_bf(u4v u) {
+  union {
+    u4v u;
+    v8bf b;
+  } c;
+  c.u = u;
+  return c.b;
+}
 
 __device__ __forceinline__ v8bf as_bf(uint4 u) {
   union {
@@ -295,16 +308,30 @@ __global__ __launch_bounds__(512) void attn_fwd(const AttnArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kDW * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn_dec(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vts[kDW][kVTile];   // per-wavefront V^T tile
-  // the 32 slots' queries [slot][dim] (row stride kKS) during the loop; then one
-  // wavefront's partials for the merge
-  __shared__ __attribute__((aligned(16))) float mrg[kQB * kPS];
-  uint16_t* qs = reinterpret_cast<uint16_t*>(mrg);
+// rows key0 + 8 i (i = 0..3, clamped to the last key) of K and V, 16 bytes each
+__device__ __forceinline__ void dec_rows(const uint16_t* kbase, const uint16_t* vbase, size_t rs, int key0,
+                                         int S, u4v (&kc)[4], u4v (&vc)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const size_t row = (size_t)min(key0 + 8 * i, S - 1) * rs;
+    kc[i] = *reinterpret_cast<const u4v*>(kbase + row);
+    vc[i] = *reinterpret_cast<const u4v*>(vbase + row);
+  }
+}
+
+__global__ __launch_bounds__(kDecW * 64) __attribute__((amdgpu_waves_per_eu(3))) void attn_dec(const AttnArgs a) {
+  // per wavefront: a tile's K rows [key][dim] (row stride kKS), then the same
+  // tile's V^T [dim][key] (row stride kVS) in the same place; finally the output
+  // per wavefront: [0, kKTile) the tile area, [kKTile, 2 kKTile) its 32 slots'
+  // queries [slot][dim] (row stride kKS)
+  __shared__ __attribute__((aligned(16))) uint16_t kv[kDecW][2 * kKTile];
+  static_assert(kVTile <= kKTile && kQB * kHD <= kKTile, "one area per wavefront");
   const int G = a.Hq / a.Hkv;
-  const int bg = blockIdx.x, c = blockIdx.y;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int nw = blockDim.x >> 6, ngr = (a.Hkv + nw - 1) / nw;
+  const int b = blockIdx.x / ngr, c = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hf = lane >> 5;
+  const int g = (blockIdx.x - b * ngr) * nw + wave;   // this wavefront's KV head
+  if (g >= a.Hkv) return;                             // (no workgroup barrier below)
   // slot lr = (query tq, head hq of the group), tq = lr / G
   const int tq = lr / G, hq = lr - tq * G;
   const bool sval = tq < a.Tq;
@@ -316,54 +343,50 @@ __global__ __launch_bounds__(kDW * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   if (a.window > 0) k0 = max(k0, qpos_lo - a.window + 1);
   const int ntile = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
 
+  uint16_t* buf = kv[wave];
+  uint16_t* qs = buf + kKTile;
   {
-    // thread tid: 16 bytes of slot tid / 8 (its query and head)
-    const int r = tid >> 3, rq = min(r / G, a.Tq - 1), col = (tid & 7) * 8;
-    *reinterpret_cast<uint4*>(&qs[r * kKS + col]) = *reinterpret_cast<const uint4*>(
-        a.q + (((size_t)b * a.Tq + rq) * a.Hq + g * G + (r - (r / G) * G)) * kHD + col);
+    // lane (slot lr, half hf): 64 bytes of its slot's query
+    const uint16_t* qr = a.q + (((size_t)b * a.Tq + tqc) * a.Hq + h) * kHD + 32 * hf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u4v*>(&qs[lr * kKS + 32 * hf + 8 * j]) = *reinterpret_cast<const u4v*>(qr + 8 * j);
   }
-  __syncthreads();
   const float sc2 = a.scale * kLog2e;
-  const bool sink = c == 0 && wave == 0;
-  float m = sink ? a.sinks[h] * kLog2e : -INFINITY;
-  float l = sink ? 1.0f : 0.0f;
+  float m = c == 0 ? a.sinks[h] * kLog2e : -INFINITY;
+  float l = c == 0 ? 1.0f : 0.0f;
   v16f_a o0 = {}, o1 = {};
 
-  // lane (key lr, half hf) of tile t: K dims 16 j + 8 hf .. +7 = its A operand
-  // of MFMA j; V the same dims, written transposed into the wavefront's tile
+  // Tile loads, whole rows: instruction i gives lane l 16 bytes (dims 8 (l%8) ..
+  // +7) of key 8 i + l/8, so each instruction reads 8 full 128-byte rows of this
+  // KV head, and the workgroup's wavefronts (its consecutive KV heads) read
+  // contiguous stretches of each position's KV row.
   const size_t rs = (size_t)a.Hkv * kHD;
-  const uint16_t* kbase = a.k + (size_t)b * a.S * rs + g * kHD + 8 * hf;
-  const uint16_t* vbase = a.v + (size_t)b * a.S * rs + g * kHD + 8 * hf;
-  // One register set: the next tile's loads go out as soon as this tile's K
-  // and V have been consumed (V^T written, scores computed) and fly during the
-  // softmax and the value product; the other wavefronts on the SIMD cover the rest.
-  uint4 kc[4], vc[4];
-  auto gload = [&](int t) {
-    const size_t row = (size_t)min(k0 + t * kKT + lr, a.S - 1) * rs;
+  const int rk = lane >> 3, cd = (lane & 7) * 8;
+  const uint16_t* kbase = a.k + (size_t)b * a.S * rs + g * kHD + cd;
+  const uint16_t* vbase = a.v + (size_t)b * a.S * rs + g * kHD + cd;
+  // two register slots: tile t in slot t % 2; a slot is refilled with tile t + 2
+  // as soon as tile t's K and V have left it, so two tiles are in flight
+  // while one is computed
+  auto tile = [&](int t, u4v (&kc)[4], u4v (&vc)[4]) __attribute__((always_inline)) {
+    // K rows -> LDS -> A operand (key lr, dims 16 j + 8 hf .. +7)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kc[j] = *reinterpret_cast<const uint4*>(kbase + row + 16 * j);
-      vc[j] = *reinterpret_cast<const uint4*>(vbase + row + 16 * j);
-    }
-  };
-  uint16_t* vt = vts[wave];
-  if (wave < ntile) gload(wave);
-  for (int t = wave; t < ntile; t += kDW) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t x[4] = {vc[j].x, vc[j].y, vc[j].z, vc[j].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vt[(16 * j + 8 * hf + e) * kVS + lr] = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
-    }
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u4v*>(&buf[(8 * i + rk) * kKS + cd]) = kc[i];
+    wave_sync();
     v16f_a s = {};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // Q^T fragment (B operand): slot lr, dims 16 j + 8 hf .. +7
-      const v8bf qf = as_bf(*reinterpret_cast<const uint4*>(&qs[lr * kKS + 16 * j + 8 * hf]));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kc[j]), qf, s, 0, 0, 0);
+      const v8bf kf = as_bf(*reinterpret_cast<const u4v*>(&buf[lr * kKS + 16 * j + 8 * hf]));
+      const v8bf qf = as_bf(*reinterpret_cast<const u4v*>(&qs[lr * kKS + 16 * j + 8 * hf]));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, s, 0, 0, 0);
     }
-    if (t + kDW < ntile) gload(t + kDW);
+    wave_sync();   // the K reads are done before V^T overwrites them
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) buf[(cd + e) * kVS + 8 * i + rk] = (uint16_t)(vc[i][e >> 1] >> (16 * (e & 1)));
+    }
+    if (t + 2 < ntile) dec_rows(kbase, vbase, rs, k0 + (t + 2) * kKT + rk, a.S, kc, vc);
     const int kb = k0 + t * kKT;
     v8bf pf[2];
     const bool full = kb + kKT <= k1 && kb + kKT - 1 <= qpos_lo && (a.window <= 0 || kb > qpos_hi - a.window);
@@ -376,41 +399,26 @@ __global__ __launch_bounds__(kDW * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     softmax_tile(s, m, l, o0, o1, sc2, pf);
     wave_sync();   // the V^T tile written by every lane
-    pv_tile(vt, lr, hf, pf, o0, o1);
-    wave_sync();   // and read before the next tile overwrites it
+    pv_tile(buf, lr, hf, pf, o0, o1);
+    wave_sync();   // and read before the next tile's K overwrites it
+  };
+  u4v ka[4], va[4], kb2[4], vb2[4];
+  if (ntile > 0) dec_rows(kbase, vbase, rs, k0 + rk, a.S, ka, va);
+  if (ntile > 1) dec_rows(kbase, vbase, rs, k0 + kKT + rk, a.S, kb2, vb2);
+  for (int t = 0; t < ntile; t += 2) {
+    tile(t, ka, va);
+    if (t + 1 < ntile) tile(t + 1, kb2, vb2);
   }
 
-  // merge wavefronts 1..3 into wavefront 0, in order
-  float* mr = mrg + lr * kPS;
-  for (int w = 1; w < kDW; ++w) {
-    __syncthreads();
-    if (wave == w) store_partial(mr, hf, m, l, o0, o1);
-    __syncthreads();
-    if (wave == 0) {
-      const float m2 = mr[0], l2 = mr[1], M = fmaxf(m, m2);
-      const float a1 = m == M ? 1.0f : ex2(m - M), a2 = m2 == M ? 1.0f : ex2(m2 - M);
-      l = l * a1 + l2 * a2;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = 8 * (i >> 2) + 4 * hf + (i & 3);
-        o0[i] = o0[i] * a1 + mr[kPO + d] * a2;
-        o1[i] = o1[i] * a1 + mr[kPO + 32 + d] * a2;
-      }
-      m = M;
-    }
-  }
-  if (wave != 0) return;
   if (a.nchunks == 1) {
-    uint16_t* st = reinterpret_cast<uint16_t*>(mrg);
-    wave_sync();   // the last partial read before the staging overwrites it
-    stage_out(st, lr, hf, l, o0, o1);
+    stage_out(buf, lr, hf, l, o0, o1);
     wave_sync();
 #pragma unroll
     for (int p2 = 0; p2 < 4; ++p2) {
       const int idx = p2 * 64 + lane, r = idx >> 3, col = (idx & 7) * 8, rq = r / G;
       if (rq < a.Tq)
         *reinterpret_cast<uint4*>(a.out + (((size_t)b * a.Tq + rq) * a.Hq + g * G + (r - rq * G)) * kHD + col) =
-            *reinterpret_cast<const uint4*>(&st[r * kHD + col]);
+            *reinterpret_cast<const uint4*>(&buf[r * kHD + col]);
     }
   } else if (sval) {
     store_partial(a.part + ((((size_t)b * a.Tq + tq) * a.Hq + h) * a.nchunks + c) * kPS, hf, m, l, o0, o1);
@@ -418,24 +426,40 @@ __global__ __launch_bounds__(kDW * 64) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // out = (sum_c O_c 2^(m_c - M)) / (sum_c l_c 2^(m_c - M)), M = max_c m_c, chunks in
-// order; one thread per output element. Chunk 0 carries the sink, so M is finite.
+// order. One wavefront per output row (batch entry, query, head): lane c < nchunks
+// reads chunk c's m and l, the row maximum is a wavefront reduction, and lane d
+// sums dimension d over the chunks in order, the weights broadcast from their
+// lanes and the loads of eight chunks issued together. Chunk 0 carries the sink,
+// so M is finite. At most 64 chunks.
 __global__ __launch_bounds__(256) void attn_merge(const AttnArgs a) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t n = (size_t)a.B * a.Tq * a.Hq * kHD;
-  if (i >= n) return;
-  const size_t row = i / kHD;
-  const int d = (int)(i - row * kHD);
-  const float* p = a.part + row * a.nchunks * kPS;
-  float M = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, p[c * kPS]);
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= a.B * a.Tq * a.Hq) return;
+  const float* p = a.part + (size_t)row * a.nchunks * kPS;
+  const float mc = lane < a.nchunks ? p[lane * kPS] : -INFINITY;
+  const float lc = lane < a.nchunks ? p[lane * kPS + 1] : 0.0f;
+  float M = mc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float w = mc == -INFINITY ? 0.0f : exp2f(mc - M);
   float L = 0.0f, O = 0.0f;
-  for (int c = 0; c < a.nchunks; ++c) {
-    const float* pc = p + c * kPS;
-    const float w = pc[0] == -INFINITY ? 0.0f : exp2f(pc[0] - M);
-    L += pc[1] * w;
-    O += pc[kPO + d] * w;
+  int c = 0;
+  for (; c + 8 <= a.nchunks; c += 8) {
+    float ov[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ov[j] = p[(c + j) * kPS + kPO + lane];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wj = __shfl(w, c + j), lj = __shfl(lc, c + j);
+      L += lj * wj;
+      O += ov[j] * wj;
+    }
   }
-  a.out[i] = f32_to_bf16(O / L);
+  for (; c < a.nchunks; ++c) {
+    const float wj = __shfl(w, c), lj = __shfl(lc, c);
+    L += lj * wj;
+    O += p[c * kPS + kPO + lane] * wj;
+  }
+  a.out[(size_t)row * kHD + lane] = f32_to_bf16(O / L);
 }
 
 struct AttnPlan {
@@ -451,14 +475,15 @@ AttnPlan attn_plan(int B, int Tq, int S, int Hq, int Hkv, int window) {
   const int span = S - kofs, nt = (span + kKT - 1) / kKT;
   int n, maxn;
   if (dec) {
-    n = (1024 + B * Hkv - 1) / (B * Hkv);            // >= 1024 workgroups of 4 wavefronts
-    maxn = (nt + 2 * kDW - 1) / (2 * kDW);            // >= 2 tiles per wavefront
+    n = (3072 + B * Hkv - 1) / (B * Hkv);            // 3072 wavefronts: 12 per CU, all resident
+    maxn = (nt + 1) / 2;                              // >= 2 tiles per wavefront
   } else {
     const int blocks = B * Hkv * ((Tq + kQB - 1) / kQB);
     n = (1024 + blocks - 1) / blocks;
     maxn = (span + 255) / 256;                        // chunks of at least 256 keys
   }
   n = n > maxn ? maxn : n;
+  n = n > 64 ? 64 : n;                                // attn_merge takes at most 64
   n = n < 1 ? 1 : n;
   const int chunk = ((nt + n - 1) / n) * kKT;
   return {dec, (span + chunk - 1) / chunk, chunk, kofs};
@@ -480,7 +505,8 @@ hipError_t launch_attention_sink(const uint16_t* q, const uint16_t* k, const uin
              p.nchunks, p.chunk, p.kofs, scale};
   const int G = Hq / Hkv;
   if (p.dec) {
-    hipLaunchKernelGGL(attn_dec, dim3(B * Hkv, p.nchunks), dim3(kDW * 64), 0, stream, a);
+    const int nw = Hkv < kDecW ? Hkv : kDecW;
+    hipLaunchKernelGGL(attn_dec, dim3(B * ((Hkv + nw - 1) / nw), p.nchunks), dim3(nw * 64), 0, stream, a);
   } else {
     // x: batch entry and KV head, so consecutive workgroups (dealt out over the
     // chip's 8 L2 slices in turn) keep one KV head per slice when Hkv = 8
@@ -494,8 +520,8 @@ hipError_t launch_attention_sink(const uint16_t* q, const uint16_t* k, const uin
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.nchunks == 1) return err;
-  const size_t n = (size_t)B * Tq * Hq * kHD;
-  hipLaunchKernelGGL(attn_merge, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+  const int rows = B * Tq * Hq;
+  hipLaunchKernelGGL(attn_merge, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
