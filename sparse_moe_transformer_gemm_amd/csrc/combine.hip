@@ -3,46 +3,64 @@
 // experts' outputs). Atomic-free: each output element is owned by one thread,
 // which gathers the token's k expert rows through pair_row and sums them in
 // fixed slot order in fp32, then rounds once to bf16 (nearest even).
-// Memory-bound: 16-byte loads of y, 8-byte stores of out; one block per (token
-// row, 1024 columns), one 4-column chunk per thread, so all of a thread's k
-// loads are in flight at once.
-#include "common.hpp"
+// Memory-bound: one workgroup per token row; each thread owns up to three
+// 4-column chunks and issues all of their k row loads (16 bytes each) before
+// it sums any, so 12 loads per thread are in flight. y is read exactly once and
+// out written once, so both go through non-temporal accesses, which keep them
+// from displacing reusable lines in the caches (measured at prefill-20b sizes:
+// 86.4 -> 72.6 us for 424 MB, against 53 us at the HBM peak).
+#include "mx6.hpp"
 
 namespace moe {
 namespace {
 
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+
+constexpr int kCombChunks = 3;   // 4-column chunks per thread: 256 x 3 x 4 >= 2880 columns
+
+// K = k, a template parameter so that the loads and sums are straight-line code
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ pair_row,
                                                       const float* __restrict__ topk_w, int d,
-                                                      int k, uint16_t* __restrict__ out) {
+                                                      uint16_t* __restrict__ out) {
+  constexpr int k = K;
   const int t = blockIdx.x;
-  const float4* rows[8];
-  float w[8];
+  // the token's k rows of y as buffer resources (wave-uniform, in SGPRs); reads
+  // past a row's end return zero
+  rsrc_t rows[K];
+  float w[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < k) {
-      rows[j] = reinterpret_cast<const float4*>(y + (size_t)pair_row[(size_t)t * k + j] * d);
-      w[j] = topk_w[(size_t)t * k + j];
-    }
+  for (int j = 0; j < K; ++j) {
+    const int row = __builtin_amdgcn_readfirstlane(pair_row[(size_t)t * k + j]);
+    rows[j] = make_rsrc(y + (size_t)row * d, (uint32_t)d * 4u);
+    w[j] = topk_w[(size_t)t * k + j];
   }
-  uint2* o = reinterpret_cast<uint2*>(out + (size_t)t * d);
-  const int c = blockIdx.y * blockDim.x + threadIdx.x;
-  if (c < d / 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  u2v* o = reinterpret_cast<u2v*>(out + (size_t)t * d);
+  for (int c0 = threadIdx.x; c0 < d / 4; c0 += 256 * kCombChunks) {
+    uint4 v[kCombChunks][K];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        const float4 v = rows[j][c];
-        acc.x = fmaf(w[j], v.x, acc.x);
-        acc.y = fmaf(w[j], v.y, acc.y);
-        acc.z = fmaf(w[j], v.z, acc.z);
-        acc.w = fmaf(w[j], v.w, acc.w);
+    for (int u = 0; u < kCombChunks; ++u)
+#pragma unroll
+      for (int j = 0; j < K; ++j) v[u][j] = bload16nt(rows[j], (uint32_t)(c0 + 256 * u) * 16u);
+#pragma unroll
+    for (int u = 0; u < kCombChunks; ++u) {
+      const int c = c0 + 256 * u;
+      if (c < d / 4) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          acc.x = fmaf(w[j], __uint_as_float(v[u][j].x), acc.x);
+          acc.y = fmaf(w[j], __uint_as_float(v[u][j].y), acc.y);
+          acc.z = fmaf(w[j], __uint_as_float(v[u][j].z), acc.z);
+          acc.w = fmaf(w[j], __uint_as_float(v[u][j].w), acc.w);
+        }
+        u2v r;
+        r.x = f32_to_bf16(acc.x) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
+        r.y = f32_to_bf16(acc.z) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
+        __builtin_nontemporal_store(r, o + c);
       }
     }
-    uint2 r;
-    r.x = f32_to_bf16(acc.x) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
-    r.y = f32_to_bf16(acc.z) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
-    o[c] = r;
   }
 }
 
@@ -50,8 +68,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_row, const float* topk_w,
                           int T, int d, int k, uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T, (d / 4 + 255) / 256), dim3(256), 0, stream, y_sorted,
-                     pair_row, topk_w, d, k, out);
+  const dim3 g(T), b(256);
+  switch (k) {
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, g, b, 0, stream, y_sorted, pair_row, topk_w, d, out); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, g, b, 0, stream, y_sorted, pair_row, topk_w, d, out); break;
+    case 3: hipLaunchKernelGGL(combine_kernel<3>, g, b, 0, stream, y_sorted, pair_row, topk_w, d, out); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, g, b, 0, stream, y_sorted, pair_row, topk_w, d, out); break;
+    case 5: hipLaunchKernelGGL(combine_kernel<5>, g, b, 0, stream, y_sorted, pair_row, topk_w, d, out); break;
+    case 6: hipLaunchKernelGGL(combine_kernel<6>, g, b, 0, stream, y_sorted, pair_row, topk_w, d, out); break;
+    case 7: hipLaunchKernelGGL(combine_kernel<7>, g, b, 0, stream, y_sorted, pair_row, topk_w, d, out); break;
+    default: hipLaunchKernelGGL(combine_kernel<8>, g, b, 0, stream, y_sorted, pair_row, topk_w, d, out); break;
+  }
   return hipGetLastError();
 }
 

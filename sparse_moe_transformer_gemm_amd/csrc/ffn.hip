@@ -723,6 +723,8 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
 // weight stream never drains between items. Loads are issued in the order they
 // are consumed, so waiting for one never waits for a younger one. All global
 // reads are buffer loads: blocks past K and rows past the count read as zero.
+// The weights, read once, are loaded non-temporal (nt), which measured 5.7% (gate/up)
+// and 10% (down) faster on decode-20b than cached loads.
 //
 // 16x16x128 layout (checked on gfx950): lane l supplies row/column l%16 and K
 // elements 32*(l/16) .. +31 of the step; result lane l holds column l%16, rows
@@ -863,7 +865,7 @@ __global__ __launch_bounds__(256, 2) void grouped_decode(const FfnArgs a, const 
     for (int u = 0; u < kDecSS; ++u) {
       const int jj = st * kDecSS + u;
       const bool live = jj < nst && (4 * jj + 2 < nblkK || q < 2);
-      pk.w[u] = bload16(I.wr, live ? wl : kOutOfRange, (uint32_t)jj * kWStep);
+      pk.w[u] = bload16nt(I.wr, live ? wl : kOutOfRange, (uint32_t)jj * kWStep);
     }
   };
   auto issue_a = [&](const Issue& I, int st, uint4 (&dst)[kDecAPerT]) {

@@ -283,6 +283,12 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off, uint32_t soff =
   const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
   return make_uint4(t[0], t[1], t[2], t[3]);
 }
+// The same with the non-temporal cache policy (nt): for data read once, so that
+// it does not displace reusable lines.
+__device__ __forceinline__ uint4 bload16nt(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 2);
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
 }
