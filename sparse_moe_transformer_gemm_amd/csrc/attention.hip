@@ -308,14 +308,15 @@ __global__ __launch_bounds__(512) void attn_fwd(const AttnArgs a) {
   }
 }
 
-// rows key0 + 8 i (i = 0..3, clamped to the last key) of K and V, 16 bytes each
+// rows key0 + 8 i (i = 0..3, clamped to the last key) of K and V, 16 bytes each,
+// non-temporal: the caches are read once
 __device__ __forceinline__ void dec_rows(const uint16_t* kbase, const uint16_t* vbase, size_t rs, int key0,
                                          int S, u4v (&kc)[4], u4v (&vc)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const size_t row = (size_t)min(key0 + 8 * i, S - 1) * rs;
-    kc[i] = *reinterpret_cast<const u4v*>(kbase + row);
-    vc[i] = *reinterpret_cast<const u4v*>(vbase + row);
+    kc[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(kbase + row));
+    vc[i] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vbase + row));
   }
 }
 

@@ -33,6 +33,8 @@
 namespace moe {
 namespace {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 // row tiles per raster group of the prefill grid (gate/up, down): chosen by
 // measurement; the 32 workgroups of an XCD then share GM row tiles of A and
 // 32/GM column tiles of the weights
@@ -685,9 +687,11 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
         for (int q = 0; q < 4; ++q) {
           const int r = 8 * q + srow;  // row within the wave's 32
           const float4 v = *reinterpret_cast<const float4*>(ep + r * C::EP_PITCH + scol);
+          // non-temporal: y is read once, by the combine, after the GEMM
           if (wm * 32 + r < c_rows)
-            *reinterpret_cast<float4*>(a.y_sorted + (size_t)(c_off + c_m0 + wm * 32 + r) * N + c_col0 +
-                                       wn * NF * 32 + f * 32 + scol) = v;
+            __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<v4f*>(a.y_sorted + (size_t)(c_off + c_m0 + wm * 32 + r) * N +
+                                                               c_col0 + wn * NF * 32 + f * 32 + scol));
         }
         __builtin_amdgcn_wave_barrier();
       }
@@ -729,7 +733,6 @@ __global__ __launch_bounds__(kPrefWaves * 64) void grouped_prefill(const FfnArgs
 // 16x16x128 layout (checked on gfx950): lane l supplies row/column l%16 and K
 // elements 32*(l/16) .. +31 of the step; result lane l holds column l%16, rows
 // 4*(l/16) + i, i = 0..3.
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int OPA>
 __device__ __forceinline__ v4f mfma16_f6f4(const v8i& a, const v8i& b, const v4f& c, int sa,
