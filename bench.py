@@ -606,10 +606,14 @@ def main():
         cpu = cpu_baseline(head, args.cpu_seconds, log)
     clk1 = clocks()
 
-    r = head
-    gu = r.get("gate_up_gemm", {})
-    decode = r.get("T", 0) <= 64
-    if decode:
+    # value and config are the first workload's; the roofline object describes the
+    # gate/up GEMM of the first single-layer workload (none if only the stack ran)
+    r = next((results[c] for c in order if "gate_up_gemm" in results[c]), None)
+    gu = r.get("gate_up_gemm", {}) if r else {}
+    decode = r is not None and r["T"] <= 64
+    if r is None:
+        roof = None
+    elif decode:
         roof = {"bound": "hbm", "achieved": gu["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gu["gbs"] / HBM_PEAK_GBS,
                 "traffic": measured_traffic(f"{r['workload']}_T{r['T']}"),
@@ -624,9 +628,11 @@ def main():
                 "traffic": measured_traffic(f"{r['workload']}_T{r['T']}"),
                 "kernel": "grouped_prefill<6, true>: the gate/up GEMM with SwiGLU (stage 1)",
                 "flops_per_launch": gu["flops"], "avg_launch_ms": gu["avg_launch_ms"]}
-    roof["timing"] = ("stage launched back to back over the rotating weight copies, HIP events "
-                      "on the launch stream around the timed launches")
-    roof["layer_frac"] = r["frac_hbm_peak"] if decode else r["frac_mxfp4_peak"]
+    if roof is not None:
+        roof["timing"] = ("stage launched back to back over the rotating weight copies, HIP events "
+                          "on the launch stream around the timed launches")
+        roof["layer_frac"] = r["frac_hbm_peak"] if decode else r["frac_mxfp4_peak"]
+    r = head
     line = {
         "metric": METRIC,
         "value": r["tokens_per_s"],
@@ -640,8 +646,9 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4 weights x 2-term mxfp6 activations, fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": f"{r['workload']}: T={r['T']} d={r['d']} F={r['F']} E={r['E']} "
-                               f"top-{r['k']}, seed {r['seed']}",
+        "config": {"workload": f"{r['workload']}: " + (f"T={r['T']} d={r['d']} F={r['F']} E={r['E']} "
+                                                         f"top-{r['k']}, seed {r['seed']}" if "d" in r else
+                                                         f"T={r['T']} per block, {r.get('blocks')} blocks"),
                    "global_batch": r["T"], "weight_copies": r.get("weight_copies"),
                    "experts_touched": r.get("experts_touched")},
         "timing": f"median of {args.repeats} runs of {args.steps} eager moe_forward steps after "
