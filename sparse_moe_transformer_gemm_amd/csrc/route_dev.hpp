@@ -67,8 +67,19 @@ __device__ __forceinline__ void select_token(const double* __restrict__ partial,
   if (tid < G * E) {
     const int e = tid % E, g = tid / E;
     double s = 0.0;
-#pragma unroll 4
-    for (int ks = g; ks < KS; ks += G) s += partial[((size_t)ks * T + t) * E + e];
+    // the slices g, g + G, ... are loaded eight at a time before any is added
+    // (one memory round trip per eight), then added in slice order
+    for (int k0 = g; k0 < KS; k0 += 8 * G) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ks = k0 + u * G;
+        v[u] = ks < KS ? partial[((size_t)ks * T + t) * E + e] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u * G < KS) s += v[u];
+    }
     part[g * E + e] = s;
   }
   __syncthreads();
