@@ -87,17 +87,19 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[0][b] = acc[1][b] = v4d{0.0, 0.0, 0.0, 0.0};
     int col[NB];
-    bool live[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      live[b] = 16 * (eb0 + b) + r < E;
-      col[b] = min(16 * (eb0 + b) + r, E - 1);
-    }
+    for (int b = 0; b < NB; ++b) col[b] = min(16 * (eb0 + b) + r, E - 1);
     auto load_x = [&](int c, uint4 (&xv)[4]) __attribute__((always_inline)) {
       const int blk = min(4 * c + q, nblk - 1);
       const uint4* p = reinterpret_cast<const uint4*>(xrow + 32 * blk);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xv[i] = p[i];
+      // a row past T or a block past K (the last chunk when K % 128 == 64)
+      // counts as zero: zeroed here once, so no step needs a select
+      if (!tv || 4 * c + q >= nblk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
     };
     auto load_w = [&](int hc, float (&wv)[kRtHalf][NB]) __attribute__((always_inline)) {
       const int c = hc >> 1, h = hc & 1;
@@ -110,18 +112,19 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
     };
     auto compute = [&](int hc, const uint4 (&xv)[4], const float (&wv)[kRtHalf][NB])
                        __attribute__((always_inline)) {
-      const bool ok = tv && 4 * (hc >> 1) + q < nblk;
       const int h = hc & 1;
       const uint32_t xw[8] = {xv[2 * h].x, xv[2 * h].y, xv[2 * h].z, xv[2 * h].w,
                               xv[2 * h + 1].x, xv[2 * h + 1].y, xv[2 * h + 1].z, xv[2 * h + 1].w};
 #pragma unroll
       for (int s2 = 0; s2 < kRtHalf; ++s2) {
         const float xf = bf16_to_f32(s2 & 1 ? (xw[s2 >> 1] >> 16) : (xw[s2 >> 1] & 0xffffu));
-        const double a = static_cast<double>(ok ? xf : 0.0f);
+        const double a = static_cast<double>(xf);
+        // columns past E read the last expert's weights: finite, and their
+        // logits are never stored
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          acc[s2 & 1][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(
-              a, static_cast<double>(live[b] ? wv[s2][b] : 0.0f), acc[s2 & 1][b], 0, 0, 0);
+          acc[s2 & 1][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, static_cast<double>(wv[s2][b]),
+                                                                acc[s2 & 1][b], 0, 0, 0);
       }
     };
     auto encode = [&](int c, const uint4 (&xv)[4]) __attribute__((always_inline)) {
