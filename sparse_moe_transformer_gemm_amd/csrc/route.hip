@@ -55,7 +55,10 @@ constexpr int kRtTok = 16;    // tokens per workgroup
 constexpr int kRtWaves = 8;   // wavefronts per workgroup, one K range each
 constexpr int kRtHalf = 16;   // K steps per half chunk (the unit of the load pipeline)
 
-template <int NB, bool ENC>
+// PAIR (NB = 2, E even): lane r of a pass holds experts 2r and 2r + 1 instead of
+// r and 16 + r, so each K row of W_r is one 8-byte load per lane (half the load
+// instructions of 4-byte loads, which the texture addresser takes at the same rate).
+template <int NB, bool ENC, bool PAIR>
 __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ bias, int T,
@@ -69,15 +72,20 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
   __shared__ int sel_e[kRtTok][8];
   constexpr int NT = kRtWaves * 64;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, q = lane >> 4;
+  // the wavefront index made uniform (SGPR), so the K-range loop needs no exec masks
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r = lane & 15,
+            q = lane >> 4;
   const int t0 = blockIdx.x * kRtTok;
   const bool tv = t0 + r < T;
   const int nblk = d / 32;
   const int nchunk = (nblk + 3) / 4;               // the last one may hold two blocks
   const int c0 = wave * nchunk / kRtWaves, c1 = (wave + 1) * nchunk / kRtWaves;
-  // rows past T read the last token (and count as zero); columns past E read the
-  // last expert, blocks past K the last block (both count as zero)
-  const uint16_t* xrow = x + (size_t)min(t0 + r, T - 1) * d;
+  // columns past E read the last expert and blocks past K the last block of W_r:
+  // valid addresses, and x is zero there
+  // the workgroup's rows of x as a buffer: a row past T, a block past K or a chunk
+  // past the wavefront's range reads zero through the range check, so no select
+  // on the loaded values (which would wait for every load in flight) is needed
+  const rsrc_t xr = make_rsrc(x + (size_t)t0 * d, (uint32_t)(min(kRtTok, T - t0) * d * 2));
   const int nbt = (E + 15) / 16;
   const uint32_t pitch = (uint32_t)nsteps_of(d) * kChunk;
 
@@ -86,29 +94,35 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
     v4d acc[2][NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[0][b] = acc[1][b] = v4d{0.0, 0.0, 0.0, 0.0};
+    static_assert(!PAIR || NB == 2, "expert pairs need two blocks per pass");
+    // the output column of block b held by lane r (the expert past 16 eb0)
+    auto ncol = [&](int b) { return PAIR ? 2 * r + b : 16 * b + r; };
     int col[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) col[b] = min(16 * (eb0 + b) + r, E - 1);
+    for (int b = 0; b < NB; ++b) col[b] = min(16 * eb0 + ncol(b), E - 1);
+    const int cpair = min(16 * eb0 + 2 * r, E - 2);   // PAIR: an even index, so 8-byte aligned
     auto load_x = [&](int c, uint4 (&xv)[4]) __attribute__((always_inline)) {
-      const int blk = min(4 * c + q, nblk - 1);
-      const uint4* p = reinterpret_cast<const uint4*>(xrow + 32 * blk);
+      const int blk = 4 * c + q;
+      const bool ok = tv && blk < nblk && c < c1;
+      const uint32_t off = (uint32_t)(r * d + 32 * blk) * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = p[i];
-      // a row past T or a block past K (the last chunk when K % 128 == 64)
-      // counts as zero: zeroed here once, so no step needs a select
-      if (!tv || 4 * c + q >= nblk) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xv[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int i = 0; i < 4; ++i) xv[i] = bload16(xr, ok ? off + 16 * i : kOutOfRange);
     };
     auto load_w = [&](int hc, float (&wv)[kRtHalf][NB]) __attribute__((always_inline)) {
       const int c = hc >> 1, h = hc & 1;
       const int blk = min(4 * c + q, nblk - 1);
       const float* wr = w + (size_t)(32 * blk + kRtHalf * h) * E;
 #pragma unroll
-      for (int s2 = 0; s2 < kRtHalf; ++s2)
+      for (int s2 = 0; s2 < kRtHalf; ++s2) {
+        if constexpr (PAIR) {
+          const float2 v2 = *reinterpret_cast<const float2*>(wr + (size_t)s2 * E + cpair);
+          wv[s2][0] = v2.x;
+          wv[s2][1] = v2.y;
+        } else {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) wv[s2][b] = wr[(size_t)s2 * E + col[b]];
+          for (int b = 0; b < NB; ++b) wv[s2][b] = wr[(size_t)s2 * E + col[b]];
+        }
+      }
     };
     auto compute = [&](int hc, const uint4 (&xv)[4], const float (&wv)[kRtHalf][NB])
                        __attribute__((always_inline)) {
@@ -160,10 +174,10 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
       // half 0 of chunk c (x in xa): prefetch half 1's weights and the next chunk's x
       const int c = hc >> 1;
       load_w(hc + 1, wb);
-      if (c + 1 < c1) load_x(c + 1, xb);
+      load_x(c + 1, xb);
       compute(hc, xa, wa);
       if (ENC && eb0 == 0) encode(c, xa);
-      if (hc + 2 < h1) load_w(hc + 2, wa);
+      load_w(min(hc + 2, h1 - 1), wa);   // past the range: a valid reload, unused
       compute(hc + 1, xa, wb);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xa[i] = xb[i];
@@ -176,7 +190,7 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            double& dst = red[q + 4 * j][16 * b + r];
+            double& dst = red[q + 4 * j][ncol(b)];
             const double v = acc[0][b][j] + acc[1][b][j];
             dst = wv2 == 0 ? v : dst + v;
           }
@@ -227,11 +241,14 @@ hipError_t launch_route_mfma(const uint16_t* x, const float* w_router, const flo
                              hipStream_t stream) {
   const dim3 grid((T + kRtTok - 1) / kRtTok), block(kRtWaves * 64);
   if (E <= 16)
-    hipLaunchKernelGGL((route_mfma<1, ENC>), grid, block, 0, stream, x, w_router, b_router, T, d, E, k,
-                       topk_idx, topk_w, xenc);
+    hipLaunchKernelGGL((route_mfma<1, ENC, false>), grid, block, 0, stream, x, w_router, b_router, T, d,
+                       E, k, topk_idx, topk_w, xenc);
+  else if (E % 2 == 0)
+    hipLaunchKernelGGL((route_mfma<2, ENC, true>), grid, block, 0, stream, x, w_router, b_router, T, d,
+                       E, k, topk_idx, topk_w, xenc);
   else
-    hipLaunchKernelGGL((route_mfma<2, ENC>), grid, block, 0, stream, x, w_router, b_router, T, d, E, k,
-                       topk_idx, topk_w, xenc);
+    hipLaunchKernelGGL((route_mfma<2, ENC, false>), grid, block, 0, stream, x, w_router, b_router, T, d,
+                       E, k, topk_idx, topk_w, xenc);
   return hipGetLastError();
 }
 

@@ -59,6 +59,8 @@ def test_decode_workload(gu):
     dict(T=96, d=512, F=4160, E=6, k=3, seed=39),         # prefill path, F not a multiple of 128
     dict(T=300, d=576, F=576, E=8, k=1, seed=43),         # prefill path, switch routing, half last step
     dict(T=5, d=512, F=512, E=1, k=1, seed=45),           # a single expert (E = k = 1)
+    dict(T=200, d=512, F=512, E=33, k=3, seed=50),        # many tokens, odd E (one expert per lane and block)
+    dict(T=150, d=576, F=512, E=34, k=5, seed=51),        # many tokens, even E past 32 (expert pairs, clamped)
 ])
 def test_edge_shapes(gu, shape):
     _full_check(gu, synth.tiny_workload(**shape))
