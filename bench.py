@@ -165,6 +165,19 @@ def _dev_inputs(L, dev):
         b_gate=bf16(L.b_gate), b_up=bf16(L.b_up), b_down=bf16(L.b_down)), bf16
 
 
+def xcd_tiles(counts: np.ndarray, d: int, F: int) -> dict:
+    """Tiles per XCD of the two persistent prefill GEMMs for these expert row
+    counts: ceil(rows / 128) row tiles per expert times the column tiles (192
+    h-columns per gate/up tile, 320 output columns per down tile), the list cut
+    into eight equal ranges, one per XCD, as the kernels schedule it."""
+    rt = int(sum((int(c) + 127) // 128 for c in counts))
+    out = {}
+    for name, ntn in (("gate_up", F // 192), ("down", d // 320)):
+        g = rt * ntn
+        out[name] = [g // 8 + (1 if x < g % 8 else 0) for x in range(8)]
+    return out
+
+
 def timed_runs(step, steps, warmup, repeats) -> list:
     """ms per step of `repeats` runs of exactly `steps` calls of step(i), each
     run between torch.cuda.synchronize() calls, after `warmup` untimed calls."""
@@ -282,6 +295,7 @@ def run_layer(cfg: int, steps: int, warmup: int, repeats: int, graph: bool, log)
     res = dict(
         workload=w.name, T=T, d=d, F=F, E=E, k=k, seed=w.seed, weight_copies=R, experts_touched=U,
         rows_per_expert=[int(counts.min()), int(counts.max())],
+        tiles_per_xcd=xcd_tiles(counts, d, F) if T > 64 else None,
         ms_per_step=ms, ms_per_step_best=float(min(eager)), ms_per_step_runs=eager,
         ms_per_step_graph=None if gr is None else float(np.median(gr)),
         ms_per_step_graph_best=None if gr is None else float(min(gr)),
