@@ -368,6 +368,18 @@ moe_status moe_rmsnorm(int32_t T, int32_t d, const moe_bf16* x, const moe_bf16* 
 moe_status moe_residual_add(int32_t T, int32_t d, const moe_bf16* x, const moe_bf16* m,
                             moe_bf16* out, void* stream);
 
+/* Residual add and the next pre-norm in one pass (the glue between two blocks
+ * of a pre-norm stack, x <- x + MoE(RMSNorm(x))):
+ *   x_out[t] = bf16(x[t] + m[t])                       as moe_residual_add,
+ *   n_out[t] = RMSNorm(x_out[t]) with gain and eps     as moe_rmsnorm,
+ * the same bytes as those two calls in that order, reading each row once.
+ * x_out may alias x; n_out must alias none of the others. x, m, x_out, n_out
+ * [device] bf16 [T][d]; gain [device] bf16 [d]; d a multiple of 8. Errors as
+ * for moe_rmsnorm. */
+moe_status moe_residual_rmsnorm(int32_t T, int32_t d, const moe_bf16* x, const moe_bf16* m,
+                                const moe_bf16* gain, float eps, moe_bf16* x_out,
+                                moe_bf16* n_out, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);
 

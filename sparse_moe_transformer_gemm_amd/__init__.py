@@ -19,7 +19,7 @@ import torch  # imported before the library so that it binds to torch's HIP runt
 
 __all__ = [
     "MoeError", "Dims", "MXFP4", "library_path", "lib", "workspace_bytes", "route",
-    "permute", "expert_ffn_mxfp4", "combine", "rmsnorm", "residual_add", "forward",
+    "permute", "expert_ffn_mxfp4", "combine", "rmsnorm", "residual_add", "residual_rmsnorm", "forward",
     "ExpertWeights", "EXPORTED", "pack_mxfp4", "packed_bytes", "load_expert_weights",
     "forward_calls", "expert_ffn_mxfp4_stage", "forward_noalloc", "Fp8Weights",
     "convert_mxfp4_to_fp8", "pack_fp8", "load_fp8_weights", "fp8_from_mxfp4", "expert_ffn_fp8",
@@ -35,6 +35,7 @@ EXPORTED = (
     "moe_forward_noalloc", "moe_forward_noalloc_max_bytes",
     "moe_convert_mxfp4_to_fp8", "moe_fp8_packed_bytes", "moe_pack_fp8", "moe_expert_ffn_fp8",
     "moe_round_weights_bf16", "moe_attention_workspace_bytes", "moe_attention_sink",
+    "moe_residual_rmsnorm",
 )
 
 
@@ -104,11 +105,12 @@ def lib() -> ctypes.CDLL:
     L.moe_pack_mxfp4.argtypes = [i32, i32, i32, MXFP4, vp, vp, vp]
     L.moe_rmsnorm.argtypes = [i32, i32, vp, vp, ctypes.c_float, vp, vp]
     L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp]
+    L.moe_residual_rmsnorm.argtypes = [i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_expert_ffn_mxfp4_stage",
               "moe_combine", "moe_rmsnorm",
               "moe_residual_add", "moe_pack_mxfp4", "moe_forward", "moe_forward_noalloc",
               "moe_convert_mxfp4_to_fp8", "moe_pack_fp8", "moe_expert_ffn_fp8", "moe_round_weights_bf16",
-              "moe_attention_sink"):
+              "moe_attention_sink", "moe_residual_rmsnorm"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -482,6 +484,23 @@ def residual_add(x, m, out=None):
                                   _dev(out, torch.bfloat16, (T, d), "out"), _stream()),
            "moe_residual_add")
     return out
+
+
+def residual_rmsnorm(x, m, gain, eps: float = 1e-5, x_out=None, n_out=None):
+    """x_out = x + m (bf16), n_out = rmsnorm(x_out): moe_residual_rmsnorm.
+    Returns (x_out, n_out); x_out may be x itself (in place)."""
+    T, d = x.shape
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    if n_out is None:
+        n_out = torch.empty_like(x)
+    _check(lib().moe_residual_rmsnorm(T, d, _dev(x, torch.bfloat16, (T, d), "x"),
+                                      _dev(m, torch.bfloat16, (T, d), "m"),
+                                      _dev(gain, torch.bfloat16, (d,), "gain"), float(eps),
+                                      _dev(x_out, torch.bfloat16, (T, d), "x_out"),
+                                      _dev(n_out, torch.bfloat16, (T, d), "n_out"), _stream()),
+           "moe_residual_rmsnorm")
+    return x_out, n_out
 
 
 def _outputs(T, d, E, k, dev, bufs: Optional[dict]) -> dict:

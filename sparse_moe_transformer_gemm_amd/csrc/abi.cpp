@@ -485,6 +485,23 @@ moe_status moe_residual_add(int32_t T, int32_t d, const moe_bf16* x, const moe_b
       moe::launch_residual_add(x, m, T, d, out, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_residual_rmsnorm(int32_t T, int32_t d, const moe_bf16* x, const moe_bf16* m,
+                                const moe_bf16* gain, float eps, moe_bf16* x_out,
+                                moe_bf16* n_out, void* stream) {
+  g_last_error[0] = 0;
+  if (T < 1 || d < 8 || d % 8 || T > (1 << 24) || d > (1 << 20) || !(eps >= 0.0f)) {
+    set_error("%s", "moe_residual_rmsnorm: need T >= 1, d a positive multiple of 8, eps >= 0");
+    return MOE_ERR_INVALID_ARG;
+  }
+  MOE_TRY(check_ptrs({x, m, gain, x_out, n_out}, "moe_residual_rmsnorm"));
+  if (n_out == x || n_out == m || n_out == x_out) {
+    set_error("%s", "moe_residual_rmsnorm: n_out must not alias x, m or x_out");
+    return MOE_ERR_INVALID_ARG;
+  }
+  return hip_status(moe::launch_residual_rmsnorm(x, m, gain, T, d, eps, x_out, n_out,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_string(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";

@@ -140,5 +140,10 @@ hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gain, int T, int d,
                           uint16_t* out, hipStream_t stream);
 hipError_t launch_residual_add(const uint16_t* x, const uint16_t* m, int T, int d,
                                uint16_t* out, hipStream_t stream);
+// xout = bf16(x + m), then nout = RMSNorm(xout) with `gain`: the bytes of
+// launch_residual_add followed by launch_rmsnorm, in one pass.
+hipError_t launch_residual_rmsnorm(const uint16_t* x, const uint16_t* m, const uint16_t* gain, int T,
+                                   int d, float eps, uint16_t* xout, uint16_t* nout,
+                                   hipStream_t stream);
 
 }  // namespace moe

@@ -198,6 +198,13 @@ def test_combine_norm_validation(moe):
     assert L.moe_rmsnorm(16, 12, FAKE, FAKE, 1e-5, FAKE, None) == -1
     assert L.moe_rmsnorm(16, 512, FAKE, FAKE, -1.0, FAKE, None) == -1
     assert L.moe_residual_add(0, 512, FAKE, FAKE, FAKE, None) == -1
+    # the fused residual + norm: bad d, bad eps, a null pointer, n_out aliasing x
+    FAKE2 = 0x20000
+    assert L.moe_residual_rmsnorm(16, 12, FAKE, FAKE2, FAKE, 1e-5, FAKE, FAKE2, None) == -1
+    assert L.moe_residual_rmsnorm(16, 512, FAKE, FAKE2, FAKE, -1.0, FAKE, FAKE2, None) == -1
+    assert L.moe_residual_rmsnorm(16, 512, FAKE, None, FAKE, 1e-5, FAKE, FAKE2, None) == -1
+    assert L.moe_residual_rmsnorm(16, 512, FAKE, FAKE2, FAKE, 1e-5, FAKE2, FAKE, None) == -1
+    assert b"alias" in L.moe_last_error()
 
 
 def test_status_strings(moe):

@@ -58,6 +58,33 @@ def test_rmsnorm_and_residual_small(gu):
     assert np.array_equal(gu.bits_host(xd), gu.bits_host(s))
 
 
+@pytest.mark.parametrize("T,d", [(37, 320), (5, 8192), (64, 2880)])
+def test_residual_rmsnorm_fused(gu, T, d):
+    """The fused residual + norm gives the bytes of residual_add then rmsnorm (d =
+    8192 takes the path past the 4096 elements a lane keeps in registers), in
+    place too, and its norm is within one bf16 ulp of the fp64 definition."""
+    import torch
+    import sparse_moe_transformer_gemm_amd as moe
+    rng = np.random.default_rng(51 + T)
+    xb = synth.bf16_bits(rng.standard_normal((T, d)) * 3)
+    gb = synth.bf16_bits(1 + 0.02 * rng.standard_normal(d))
+    mb = synth.bf16_bits(rng.standard_normal((T, d)) * 50)
+    g = gu.bf16_dev(gb)
+    s_sep = moe.residual_add(gu.bf16_dev(xb), gu.bf16_dev(mb))
+    n_sep = moe.rmsnorm(s_sep, g, 1e-5)
+    s_f, n_f = moe.residual_rmsnorm(gu.bf16_dev(xb), gu.bf16_dev(mb), g, 1e-5)
+    xd = gu.bf16_dev(xb)
+    s_ip, n_ip = moe.residual_rmsnorm(xd, gu.bf16_dev(mb), g, 1e-5, x_out=xd)
+    torch.cuda.synchronize()
+    for a, b in ((s_f, s_sep), (n_f, n_sep), (s_ip, s_sep), (n_ip, n_sep)):
+        assert np.array_equal(gu.bits_host(a), gu.bits_host(b))
+    s64 = oracle.bf16_to_f64(gu.bits_host(s_f))
+    assert np.all(np.abs(s64 - (oracle.bf16_to_f64(xb) + oracle.bf16_to_f64(mb)))
+                  <= 0.5 * _bf16_ulp(oracle.bf16_to_f64(xb) + oracle.bf16_to_f64(mb)))
+    n_ref = oracle.rmsnorm(s64, oracle.bf16_to_f64(gb), 1e-5)
+    assert np.all(np.abs(oracle.bf16_to_f64(gu.bits_host(n_f)) - n_ref) <= _bf16_ulp(n_ref))
+
+
 def test_stack24_teacher_forced(gu):
     import torch
     import sparse_moe_transformer_gemm_amd as moe
@@ -66,12 +93,19 @@ def test_stack24_teacher_forced(gu):
     x = gu.bf16_dev(w.x)
     ws = gu.workspace(T, d, F, E, k)
     saved = {}
+    # as bench.py runs it: the first block's norm alone, then each block's
+    # residual fused with the next block's norm
+    L_next = synth.stack_layer(4, 0)
+    n = moe.rmsnorm(x, gu.bf16_dev(L_next.gain), w.eps)
     for l in range(w.n_layers):
-        L = synth.stack_layer(4, l)
+        L = L_next
         wt = gu.weights_dev(L)
-        n = moe.rmsnorm(x, gu.bf16_dev(L.gain), w.eps)
         r = moe.forward(n, wt, k, ws)
-        x_new = moe.residual_add(x, r["out"])
+        if l + 1 < w.n_layers:
+            L_next = synth.stack_layer(4, l + 1)
+            x_new, n_next = moe.residual_rmsnorm(x, r["out"], gu.bf16_dev(L_next.gain), w.eps)
+        else:
+            x_new, n_next = moe.residual_add(x, r["out"]), None
         if l in CHECKED:
             torch.cuda.synchronize()
             saved[l] = dict(x=gu.bits_host(x), n=gu.bits_host(n), m=gu.bits_host(r["out"]),
@@ -80,7 +114,7 @@ def test_stack24_teacher_forced(gu):
                             offsets=r["perm"][1].cpu().numpy(),
                             sorted_pair=r["perm"][2].cpu().numpy(),
                             pair_row=r["perm"][3].cpu().numpy())
-        x = x_new
+        x, n = x_new, n_next
         del wt
     torch.cuda.synchronize()
 
