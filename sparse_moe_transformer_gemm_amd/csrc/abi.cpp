@@ -87,8 +87,9 @@ size_t workspace_for(const moe_dims& m) {
     const size_t f = moe::forward_front_bytes(m.T, m.d, m.F, m.E, m.k);
     r = r > f ? r : f;
   } else if (m.T > 64) {
-    // the whole-block call keeps the permutation's histograms past the FFN's regions
-    const size_t f = b + c;
+    // the whole-block call keeps the router's partial logits, then the
+    // permutation's histograms, past the FFN's regions
+    const size_t f = b + (a > c ? a : c);
     r = r > f ? r : f;
   }
   return (r + 255) & ~static_cast<size_t>(255);
@@ -296,7 +297,8 @@ static moe_status forward_launch(const moe_dims& dims, const moe_bf16* x, const 
                                                  sorted_pair, pair_row, ws, s)));
   } else if (many) {
     MOE_TRY(hip_status(moe::launch_route_encode(x, w_router, b_router, dims.T, dims.d, dims.E,
-                                                dims.k, topk_idx, topk_w, moe::ffn_xenc(a), s)));
+                                                dims.k, topk_idx, topk_w, moe::ffn_xenc(a),
+                                                moe::ffn_ws_end(a), s)));
     MOE_TRY(hip_status(moe::launch_permute(topk_idx, dims.T, dims.E, dims.k, counts, offsets,
                                            sorted_pair, pair_row, moe::ffn_ws_end(a), s,
                                            moe::ffn_tiles(a))));

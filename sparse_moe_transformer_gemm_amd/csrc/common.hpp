@@ -49,10 +49,11 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
                         void* ws, hipStream_t stream);
 
 // The many-token routing (T > 64) that also writes x encoded for the expert
-// GEMMs into xenc (rows of nsteps(d) * 208 bytes), as the FFN's own encode would.
+// GEMMs into xenc (rows of nsteps(d) * 208 bytes), as the FFN's own encode would;
+// ws: route_workspace_bytes(T, d, E) of scratch (its partial logits).
 hipError_t launch_route_encode(const uint16_t* x, const float* w_router, const float* b_router,
                                int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
-                               uint8_t* xenc, hipStream_t stream);
+                               uint8_t* xenc, void* ws, hipStream_t stream);
 
 // Several chunks of pairs (T * k > 512): per-chunk histograms in the workspace
 // (permute_workspace_bytes), then the ranks.

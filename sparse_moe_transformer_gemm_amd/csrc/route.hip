@@ -55,9 +55,26 @@ constexpr int kRtTok = 16;    // tokens per workgroup
 constexpr int kRtWaves = 8;   // wavefronts per workgroup, one K range each
 constexpr int kRtHalf = 16;   // K steps per half chunk (the unit of the load pipeline)
 
+// K ranges per 16-token group: two when the groups are fewer than the 256 CUs
+// of the MI355X and K has at least two chunks per wavefront in each range
+// (d >= 2048), else one (a pure function of T and d: the separate routing call
+// and the whole-block call make the same choice, so their logits are summed in
+// the same order).
+int route_ksplit(int T, int d) {
+  const int groups = (T + kRtTok - 1) / kRtTok;
+  const int nchunk = (d / 32 + 3) / 4;
+  return groups < 256 && nchunk >= 2 * kRtWaves ? 2 : 1;
+}
+
 // PAIR (NB = 2, E even): lane r of a pass holds experts 2r and 2r + 1 instead of
 // r and 16 + r, so each K row of W_r is one 8-byte load per lane (half the load
 // instructions of 4-byte loads, which the texture addresser takes at the same rate).
+//
+// K split (partial non-null, gridDim.y = KS > 1): workgroup (g, s) takes the
+// s-th of KS equal ranges of the K chunks for its 16 tokens and stores their
+// logit sums without bias to partial[s][t][e]; route_select then adds the KS
+// ranges in order, the bias, and takes the top k and the softmax. Used when the
+// 16-token groups are fewer than the CUs, so that K keeps every CU busy.
 template <int NB, bool ENC, bool PAIR>
 __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ w,
@@ -65,7 +82,8 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
                                                             int d, int E, int k,
                                                             int32_t* __restrict__ topk_idx,
                                                             float* __restrict__ topk_w,
-                                                            uint8_t* __restrict__ xenc) {
+                                                            uint8_t* __restrict__ xenc,
+                                                            double* __restrict__ partial) {
   __shared__ double red[kRtTok][16 * NB + 1];     // one pass: the K ranges, added in order
   __shared__ double logit[kRtTok][rt::kMaxE + 1];
   __shared__ double sel_v[kRtTok][8], sel_x[kRtTok][8];
@@ -79,7 +97,10 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
   const bool tv = t0 + r < T;
   const int nblk = d / 32;
   const int nchunk = (nblk + 3) / 4;               // the last one may hold two blocks
-  const int c0 = wave * nchunk / kRtWaves, c1 = (wave + 1) * nchunk / kRtWaves;
+  // this workgroup's K chunks [kc0, kc1), dealt over its wavefronts
+  const int ks = blockIdx.y, nks = gridDim.y;
+  const int kc0 = ks * nchunk / nks, kc1 = (ks + 1) * nchunk / nks;
+  const int c0 = kc0 + wave * (kc1 - kc0) / kRtWaves, c1 = kc0 + (wave + 1) * (kc1 - kc0) / kRtWaves;
   // columns past E read the last expert and blocks past K the last block of W_r:
   // valid addresses, and x is zero there
   // the workgroup's rows of x as a buffer: a row past T, a block past K or a chunk
@@ -202,12 +223,17 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
       const int e = 16 * eb0 + n;
       if (e < E) {
         double v = red[m][n];
-        if (bias) v += static_cast<double>(bias[e]);
-        logit[m][e] = v == v ? v : -INFINITY;
+        if (partial) {
+          if (t0 + m < T) partial[((size_t)ks * T + t0 + m) * E + e] = v;
+        } else {
+          if (bias) v += static_cast<double>(bias[e]);
+          logit[m][e] = v == v ? v : -INFINITY;
+        }
       }
     }
     __syncthreads();
   }
+  if (partial) return;   // the selection is route_select's
 
   // top k of each token: the rank of expert e is the number of experts before it
   // in (logit descending, index ascending) order; ranks are distinct
@@ -238,17 +264,23 @@ __global__ __launch_bounds__(kRtWaves * 64) void route_mfma(const uint16_t* __re
 template <bool ENC>
 hipError_t launch_route_mfma(const uint16_t* x, const float* w_router, const float* b_router, int T,
                              int d, int E, int k, int32_t* topk_idx, float* topk_w, uint8_t* xenc,
-                             hipStream_t stream) {
-  const dim3 grid((T + kRtTok - 1) / kRtTok), block(kRtWaves * 64);
+                             double* partial, hipStream_t stream) {
+  const int KS = route_ksplit(T, d);
+  double* part = KS > 1 ? partial : nullptr;
+  const dim3 grid((T + kRtTok - 1) / kRtTok, KS), block(kRtWaves * 64);
   if (E <= 16)
     hipLaunchKernelGGL((route_mfma<1, ENC, false>), grid, block, 0, stream, x, w_router, b_router, T, d,
-                       E, k, topk_idx, topk_w, xenc);
+                       E, k, topk_idx, topk_w, xenc, part);
   else if (E % 2 == 0)
     hipLaunchKernelGGL((route_mfma<2, ENC, true>), grid, block, 0, stream, x, w_router, b_router, T, d,
-                       E, k, topk_idx, topk_w, xenc);
+                       E, k, topk_idx, topk_w, xenc, part);
   else
     hipLaunchKernelGGL((route_mfma<2, ENC, false>), grid, block, 0, stream, x, w_router, b_router, T, d,
-                       E, k, topk_idx, topk_w, xenc);
+                       E, k, topk_idx, topk_w, xenc, part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || KS == 1) return err;
+  hipLaunchKernelGGL(route_select, dim3(T), dim3(256), 0, stream, part, KS, b_router, T, E, k, topk_idx,
+                     topk_w);
   return hipGetLastError();
 }
 
@@ -264,9 +296,10 @@ size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
 size_t route_workspace_bytes(int T, int d, int E) {
-  // the many-token kernel needs no scratch
   if (T <= rt::kSmallT) return al256((size_t)(d / 64) * T * E * sizeof(double));
-  return 0;
+  // the many-token kernel's partial logits when it splits K
+  const int KS = route_ksplit(T, d);
+  return KS > 1 ? al256((size_t)KS * T * E * sizeof(double)) : 0;
 }
 
 hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b_router, int T,
@@ -282,13 +315,15 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
                        E, k, topk_idx, topk_w);
     return hipGetLastError();
   }
-  return launch_route_mfma<false>(x, w_router, b_router, T, d, E, k, topk_idx, topk_w, nullptr, stream);
+  return launch_route_mfma<false>(x, w_router, b_router, T, d, E, k, topk_idx, topk_w, nullptr,
+                                  static_cast<double*>(ws), stream);
 }
 
 hipError_t launch_route_encode(const uint16_t* x, const float* w_router, const float* b_router,
                                int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
-                               uint8_t* xenc, hipStream_t stream) {
-  return launch_route_mfma<true>(x, w_router, b_router, T, d, E, k, topk_idx, topk_w, xenc, stream);
+                               uint8_t* xenc, void* ws, hipStream_t stream) {
+  return launch_route_mfma<true>(x, w_router, b_router, T, d, E, k, topk_idx, topk_w, xenc,
+                                 static_cast<double*>(ws), stream);
 }
 
 }  // namespace moe

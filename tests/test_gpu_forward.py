@@ -21,6 +21,7 @@ SHAPES = [
     dict(T=40, d=768, F=512, E=64, k=4, seed=44),    # F < d
     dict(T=8, d=4608, F=512, E=4, k=2, seed=38),     # K beyond the decode kernels: separate launches
     dict(T=128, d=512, F=512, E=32, k=4, seed=40),   # T above the decode limit: separate launches
+    dict(T=200, d=2304, F=512, E=16, k=2, seed=52),  # many tokens, router K split in two
 ]
 
 

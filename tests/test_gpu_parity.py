@@ -61,6 +61,8 @@ def test_decode_workload(gu):
     dict(T=5, d=512, F=512, E=1, k=1, seed=45),           # a single expert (E = k = 1)
     dict(T=200, d=512, F=512, E=33, k=3, seed=50),        # many tokens, odd E (one expert per lane and block)
     dict(T=150, d=576, F=512, E=34, k=5, seed=51),        # many tokens, even E past 32 (expert pairs, clamped)
+    dict(T=200, d=2304, F=512, E=16, k=2, seed=52),       # router K split in two (few token groups, long K)
+    dict(T=100, d=2048, F=512, E=40, k=3, seed=53),       # K split, expert pairs over two passes
 ])
 def test_edge_shapes(gu, shape):
     _full_check(gu, synth.tiny_workload(**shape))
