@@ -63,6 +63,7 @@ def test_decode_workload(gu):
     dict(T=150, d=576, F=512, E=34, k=5, seed=51),        # many tokens, even E past 32 (expert pairs, clamped)
     dict(T=200, d=2304, F=512, E=16, k=2, seed=52),       # router K split in two (few token groups, long K)
     dict(T=100, d=2048, F=512, E=40, k=3, seed=53),       # K split, expert pairs over two passes
+    dict(T=90, d=2112, F=512, E=8, k=2, seed=54),         # K split with a half last chunk (17 chunks)
 ])
 def test_edge_shapes(gu, shape):
     _full_check(gu, synth.tiny_workload(**shape))
