@@ -164,6 +164,12 @@ moe_status moe_pack_mxfp4(int32_t E, int32_t N, int32_t K, moe_mxfp4 src, uint8_
  *     weights on every call; the packed bytes are the stored bytes reordered;
  *   - d and F are multiples of 64 (the MFMA step covers two 32-element blocks)
  *     and at least MOE_MIN_FFN_K.
+ * With more than 64 tokens the down GEMM tiles its d output columns by 320, 192
+ * or 128; a d that none of them divides (64 mod 128 and a multiple of neither
+ * 192 nor 320, e.g. 704, 832, 2752) takes the weight-streaming kernel of the
+ * small batches instead (correct, slower: it reads each expert's weights once
+ * per 16 rows), which needs F <= 4096: otherwise MOE_ERR_UNSUPPORTED. This also
+ * holds for moe_expert_ffn_mxfp4_stage, moe_forward and moe_forward_noalloc.
  * For every expert e and row p in [offsets[e], offsets[e+1]), with
  * t = sorted_pair[p] / k:
  *   g = x[t] Wg[e]^T + b_gate[e],  u = x[t] Wu[e]^T + b_up[e],

@@ -49,6 +49,17 @@ moe_status check_dims(const moe_dims& m) {
 // bound (at K = 64 about 18 in a million outputs of y exceed it; at K = 256 a
 // few of 4e7 do), while at K >= 512 its largest value over 4e7 outputs stays
 // below two thirds of it.
+// The MXFP4 expert GEMMs: for T > 64 an output width d that no prefill column
+// tile divides (d = 64 mod 128, a multiple of neither 192 nor 320) takes the
+// weight-streaming down kernel, which unrolls K = F up to 4096.
+moe_status check_mxfp4_tiles(const moe_dims& m) {
+  if (!moe::ffn_supported(m.T, m.d, m.F)) {
+    set_error("%s", "dims: for T > 64, a d that 128, 192 and 320 do not divide needs F <= 4096");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
 moe_status check_ffn_k(const moe_dims& m) {
   if (m.d < MOE_MIN_FFN_K || m.F < MOE_MIN_FFN_K) {
     set_error("%s", "dims: the expert FFN needs d >= 512 and F >= 512 (MOE_MIN_FFN_K)");
@@ -213,6 +224,7 @@ moe_status moe_expert_ffn_mxfp4(moe_dims dims, const moe_bf16* x, const int32_t*
                                 size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   moe::FfnArgs a;
+  MOE_TRY(check_mxfp4_tiles(dims));
   MOE_TRY(ffn_args(dims, x, sorted_pair, offsets, w_gate, w_up, w_down, b_gate, b_up, b_down,
                    y_sorted, ws, ws_bytes, "moe_expert_ffn_mxfp4", a));
   return hip_status(moe::launch_expert_ffn(a, static_cast<hipStream_t>(stream)));
@@ -230,6 +242,7 @@ moe_status moe_expert_ffn_mxfp4_stage(moe_dims dims, const moe_bf16* x, const in
     return MOE_ERR_INVALID_ARG;
   }
   moe::FfnArgs a;
+  MOE_TRY(check_mxfp4_tiles(dims));
   MOE_TRY(ffn_args(dims, x, sorted_pair, offsets, w_gate, w_up, w_down, b_gate, b_up, b_down,
                    y_sorted, ws, ws_bytes, "moe_expert_ffn_mxfp4_stage", a));
   return hip_status(moe::launch_expert_ffn_stage(a, static_cast<hipStream_t>(stream), (int)stage));
@@ -247,6 +260,7 @@ static moe_status forward_checks(const moe_dims& dims, const moe_bf16* x, const 
                                  const char* who) {
   MOE_TRY(check_dims(dims));
   MOE_TRY(check_ffn_k(dims));
+  MOE_TRY(check_mxfp4_tiles(dims));
   MOE_TRY(check_ptrs({x, w_router, w_gate.codes, w_gate.scales, w_up.codes, w_up.scales,
                       w_down.codes, w_down.scales, b_gate, b_up, b_down, topk_idx, topk_w,
                       counts, offsets, sorted_pair, pair_row, y_sorted, out},
@@ -299,9 +313,10 @@ static moe_status forward_launch(const moe_dims& dims, const moe_bf16* x, const 
     MOE_TRY(hip_status(moe::launch_route_encode(x, w_router, b_router, dims.T, dims.d, dims.E,
                                                 dims.k, topk_idx, topk_w, moe::ffn_xenc(a),
                                                 moe::ffn_ws_end(a), s)));
-    MOE_TRY(hip_status(moe::launch_permute(topk_idx, dims.T, dims.E, dims.k, counts, offsets,
-                                           sorted_pair, pair_row, moe::ffn_ws_end(a), s,
-                                           moe::ffn_tiles(a))));
+    MOE_TRY(hip_status(moe::launch_permute(
+        topk_idx, dims.T, dims.E, dims.k, counts, offsets, sorted_pair, pair_row, moe::ffn_ws_end(a), s,
+        moe::ffn_tiles(a),
+        moe::ffn_down_decode(dims.T, dims.d, dims.F) ? moe::ffn_passes(a) : nullptr)));
   } else {
     MOE_TRY(hip_status(moe::launch_route(x, w_router, b_router, dims.T, dims.d, dims.E, dims.k,
                                          topk_idx, topk_w, ws, s)));

@@ -58,11 +58,12 @@ hipError_t launch_route_encode(const uint16_t* x, const float* w_router, const f
 // Several chunks of pairs (T * k > 512): per-chunk histograms in the workspace
 // (permute_workspace_bytes), then the ranks.
 size_t permute_workspace_bytes(int T, int E, int k);
-// With tiles non-null, the workgroup that writes the offsets also builds the
-// expert GEMMs' 128-row tile table there (as the FFN's encode launch would).
+// With tiles (passes) non-null, the workgroup that writes the offsets also
+// builds the expert GEMMs' 128-row tile table (16-row pass table) there, as the
+// FFN's encode launch would.
 hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row, void* ws,
-                          hipStream_t stream, int4* tiles = nullptr);
+                          hipStream_t stream, int4* tiles = nullptr, int4* passes = nullptr);
 
 // Repack one [E][N][K] MXFP4 tensor from the OCP layout into the packed
 // fragment layout (layout.hpp).
@@ -83,6 +84,11 @@ struct FfnArgs {
 size_t ffn_workspace_bytes(int T, int d, int F, int E, int k);
 // Both expert GEMMs take the weight-streaming decode kernels at this shape.
 bool ffn_decode_shape(int T, int d, int F);
+// The down GEMM takes the weight-streaming kernel (T <= 64, or an output width
+// that no prefill column tile divides); such widths then need F <= 4096, which
+// ffn_supported checks.
+bool ffn_down_decode(int T, int d, int F);
+bool ffn_supported(int T, int d, int F);
 // front_done: x is already encoded and the tile tables the GEMMs need are
 // built in the workspace (by launch_forward_front at decode sizes, by
 // launch_route_encode and launch_permute with the tile table otherwise).
@@ -91,6 +97,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, bool front_do
 // workspace (for callers that fill them themselves).
 uint8_t* ffn_xenc(const FfnArgs& a);
 int4* ffn_tiles(const FfnArgs& a);
+int4* ffn_passes(const FfnArgs& a);  // the 16-row pass table of the decode kernels
 // The workspace past the FFN's regions (ffn_workspace_bytes from the start):
 // where the whole-block call keeps the permutation's chunk histograms while the
 // encoded x already sits in the FFN's region.

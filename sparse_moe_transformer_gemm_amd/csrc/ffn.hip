@@ -1083,6 +1083,19 @@ bool ffn_decode_shape(int T, int d, int F) {
   return T <= kDecodeMaxT && decode_fits(d) && decode_fits(F);
 }
 
+// The prefill down GEMM tiles the output columns by 320, 192 or 128; a width
+// that none of them divides (d = 64 mod 128 and a multiple of neither 192 nor
+// 320) takes the weight-streaming kernel at any T.
+bool ffn_down_decode(int T, int d, int F) {
+  const bool no_tile = d % 320 != 0 && d % 192 != 0 && d % 128 != 0;
+  return decode_fits(F) && (T <= kDecodeMaxT || no_tile);
+}
+
+bool ffn_supported(int T, int d, int F) {
+  const bool no_tile = d % 320 != 0 && d % 192 != 0 && d % 128 != 0;
+  return !(T > kDecodeMaxT && no_tile && !decode_fits(F));
+}
+
 hipError_t launch_expert_ffn_stage(const FfnArgs& a, hipStream_t stream, int stage, bool front_done) {
   const WsLayout L = ws_layout(a.T, a.d, a.F, a.E, a.k);
   int dev = 0, ncu = 0;
@@ -1098,7 +1111,7 @@ hipError_t launch_expert_ffn_stage(const FfnArgs& a, hipStream_t stream, int sta
   // it can unroll, the LDS-tiled kernel otherwise (both read/write the same
   // encoded layouts, so they can be mixed).
   const bool dec_gu = a.T <= kDecodeMaxT && decode_fits(a.d);
-  const bool dec_dn = a.T <= kDecodeMaxT && decode_fits(a.F);
+  const bool dec_dn = ffn_down_decode(a.T, a.d, a.F);
   int4* pp = reinterpret_cast<int4*>(ws + L.passes);
   const TableJob tj{a.offsets, a.E, (!dec_gu || !dec_dn) ? tp : nullptr, (dec_gu || dec_dn) ? pp : nullptr};
 
@@ -1129,7 +1142,7 @@ hipError_t launch_expert_ffn_stage(const FfnArgs& a, hipStream_t stream, int sta
     if (a.d % 320 == 0) return launch_prefill<5, false>(a, henc, henc, tp, ncu, stream);
     if (a.d % 192 == 0) return launch_prefill<3, false>(a, henc, henc, tp, ncu, stream);
     if (a.d % 128 == 0) return launch_prefill<2, false>(a, henc, henc, tp, ncu, stream);
-    return launch_prefill<1, false>(a, henc, henc, tp, ncu, stream);
+    return hipErrorInvalidValue;   // rejected by ffn_supported
   }
   return hipErrorInvalidValue;
 }
@@ -1140,6 +1153,10 @@ uint8_t* ffn_xenc(const FfnArgs& a) {
 
 int4* ffn_tiles(const FfnArgs& a) {
   return reinterpret_cast<int4*>(static_cast<uint8_t*>(a.ws) + ws_layout(a.T, a.d, a.F, a.E, a.k).tiles);
+}
+
+int4* ffn_passes(const FfnArgs& a) {
+  return reinterpret_cast<int4*>(static_cast<uint8_t*>(a.ws) + ws_layout(a.T, a.d, a.F, a.E, a.k).passes);
 }
 
 void* ffn_ws_end(const FfnArgs& a) {

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(pm::kThreads) void permute_kernel(const int32_t* __
                                                                int32_t* __restrict__ sorted_pair,
                                                                int32_t* __restrict__ pair_row,
                                                                const int32_t* __restrict__ chist,
-                                                               int4* __restrict__ tiles) {
+                                                               int4* __restrict__ tiles,
+                                                               int4* __restrict__ passes) {
   __shared__ int offs[pm::kMaxE + 1];
   __shared__ int s[257];
   pm::permute_chunk(idx, P, E, blockIdx.x * pm::kChunk, blockIdx.x == 0, counts, offsets, sorted_pair,
@@ -40,6 +41,10 @@ __global__ __launch_bounds__(pm::kThreads) void permute_kernel(const int32_t* __
   if (tiles && blockIdx.x == 0) {
     __syncthreads();
     build_tile_table<kBM>(offs, E, tiles, s);
+  }
+  if (passes && blockIdx.x == 0) {
+    __syncthreads();
+    build_tile_table<kDecRows>(offs, E, passes, s);
   }
 }
 
@@ -52,7 +57,7 @@ size_t permute_workspace_bytes(int T, int E, int k) {
 
 hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_row, void* ws,
-                          hipStream_t stream, int4* tiles) {
+                          hipStream_t stream, int4* tiles, int4* passes) {
   const int P = T * k;
   const int blocks = (P + pm::kChunk - 1) / pm::kChunk;
   int32_t* chist = nullptr;
@@ -63,7 +68,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t*
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(pm::kThreads), 0, stream, topk_idx, P, E,
-                     counts, offsets, sorted_pair, pair_row, chist, tiles);
+                     counts, offsets, sorted_pair, pair_row, chist, tiles, passes);
   return hipGetLastError();
 }
 

@@ -109,6 +109,15 @@ def test_ffn_validation(moe):
         assert a[11] > 0  # routing and dispatch still accept the widths
         assert L.moe_expert_ffn_mxfp4(small, *a) == -2, (dd, ff)
         assert b"512" in L.moe_last_error()
+    # many tokens at a width no prefill column tile divides (d = 64 mod 128, not a
+    # multiple of 192 or 320): the down GEMM streams, which needs F <= 4096
+    wide = D(100, 832, 8192, 32, 4)
+    a = list(args); a[11] = L.moe_workspace_bytes(wide)
+    assert L.moe_expert_ffn_mxfp4(wide, *a) == -2
+    assert b"4096" in L.moe_last_error()
+    fine = D(100, 832, 4096, 32, 4)
+    a = list(args); a[3] = bad; a[11] = L.moe_workspace_bytes(fine)
+    assert L.moe_expert_ffn_mxfp4(fine, *a) == -1   # accepted dims, rejected for the null pointer
 
 
 def test_pack_sizes_and_validation(moe):

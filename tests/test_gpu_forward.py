@@ -22,6 +22,7 @@ SHAPES = [
     dict(T=8, d=4608, F=512, E=4, k=2, seed=38),     # K beyond the decode kernels: separate launches
     dict(T=128, d=512, F=512, E=32, k=4, seed=40),   # T above the decode limit: separate launches
     dict(T=200, d=2304, F=512, E=16, k=2, seed=52),  # many tokens, router K split in two
+    dict(T=150, d=832, F=576, E=12, k=2, seed=57),   # many tokens, streaming down GEMM (pass table from the permutation)
 ]
 
 

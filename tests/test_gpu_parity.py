@@ -64,6 +64,8 @@ def test_decode_workload(gu):
     dict(T=200, d=2304, F=512, E=16, k=2, seed=52),       # router K split in two (few token groups, long K)
     dict(T=100, d=2048, F=512, E=40, k=3, seed=53),       # K split, expert pairs over two passes
     dict(T=90, d=2112, F=512, E=8, k=2, seed=54),         # K split with a half last chunk (17 chunks)
+    dict(T=300, d=704, F=512, E=8, k=2, seed=55),         # d no prefill column tile divides: streaming down GEMM
+    dict(T=442, d=2752, F=832, E=34, k=3, seed=1165, zipf=True),  # the same at a wide d, K split, expert pairs
 ])
 def test_edge_shapes(gu, shape):
     _full_check(gu, synth.tiny_workload(**shape))
