@@ -23,11 +23,13 @@ def gu():
     return gpu_util
 
 
-def _shapes(n: int = 14, seed: int = 2026):
+def _shapes(n: int = 14, seed: int = 2026, many: bool = False):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
         T = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 601))]))
+        if many:   # the prefill kernels only
+            T = int(rng.integers(65, 601))
         d = 64 * int(rng.integers(8, 57))          # 512 .. 3584
         F = 64 * int(rng.integers(8, 41))          # 512 .. 2560
         E = int(rng.choice([int(rng.integers(1, 40)), int(rng.integers(40, 257))]))
@@ -40,6 +42,7 @@ def _shapes(n: int = 14, seed: int = 2026):
     return out
 
 
-@pytest.mark.parametrize("shape", _shapes(), ids=lambda s: f"T{s['T']}-d{s['d']}-F{s['F']}-E{s['E']}-k{s['k']}")
+@pytest.mark.parametrize("shape", _shapes() + _shapes(10, 7, many=True),
+                         ids=lambda s: f"T{s['T']}-d{s['d']}-F{s['F']}-E{s['E']}-k{s['k']}")
 def test_random_shape(gu, shape):
     _full_check(gu, synth.tiny_workload(**shape))
