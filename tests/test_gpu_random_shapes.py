@@ -46,3 +46,55 @@ def _shapes(n: int = 14, seed: int = 2026, many: bool = False):
                          ids=lambda s: f"T{s['T']}-d{s['d']}-F{s['F']}-E{s['E']}-k{s['k']}")
 def test_random_shape(gu, shape):
     _full_check(gu, synth.tiny_workload(**shape))
+
+
+def _fp8_shapes(n: int = 8, seed: int = 31):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(rng.integers(1, 65)) if len(out) % 2 else int(rng.integers(65, 601))
+        d, F = 64 * int(rng.integers(8, 41)), 64 * int(rng.integers(8, 41))
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(8, E) + 1))
+        if T * k * d * F * 3 > 4e10 or E * d * F > 4e8:
+            continue
+        out.append(dict(T=T, d=d, F=F, E=E, k=k, seed=int(rng.integers(3000, 4000))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _fp8_shapes(), ids=lambda s: f"fp8-T{s['T']}-d{s['d']}-F{s['F']}-E{s['E']}-k{s['k']}")
+def test_random_shape_fp8(gu, shape):
+    """The FP8 expert FFN on MXFP4 weights converted on the GPU (the same numbers,
+    so the MXFP4 oracle is the reference)."""
+    import oracle
+    from test_gpu_fp8 import _ffn_fp8_check, _fp8_layer_from_mxfp4
+    w = synth.tiny_workload(**shape)
+    L = w.layers[0]
+    wt8 = _fp8_layer_from_mxfp4(gu, L)
+    x = oracle.bf16_to_f64(w.x)
+    _ffn_fp8_check(gu, w, wt8, lambda g: oracle.ffn_sorted(x, g["sorted_pair"], g["offsets"], w.k, L))
+
+
+def _attn_shapes(n: int = 10, seed: int = 41):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B = int(rng.integers(1, 5))
+        S = int(rng.integers(1, 3001))
+        Tq = int(rng.integers(1, min(S, 400) + 1)) if len(out) % 2 else int(rng.integers(1, min(S, 6) + 1))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.integers(1, 9))
+        window = 0 if rng.integers(0, 2) else int(rng.integers(1, S + 1))
+        if B * Hq * Tq * S > 3e8:
+            continue
+        out.append(dict(B=B, Tq=Tq, S=S, Hq=Hq, Hkv=Hkv, window=window, seed=int(rng.integers(5000, 6000))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _attn_shapes(),
+                         ids=lambda d: f"attn-B{d['B']}-Tq{d['Tq']}-S{d['S']}-H{d['Hq']}/{d['Hkv']}-w{d['window']}")
+def test_random_shape_attention(gu, shape):
+    """Attention with sinks (causal, grouped heads, optional window, split or
+    unsplit keys) against the oracle under the per-element bound."""
+    from test_gpu_attention import _check
+    _check(gu, **shape)
