@@ -33,7 +33,9 @@ def _snapshot(r: dict) -> dict:
 @pytest.mark.parametrize("shape", [
     dict(T=16, d=2880, F=2880, E=32, k=4, seed=1),   # decode-20b shape: the fused front end
     dict(T=200, d=512, F=576, E=16, k=4, seed=48),   # separate launches (T > 64)
-], ids=["decode", "prefill-path"])
+    dict(T=200, d=2304, F=512, E=16, k=2, seed=52),  # router K split (partials, then the selection launch)
+    dict(T=150, d=832, F=576, E=12, k=2, seed=57),   # streaming down GEMM, pass table from the permutation
+], ids=["decode", "prefill-path", "k-split", "streaming-down"])
 def test_forward_graph_replays(gu, shape):
     import torch
 
