@@ -32,10 +32,12 @@
 //                   step accumulator with unit B scale, then acc += block scale
 //                   * step (the block scale is per 128 rows x 128 K, one value
 //                   per group and step). Accumulators start at the bias.
-//                   Operands come straight from global memory, the next
-//                   step's loaded while the current step's MFMAs run (2
-//                   wavefronts per SIMD). With many rows a workgroup of four
-//                   wavefronts takes a 128-row tile (see grouped_fp8).
+//                   The next step's operands are loaded while the current
+//                   step's MFMAs run. With one wavefront everything comes
+//                   straight from global memory (2 wavefronts per SIMD). With
+//                   many rows a workgroup of four wavefronts takes a 128-row
+//                   tile; the four share each step's weight codes, loaded once
+//                   per workgroup into a double-buffered LDS stage.
 #include "ffn_dev.hpp"
 #include "mx6.hpp"
 
@@ -155,6 +157,11 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const
                                                           uint8_t* __restrict__ hout,
                                                           const int4* __restrict__ tiles, int ncolu) {
   __shared__ __attribute__((aligned(16))) float stage_all[WAVES][32 * 36];
+  // WAVES = 4: each K step's weight codes (both 32-row groups, 8 KB) are loaded
+  // once per workgroup into one of two LDS buffers, a step ahead, and every
+  // wavefront reads its operands there (instead of each wavefront loading all
+  // of them: the texture addressers were the bound)
+  __shared__ __attribute__((aligned(16))) uint8_t bsm[WAVES == 4 ? 4 * 4096 : 16];
   int mt, u;
   if constexpr (WAVES == 1) {
     mt = blockIdx.x;
@@ -174,18 +181,28 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const
   const int r0 = __builtin_amdgcn_readfirstlane(ent.y) + 32 * wave;
   const int off = __builtin_amdgcn_readfirstlane(ent.z);
   const int rows = min(32, __builtin_amdgcn_readfirstlane(ent.w) - r0);
-  if (rows <= 0) return;   // (no workgroup barrier below)
+  // WAVES = 1 has no workgroup barrier; with WAVES = 4 a wavefront without rows
+  // still takes part in the weight staging and its barriers (it reads the tile's
+  // first row and stores nothing)
+  if (WAVES == 1 && rows <= 0) return;
+  const int rbase = rows > 0 ? r0 : __builtin_amdgcn_readfirstlane(ent.y);
   float* stage = stage_all[wave];
   const int K = GATEUP ? a.d : a.F, N = GATEUP ? a.F : a.d;
   const int nst = nsteps_of(K), nblkK = K / 32;
   const int nbN = (N + 127) / 128;
   const int g0 = GATEUP ? u : 2 * u, g1 = GATEUP ? u : 2 * u + 1;
 
-  const int rr = min(lr, rows - 1);
-  const uint32_t arow = GATEUP ? (uint32_t)a.sorted_pair[off + r0 + rr] / (uint32_t)a.k : (uint32_t)(off + r0 + rr);
+  const int rr = rows > 0 ? min(lr, rows - 1) : 0;
+  const uint32_t arow =
+      GATEUP ? (uint32_t)a.sorted_pair[off + rbase + rr] / (uint32_t)a.k : (uint32_t)(off + rbase + rr);
   const uint8_t* A = ain + (size_t)arow * nst * kChunk;
-  const uint8_t* B0 = (GATEUP ? a.wg_codes : a.wd_codes) + ((size_t)e * (N / 32) + g0) * nst * kF8Step + lane * 32;
-  const uint8_t* B1 = (GATEUP ? a.wu_codes : a.wd_codes) + ((size_t)e * (N / 32) + g1) * nst * kF8Step + lane * 32;
+  const uint8_t* Bg0 = (GATEUP ? a.wg_codes : a.wd_codes) + ((size_t)e * (N / 32) + g0) * nst * kF8Step;
+  const uint8_t* Bg1 = (GATEUP ? a.wu_codes : a.wd_codes) + ((size_t)e * (N / 32) + g1) * nst * kF8Step;
+  const uint8_t* B0 = Bg0 + lane * 32;
+  const uint8_t* B1 = Bg1 + lane * 32;
+  // WAVES = 4 staging: thread t copies bytes 32 (t % 128) .. + 31 of group t / 128
+  const uint8_t* Bst = (threadIdx.x < 128 ? Bg0 : Bg1) + (threadIdx.x & 127) * 32;
+  const uint32_t bst_lds = (threadIdx.x >> 7) * kF8Step + (threadIdx.x & 127) * 32;
   const float* S0 = reinterpret_cast<const float*>(GATEUP ? a.wg_scales : a.wd_scales) +
                     ((size_t)e * nbN + (32 * g0) / 128) * nst;
   const float* S1 = reinterpret_cast<const float*>(GATEUP ? a.wu_scales : a.wd_scales) +
@@ -220,22 +237,58 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const
 #pragma unroll
     for (int i = 0; i < 6; ++i) o.a[i] = ap[i];
     o.sa = *reinterpret_cast<const int*>(A + (size_t)j * kChunk + kChunkScales + 4 * half);
-    const v8i* p0 = reinterpret_cast<const v8i*>(B0 + (size_t)j * kF8Step);
-    const v8i* p1 = reinterpret_cast<const v8i*>(B1 + (size_t)j * kF8Step);
-    o.b00 = p0[0];
-    o.b01 = p0[64];
-    o.b10 = p1[0];
-    o.b11 = p1[64];
+    if constexpr (WAVES == 1) {
+      const v8i* p0 = reinterpret_cast<const v8i*>(B0 + (size_t)j * kF8Step);
+      const v8i* p1 = reinterpret_cast<const v8i*>(B1 + (size_t)j * kF8Step);
+      o.b00 = p0[0];
+      o.b01 = p0[64];
+      o.b10 = p1[0];
+      o.b11 = p1[64];
+    }
     o.s0 = S0[j];
     o.s1 = S1[j];
   };
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  auto stage_load = [&](int j, u4v (&r)[2]) __attribute__((always_inline)) {
+    const u4v* p = reinterpret_cast<const u4v*>(Bst + (size_t)j * kF8Step);
+    r[0] = p[0];
+    r[1] = p[1];
+  };
+  auto stage_store = [&](int buf, const u4v (&r)[2]) __attribute__((always_inline)) {
+    u4v* q = reinterpret_cast<u4v*>(bsm + buf * 2 * kF8Step + bst_lds);
+    q[0] = r[0];
+    q[1] = r[1];
+  };
   Ops cur, nxt;
   load_ops(0, cur);
+  if constexpr (WAVES == 4) {
+    u4v r[2];
+    stage_load(0, r);
+    stage_store(0, r);
+    __syncthreads();
+  }
   for (int j = 0; j < nst; ++j) {
+    u4v bnext[2];
+    if constexpr (WAVES == 4) {
+      if (j + 1 < nst) stage_load(j + 1, bnext);
+    }
     if (j + 1 < nst) load_ops(j + 1, nxt);
     const v4i a0 = cur.a[0], a1 = cur.a[1], a2 = cur.a[2], a3 = cur.a[3], a4 = cur.a[4], a5 = cur.a[5];
     int sa = cur.sa;
-    const v8i b00 = cur.b00, b01 = cur.b01, b10 = cur.b10, b11 = cur.b11;
+    v8i b00, b01, b10, b11;
+    if constexpr (WAVES == 4) {
+      const v8i* l0 = reinterpret_cast<const v8i*>(bsm + (j & 1) * 2 * kF8Step + lane * 32);
+      const v8i* l1 = reinterpret_cast<const v8i*>(bsm + (j & 1) * 2 * kF8Step + kF8Step + lane * 32);
+      b00 = l0[0];
+      b01 = l0[64];
+      b10 = l1[0];
+      b11 = l1[64];
+    } else {
+      b00 = cur.b00;
+      b01 = cur.b01;
+      b10 = cur.b10;
+      b11 = cur.b11;
+    }
     const float s0 = cur.s0, s1 = cur.s1;
     // in a half step at the end of K (K % 128 == 64) lane half 1 has no blocks:
     // its B codes are zero and its A codes finite (E2M3 has no NaN), so only the
@@ -257,6 +310,11 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const
     for (int i = 0; i < 16; ++i) {
       acc0[i] = fmaf(s0, t0[i], acc0[i]);
       acc1[i] = fmaf(s1, t1[i], acc1[i]);
+    }
+    if constexpr (WAVES == 4) {
+      // the buffer of step j - 1, free since the last barrier
+      if (j + 1 < nst) stage_store((j + 1) & 1, bnext);
+      __syncthreads();
     }
     cur = nxt;
   }
