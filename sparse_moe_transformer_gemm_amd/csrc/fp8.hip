@@ -23,21 +23,22 @@
 //                   elements 16h.. of block 4j + 2 + s (the A halves of MFMA
 //                   half s being blocks 4j + s and 4j + 2 + s, as for MXFP4);
 //                   zero past K.
-//   grouped_fp8     the expert GEMMs. A workgroup is one wavefront and takes
-//                   one 32-row tile of the dispatch rows of an expert (a 32-row
-//                   tile table) and one column unit: 32 h-columns (their gate
-//                   and up rows) for gate/up, 64 output columns for down. Per
-//                   128-deep K step: four MFMAs (two K halves x the hi and lo
-//                   MXFP6 terms of the activations) per 32-column group into a
-//                   step accumulator with unit B scale, then acc += block scale
-//                   * step (the block scale is per 128 rows x 128 K, one value
-//                   per group and step). Accumulators start at the bias.
-//                   The next step's operands are loaded while the current
-//                   step's MFMAs run. With one wavefront everything comes
-//                   straight from global memory (2 wavefronts per SIMD). With
-//                   many rows a workgroup of four wavefronts takes a 128-row
-//                   tile; the four share each step's weight codes, loaded once
-//                   per workgroup into a double-buffered LDS stage.
+//   grouped_fp8     the expert GEMMs for few rows (T <= 64). A workgroup is one
+//                   wavefront and takes one 32-row tile of the dispatch rows of
+//                   an expert (a 32-row tile table) and one column unit: 32
+//                   h-columns (their gate and up rows) for gate/up, 64 output
+//                   columns for down. Per 128-deep K step: four MFMAs (two K
+//                   halves x the hi and lo MXFP6 terms of the activations) per
+//                   32-column group into a step accumulator with unit B scale,
+//                   then acc += block scale * step (the block scale is per 128
+//                   rows x 128 K, one value per group and step). Accumulators
+//                   start at the bias. Operands come straight from global
+//                   memory, the next step's loaded while the current step's
+//                   MFMAs run.
+//   grouped_fp8_tile the same arithmetic for many rows: four wavefronts per
+//                   128-row tile and a wider column unit (64 h-columns for
+//                   gate/up; 128, 96 or 64 output columns for down), each K
+//                   step's weight codes staged once per workgroup in LDS.
 #include "ffn_dev.hpp"
 #include "mx6.hpp"
 
@@ -144,65 +145,34 @@ __device__ __forceinline__ v16f mfma_f6f8(const v8i& a, const v8i& b, const v16f
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 0, OPA, sa, 0, 0x7F7F7F7F);
 }
 
-// WAVES = 1: grid (32-row tiles, column units), the tile table of 32 rows.
-// WAVES = 4 (many rows): one workgroup per (128-row tile, column unit), wave w
-// taking rows 32w .. 32w+31 of the tile: the four wavefronts read the same
-// weights, so three of the four reads of each weight byte hit the CU's L1; a
-// one-dimensional grid whose logical tiles (column unit fastest) are dealt to
-// the 8 XCDs in contiguous ranges, so the column units of one row tile run on
-// one XCD and read its encoded rows from that XCD's L2 (measured: 6.5 -> 5.1 ms
-// for the prefill-20b FP8 call, against row tiles fastest).
-template <bool GATEUP, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const uint8_t* __restrict__ ain,
-                                                          uint8_t* __restrict__ hout,
-                                                          const int4* __restrict__ tiles, int ncolu) {
-  __shared__ __attribute__((aligned(16))) float stage_all[WAVES][32 * 36];
-  // WAVES = 4: each K step's weight codes (both 32-row groups, 8 KB) are loaded
-  // once per workgroup into one of two LDS buffers, a step ahead, and every
-  // wavefront reads its operands there (instead of each wavefront loading all
-  // of them: the texture addressers were the bound)
-  __shared__ __attribute__((aligned(16))) uint8_t bsm[WAVES == 4 ? 4 * 4096 : 16];
-  int mt, u;
-  if constexpr (WAVES == 1) {
-    mt = blockIdx.x;
-    u = blockIdx.y;
-  } else {
-    const int total = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int per = total >> 3, rem = total & 7;
-    const int L = xcd * per + min(xcd, rem) + slot;   // a bijection onto [0, total)
-    mt = L / ncolu;
-    u = L - mt * ncolu;
-  }
+// Few rows (T <= 64): one wavefront per (32-row tile, column unit), grid (32-row
+// tiles of the tile table, column units). A column unit is two 32-row weight
+// groups: gate group u and up group u (32 h-columns) for gate/up, output groups
+// 2u and 2u + 1 for down. Operands come straight from global memory, the next
+// step's loaded while the current step's MFMAs run.
+template <bool GATEUP>
+__global__ __launch_bounds__(64) void grouped_fp8(const FfnArgs a, const uint8_t* __restrict__ ain,
+                                                  uint8_t* __restrict__ hout, const int4* __restrict__ tiles) {
+  __shared__ __attribute__((aligned(16))) float stage[32 * 36];
+  const int mt = blockIdx.x, u = blockIdx.y;
   if (mt >= __builtin_amdgcn_readfirstlane(tiles[0].x)) return;
   const int4 ent = tiles[1 + mt];  // {expert, first row within the expert, offsets[e], count_e}
-  const int wave = WAVES == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, lr = lane & 31, half = lane >> 5;
   const int e = __builtin_amdgcn_readfirstlane(ent.x);
-  const int r0 = __builtin_amdgcn_readfirstlane(ent.y) + 32 * wave;
+  const int r0 = __builtin_amdgcn_readfirstlane(ent.y);
   const int off = __builtin_amdgcn_readfirstlane(ent.z);
   const int rows = min(32, __builtin_amdgcn_readfirstlane(ent.w) - r0);
-  // WAVES = 1 has no workgroup barrier; with WAVES = 4 a wavefront without rows
-  // still takes part in the weight staging and its barriers (it reads the tile's
-  // first row and stores nothing)
-  if (WAVES == 1 && rows <= 0) return;
-  const int rbase = rows > 0 ? r0 : __builtin_amdgcn_readfirstlane(ent.y);
-  float* stage = stage_all[wave];
+  if (rows <= 0) return;   // (no workgroup barrier below)
   const int K = GATEUP ? a.d : a.F, N = GATEUP ? a.F : a.d;
   const int nst = nsteps_of(K), nblkK = K / 32;
   const int nbN = (N + 127) / 128;
   const int g0 = GATEUP ? u : 2 * u, g1 = GATEUP ? u : 2 * u + 1;
 
-  const int rr = rows > 0 ? min(lr, rows - 1) : 0;
-  const uint32_t arow =
-      GATEUP ? (uint32_t)a.sorted_pair[off + rbase + rr] / (uint32_t)a.k : (uint32_t)(off + rbase + rr);
+  const int rr = min(lr, rows - 1);
+  const uint32_t arow = GATEUP ? (uint32_t)a.sorted_pair[off + r0 + rr] / (uint32_t)a.k : (uint32_t)(off + r0 + rr);
   const uint8_t* A = ain + (size_t)arow * nst * kChunk;
-  const uint8_t* Bg0 = (GATEUP ? a.wg_codes : a.wd_codes) + ((size_t)e * (N / 32) + g0) * nst * kF8Step;
-  const uint8_t* Bg1 = (GATEUP ? a.wu_codes : a.wd_codes) + ((size_t)e * (N / 32) + g1) * nst * kF8Step;
-  const uint8_t* B0 = Bg0 + lane * 32;
-  const uint8_t* B1 = Bg1 + lane * 32;
-  // WAVES = 4 staging: thread t copies bytes 32 (t % 128) .. + 31 of group t / 128
-  const uint8_t* Bst = (threadIdx.x < 128 ? Bg0 : Bg1) + (threadIdx.x & 127) * 32;
-  const uint32_t bst_lds = (threadIdx.x >> 7) * kF8Step + (threadIdx.x & 127) * 32;
+  const uint8_t* B0 = (GATEUP ? a.wg_codes : a.wd_codes) + ((size_t)e * (N / 32) + g0) * nst * kF8Step + lane * 32;
+  const uint8_t* B1 = (GATEUP ? a.wu_codes : a.wd_codes) + ((size_t)e * (N / 32) + g1) * nst * kF8Step + lane * 32;
   const float* S0 = reinterpret_cast<const float*>(GATEUP ? a.wg_scales : a.wd_scales) +
                     ((size_t)e * nbN + (32 * g0) / 128) * nst;
   const float* S1 = reinterpret_cast<const float*>(GATEUP ? a.wu_scales : a.wd_scales) +
@@ -224,8 +194,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const
 
   // Step j's operands: the lane's two A blocks (96 B: hi, lo of block 2h, then
   // of block 2h+1) and their four E8M0 bytes; B: 32 codes per lane and K half
-  // (half 1 is 2048 B on); the block scales. Step j+1's are loaded before step
-  // j's MFMAs.
+  // (half 1 is 2048 B on); the block scales.
   struct Ops {
     v4i a[6];
     int sa;
@@ -237,58 +206,22 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const
 #pragma unroll
     for (int i = 0; i < 6; ++i) o.a[i] = ap[i];
     o.sa = *reinterpret_cast<const int*>(A + (size_t)j * kChunk + kChunkScales + 4 * half);
-    if constexpr (WAVES == 1) {
-      const v8i* p0 = reinterpret_cast<const v8i*>(B0 + (size_t)j * kF8Step);
-      const v8i* p1 = reinterpret_cast<const v8i*>(B1 + (size_t)j * kF8Step);
-      o.b00 = p0[0];
-      o.b01 = p0[64];
-      o.b10 = p1[0];
-      o.b11 = p1[64];
-    }
+    const v8i* p0 = reinterpret_cast<const v8i*>(B0 + (size_t)j * kF8Step);
+    const v8i* p1 = reinterpret_cast<const v8i*>(B1 + (size_t)j * kF8Step);
+    o.b00 = p0[0];
+    o.b01 = p0[64];
+    o.b10 = p1[0];
+    o.b11 = p1[64];
     o.s0 = S0[j];
     o.s1 = S1[j];
   };
-  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-  auto stage_load = [&](int j, u4v (&r)[2]) __attribute__((always_inline)) {
-    const u4v* p = reinterpret_cast<const u4v*>(Bst + (size_t)j * kF8Step);
-    r[0] = p[0];
-    r[1] = p[1];
-  };
-  auto stage_store = [&](int buf, const u4v (&r)[2]) __attribute__((always_inline)) {
-    u4v* q = reinterpret_cast<u4v*>(bsm + buf * 2 * kF8Step + bst_lds);
-    q[0] = r[0];
-    q[1] = r[1];
-  };
   Ops cur, nxt;
   load_ops(0, cur);
-  if constexpr (WAVES == 4) {
-    u4v r[2];
-    stage_load(0, r);
-    stage_store(0, r);
-    __syncthreads();
-  }
   for (int j = 0; j < nst; ++j) {
-    u4v bnext[2];
-    if constexpr (WAVES == 4) {
-      if (j + 1 < nst) stage_load(j + 1, bnext);
-    }
     if (j + 1 < nst) load_ops(j + 1, nxt);
     const v4i a0 = cur.a[0], a1 = cur.a[1], a2 = cur.a[2], a3 = cur.a[3], a4 = cur.a[4], a5 = cur.a[5];
     int sa = cur.sa;
-    v8i b00, b01, b10, b11;
-    if constexpr (WAVES == 4) {
-      const v8i* l0 = reinterpret_cast<const v8i*>(bsm + (j & 1) * 2 * kF8Step + lane * 32);
-      const v8i* l1 = reinterpret_cast<const v8i*>(bsm + (j & 1) * 2 * kF8Step + kF8Step + lane * 32);
-      b00 = l0[0];
-      b01 = l0[64];
-      b10 = l1[0];
-      b11 = l1[64];
-    } else {
-      b00 = cur.b00;
-      b01 = cur.b01;
-      b10 = cur.b10;
-      b11 = cur.b11;
-    }
+    const v8i b00 = cur.b00, b01 = cur.b01, b10 = cur.b10, b11 = cur.b11;
     const float s0 = cur.s0, s1 = cur.s1;
     // in a half step at the end of K (K % 128 == 64) lane half 1 has no blocks:
     // its B codes are zero and its A codes finite (E2M3 has no NaN), so only the
@@ -310,11 +243,6 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const
     for (int i = 0; i < 16; ++i) {
       acc0[i] = fmaf(s0, t0[i], acc0[i]);
       acc1[i] = fmaf(s1, t1[i], acc1[i]);
-    }
-    if constexpr (WAVES == 4) {
-      // the buffer of step j - 1, free since the last barrier
-      if (j + 1 < nst) stage_store((j + 1) & 1, bnext);
-      __syncthreads();
     }
     cur = nxt;
   }
@@ -348,6 +276,204 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_fp8(const FfnArgs a, const
         float* yr = a.y_sorted + (size_t)(off + r0 + row) * N;
         yr[32 * g0 + lr] = acc0[i];
         yr[32 * g1 + lr] = acc1[i];
+      }
+    }
+  }
+}
+
+// Many rows (T > 64): one workgroup of four wavefronts per (128-row tile,
+// column unit), wave w taking rows 32w .. 32w+31 of the tile. A column unit is
+// NB 32-row weight groups: for gate/up the gate groups NG u .. NG u + NG - 1
+// and the up groups of the same h-columns (NG = NB / 2), for down the output
+// groups NB u .. NB u + NB - 1. Each K step's weight codes (NB x 4 KB) are
+// loaded once per workgroup, a step ahead, into one of two LDS buffers, and
+// every wavefront reads its B operands there; the activations come straight
+// from global memory, the next step's loaded while the current step's MFMAs
+// run. The grid is one-dimensional: logical tiles (column unit fastest) are
+// dealt to the 8 XCDs in contiguous ranges, so the column units of one row
+// tile run on one XCD and read its encoded rows from that XCD's L2.
+template <bool GATEUP, int NB>
+__global__ __launch_bounds__(256) void grouped_fp8_tile(const FfnArgs a, const uint8_t* __restrict__ ain,
+                                                        uint8_t* __restrict__ hout,
+                                                        const int4* __restrict__ tiles, int ncolu) {
+  constexpr int NG = GATEUP ? NB / 2 : NB;   // groups per weight matrix
+  static_assert(!GATEUP || NB % 2 == 0, "gate/up units pair gate and up groups");
+  static_assert(kF8Step == 256 * 16, "thread t stages the 16 bytes at 16 t of each group's step");
+  __shared__ __attribute__((aligned(16))) float stage_all[4][32 * 36];
+  __shared__ __attribute__((aligned(16))) uint8_t bsm[2 * NB * kF8Step];
+  const int total = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int L = xcd * per + min(xcd, rem) + slot;   // a bijection onto [0, total)
+  const int mt = L / ncolu, u = L - mt * ncolu;
+  // (the whole workgroup leaves together: no barrier has been reached)
+  if (mt >= __builtin_amdgcn_readfirstlane(tiles[0].x)) return;
+  const int4 ent = tiles[1 + mt];  // {expert, first row within the expert, offsets[e], count_e}
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lr = lane & 31, half = lane >> 5;
+  const int e = __builtin_amdgcn_readfirstlane(ent.x);
+  const int r0 = __builtin_amdgcn_readfirstlane(ent.y) + 32 * wave;
+  const int off = __builtin_amdgcn_readfirstlane(ent.z);
+  const int rows = min(32, __builtin_amdgcn_readfirstlane(ent.w) - r0);
+  // a wavefront without rows still stages weights and meets every barrier (it
+  // reads the tile's first row and stores nothing)
+  const int rbase = rows > 0 ? r0 : __builtin_amdgcn_readfirstlane(ent.y);
+  float* stage = stage_all[wave];
+  const int K = GATEUP ? a.d : a.F, N = GATEUP ? a.F : a.d;
+  const int nst = nsteps_of(K), nblkK = K / 32;
+  const int nbN = (N + 127) / 128;
+  auto grp = [&](int i) { return GATEUP ? NG * u + (i % NG) : NB * u + i; };
+  auto codes = [&](int i) { return GATEUP ? (i < NG ? a.wg_codes : a.wu_codes) : a.wd_codes; };
+  auto bscales = [&](int i) {
+    return reinterpret_cast<const float*>(GATEUP ? (i < NG ? a.wg_scales : a.wu_scales) : a.wd_scales) +
+           ((size_t)e * nbN + (32 * grp(i)) / 128) * nst;
+  };
+
+  const int rr = rows > 0 ? min(lr, rows - 1) : 0;
+  const uint32_t arow =
+      GATEUP ? (uint32_t)a.sorted_pair[off + rbase + rr] / (uint32_t)a.k : (uint32_t)(off + rbase + rr);
+  const uint8_t* A = ain + (size_t)arow * nst * kChunk;
+  // staging: thread t copies bytes 16 t .. 16 t + 15 of every group's step
+  const uint8_t* Bst[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) Bst[i] = codes(i) + ((size_t)e * (N / 32) + grp(i)) * nst * kF8Step + 16 * threadIdx.x;
+  const float* S[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) S[i] = bscales(i);
+
+  // bias-initialised accumulators: lane l holds column l%32 of its group
+  v16f acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const uint16_t* bs = GATEUP ? (i < NG ? a.b_gate : a.b_up) : a.b_down;
+    const float b = bf16_to_f32(bs[(size_t)e * N + 32 * grp(i) + lr]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = b;
+  }
+
+  // step j's activation operands: the lane's two A blocks (96 B: hi, lo of
+  // block 2h, then of block 2h+1) and their four E8M0 bytes; the block scales
+  struct Ops {
+    v4i a[6];
+    int sa;
+    float s[NB];
+  };
+  auto load_ops = [&](int j, Ops& o) __attribute__((always_inline)) {
+    const v4i* ap = reinterpret_cast<const v4i*>(A + (size_t)j * kChunk + half * 96);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) o.a[i] = ap[i];
+    o.sa = *reinterpret_cast<const int*>(A + (size_t)j * kChunk + kChunkScales + 4 * half);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) o.s[i] = S[i][j];
+  };
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  auto stage_load = [&](int j, u4v (&r)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) r[i] = *reinterpret_cast<const u4v*>(Bst[i] + (size_t)j * kF8Step);
+  };
+  auto stage_store = [&](int buf, const u4v (&r)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      *reinterpret_cast<u4v*>(bsm + (buf * NB + i) * kF8Step + 16 * threadIdx.x) = r[i];
+  };
+  Ops cur, nxt;
+  load_ops(0, cur);
+  {
+    u4v r[NB];
+    stage_load(0, r);
+    stage_store(0, r);
+    __syncthreads();
+  }
+  for (int j = 0; j < nst; ++j) {
+    u4v bnext[NB];
+    if (j + 1 < nst) {
+      stage_load(j + 1, bnext);
+      load_ops(j + 1, nxt);
+    }
+    const v4i a0 = cur.a[0], a1 = cur.a[1], a2 = cur.a[2], a3 = cur.a[3], a4 = cur.a[4], a5 = cur.a[5];
+    int sa = cur.sa;
+    // in a half step at the end of K (K % 128 == 64) lane half 1 has no blocks:
+    // its B codes are zero and its A codes finite (E2M3 has no NaN), so only the
+    // never-written scale bytes are replaced by finite ones
+    if (half && 4 * j + 2 >= nblkK) sa = 0x7F7F7F7F;
+    const v8i hi0 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, -1, -1);
+    const v8i lo0 = __builtin_shufflevector(a1, a2, 2, 3, 4, 5, 6, 7, -1, -1);
+    const v8i hi1 = __builtin_shufflevector(a3, a4, 0, 1, 2, 3, 4, 5, -1, -1);
+    const v8i lo1 = __builtin_shufflevector(a4, a5, 2, 3, 4, 5, 6, 7, -1, -1);
+    const uint8_t* bb = bsm + (j & 1) * NB * kF8Step + lane * 32;
+    // groups in pairs: two independent MFMA chains of four, then their scaled
+    // sums into the accumulators (an odd last group alone)
+#pragma unroll
+    for (int p = 0; p < NB; p += 2) {
+      if (p + 1 < NB) {
+        const v8i* l0 = reinterpret_cast<const v8i*>(bb + p * kF8Step);
+        const v8i* l1 = reinterpret_cast<const v8i*>(bb + (p + 1) * kF8Step);
+        const v8i b00 = l0[0], b10 = l1[0];
+        v16f t0 = mfma_f6f8<0>(hi0, b00, v16f{}, sa);
+        v16f t1 = mfma_f6f8<0>(hi0, b10, v16f{}, sa);
+        t0 = mfma_f6f8<1>(lo0, b00, t0, sa);
+        t1 = mfma_f6f8<1>(lo0, b10, t1, sa);
+        const v8i b01 = l0[64], b11 = l1[64];
+        t0 = mfma_f6f8<2>(hi1, b01, t0, sa);
+        t1 = mfma_f6f8<2>(hi1, b11, t1, sa);
+        t0 = mfma_f6f8<3>(lo1, b01, t0, sa);
+        t1 = mfma_f6f8<3>(lo1, b11, t1, sa);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[p][r] = fmaf(cur.s[p], t0[r], acc[p][r]);
+          acc[p + 1][r] = fmaf(cur.s[p + 1], t1[r], acc[p + 1][r]);
+        }
+      } else {
+        const v8i* l0 = reinterpret_cast<const v8i*>(bb + p * kF8Step);
+        v16f t0 = mfma_f6f8<0>(hi0, l0[0], v16f{}, sa);
+        t0 = mfma_f6f8<1>(lo0, l0[0], t0, sa);
+        t0 = mfma_f6f8<2>(hi1, l0[64], t0, sa);
+        t0 = mfma_f6f8<3>(lo1, l0[64], t0, sa);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[p][r] = fmaf(cur.s[p], t0[r], acc[p][r]);
+      }
+    }
+    // the buffer of step j - 1, free since the last barrier
+    if (j + 1 < nst) stage_store((j + 1) & 1, bnext);
+    __syncthreads();
+    cur = nxt;
+  }
+
+  if constexpr (GATEUP) {
+    // h = silu(g) * u per h group through the wavefront's LDS staging area;
+    // lane r < rows encodes row r's block
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+        stage[row * 36 + lr] = silu_mul(acc[q][i], acc[NG + q][i]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane < rows) {
+        float v[32];
+#pragma unroll
+        for (int c = 0; c < 32; ++c) v[c] = stage[lane * 36 + c];
+        uint32_t hw[6], lw[6], sc;
+        encode_block(v, hw, lw, sc);
+        uint8_t* hrow = hout + (size_t)(off + r0 + lane) * enc_pitch(a.F);
+        store_enc(hrow + enc_codes_at(grp(q)), hw, lw);
+        *reinterpret_cast<uint16_t*>(hrow + enc_scale_at(grp(q))) = static_cast<uint16_t>(sc);
+      }
+      // every lane's reads of the area come before the next group's writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      if (row < rows) {
+        float* yr = a.y_sorted + (size_t)(off + r0 + row) * N;
+#pragma unroll
+        for (int g = 0; g < NB; ++g) yr[32 * grp(g) + lr] = acc[g][i];
       }
     }
   }
@@ -411,6 +537,9 @@ hipError_t launch_pack_fp8(const uint8_t* codes, int E, int N, int K, uint8_t* o
   return hipGetLastError();
 }
 
+// 32-column weight groups per down workgroup with many rows
+static int fp8_down_groups(int d) { return d % 128 == 0 ? 4 : (d % 96 == 0 ? 3 : 2); }
+
 hipError_t launch_expert_ffn_fp8(const FfnArgs& a, hipStream_t stream) {
   const WsLayout L = ws_layout(a.T, a.d, a.F, a.E, a.k);
   uint8_t* ws = static_cast<uint8_t*>(a.ws);
@@ -429,18 +558,28 @@ hipError_t launch_expert_ffn_fp8(const FfnArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (wide) {
-    const int mts = max_row_tiles(a.T, a.E, a.k, kF8Rows * 4);
-    hipLaunchKernelGGL((grouped_fp8<true, 4>), dim3((unsigned)(mts * (a.F / 32))), dim3(256), 0, stream, a, xenc,
-                       henc, tp, a.F / 32);
+    // gate/up: 64 h-columns per workgroup (F is a multiple of 64); down: the
+    // widest of 128, 96 and 64 output columns that divides d (six gate/up
+    // groups or more than four down groups take more than half a SIMD's
+    // registers)
+    const unsigned mts = (unsigned)max_row_tiles(a.T, a.E, a.k, kF8Rows * 4);
+    hipLaunchKernelGGL((grouped_fp8_tile<true, 4>), dim3(mts * (a.F / 64)), dim3(256), 0, stream, a, xenc, henc, tp,
+                       a.F / 64);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((grouped_fp8<false, 4>), dim3((unsigned)(mts * (a.d / 64))), dim3(256), 0, stream, a, henc,
-                       henc, tp, a.d / 64);
+    const int dg = fp8_down_groups(a.d);
+    const int nu = a.d / (32 * dg);
+    if (dg == 4)
+      hipLaunchKernelGGL((grouped_fp8_tile<false, 4>), dim3(mts * nu), dim3(256), 0, stream, a, henc, henc, tp, nu);
+    else if (dg == 3)
+      hipLaunchKernelGGL((grouped_fp8_tile<false, 3>), dim3(mts * nu), dim3(256), 0, stream, a, henc, henc, tp, nu);
+    else
+      hipLaunchKernelGGL((grouped_fp8_tile<false, 2>), dim3(mts * nu), dim3(256), 0, stream, a, henc, henc, tp, nu);
     return hipGetLastError();
   }
   const unsigned mts = (unsigned)max_row_tiles(a.T, a.E, a.k, kF8Rows);
-  hipLaunchKernelGGL((grouped_fp8<true, 1>), dim3(mts, a.F / 32), dim3(64), 0, stream, a, xenc, henc, tp, a.F / 32);
+  hipLaunchKernelGGL((grouped_fp8<true>), dim3(mts, a.F / 32), dim3(64), 0, stream, a, xenc, henc, tp);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_fp8<false, 1>), dim3(mts, a.d / 64), dim3(64), 0, stream, a, henc, henc, tp, a.d / 64);
+  hipLaunchKernelGGL((grouped_fp8<false>), dim3(mts, a.d / 64), dim3(64), 0, stream, a, henc, henc, tp);
   return hipGetLastError();
 }
 

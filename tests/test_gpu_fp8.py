@@ -122,6 +122,8 @@ def _ffn_fp8_check(gu, w, wt8, y_ref_fn):
     dict(T=128, d=512, F=512, E=32, k=4, seed=0),        # tiny
     dict(T=37, d=512, F=704, E=8, k=2, seed=31),         # ragged, F % 128 = 64
     dict(T=600, d=576, F=640, E=8, k=4, seed=55),        # several 32-row tiles per expert, d % 128 = 64
+    dict(T=260, d=2880, F=1472, E=6, k=2, seed=58),      # many rows at d = 2880: 96-column down tiles, F % 128 = 64
+    dict(T=150, d=1024, F=704, E=5, k=3, seed=59),       # many rows, 128-column down tiles, F % 128 = 64
 ], ids=lambda s: f"T{s['T']}-d{s['d']}-F{s['F']}-E{s['E']}-k{s['k']}")
 def test_ffn_fp8_converted(gu, shape):
     """MXFP4 weights converted to FP8 on the GPU are the same numbers, so the
