@@ -370,10 +370,18 @@ __global__ __launch_bounds__(256) void grouped_fp8_tile(const FfnArgs a, const u
 #pragma unroll
     for (int i = 0; i < NB; ++i) r[i] = *reinterpret_cast<const u4v*>(Bst[i] + (size_t)j * kF8Step);
   };
+  // In LDS a group's step is [K half s][16-byte piece q][lane][16 B] (in memory
+  // it is [s][lane][32 B]), so that each 16-byte operand read of a wavefront
+  // covers 1 KB of consecutive bytes (with lanes 32 B apart it took two passes)
+  const uint32_t st_lds = (threadIdx.x >> 7) * 2048 + (threadIdx.x & 1) * 1024 + ((threadIdx.x >> 1) & 63) * 16;
   auto stage_store = [&](int buf, const u4v (&r)[NB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-      *reinterpret_cast<u4v*>(bsm + (buf * NB + i) * kF8Step + 16 * threadIdx.x) = r[i];
+    for (int i = 0; i < NB; ++i) *reinterpret_cast<u4v*>(bsm + (buf * NB + i) * kF8Step + st_lds) = r[i];
+  };
+  // the lane's 32 codes of K half s of group i (the B operand of one MFMA)
+  auto ldb = [&](const uint8_t* buf, int i, int hs) __attribute__((always_inline)) {
+    const v4i* q = reinterpret_cast<const v4i*>(buf + i * kF8Step + hs * 2048 + lane * 16);
+    return __builtin_shufflevector(q[0], q[64], 0, 1, 2, 3, 4, 5, 6, 7);
   };
   Ops cur, nxt;
   load_ops(0, cur);
@@ -399,20 +407,18 @@ __global__ __launch_bounds__(256) void grouped_fp8_tile(const FfnArgs a, const u
     const v8i lo0 = __builtin_shufflevector(a1, a2, 2, 3, 4, 5, 6, 7, -1, -1);
     const v8i hi1 = __builtin_shufflevector(a3, a4, 0, 1, 2, 3, 4, 5, -1, -1);
     const v8i lo1 = __builtin_shufflevector(a4, a5, 2, 3, 4, 5, 6, 7, -1, -1);
-    const uint8_t* bb = bsm + (j & 1) * NB * kF8Step + lane * 32;
+    const uint8_t* bb = bsm + (j & 1) * NB * kF8Step;
     // groups in pairs: two independent MFMA chains of four, then their scaled
     // sums into the accumulators (an odd last group alone)
 #pragma unroll
     for (int p = 0; p < NB; p += 2) {
       if (p + 1 < NB) {
-        const v8i* l0 = reinterpret_cast<const v8i*>(bb + p * kF8Step);
-        const v8i* l1 = reinterpret_cast<const v8i*>(bb + (p + 1) * kF8Step);
-        const v8i b00 = l0[0], b10 = l1[0];
+        const v8i b00 = ldb(bb, p, 0), b10 = ldb(bb, p + 1, 0);
         v16f t0 = mfma_f6f8<0>(hi0, b00, v16f{}, sa);
         v16f t1 = mfma_f6f8<0>(hi0, b10, v16f{}, sa);
         t0 = mfma_f6f8<1>(lo0, b00, t0, sa);
         t1 = mfma_f6f8<1>(lo0, b10, t1, sa);
-        const v8i b01 = l0[64], b11 = l1[64];
+        const v8i b01 = ldb(bb, p, 1), b11 = ldb(bb, p + 1, 1);
         t0 = mfma_f6f8<2>(hi1, b01, t0, sa);
         t1 = mfma_f6f8<2>(hi1, b11, t1, sa);
         t0 = mfma_f6f8<3>(lo1, b01, t0, sa);
@@ -423,11 +429,11 @@ __global__ __launch_bounds__(256) void grouped_fp8_tile(const FfnArgs a, const u
           acc[p + 1][r] = fmaf(cur.s[p + 1], t1[r], acc[p + 1][r]);
         }
       } else {
-        const v8i* l0 = reinterpret_cast<const v8i*>(bb + p * kF8Step);
-        v16f t0 = mfma_f6f8<0>(hi0, l0[0], v16f{}, sa);
-        t0 = mfma_f6f8<1>(lo0, l0[0], t0, sa);
-        t0 = mfma_f6f8<2>(hi1, l0[64], t0, sa);
-        t0 = mfma_f6f8<3>(lo1, l0[64], t0, sa);
+        const v8i b00 = ldb(bb, p, 0), b01 = ldb(bb, p, 1);
+        v16f t0 = mfma_f6f8<0>(hi0, b00, v16f{}, sa);
+        t0 = mfma_f6f8<1>(lo0, b00, t0, sa);
+        t0 = mfma_f6f8<2>(hi1, b01, t0, sa);
+        t0 = mfma_f6f8<3>(lo1, b01, t0, sa);
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[p][r] = fmaf(cur.s[p], t0[r], acc[p][r]);
       }
