@@ -386,6 +386,48 @@ moe_status moe_residual_rmsnorm(int32_t T, int32_t d, const moe_bf16* x, const m
                                 const moe_bf16* gain, float eps, moe_bf16* x_out,
                                 moe_bf16* n_out, void* stream);
 
+/* The block's weighted combine, its residual add and the next block's pre-norm
+ * in one pass over each token row, so that the block output never makes a round
+ * trip through memory (the combine is the weighted accumulation of "GPT-OSS el
+ * dia 0", section "Nuclis per a GPT-OSS / MoE"; the norm as for moe_rmsnorm):
+ *   m[t]         = bf16(sum_j topk_w[t][j] * y_sorted[pair_row[t*k+j]])  as moe_combine,
+ *   resid_out[t] = bf16(resid[t] + m[t])                                 as moe_residual_add,
+ *   n_out[t]     = RMSNorm(resid_out[t]) with gain and eps               as moe_rmsnorm,
+ * the same bytes as those calls in that order.
+ *   y_sorted, pair_row, topk_w  as for moe_combine (dims.T, dims.d, dims.k used)
+ *   resid      [device] bf16 [T][d]  the residual stream before the block
+ *   gain       [device] bf16 [d]     the next block's norm gain, or NULL: then no
+ *                                    norm is taken and n_out is not used
+ *   m_out      [device] bf16 [T][d]  out: the block output m, or NULL (not stored)
+ *   resid_out  [device] bf16 [T][d]  out: may alias resid
+ *   n_out      [device] bf16 [T][d]  out: aliases none of the others
+ * Errors as for moe_combine, plus MOE_ERR_INVALID_ARG for a negative eps or an
+ * alias other than resid_out == resid. */
+moe_status moe_combine_residual_rmsnorm(moe_dims dims, const float* y_sorted,
+                                        const int32_t* pair_row, const float* topk_w,
+                                        const moe_bf16* resid, const moe_bf16* gain, float eps,
+                                        moe_bf16* m_out, moe_bf16* resid_out, moe_bf16* n_out,
+                                        void* stream);
+
+/* moe_forward whose last step is moe_combine_residual_rmsnorm instead of
+ * moe_combine: one block of a pre-norm stack x <- x + MoE(RMSNorm(x)) after its
+ * norm (x is the normalised block input, resid the residual stream). Arguments
+ * as moe_forward, except that `out` (the block output m) may be NULL, followed
+ * by those of moe_combine_residual_rmsnorm. Same bytes as moe_forward followed
+ * by moe_residual_rmsnorm (or moe_residual_add when gain is NULL). n_out may be
+ * the block input x itself (x is not read after the expert GEMMs), so a stack
+ * can keep its normalised activations and its residual stream in place. */
+moe_status moe_forward_residual_rmsnorm(moe_dims dims, const moe_bf16* x, const float* w_router,
+                                        const float* b_router, moe_mxfp4_packed w_gate,
+                                        moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                                        const moe_bf16* b_gate, const moe_bf16* b_up,
+                                        const moe_bf16* b_down, int32_t* topk_idx, float* topk_w,
+                                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                        int32_t* pair_row, float* y_sorted, moe_bf16* out,
+                                        const moe_bf16* resid, const moe_bf16* gain, float eps,
+                                        moe_bf16* resid_out, moe_bf16* n_out, void* ws,
+                                        size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -6,7 +6,8 @@ current stream; no torch operator computes any part of the layer here, and there
 is no fallback: if the library is missing or a call fails, an exception says so.
 
 The names follow the C ABI: route, permute, expert_ffn_mxfp4, combine (plus
-rmsnorm and residual_add for a pre-norm stack, and workspace_bytes).
+rmsnorm, residual_add and the fused block glue for a pre-norm stack, and
+workspace_bytes).
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ __all__ = [
     "forward_calls", "expert_ffn_mxfp4_stage", "forward_noalloc", "Fp8Weights",
     "convert_mxfp4_to_fp8", "pack_fp8", "load_fp8_weights", "fp8_from_mxfp4", "expert_ffn_fp8",
     "round_weights_bf16", "AttnDims", "attention_workspace_bytes", "attention_sink",
+    "combine_residual_rmsnorm", "forward_residual_rmsnorm",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +37,7 @@ EXPORTED = (
     "moe_forward_noalloc", "moe_forward_noalloc_max_bytes",
     "moe_convert_mxfp4_to_fp8", "moe_fp8_packed_bytes", "moe_pack_fp8", "moe_expert_ffn_fp8",
     "moe_round_weights_bf16", "moe_attention_workspace_bytes", "moe_attention_sink",
-    "moe_residual_rmsnorm",
+    "moe_residual_rmsnorm", "moe_combine_residual_rmsnorm", "moe_forward_residual_rmsnorm",
 )
 
 
@@ -106,11 +108,17 @@ def lib() -> ctypes.CDLL:
     L.moe_rmsnorm.argtypes = [i32, i32, vp, vp, ctypes.c_float, vp, vp]
     L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp]
     L.moe_residual_rmsnorm.argtypes = [i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    L.moe_combine_residual_rmsnorm.argtypes = [Dims, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                               vp]
+    L.moe_forward_residual_rmsnorm.argtypes = [Dims, vp, vp, vp, MXFP4, MXFP4, MXFP4, vp, vp, vp, vp,
+                                               vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                               vp, vp, vp, sz, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn_mxfp4", "moe_expert_ffn_mxfp4_stage",
               "moe_combine", "moe_rmsnorm",
               "moe_residual_add", "moe_pack_mxfp4", "moe_forward", "moe_forward_noalloc",
               "moe_convert_mxfp4_to_fp8", "moe_pack_fp8", "moe_expert_ffn_fp8", "moe_round_weights_bf16",
-              "moe_attention_sink", "moe_residual_rmsnorm"):
+              "moe_attention_sink", "moe_residual_rmsnorm", "moe_combine_residual_rmsnorm",
+              "moe_forward_residual_rmsnorm"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -503,7 +511,30 @@ def residual_rmsnorm(x, m, gain, eps: float = 1e-5, x_out=None, n_out=None):
     return x_out, n_out
 
 
-def _outputs(T, d, E, k, dev, bufs: Optional[dict]) -> dict:
+def combine_residual_rmsnorm(y_sorted, pair_row, topk_w, resid, gain, eps: float = 1e-5,
+                             resid_out=None, n_out=None, m_out=None):
+    """m = combine(y), resid_out = resid + m, n_out = rmsnorm(resid_out) in one pass
+    (moe_combine_residual_rmsnorm). gain None: no norm (n_out None). m_out, if
+    given, receives m. Returns (resid_out, n_out); resid_out may be resid."""
+    T, k = topk_w.shape
+    P, d = y_sorted.shape
+    if resid_out is None:
+        resid_out = torch.empty_like(resid)
+    if gain is not None and n_out is None:
+        n_out = torch.empty_like(resid)
+    _check(lib().moe_combine_residual_rmsnorm(
+        _dims(T, d, 64, max(k, 1), k), _dev(y_sorted, torch.float32, (T * k, d), "y_sorted"),
+        _dev(pair_row, torch.int32, (T * k,), "pair_row"), _dev(topk_w, torch.float32, (T, k), "topk_w"),
+        _dev(resid, torch.bfloat16, (T, d), "resid"),
+        None if gain is None else _dev(gain, torch.bfloat16, (d,), "gain"), float(eps),
+        None if m_out is None else _dev(m_out, torch.bfloat16, (T, d), "m_out"),
+        _dev(resid_out, torch.bfloat16, (T, d), "resid_out"),
+        None if n_out is None else _dev(n_out, torch.bfloat16, (T, d), "n_out"), _stream()),
+        "moe_combine_residual_rmsnorm")
+    return resid_out, n_out
+
+
+def _outputs(T, d, E, k, dev, bufs: Optional[dict], store_out: bool = True) -> dict:
     b = dict(bufs or {})
     P = T * k
     if b.get("topk_idx") is None:
@@ -517,8 +548,9 @@ def _outputs(T, d, E, k, dev, bufs: Optional[dict]) -> dict:
                      torch.empty(P, dtype=torch.int32, device=dev))
     if b.get("y_sorted") is None:
         b["y_sorted"] = torch.empty((P, d), dtype=torch.float32, device=dev)
-    if b.get("out") is None:
+    if b.get("out") is None and store_out:
         b["out"] = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    b.setdefault("out", None)
     return b
 
 
@@ -535,13 +567,36 @@ def forward_noalloc(x, w: ExpertWeights, k: int, bufs: Optional[dict] = None) ->
     return _forward(x, w, k, None, bufs)
 
 
-def _forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict]) -> dict:
+def forward_residual_rmsnorm(x, w: ExpertWeights, k: int, ws, resid, gain, eps: float = 1e-5,
+                             resid_out=None, n_out=None, bufs: Optional[dict] = None,
+                             store_out: bool = False) -> dict:
+    """One block of a pre-norm stack after its norm (moe_forward_residual_rmsnorm):
+    the whole block on the normalised input x, then resid_out = resid + MoE(x) and
+    n_out = rmsnorm(resid_out, gain) (no norm when gain is None). The block output
+    itself is stored only with store_out (key "out"). Returns the dict of
+    `forward` plus resid_out and n_out."""
+    T, d = x.shape
+    if resid_out is None:
+        resid_out = torch.empty_like(resid)
+    if gain is not None and n_out is None:
+        n_out = torch.empty_like(resid)
+    rn = (_dev(resid, torch.bfloat16, (T, d), "resid"),
+          None if gain is None else _dev(gain, torch.bfloat16, (d,), "gain"), float(eps),
+          _dev(resid_out, torch.bfloat16, (T, d), "resid_out"),
+          None if n_out is None else _dev(n_out, torch.bfloat16, (T, d), "n_out"))
+    r = _forward(x, w, k, ws, bufs, resid_norm=rn, store_out=store_out)
+    r["resid_out"], r["n_out"] = resid_out, n_out
+    return r
+
+
+def _forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict], resid_norm=None,
+             store_out: bool = True) -> dict:
     T, d = x.shape
     dw, F, E = w.dims
     if dw != d:
         raise ValueError("x width does not match the router weight")
     P = T * k
-    b = _outputs(T, d, E, k, x.device, bufs)
+    b = _outputs(T, d, E, k, x.device, bufs, store_out)
     counts, offsets, sorted_pair, pair_row = b["perm"]
     mg, mu, md = _packed_args(w)
     br = None if w.b_router is None else _dev(w.b_router, torch.float32, (E,), "b_router")
@@ -558,8 +613,12 @@ def _forward(x, w: ExpertWeights, k: int, ws, bufs: Optional[dict]) -> dict:
         _dev(sorted_pair, torch.int32, (P,), "sorted_pair"),
         _dev(pair_row, torch.int32, (P,), "pair_row"),
         _dev(b["y_sorted"], torch.float32, (P, d), "y_sorted"),
-        _dev(b["out"], torch.bfloat16, (T, d), "out")]
-    if ws is None:
+        None if b["out"] is None else _dev(b["out"], torch.bfloat16, (T, d), "out")]
+    if resid_norm is not None:
+        _check(lib().moe_forward_residual_rmsnorm(*args, *resid_norm, ws.data_ptr(),
+                                                  ws.numel() * ws.element_size(), _stream()),
+               "moe_forward_residual_rmsnorm")
+    elif ws is None:
         _check(lib().moe_forward_noalloc(*args, _stream()), "moe_forward_noalloc")
     else:
         _check(lib().moe_forward(*args, ws.data_ptr(), ws.numel() * ws.element_size(), _stream()),

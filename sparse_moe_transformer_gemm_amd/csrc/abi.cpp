@@ -248,6 +248,36 @@ moe_status moe_expert_ffn_mxfp4_stage(moe_dims dims, const moe_bf16* x, const in
   return hip_status(moe::launch_expert_ffn_stage(a, static_cast<hipStream_t>(stream), (int)stage));
 }
 
+// The residual stream and next norm of moe_combine_residual_rmsnorm and
+// moe_forward_residual_rmsnorm.
+struct ResidNorm {
+  const moe_bf16* resid;
+  const moe_bf16* gain;  // null: no norm
+  float eps;
+  moe_bf16* resid_out;
+  moe_bf16* n_out;
+};
+
+static moe_status resid_norm_checks(const ResidNorm& r, const moe_bf16* m_out, const char* who) {
+  MOE_TRY(check_ptrs({r.resid, r.resid_out}, who));
+  if (m_out && (m_out == r.resid || m_out == r.resid_out)) {
+    set_error("%s: the block output must not alias resid or resid_out", who);
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (r.gain) {
+    MOE_TRY(check_ptrs({r.gain, r.n_out}, who));
+    if (!(r.eps >= 0.0f)) {
+      set_error("%s: need eps >= 0", who);
+      return MOE_ERR_INVALID_ARG;
+    }
+    if (r.n_out == r.resid || r.n_out == r.resid_out || (m_out && r.n_out == m_out)) {
+      set_error("%s: n_out must not alias resid, resid_out or the block output", who);
+      return MOE_ERR_INVALID_ARG;
+    }
+  }
+  return MOE_OK;
+}
+
 // moe_forward and moe_forward_noalloc: argument checks other than the
 // workspace's, then the launches on `ws`.
 static moe_status forward_checks(const moe_dims& dims, const moe_bf16* x, const float* w_router,
@@ -257,14 +287,15 @@ static moe_status forward_checks(const moe_dims& dims, const moe_bf16* x, const 
                                  const moe_bf16* b_down, int32_t* topk_idx, float* topk_w,
                                  int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                                  int32_t* pair_row, float* y_sorted, moe_bf16* out,
-                                 const char* who) {
+                                 const char* who, bool out_optional = false) {
   MOE_TRY(check_dims(dims));
   MOE_TRY(check_ffn_k(dims));
   MOE_TRY(check_mxfp4_tiles(dims));
   MOE_TRY(check_ptrs({x, w_router, w_gate.codes, w_gate.scales, w_up.codes, w_up.scales,
                       w_down.codes, w_down.scales, b_gate, b_up, b_down, topk_idx, topk_w,
-                      counts, offsets, sorted_pair, pair_row, y_sorted, out},
+                      counts, offsets, sorted_pair, pair_row, y_sorted},
                      who));
+  if (!(out_optional && out == nullptr)) MOE_TRY(check_ptrs({out}, who));
   if (b_router && !aligned16(b_router)) {
     set_error("%s", "b_router not 16-byte aligned");
     return MOE_ERR_INVALID_ARG;
@@ -279,7 +310,7 @@ static moe_status forward_launch(const moe_dims& dims, const moe_bf16* x, const 
                                  const moe_bf16* b_down, int32_t* topk_idx, float* topk_w,
                                  int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                                  int32_t* pair_row, float* y_sorted, moe_bf16* out, void* ws,
-                                 hipStream_t s) {
+                                 hipStream_t s, const ResidNorm* rn = nullptr) {
   moe::FfnArgs a;
   a.T = dims.T;
   a.d = dims.d;
@@ -324,6 +355,10 @@ static moe_status forward_launch(const moe_dims& dims, const moe_bf16* x, const 
                                            sorted_pair, pair_row, ws, s)));
   }
   MOE_TRY(hip_status(moe::launch_expert_ffn(a, s, front || many)));
+  if (rn)
+    return hip_status(moe::launch_combine_residual_rmsnorm(y_sorted, pair_row, topk_w, rn->resid,
+                                                           rn->gain, dims.T, dims.d, dims.k, rn->eps,
+                                                           out, rn->resid_out, rn->n_out, s));
   return hip_status(moe::launch_combine(y_sorted, pair_row, topk_w, dims.T, dims.d, dims.k, out, s));
 }
 
@@ -368,6 +403,29 @@ moe_status moe_forward_noalloc(moe_dims dims, const moe_bf16* x, const float* w_
   return forward_launch(dims, x, w_router, b_router, w_gate, w_up, w_down, b_gate, b_up, b_down,
                         topk_idx, topk_w, counts, offsets, sorted_pair, pair_row, y_sorted, out,
                         ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_forward_residual_rmsnorm(moe_dims dims, const moe_bf16* x, const float* w_router,
+                                        const float* b_router, moe_mxfp4_packed w_gate,
+                                        moe_mxfp4_packed w_up, moe_mxfp4_packed w_down,
+                                        const moe_bf16* b_gate, const moe_bf16* b_up,
+                                        const moe_bf16* b_down, int32_t* topk_idx, float* topk_w,
+                                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                        int32_t* pair_row, float* y_sorted, moe_bf16* out,
+                                        const moe_bf16* resid, const moe_bf16* gain, float eps,
+                                        moe_bf16* resid_out, moe_bf16* n_out, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  const char* who = "moe_forward_residual_rmsnorm";
+  MOE_TRY(forward_checks(dims, x, w_router, b_router, w_gate, w_up, w_down, b_gate, b_up, b_down,
+                         topk_idx, topk_w, counts, offsets, sorted_pair, pair_row, y_sorted, out,
+                         who, true));
+  const ResidNorm rn{resid, gain, eps, resid_out, n_out};
+  MOE_TRY(resid_norm_checks(rn, out, who));
+  MOE_TRY(check_ws(dims, ws, ws_bytes));
+  return forward_launch(dims, x, w_router, b_router, w_gate, w_up, w_down, b_gate, b_up, b_down,
+                        topk_idx, topk_w, counts, offsets, sorted_pair, pair_row, y_sorted, out,
+                        ws, static_cast<hipStream_t>(stream), &rn);
 }
 
 moe_status moe_convert_mxfp4_to_fp8(int32_t E, int32_t N, int32_t K, moe_mxfp4 src,
@@ -477,6 +535,23 @@ moe_status moe_combine(moe_dims dims, const float* y_sorted, const int32_t* pair
   MOE_TRY(check_ptrs({y_sorted, pair_row, topk_w, out}, "moe_combine"));
   return hip_status(moe::launch_combine(y_sorted, pair_row, topk_w, dims.T, dims.d, dims.k, out,
                                         static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine_residual_rmsnorm(moe_dims dims, const float* y_sorted,
+                                        const int32_t* pair_row, const float* topk_w,
+                                        const moe_bf16* resid, const moe_bf16* gain, float eps,
+                                        moe_bf16* m_out, moe_bf16* resid_out, moe_bf16* n_out,
+                                        void* stream) {
+  g_last_error[0] = 0;
+  const char* who = "moe_combine_residual_rmsnorm";
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_ptrs({y_sorted, pair_row, topk_w}, who));
+  if (m_out) MOE_TRY(check_ptrs({m_out}, who));
+  const ResidNorm rn{resid, gain, eps, resid_out, n_out};
+  MOE_TRY(resid_norm_checks(rn, m_out, who));
+  return hip_status(moe::launch_combine_residual_rmsnorm(
+      y_sorted, pair_row, topk_w, resid, gain, dims.T, dims.d, dims.k, eps, m_out, resid_out,
+      gain ? n_out : nullptr, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_rmsnorm(int32_t T, int32_t d, const moe_bf16* x, const moe_bf16* gain, float eps,

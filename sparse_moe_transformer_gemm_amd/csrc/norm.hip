@@ -4,13 +4,17 @@
 // Residual: out = bf16(x + m), fp32 add, round to nearest even.
 // Residual + RMSNorm: the residual add of one block and the pre-norm of the
 // next in one pass over the row.
+// Combine + residual + RMSNorm: the block's weighted combine (Perplexity, "GPT-OSS
+// el dia 0", section "Nuclis per a GPT-OSS / MoE": the weighted accumulation of
+// the experts' outputs), the residual add and the next block's pre-norm in one
+// pass, so the block output m never makes a round trip through memory.
 // All memory-bound. The norms take one wavefront per row (four rows per
 // workgroup, no workgroup barrier): lane l holds 16-byte chunks l, l + 64, ...
 // of its row, the first kRegChunks of them in registers between the sum of
 // squares and the scaling (the rest are read again), and sums its squares in
 // chunk order before a butterfly over the wavefront, so both norm kernels sum
 // in the same order and give the same bytes for the same row.
-#include "common.hpp"
+#include "mx6.hpp"
 
 namespace moe {
 namespace {
@@ -154,6 +158,103 @@ __global__ __launch_bounds__(256) void residual_kernel(const uint4* x, const uin
     out[i] = add8(x[i], m[i]);
 }
 
+// One token row per workgroup of four wavefronts: m = bf16(sum over j of w_j *
+// y_j), the fp32 multiply-adds in slot order from zero and one rounding (the
+// arithmetic of the combine kernel); s = bf16(resid + m) is stored to resid_out
+// (and m to mout when it is given) and kept in LDS; with NORM, wavefront 0 then
+// sums the squares as norm_row does (lane l over the 8-column chunks l, l + 64,
+// ... in order, then the butterfly), and every thread scales its share of s. So
+// every output has the bytes of the separate combine, residual and norm kernels,
+// while the loads of a row are spread over four wavefronts: wavefront v takes
+// the chunk rounds i = v, v + 4, ... (chunk l + 64 i for lane l), kGlueChunks
+// rounds at a time with all of their loads (2k quarter rows of y and the
+// residual) issued before their sums. resid_out may alias resid (each chunk is
+// read, then written, by one thread).
+constexpr int kGlueWaves = 4;
+constexpr int kGlueChunks = 2;
+constexpr int kGlueMaxD = 16384;
+
+template <int K, bool NORM>
+__global__ __launch_bounds__(kGlueWaves * kWave) void combine_residual_norm_kernel(
+    const float* __restrict__ y, const int32_t* __restrict__ pair_row,
+    const float* __restrict__ topk_w, const uint16_t* resid, const uint16_t* __restrict__ gain,
+    int d, float eps, uint16_t* __restrict__ mout, uint16_t* resid_out,
+    uint16_t* __restrict__ nout) {
+  extern __shared__ uint4 srow[];  // the row's s (NORM only): d / 8 chunks
+  __shared__ float sinv;
+  const int t = blockIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n8 = d / 8;
+  rsrc_t rows[K];
+  float w[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int row = __builtin_amdgcn_readfirstlane(pair_row[(size_t)t * K + j]);
+    rows[j] = make_rsrc(y + (size_t)row * d, (uint32_t)d * 4u);
+    w[j] = topk_w[(size_t)t * K + j];
+  }
+  const size_t o = (size_t)t * d;
+  const rsrc_t rx = make_rsrc(resid + o, (uint32_t)d * 2u);
+  uint4* ro = reinterpret_cast<uint4*>(resid_out + o);
+  uint4* mo = mout ? reinterpret_cast<uint4*>(mout + o) : nullptr;
+  for (int i0 = wv; kWave * i0 < n8; i0 += kGlueWaves * kGlueChunks) {
+    uint4 va[kGlueChunks][K], vb[kGlueChunks][K], vx[kGlueChunks];
+#pragma unroll
+    for (int u = 0; u < kGlueChunks; ++u) {
+      const int c = lane + kWave * (i0 + kGlueWaves * u);
+      const uint32_t off = c < n8 ? (uint32_t)c * 32u : kOutOfRange;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        va[u][j] = bload16nt(rows[j], off);
+        vb[u][j] = bload16nt(rows[j], off, 16u);
+      }
+      vx[u] = bload16(rx, c < n8 ? (uint32_t)c * 16u : kOutOfRange);
+    }
+#pragma unroll
+    for (int u = 0; u < kGlueChunks; ++u) {
+      const int c = lane + kWave * (i0 + kGlueWaves * u);
+      if (c < n8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          acc[0] = fmaf(w[j], __uint_as_float(va[u][j].x), acc[0]);
+          acc[1] = fmaf(w[j], __uint_as_float(va[u][j].y), acc[1]);
+          acc[2] = fmaf(w[j], __uint_as_float(va[u][j].z), acc[2]);
+          acc[3] = fmaf(w[j], __uint_as_float(va[u][j].w), acc[3]);
+          acc[4] = fmaf(w[j], __uint_as_float(vb[u][j].x), acc[4]);
+          acc[5] = fmaf(w[j], __uint_as_float(vb[u][j].y), acc[5]);
+          acc[6] = fmaf(w[j], __uint_as_float(vb[u][j].z), acc[6]);
+          acc[7] = fmaf(w[j], __uint_as_float(vb[u][j].w), acc[7]);
+        }
+        uint4 m;
+        m.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+        m.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+        m.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+        m.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+        const uint4 sv = add8(vx[u], m);
+        ro[c] = sv;
+        if (mo) mo[c] = m;
+        if constexpr (NORM) srow[c] = sv;
+      }
+    }
+  }
+  if constexpr (NORM) {
+    __syncthreads();
+    if (wv == 0) {
+      float ss = 0.f;
+      for (int c = lane; c < n8; c += kWave) ss = sumsq8(srow[c], ss);
+      const float inv = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(d) + eps);
+      if (lane == 0) sinv = inv;
+    }
+    __syncthreads();
+    const float inv = sinv;
+    const uint4* g = reinterpret_cast<const uint4*>(gain);
+    uint4* no = reinterpret_cast<uint4*>(nout + o);
+    for (int c = threadIdx.x; c < n8; c += kGlueWaves * kWave) no[c] = scale8(srow[c], g[c], inv);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gain, int T, int d, float eps,
@@ -179,6 +280,40 @@ hipError_t launch_residual_add(const uint16_t* x, const uint16_t* m, int T, int 
   hipLaunchKernelGGL(residual_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<const uint4*>(x), reinterpret_cast<const uint4*>(m), n8,
                      reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
+template <int K>
+static void launch_crn(int T, hipStream_t stream, const float* y, const int32_t* pair_row,
+                       const float* topk_w, const uint16_t* resid, const uint16_t* gain, int d,
+                       float eps, uint16_t* mout, uint16_t* resid_out, uint16_t* nout) {
+  const dim3 g(T), b(kGlueWaves * kWave);
+  if (gain)
+    hipLaunchKernelGGL((combine_residual_norm_kernel<K, true>), g, b, (size_t)d * 2, stream, y, pair_row, topk_w,
+                       resid, gain, d, eps, mout, resid_out, nout);
+  else
+    hipLaunchKernelGGL((combine_residual_norm_kernel<K, false>), g, b, 0, stream, y, pair_row, topk_w,
+                       resid, gain, d, eps, mout, resid_out, nout);
+}
+
+hipError_t launch_combine_residual_rmsnorm(const float* y_sorted, const int32_t* pair_row,
+                                           const float* topk_w, const uint16_t* resid,
+                                           const uint16_t* gain, int T, int d, int k, float eps,
+                                           uint16_t* mout, uint16_t* resid_out, uint16_t* nout,
+                                           hipStream_t stream) {
+  if (d > kGlueMaxD) return hipErrorInvalidValue;
+#define MOE_CRN(KK) launch_crn<KK>(T, stream, y_sorted, pair_row, topk_w, resid, gain, d, eps, mout, resid_out, nout)
+  switch (k) {
+    case 1: MOE_CRN(1); break;
+    case 2: MOE_CRN(2); break;
+    case 3: MOE_CRN(3); break;
+    case 4: MOE_CRN(4); break;
+    case 5: MOE_CRN(5); break;
+    case 6: MOE_CRN(6); break;
+    case 7: MOE_CRN(7); break;
+    default: MOE_CRN(8); break;
+  }
+#undef MOE_CRN
   return hipGetLastError();
 }
 

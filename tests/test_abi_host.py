@@ -216,6 +216,49 @@ def test_combine_norm_validation(moe):
     assert b"alias" in L.moe_last_error()
 
 
+def test_combine_residual_norm_validation(moe):
+    """The fused combine + residual + norm and the whole block with it: null or
+    misaligned pointers, a negative eps and forbidden aliases are rejected on the
+    host; the block output and, without a gain, n_out may be null."""
+    L = moe.lib()
+    D = moe.Dims
+    ok = D(16, 512, 512, 32, 4)
+    R, RO, N, M = 0x20000, 0x30000, 0x40000, 0x50000
+    # y_sorted, pair_row, topk_w, resid, gain, eps, m_out, resid_out, n_out, stream
+    args = [FAKE, FAKE, FAKE, R, FAKE, 1e-5, M, RO, N, None]
+    for i in (0, 1, 2, 3, 7, 8):
+        a = list(args); a[i] = None
+        assert L.moe_combine_residual_rmsnorm(ok, *a) == -1, i
+    a = list(args); a[5] = -1.0
+    assert L.moe_combine_residual_rmsnorm(ok, *a) == -1
+    for i, v in ((8, R), (8, RO), (8, M), (6, R), (6, RO)):
+        a = list(args); a[i] = v
+        assert L.moe_combine_residual_rmsnorm(ok, *a) == -1, (i, v)
+        assert b"alias" in L.moe_last_error()
+    a = list(args); a[3] = R + 8
+    assert L.moe_combine_residual_rmsnorm(ok, *a) == -1
+    assert L.moe_combine_residual_rmsnorm(D(16, 512, 512, 300, 4), *args) == -2
+    ws = L.moe_workspace_bytes(ok)
+    m = moe.MXFP4(FAKE, FAKE)
+    # moe_forward's arguments (out may be null), then resid, gain, eps, resid_out,
+    # n_out, ws, ws_bytes, stream
+    fw = [FAKE, FAKE, None, m, m, m, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+          FAKE, None, R, FAKE, 1e-5, RO, N, FAKE, ws, None]
+    for i in (0, 9, 15, 17, 20, 21, 22):
+        a = list(fw); a[i] = None
+        assert L.moe_forward_residual_rmsnorm(ok, *a) == -1, i
+    a = list(fw); a[21] = RO
+    assert L.moe_forward_residual_rmsnorm(ok, *a) == -1
+    a = list(fw); a[19] = -1.0
+    assert L.moe_forward_residual_rmsnorm(ok, *a) == -1
+    a = list(fw); a[23] = ws - 256
+    assert L.moe_forward_residual_rmsnorm(ok, *a) == -3
+    a = list(fw); a[16] = R                                   # the block output on resid
+    assert L.moe_forward_residual_rmsnorm(ok, *a) == -1
+    a = list(fw); a[23] = L.moe_workspace_bytes(D(16, 256, 512, 32, 4))
+    assert L.moe_forward_residual_rmsnorm(D(16, 256, 512, 32, 4), *a) == -2
+
+
 def test_status_strings(moe):
     L = moe.lib()
     for s, txt in ((0, b"ok"), (-1, b"invalid argument"), (-3, b"workspace too small"),

@@ -85,6 +85,80 @@ def test_residual_rmsnorm_fused(gu, T, d):
     assert np.all(np.abs(oracle.bf16_to_f64(gu.bits_host(n_f)) - n_ref) <= _bf16_ulp(n_ref))
 
 
+@pytest.mark.parametrize("T,d,k,gain,inplace", [(37, 320, 4, True, False), (5, 8192, 2, True, True),
+                                                 (64, 2880, 8, True, False), (33, 2880, 4, False, True),
+                                                 (130, 2880, 1, True, True)])
+def test_combine_residual_rmsnorm_bytes(gu, T, d, k, gain, inplace):
+    """The fused combine + residual + norm gives the bytes of moe_combine, then
+    moe_residual_rmsnorm (or moe_residual_add without a gain), with the block
+    output stored or not, in place or not; d = 8192 takes the path past the
+    chunks a lane keeps in registers."""
+    import torch
+    import sparse_moe_transformer_gemm_amd as moe
+    rng = np.random.default_rng(60 + T)
+    P = T * k
+    y = torch.from_numpy(rng.standard_normal((P, d)).astype(np.float32) * 0.3).to(gu.DEV)
+    pair_row = torch.from_numpy(rng.permutation(P).astype(np.int32)).to(gu.DEV)
+    tw = rng.random((T, k))
+    tw = torch.from_numpy((tw / tw.sum(1, keepdims=True)).astype(np.float32)).to(gu.DEV)
+    rb = synth.bf16_bits(rng.standard_normal((T, d)) * 3)
+    gb = synth.bf16_bits(1 + 0.02 * rng.standard_normal(d))
+    g = gu.bf16_dev(gb) if gain else None
+    m_sep = moe.combine(y, pair_row, tw)
+    if gain:
+        x_sep, n_sep = moe.residual_rmsnorm(gu.bf16_dev(rb), m_sep, g, 1e-5)
+    else:
+        x_sep, n_sep = moe.residual_add(gu.bf16_dev(rb), m_sep), None
+    for store_m in (True, False):
+        resid = gu.bf16_dev(rb)
+        m_out = torch.empty_like(resid) if store_m else None
+        x_f, n_f = moe.combine_residual_rmsnorm(y, pair_row, tw, resid, g, 1e-5,
+                                               resid_out=resid if inplace else None, m_out=m_out)
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.bits_host(x_f), gu.bits_host(x_sep)), store_m
+        if gain:
+            assert np.array_equal(gu.bits_host(n_f), gu.bits_host(n_sep)), store_m
+        else:
+            assert n_f is None
+        if store_m:
+            assert np.array_equal(gu.bits_host(m_out), gu.bits_host(m_sep))
+
+
+@pytest.mark.parametrize("T,d,F,E,k,seed", [(16, 2880, 2880, 32, 4, 1), (200, 512, 640, 16, 2, 61)])
+def test_forward_residual_rmsnorm_bytes(gu, T, d, F, E, k, seed):
+    """The whole block with the fused glue gives the bytes of moe_forward followed
+    by moe_residual_rmsnorm (decode front end and the many-token launches)."""
+    import torch
+    import sparse_moe_transformer_gemm_amd as moe
+    wl = synth.tiny_workload(T=T, d=d, F=F, E=E, k=k, seed=seed)
+    L, nb = wl.layers[0], wl.x
+    print(f"[forward+glue] {wl.name}", flush=True)
+    rng = np.random.default_rng(seed + 1000)
+    rb = synth.bf16_bits(rng.standard_normal((T, d)) * 3)
+    gb = synth.bf16_bits(1 + 0.02 * rng.standard_normal(d))
+    wt = gu.weights_dev(L)
+    ws = gu.workspace(T, d, F, E, k)
+    n, g = gu.bf16_dev(nb), gu.bf16_dev(gb)
+    r = moe.forward(n, wt, k, ws)
+    x_sep, n_sep = moe.residual_rmsnorm(gu.bf16_dev(rb), r["out"], g, 1e-5)
+    torch.cuda.synchronize()
+    ref = {key: r[key].cpu().numpy() for key in ("topk_idx", "topk_w", "y_sorted")}
+    ref_out = gu.bits_host(r["out"])
+    for store_out in (False, True):
+        resid = gu.bf16_dev(rb)
+        f = moe.forward_residual_rmsnorm(n, wt, k, ws, resid, g, 1e-5, resid_out=resid,
+                                         store_out=store_out)
+        torch.cuda.synchronize()
+        for key in ref:
+            assert np.array_equal(f[key].cpu().numpy(), ref[key]), key
+        assert np.array_equal(gu.bits_host(f["resid_out"]), gu.bits_host(x_sep))
+        assert np.array_equal(gu.bits_host(f["n_out"]), gu.bits_host(n_sep))
+        if store_out:
+            assert np.array_equal(gu.bits_host(f["out"]), ref_out)
+        else:
+            assert f["out"] is None
+
+
 def test_stack24_teacher_forced(gu):
     import torch
     import sparse_moe_transformer_gemm_amd as moe
@@ -93,19 +167,20 @@ def test_stack24_teacher_forced(gu):
     x = gu.bf16_dev(w.x)
     ws = gu.workspace(T, d, F, E, k)
     saved = {}
-    # as bench.py runs it: the first block's norm alone, then each block's
-    # residual fused with the next block's norm
+    # as bench.py runs it: the first block's norm alone, then each block with its
+    # combine, residual add and the next block's norm in one pass (the block
+    # output m stored only at the checked blocks)
     L_next = synth.stack_layer(4, 0)
     n = moe.rmsnorm(x, gu.bf16_dev(L_next.gain), w.eps)
     for l in range(w.n_layers):
         L = L_next
         wt = gu.weights_dev(L)
-        r = moe.forward(n, wt, k, ws)
+        gain_next = None
         if l + 1 < w.n_layers:
             L_next = synth.stack_layer(4, l + 1)
-            x_new, n_next = moe.residual_rmsnorm(x, r["out"], gu.bf16_dev(L_next.gain), w.eps)
-        else:
-            x_new, n_next = moe.residual_add(x, r["out"]), None
+            gain_next = gu.bf16_dev(L_next.gain)
+        r = moe.forward_residual_rmsnorm(n, wt, k, ws, x, gain_next, w.eps, store_out=l in CHECKED)
+        x_new, n_next = r["resid_out"], r["n_out"]
         if l in CHECKED:
             torch.cuda.synchronize()
             saved[l] = dict(x=gu.bits_host(x), n=gu.bits_host(n), m=gu.bits_host(r["out"]),
