@@ -7,6 +7,7 @@
 
 #include "moe.h"
 #include "common.hpp"
+#include "glue.hpp"
 #include "layout.hpp"
 
 namespace {

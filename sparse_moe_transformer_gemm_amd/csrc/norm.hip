@@ -14,6 +14,7 @@
 // squares and the scaling (the rest are read again), and sums its squares in
 // chunk order before a butterfly over the wavefront, so both norm kernels sum
 // in the same order and give the same bytes for the same row.
+#include "glue.hpp"
 #include "mx6.hpp"
 
 namespace moe {
