@@ -12,7 +12,8 @@
 //                          builds the stable permutation of all pairs (section
 //                          "Nuclis per a GPT-OSS / MoE": dispatch selects each
 //                          expert's tokens) and the 16-row pass table of the
-//                          decode GEMMs.
+//                          decode GEMMs (with at most 64 pairs, one wavefront
+//                          does both).
 // Each workgroup publishes its top-k with a device-scope release before it
 // counts itself in, and the last one acquires before it reads them, so the
 // permutation sees every token's choice whichever XCD computed it. The outputs
@@ -39,6 +40,96 @@ __global__ __launch_bounds__(256) void front_partials_encode(const uint16_t* __r
   }
 }
 
+// The stable permutation and the decode pass table of at most 64 pairs, by the
+// workgroup's first wavefront from one load of the routing table (the other
+// wavefronts only take part in the barriers): lane q holds pair q; lanes with
+// the same expert are found with one ballot per expert-index bit, as in
+// permute_chunk, and ranked by popcount of the lower lanes; per-expert counts
+// and pass counts go through LDS, and each lane scans four experts' worth
+// before a wavefront scan. The outputs are the bytes of permute_chunk followed
+// by build_tile_table<kDecRows> (the unique stable counting sort and its table).
+constexpr int kWavePairs = 64;
+
+__device__ __forceinline__ void permute_wave(const int32_t* __restrict__ idx, int P, int E,
+                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                             int32_t* __restrict__ sorted_pair,
+                                             int32_t* __restrict__ pair_row, int4* __restrict__ passes) {
+  __shared__ int cnt[rt::kMaxE], npass[rt::kMaxE], off[rt::kMaxE], pst[rt::kMaxE];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const bool w0 = tid < kWave, valid = w0 && lane < P;
+  for (int i = tid; i < rt::kMaxE; i += blockDim.x) {
+    cnt[i] = 0;
+    npass[i] = 0;
+  }
+  const int e = valid ? idx[lane] : 0;
+  int rank = 0, c = 0;
+  __syncthreads();
+  if (w0) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t set = __ballot(valid && bit);
+      same &= bit ? set : ~set;
+    }
+    const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+    rank = __popcll(same & lower);
+    c = __popcll(same);
+    if (valid && rank == 0) {
+      cnt[e] = c;
+      npass[e] = (c + kDecRows - 1) / kDecRows;
+    }
+  }
+  __syncthreads();
+  if (w0) {
+    // experts 4 lane .. 4 lane + 3, then an exclusive scan over the wavefront
+    int cs[4], ps[4], sc = 0, sp = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int x = 4 * lane + j;
+      cs[j] = x < E ? cnt[x] : 0;
+      ps[j] = x < E ? npass[x] : 0;
+      sc += cs[j];
+      sp += ps[j];
+    }
+    int ic = sc, ip = sp;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t1 = __shfl_up(ic, o), t2 = __shfl_up(ip, o);
+      if (lane >= o) {
+        ic += t1;
+        ip += t2;
+      }
+    }
+    int ec = ic - sc, ep = ip - sp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int x = 4 * lane + j;
+      if (x < E) {
+        counts[x] = cs[j];
+        offsets[x] = ec;
+        off[x] = ec;
+        pst[x] = ep;
+        if (x == E - 1) offsets[E] = ec + cs[j];
+      }
+      ec += cs[j];
+      ep += ps[j];
+    }
+    const int total = __shfl(ip, kWave - 1);
+    if (lane == 0) passes[0] = make_int4(total, 0, 0, 0);
+  }
+  __syncthreads();
+  if (valid) {
+    const int pos = off[e] + rank;
+    sorted_pair[pos] = lane;
+    pair_row[lane] = pos;
+    if (rank == 0)
+      for (int p = 0; p < npass[e]; ++p)
+        passes[1 + pst[e] + p] = make_int4(e, p * kDecRows, off[e], c);
+  }
+}
+
 __global__ __launch_bounds__(256) void front_select_permute(
     const double* __restrict__ partial, int nslices, const float* __restrict__ b_router, int T,
     int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -57,6 +148,10 @@ __global__ __launch_bounds__(256) void front_select_permute(
   __syncthreads();
   if (!last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every other token's top-k
+  if (T * k <= kWavePairs) {
+    permute_wave(topk_idx, T * k, E, counts, offsets, sorted_pair, pair_row, passes);
+    return;
+  }
   pm::permute_chunk(topk_idx, T * k, E, 0, true, counts, offsets, sorted_pair, pair_row, offs);
   __syncthreads();
   build_tile_table<kDecRows>(offs, E, passes, s);
