@@ -2,12 +2,11 @@
 // inverse (Perplexity, "GPT-OSS el dia 0", section "Nuclis per a GPT-OSS / MoE":
 // dispatch selects each expert's tokens).
 //
-// No inter-block communication. Block b owns the pairs [b*kChunk,
-// (b+1)*kChunk). Up to kOneLaunchPairs pairs, every block first histograms the
-// whole routing table in LDS (the table is tiny: 4*T int32, L2-resident),
-// counting separately the pairs before its chunk; above that, a first launch
-// writes one histogram per chunk and each block sums those. From that it knows
-// the exclusive scan of the totals and where its own pairs of each expert start. It then ranks its pairs 256 at a
+// One kernel, no inter-block communication. Block b owns the pairs
+// [b*kChunk, (b+1)*kChunk). Every block first histograms the whole routing table
+// in LDS (the table is tiny: 4*T int32, L2-resident), counting separately the
+// pairs before its chunk; from that it knows the exclusive scan of the totals
+// and where its own pairs of each expert start. It then ranks its pairs 256 at a
 // time: inside a wavefront, lanes holding the same expert are found with one
 // ballot per expert-index bit and ranked by popcount of the lower lanes; per-
 // wave counts in LDS give the offset across the block's four wavefronts. The
@@ -49,19 +48,11 @@ __global__ __launch_bounds__(pm::kThreads) void permute_kernel(const int32_t* __
   }
 }
 
-// Up to this many pairs every workgroup counts the whole routing table itself
-// (one launch); above it a first launch writes one histogram per chunk. Timed
-// back to back (moe_permute): 8192 pairs 9.9 us in one launch against 12.6 us in
-// two, 16384 pairs 12.3 against 12.5, 32768 pairs 20.2 against 13.1.
-constexpr int kOneLaunchPairs = 8192;
-
-bool two_launches(int P) { return P > pm::kChunk && P > kOneLaunchPairs; }
-
 }  // namespace
 
 size_t permute_workspace_bytes(int T, int E, int k) {
   const size_t blocks = ((size_t)T * k + pm::kChunk - 1) / pm::kChunk;
-  return two_launches(T * k) ? blocks * E * sizeof(int32_t) : 0;
+  return blocks > 1 ? blocks * E * sizeof(int32_t) : 0;
 }
 
 hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
@@ -70,7 +61,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t*
   const int P = T * k;
   const int blocks = (P + pm::kChunk - 1) / pm::kChunk;
   int32_t* chist = nullptr;
-  if (two_launches(P)) {
+  if (blocks > 1) {
     chist = static_cast<int32_t*>(ws);
     hipLaunchKernelGGL(permute_hist, dim3(blocks), dim3(pm::kThreads), 0, stream, topk_idx, P, E, chist);
     hipError_t err = hipGetLastError();
