@@ -154,6 +154,8 @@ template <bool GATEUP>
 __global__ __launch_bounds__(64) void grouped_fp8(const FfnArgs a, const uint8_t* __restrict__ ain,
                                                   uint8_t* __restrict__ hout, const int4* __restrict__ tiles) {
   __shared__ __attribute__((aligned(16))) float stage[32 * 36];
+  // the valid rows' chunks of one K step (the wavefront's activation window)
+  __shared__ __attribute__((aligned(16))) uint8_t awin[32 * kChunk];
   const int mt = blockIdx.x, u = blockIdx.y;
   if (mt >= __builtin_amdgcn_readfirstlane(tiles[0].x)) return;
   const int4 ent = tiles[1 + mt];  // {expert, first row within the expert, offsets[e], count_e}
@@ -169,8 +171,18 @@ __global__ __launch_bounds__(64) void grouped_fp8(const FfnArgs a, const uint8_t
   const int g0 = GATEUP ? u : 2 * u, g1 = GATEUP ? u : 2 * u + 1;
 
   const int rr = min(lr, rows - 1);
-  const uint32_t arow = GATEUP ? (uint32_t)a.sorted_pair[off + r0 + rr] / (uint32_t)a.k : (uint32_t)(off + r0 + rr);
-  const uint8_t* A = ain + (size_t)arow * nst * kChunk;
+  // window piece c = lane + 64 i: row c / 13 (valid rows only), piece c % 13 of
+  // the row's 208-byte chunk; each lane's source row
+  constexpr int kWinPieces = (32 * kChunkPieces + 63) / 64;   // loads per lane, at most
+  const int npieces = rows * kChunkPieces;
+  const uint8_t* wsrc[kWinPieces];
+#pragma unroll
+  for (int i = 0; i < kWinPieces; ++i) {
+    const int c = lane + 64 * i;
+    const int wr = min(c / kChunkPieces, rows - 1), pc = c % kChunkPieces;
+    const uint32_t arw = GATEUP ? (uint32_t)a.sorted_pair[off + r0 + wr] / (uint32_t)a.k : (uint32_t)(off + r0 + wr);
+    wsrc[i] = ain + (size_t)arw * nst * kChunk + pc * 16;
+  }
   const uint8_t* B0 = (GATEUP ? a.wg_codes : a.wd_codes) + ((size_t)e * (N / 32) + g0) * nst * kF8Step + lane * 32;
   const uint8_t* B1 = (GATEUP ? a.wu_codes : a.wd_codes) + ((size_t)e * (N / 32) + g1) * nst * kF8Step + lane * 32;
   const float* S0 = reinterpret_cast<const float*>(GATEUP ? a.wg_scales : a.wd_scales) +
@@ -192,20 +204,21 @@ __global__ __launch_bounds__(64) void grouped_fp8(const FfnArgs a, const uint8_t
     }
   }
 
-  // Step j's operands: the lane's two A blocks (96 B: hi, lo of block 2h, then
-  // of block 2h+1) and their four E8M0 bytes; B: 32 codes per lane and K half
-  // (half 1 is 2048 B on); the block scales.
+  // Step j's operands: the activation window (the valid rows' 208-byte chunks,
+  // 16 bytes per lane and load, staged through LDS so that each row is loaded
+  // once, not once per lane that uses it); B: 32 codes per lane and K half (half
+  // 1 is 2048 B on); the block scales. From the window each lane reads its two A
+  // blocks (96 B: hi, lo of block 2h, then of block 2h+1) and their four E8M0 bytes.
   struct Ops {
-    v4i a[6];
-    int sa;
+    v4i w[kWinPieces];
     v8i b00, b01, b10, b11;
     float s0, s1;
   };
   auto load_ops = [&](int j, Ops& o) __attribute__((always_inline)) {
-    const v4i* ap = reinterpret_cast<const v4i*>(A + (size_t)j * kChunk + half * 96);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) o.a[i] = ap[i];
-    o.sa = *reinterpret_cast<const int*>(A + (size_t)j * kChunk + kChunkScales + 4 * half);
+    for (int i = 0; i < kWinPieces; ++i)
+      if (64 * i < npieces && lane + 64 * i < npieces)
+        o.w[i] = *reinterpret_cast<const v4i*>(wsrc[i] + (size_t)j * kChunk);
     const v8i* p0 = reinterpret_cast<const v8i*>(B0 + (size_t)j * kF8Step);
     const v8i* p1 = reinterpret_cast<const v8i*>(B1 + (size_t)j * kF8Step);
     o.b00 = p0[0];
@@ -218,9 +231,21 @@ __global__ __launch_bounds__(64) void grouped_fp8(const FfnArgs a, const uint8_t
   Ops cur, nxt;
   load_ops(0, cur);
   for (int j = 0; j < nst; ++j) {
+    // this step's window to LDS (the previous step's reads of it are complete:
+    // a wavefront's LDS accesses run in order), then each lane's A operands
+#pragma unroll
+    for (int i = 0; i < kWinPieces; ++i) {
+      const int c = lane + 64 * i;
+      if (64 * i < npieces && c < npieces)
+        *reinterpret_cast<v4i*>(awin + (c / kChunkPieces) * kChunk + (c % kChunkPieces) * 16) = cur.w[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (j + 1 < nst) load_ops(j + 1, nxt);
-    const v4i a0 = cur.a[0], a1 = cur.a[1], a2 = cur.a[2], a3 = cur.a[3], a4 = cur.a[4], a5 = cur.a[5];
-    int sa = cur.sa;
+    const v4i* ap = reinterpret_cast<const v4i*>(awin + rr * kChunk + half * 96);
+    const v4i a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3], a4 = ap[4], a5 = ap[5];
+    int sa = *reinterpret_cast<const int*>(awin + rr * kChunk + kChunkScales + 4 * half);
     const v8i b00 = cur.b00, b01 = cur.b01, b10 = cur.b10, b11 = cur.b11;
     const float s0 = cur.s0, s1 = cur.s1;
     // in a half step at the end of K (K % 128 == 64) lane half 1 has no blocks:
