@@ -87,12 +87,14 @@ def test_residual_rmsnorm_fused(gu, T, d):
 
 @pytest.mark.parametrize("T,d,k,gain,inplace", [(37, 320, 4, True, False), (5, 8192, 2, True, True),
                                                  (64, 2880, 8, True, False), (33, 2880, 4, False, True),
-                                                 (130, 2880, 1, True, True)])
+                                                 (130, 2880, 1, True, True), (1, 64, 3, True, True),
+                                                 (300, 1024, 7, True, False), (17, 16384, 5, True, True),
+                                                 (9, 704, 6, False, False)])
 def test_combine_residual_rmsnorm_bytes(gu, T, d, k, gain, inplace):
     """The fused combine + residual + norm gives the bytes of moe_combine, then
     moe_residual_rmsnorm (or moe_residual_add without a gain), with the block
-    output stored or not, in place or not; d = 8192 takes the path past the
-    chunks a lane keeps in registers."""
+    output stored or not, in place or not, every k from 1 to 8, d from 64 to
+    16384 (the largest width the calls accept)."""
     import torch
     import sparse_moe_transformer_gemm_amd as moe
     rng = np.random.default_rng(60 + T)
