@@ -82,17 +82,29 @@ __device__ __forceinline__ void permute_chunk(const int32_t* __restrict__ idx, i
   __syncthreads();
 
   if (chist) {
+    // every thread takes entries i = tid, tid + 256, ... of the nchunks x E
+    // histograms, eight loads in flight at a time, and adds them into the
+    // totals (and, for chunks before this one, into `before`) with LDS integer
+    // atomics: integer sums do not depend on the order, so the result is exact
+    // and deterministic
     const int mine = start / kChunk;
-    for (int e = tid; e < E; e += kThreads) {
-      int t = 0, b = 0;
-#pragma unroll 8
-      for (int c = 0; c < nchunks; ++c) {
-        const int h = chist[(size_t)c * E + e];
-        t += h;
-        b += c < mine ? h : 0;
+    const int n = nchunks * E;
+    for (int i0 = tid; i0 < n; i0 += 8 * kThreads) {
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kThreads;
+        h[u] = i < n ? chist[i] : 0;
       }
-      total[e] = t;
-      before[e] = b;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kThreads;
+        if (i < n && h[u]) {
+          const int c = i / E, e = i - c * E;
+          atomicAdd(&total[e], h[u]);
+          if (c < mine) atomicAdd(&before[e], h[u]);
+        }
+      }
     }
   } else {
     for (int q = tid; q < P; q += kThreads) {
