@@ -1131,10 +1131,15 @@ hipError_t launch_expert_ffn_stage(const FfnArgs& a, hipStream_t stream, int sta
   }
   if (stage == 1) {
     // Column tiles: the widest that divides N (gate/up: 32*NF h-columns, down:
-    // 64*NF output columns per workgroup).
+    // 64*NF output columns per workgroup) -- for gate/up only while that many
+    // tiles, at the most the row tiles can be, still give every CU one;
+    // otherwise the 64-column tile, so that few rows spread over more CUs
+    // (measured at T = 128, d = F = 512: 33.0 -> 31.5 us per layer). The tile
+    // width does not change any output's summation order.
     if (dec_gu) return launch_decode<true>(a, xenc, henc, pp, ncu, stream);
-    if (a.F % 192 == 0) return launch_prefill<6, true>(a, xenc, henc, tp, ncu, stream);
-    if (a.F % 128 == 0) return launch_prefill<4, true>(a, xenc, henc, tp, ncu, stream);
+    const long long mts = max_row_tiles(a.T, a.E, a.k, kBM);
+    if (a.F % 192 == 0 && mts * (a.F / 192) >= ncu) return launch_prefill<6, true>(a, xenc, henc, tp, ncu, stream);
+    if (a.F % 128 == 0 && mts * (a.F / 128) >= ncu) return launch_prefill<4, true>(a, xenc, henc, tp, ncu, stream);
     return launch_prefill<2, true>(a, xenc, henc, tp, ncu, stream);
   }
   if (stage == 2) {
